@@ -1,0 +1,256 @@
+"""Seeded synthetic factors, queries and dense tails.
+
+Every array is drawn from its own counter-free stream:
+``PCG64(SeedSequence([seed, variant_id, stream, ...]))``, so the values of one
+sequence or one block do not depend on which other sequences are generated or
+on thread scheduling.  Floating values are drawn in float32 and stored either
+as float32 or rounded to bfloat16 (round-to-nearest-even); bfloat16 arrays are
+kept as their uint16 bit patterns.
+
+Distributions (MILO compresses each block's keys and values separately with
+a low-rank approximation, MILO summary "4.2 Block-wise Low-Rank Compression";
+the synthetic stand-in for a truncated SVD is):
+  U_b, U'_b ~ N(0, 1)                       (T_b x r_b, T_b x r'_b)
+  W_b = diag(0.8^i) * Q^T                    (r_b x d), Q = orthonormal d x r_b
+  q ~ N(0, 1)
+  dense tail K_t = U_t W_t, V_t = U'_t W'_t with full rank r = d.
+U is drawn rank-major (as U^T, r_b x T_b); any order of iid draws is valid.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+from .configs import Config
+
+VARIANTS = {"base": 0, "sharp": 1}
+
+# stream ids
+_S_RANK, _S_Q, _S_BLOCK, _S_TAIL = 0, 1, 2, 3
+
+
+def _rng(*key: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(k) for k in key])))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (round-to-nearest-even); return uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _store(x: np.ndarray, dtype: str) -> np.ndarray:
+    x = np.asarray(x, dtype=np.float32)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    if dtype == "f32":
+        return np.ascontiguousarray(x)
+    raise ValueError(dtype)
+
+
+def stored_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact value of a stored array as float64."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(a).astype(np.float64)
+    return np.asarray(a, dtype=np.float64)
+
+
+def _orth_rows(rng: np.random.Generator, r: int, d: int) -> np.ndarray:
+    """diag(0.8^i) * Q^T with Q from the QR of a d x r Gaussian, sign-fixed."""
+    if r == 0:
+        return np.zeros((0, d), np.float64)
+    g = rng.standard_normal((d, r))
+    qm, rm = np.linalg.qr(g)
+    sgn = np.sign(np.diag(rm))
+    sgn[sgn == 0] = 1.0
+    qm = qm * sgn[None, :]
+    return (0.8 ** np.arange(r))[:, None] * qm.T
+
+
+@dataclass
+class LogicalBlock:
+    """One compressed block, all KV heads, in the stored dtype.
+
+    ut  [Hkv][rank_k][n_tok]  U_b^T   (keys:  K_b ~= U_b W_b)
+    w   [Hkv][rank_k][d]      W_b
+    upt [Hkv][rank_v][n_tok]  U'_b^T  (values: V_b ~= U'_b W'_b)
+    wp  [Hkv][rank_v][d]      W'_b
+    """
+    n_tok: int
+    rank_k: int
+    rank_v: int
+    ut: np.ndarray
+    w: np.ndarray
+    upt: np.ndarray
+    wp: np.ndarray
+
+
+@dataclass
+class Workload:
+    cfg: Config
+    variant: str
+    seqs: List[int]                 # which sequences of the config these are
+    q: np.ndarray                   # [B][Q][Hq][d] stored dtype
+    blocks: List[List[LogicalBlock]]  # per sequence, the blocks its CSR lists
+    k_tail: np.ndarray              # [B][Hkv][L_cap][d]
+    v_tail: np.ndarray
+    tail_len: np.ndarray            # int32 [B]
+    scale: float
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def dtype(self) -> str:
+        return self.cfg.dtype
+
+    @property
+    def batch(self) -> int:
+        return len(self.seqs)
+
+    @property
+    def tail_cap(self) -> int:
+        return int(self.k_tail.shape[2])
+
+    def context_tokens(self) -> int:
+        """Tokens attended per call: all block tokens plus the tails."""
+        return int(sum(b.n_tok for s in self.blocks for b in s) + int(self.tail_len.sum()))
+
+    def factor_bytes(self) -> int:
+        """Bytes of U, W, U', W' at their actual ranks, unpadded."""
+        es = 2 if self.dtype == "bf16" else 4
+        d = self.cfg.head_dim
+        h = self.cfg.n_kv_heads
+        return int(sum(h * es * (b.rank_k + b.rank_v) * (b.n_tok + d)
+                       for s in self.blocks for b in s))
+
+    def tail_bytes(self) -> int:
+        es = 2 if self.dtype == "bf16" else 4
+        return int(2 * es * self.cfg.n_kv_heads * self.cfg.head_dim * int(self.tail_len.sum()))
+
+
+def draw_ranks(cfg: Config, variant: str, n_blocks: Sequence[int]) -> List[np.ndarray]:
+    """Per sequence an int array [n_blocks][2] of (r_b, r'_b)."""
+    rd = cfg.ranks
+    rng = _rng(cfg.seed, VARIANTS[variant], _S_RANK)
+    out = []
+    for nb in n_blocks:
+        if rd.kind == "list":
+            rk = np.array([rd.values[b % len(rd.values)] for b in range(nb)], np.int64)
+            rv = rk.copy()
+        else:
+            def draw(n):
+                if rd.kind == "uniform":
+                    return rng.integers(rd.lo, rd.hi + 1, size=n)
+                if rd.kind == "lognormal":
+                    x = np.rint(rd.median * np.exp(rd.sigma * rng.standard_normal(n)))
+                    return np.clip(x, rd.lo, rd.hi).astype(np.int64)
+                if rd.kind == "bimodal":
+                    hi = rng.random(n) < rd.p_hi
+                    a = rng.integers(rd.hi_lo, rd.hi_hi + 1, size=n)
+                    b = rng.integers(rd.lo, rd.hi + 1, size=n)
+                    return np.where(hi, a, b)
+                raise ValueError(rd.kind)
+            rk = draw(nb)
+            rv = rk.copy() if cfg.v_rank_equals_k else draw(nb)
+        out.append(np.stack([rk, rv], axis=1).astype(np.int64))
+    return out
+
+
+def _gen_block(cfg: Config, variant: str, seq: int, b: int, n_tok: int, rk: int, rv: int,
+               u_scale: float) -> LogicalBlock:
+    rng = _rng(cfg.seed, VARIANTS[variant], _S_BLOCK, seq, b)
+    d, h = cfg.head_dim, cfg.n_kv_heads
+    ut = np.empty((h, rk, n_tok), np.float32)
+    upt = np.empty((h, rv, n_tok), np.float32)
+    w = np.empty((h, rk, d), np.float32)
+    wp = np.empty((h, rv, d), np.float32)
+    for g in range(h):
+        ut[g] = rng.standard_normal((rk, n_tok), dtype=np.float32)
+        w[g] = _orth_rows(rng, rk, d)
+        upt[g] = rng.standard_normal((rv, n_tok), dtype=np.float32)
+        wp[g] = _orth_rows(rng, rv, d)
+    if u_scale != 1.0:
+        ut *= np.float32(u_scale)
+    if variant == "sharp":
+        upt += np.float32(1.0)
+    return LogicalBlock(n_tok, rk, rv, _store(ut, cfg.dtype), _store(w, cfg.dtype),
+                        _store(upt, cfg.dtype), _store(wp, cfg.dtype))
+
+
+def make_workload(cfg: Config, variant: str = "base", seqs: Optional[Sequence[int]] = None,
+                  n_blocks: Optional[Sequence[int]] = None,
+                  tokens: Optional[Sequence[Sequence[int]]] = None,
+                  tail_len: Optional[Sequence[int]] = None,
+                  threads: Optional[int] = None) -> Workload:
+    """Draw the inputs of one call.
+
+    seqs      which sequences of the workload to draw (default: all); a subset
+              has exactly the values the full draw has for those sequences.
+    n_blocks  per-sequence block counts (default cfg.n_blocks for every one).
+    tokens    per-sequence list of T_b (default cfg.block_tokens).
+    tail_len  per-sequence visible tail lengths (default cfg.tail_len).
+    """
+    B = cfg.batch
+    nbs = list(n_blocks) if n_blocks is not None else [cfg.n_blocks] * B
+    if len(nbs) != B:
+        raise ValueError("n_blocks must list every sequence of the workload")
+    seqs = list(range(B)) if seqs is None else [int(s) for s in seqs]
+    ranks = draw_ranks(cfg, variant, nbs)
+    d, hq, hkv, Q = cfg.head_dim, cfg.n_q_heads, cfg.n_kv_heads, cfg.q_len
+
+    tl = np.array(tail_len if tail_len is not None else [cfg.tail_len] * B, np.int32)
+    cap = int(max(cfg.tail_len, int(tl.max()) if len(tl) else 0))
+
+    # sharp variant: q scaled so that the score std is about 3 (the synthetic
+    # score std is scale * sqrt(sum_i 0.64^i) ~= 1.667 * scale), and key
+    # factors of later blocks scaled up so the running max rises block by block.
+    q_mult = 1.0
+    if variant == "sharp":
+        q_mult = 3.0 / (cfg.scale * np.sqrt(1.0 / (1.0 - 0.64)))
+
+    tasks = []
+    for si, s in enumerate(seqs):
+        nb = nbs[s]
+        for b in range(nb):
+            T = int(tokens[s][b]) if tokens is not None else cfg.block_tokens
+            u_scale = 1.0
+            if variant == "sharp":
+                u_scale = 0.5 + (b / max(1, nb - 1))
+            tasks.append((si, s, b, T, int(ranks[s][b, 0]), int(ranks[s][b, 1]), u_scale))
+
+    nthr = threads or min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(max_workers=nthr) as ex:
+        res = list(ex.map(lambda t: _gen_block(cfg, variant, t[1], t[2], t[3], t[4], t[5], t[6]), tasks))
+    blocks: List[List[LogicalBlock]] = [[] for _ in seqs]
+    for t, blk in zip(tasks, res):
+        blocks[t[0]].append(blk)
+
+    q = np.empty((len(seqs), Q, hq, d), np.float32)
+    kt = np.zeros((len(seqs), hkv, cap, d), np.float32)
+    vt = np.zeros((len(seqs), hkv, cap, d), np.float32)
+    for si, s in enumerate(seqs):
+        rq = _rng(cfg.seed, VARIANTS[variant], _S_Q, s)
+        q[si] = rq.standard_normal((Q, hq, d), dtype=np.float32) * np.float32(q_mult)
+        rt = _rng(cfg.seed, VARIANTS[variant], _S_TAIL, s)
+        for g in range(hkv):
+            if cap == 0:
+                continue
+            uk = rt.standard_normal((cap, d))
+            wk = _orth_rows(rt, d, d)
+            uv = rt.standard_normal((cap, d))
+            wv = _orth_rows(rt, d, d)
+            kt[si, g] = (uk @ wk).astype(np.float32)
+            vt[si, g] = (uv @ wv).astype(np.float32)
+            if variant == "sharp":
+                vt[si, g] += np.float32(1.0)
+    return Workload(cfg=cfg, variant=variant, seqs=seqs, q=_store(q, cfg.dtype), blocks=blocks,
+                    k_tail=_store(kt, cfg.dtype), v_tail=_store(vt, cfg.dtype),
+                    tail_len=tl[seqs].astype(np.int32), scale=cfg.scale)
