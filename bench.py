@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark over a block-wise low-rank KV cache on one MI355X.
+
+One step = one decode call (split-K attention kernel + merge kernel) over the
+whole batch of one layer, inputs resident in HBM.  Prints one JSON line:
+context tokens/s for the step, the attention kernel's achieved HBM bandwidth
+on algorithmic bytes against the 8 TB/s peak (timed with HIP events on the
+launch stream), and the fp64 CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen7b_64k]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "low-rank-KV decode attn: context tokens/s and % of HBM peak (7B, 64k)"
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["rank_attention_amd/csrc/decode.hip", "rank_attention_amd/csrc/device_common.h"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime's C API (timing plumbing)."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (loads the HIP runtime)
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return ev.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def destroy(self, ev: int) -> None:
+        self.hip.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, f"decode_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, seconds: float):
+    """fp64 oracle on whole sequences of the same workload until `seconds` pass."""
+    import oracle
+    toks, elapsed, done = 0, 0.0, 0
+    for i in range(wl.batch):
+        q, blocks, kt, vt, tl = oracle.logical_from_workload(wl, [i])
+        t0 = time.perf_counter()
+        oracle.attend_logical(q, blocks, kt, vt, tl, wl.scale)
+        elapsed += time.perf_counter() - t0
+        toks += sum(b.n_tok for b in wl.blocks[i]) + int(wl.tail_len[i])
+        done += 1
+        if elapsed >= seconds:
+            break
+    return {"value": toks / elapsed, "unit": "context tokens/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{done} of {wl.batch} sequences ({toks} context tokens, all {wl.cfg.n_q_heads} "
+                      f"query heads), fp64 reconstruct-then-attend, {elapsed:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen7b_64k")
+    ap.add_argument("--variant", default="base")
+    ap.add_argument("--copies", type=int, default=2,
+                    help="pool copies read in rotation so no step finds the last one's bytes in cache")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus must be 1).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import rank_attention_amd as ra
+    import synth
+    from rank_attention_amd import _lib
+
+    if not os.path.exists(ra.library_path):
+        import __graft_entry__
+        __graft_entry__.build()
+    lib = _lib.load()
+
+    cfg = synth.get_config(args.workload)
+    if cfg.path != "decode":
+        raise SystemExit(f"{args.workload} is a {cfg.path} workload; bench.py times decode")
+    t0 = time.time()
+    wl = synth.make_workload(cfg, variant=args.variant)
+    pc = ra.pack(wl)
+    dc = ra.DeviceCache(pc, device="cuda:0", scale=wl.scale)
+    pools = [dc.pool] + [dc.pool.clone() for _ in range(max(0, args.copies - 1))]
+    B, Q, Hq, d = (int(x) for x in dc.q.shape)
+    out = torch.empty((B, Q, Hq, d), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((B, Q, Hq), dtype=torch.float32, device="cuda:0")
+    a0 = ra.make_args(*dc.tensors(), n_kv_heads=dc.n_kv_heads, scale=dc.scale, max_blocks=dc.max_blocks,
+                      out=out, lse=lse)
+    need = lib.milo_attn_workspace_bytes(ctypes.byref(a0), _lib.MILO_PATH_DECODE)
+    ws = torch.empty(int(need), dtype=torch.uint8, device="cuda:0")
+    argsets = []
+    for pool in pools:
+        a = ra.make_args(dc.q, pool, dc.blocks, dc.seq_blocks, dc.k_tail, dc.v_tail, dc.tail_len,
+                         n_kv_heads=dc.n_kv_heads, scale=dc.scale, max_blocks=dc.max_blocks, out=out,
+                         lse=lse, workspace=ws)
+        argsets.append(a)
+    stream = torch.cuda.current_stream().cuda_stream
+    setup_s = time.time() - t0
+    print(f"[bench] {cfg.desc}: factor {wl.factor_bytes() / 1e6:.1f} MB, tail {wl.tail_bytes() / 1e6:.1f} MB, "
+          f"setup {setup_s:.1f} s", file=sys.stderr, flush=True)
+
+    def step(k, evs=None):
+        a = argsets[k % len(argsets)]
+        if evs is not None:
+            a.prof_events[0], a.prof_events[1] = evs
+        else:
+            a.prof_events[0] = a.prof_events[1] = None
+        rc = lib.milo_attn_decode(ctypes.byref(a), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"milo_attn_decode failed: {ra.status_str(rc)}")
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    hip = HipEvents()
+    evs = [(hip.create(), hip.create()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(k, evs[k])
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    kern_ms = [hip.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+
+    ms_per_step = (t_end - t_start) * 1e3 / args.steps
+    ctx = wl.context_tokens()
+    alg_bytes = wl.factor_bytes() + wl.tail_bytes()
+    kmean = sum(kern_ms) / len(kern_ms)
+    achieved = alg_bytes / (kmean * 1e-3) / 1e9
+    kern_sorted = sorted(kern_ms)
+    print(f"[bench] attention kernel: mean {kmean * 1e3:.1f} us, median {kern_sorted[len(kern_sorted) // 2] * 1e3:.1f} us, "
+          f"min {kern_sorted[0] * 1e3:.1f} us; step {ms_per_step * 1e3:.1f} us; "
+          f"{achieved:.0f} GB/s on {alg_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
+
+    res = {
+        "metric": METRIC,
+        "value": ctx / (ms_per_step * 1e-3),
+        "unit": "context tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "desc": cfg.desc, "batch": cfg.batch,
+                   "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
+                   "blocks_per_seq": cfg.n_blocks, "block_tokens": cfg.block_tokens,
+                   "tail_len": cfg.tail_len, "context_tokens_per_step": ctx,
+                   "variant": args.variant, "pool_copies": len(pools)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profiles(cfg.name),
+                     "kernel": "milo_decode_kernel", "kernel_us_mean": kmean * 1e3,
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "kernel_source_sha": kernel_source_sha()},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

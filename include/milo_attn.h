@@ -1,0 +1,145 @@
+/*
+ * milo_attn.h -- C ABI of attention over a block-wise low-rank compressed KV
+ * cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The method (MILO: Efficient Many-shot In-Context Learning with Block-wise
+ * Low-rank Compression, summary at paperlayer.ai/abs/2609.29913v1):
+ *  - the pre-encoded demonstration cache is split into blocks of several
+ *    examples ("4.2 Block-wise Low-Rank Compression");
+ *  - each block b keeps its keys and values separately as low-rank factors,
+ *        K_b ~= U_b W_b      U_b: T_b x r_b,   W_b: r_b x d
+ *        V_b ~= U'_b W'_b    U'_b: T_b x r'_b, W'_b: r'_b x d
+ *    with block-specific ranks ("4.3 Dynamic Rank Allocation"), which may
+ *    differ between keys and values ("4.4 MILO Workflow");
+ *  - at inference the selected blocks are used for attention together
+ *    ("4.4 MILO Workflow": retrieve selected blocks, reconstruct, attend).
+ *
+ * These entry points compute exactly that attention in the absorbed order
+ * p = W_b q, s = scale * U_b p, one softmax over every listed block and a
+ * dense recent-token tail, o = sum_b (a_b U'_b) W'_b + a_t V_t, without
+ * materialising K_b or V_b.  For each query row (sequence i, position j,
+ * query head h, KV head g = h / (n_q_heads / n_kv_heads)):
+ *
+ *   out[i][j][h] = sum_t softmax(s)_t v_t ,  lse[i][j][h] = log sum_t exp(s_t)
+ *
+ * over every token of every block listed for sequence i and the tail tokens
+ * l < tail_len[i] - q_len + j + 1 (bottom-right causal; with q_len = 1 the
+ * whole tail).  With nothing visible, out = 0 and lse = -inf.
+ *
+ * Conventions for every entry point:
+ *  - all pointers in milo_attn_args are DEVICE pointers, except the args
+ *    struct itself (host);  the caller owns every buffer;
+ *  - calls are asynchronous on the given hipStream_t (NULL = default stream),
+ *    never synchronise, never allocate and keep no pointer after returning;
+ *  - host-checkable faults (null pointers, shapes, alignment, dtype, scale,
+ *    workspace size) return a status before any HIP call and leave out/lse
+ *    untouched;  a failed kernel launch returns MILO_ERR_DEVICE;
+ *  - device-resident tables (blocks, seq_blocks, tail_len) are the caller's
+ *    contract: ranks in [0, head_dim], n_tok >= 0, ld_tok >= n_tok and a
+ *    multiple of 8, off a multiple of 8, every factor inside the pool,
+ *    0 <= seq_blocks[i+1] - seq_blocks[i] <= max_blocks_per_seq (more are
+ *    ignored), tail_len[i] in [0, tail_cap] (decode) or [q_len, tail_cap]
+ *    (chunk).  Counts and lengths are clamped on the device;  offsets are not.
+ *  - the library never prints, aborts or throws.
+ */
+#ifndef MILO_ATTN_H
+#define MILO_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MILO_ABI_VERSION 1
+
+typedef enum milo_status {
+  MILO_OK = 0,
+  MILO_ERR_INVALID = 1,      /* null pointer, shape rule, misalignment, non-finite scale */
+  MILO_ERR_UNSUPPORTED = 2,  /* well-formed but not built: head_dim, group size, dtype   */
+  MILO_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required               */
+  MILO_ERR_DEVICE = 4        /* a HIP call failed (launch error)                         */
+} milo_status;
+
+typedef enum milo_dtype {
+  MILO_F32 = 0,              /* IEEE fp32 storage                                        */
+  MILO_BF16 = 1              /* bfloat16 storage                                         */
+} milo_dtype;
+
+typedef enum milo_path {
+  MILO_PATH_DECODE = 0,      /* one new query token per sequence                         */
+  MILO_PATH_CHUNK = 1        /* q_len new query tokens per sequence                      */
+} milo_path;
+
+/*
+ * One compressed block, all KV heads (24 bytes, device memory).
+ * KV head g's factors start at element  off + g * (rank_k + rank_v) * (ld_tok + head_dim)
+ * of the pool and are laid out back to back:
+ *     U^T  [rank_k][ld_tok]   keys' token factor, rank-major (row k = column k of U_b)
+ *     W    [rank_k][head_dim]
+ *     U'^T [rank_v][ld_tok]   values' token factor, rank-major
+ *     W'   [rank_v][head_dim]
+ * Elements n_tok..ld_tok-1 of each U^T / U'^T row are padding and are never
+ * used (they may hold anything, NaN included).
+ */
+typedef struct milo_block {
+  int64_t off;      /* element offset of KV head 0's U^T; multiple of 8           */
+  int32_t n_tok;    /* T_b >= 0                                                    */
+  int32_t ld_tok;   /* row stride of U^T and U'^T in elements; >= n_tok, mult. of 8 */
+  int32_t rank_k;   /* r_b  in [0, head_dim]                                       */
+  int32_t rank_v;   /* r'_b in [0, head_dim]                                       */
+} milo_block;
+
+typedef struct milo_attn_args {
+  int32_t struct_size;         /* sizeof(milo_attn_args)                                   */
+  int32_t dtype;               /* milo_dtype of q, pool, k_tail, v_tail                    */
+  int32_t batch;               /* sequences, >= 0                                           */
+  int32_t q_len;               /* query tokens per sequence: 1 (decode) or Q >= 1 (chunk)   */
+  int32_t n_q_heads;           /* >= 1, multiple of n_kv_heads                              */
+  int32_t n_kv_heads;          /* >= 1; group size n_q_heads / n_kv_heads in [1, 8]         */
+  int32_t head_dim;            /* 64 or 128                                                 */
+  float scale;                 /* softmax scale (e.g. 1/sqrt(head_dim)); finite             */
+  const void* q;               /* [batch][q_len][n_q_heads][head_dim], 16-B aligned         */
+  const void* pool;            /* factor pool, 16-B aligned; may be NULL if no block listed */
+  const milo_block* blocks;    /* descriptor table                                          */
+  const int32_t* seq_blocks;   /* [batch+1] CSR: sequence i uses blocks[seq_blocks[i] ..
+                                  seq_blocks[i+1]-1] (order irrelevant)                     */
+  int32_t max_blocks_per_seq;  /* host-known bound on blocks per sequence, >= 0             */
+  int32_t tail_cap;            /* tail capacity in tokens, >= 0 (chunk: >= q_len)           */
+  const void* k_tail;          /* [batch][n_kv_heads][tail_cap][head_dim]; NULL iff cap 0   */
+  const void* v_tail;          /* same shape, 16-B aligned                                  */
+  const int32_t* tail_len;     /* [batch] visible tail tokens; NULL iff tail_cap == 0       */
+  float* out;                  /* [batch][q_len][n_q_heads][head_dim] fp32, 16-B aligned    */
+  float* lse;                  /* [batch][q_len][n_q_heads] fp32 natural-log; may be NULL   */
+  void* workspace;             /* scratch of milo_attn_workspace_bytes(), 256-B aligned     */
+  size_t workspace_bytes;
+  void* prof_events[2];        /* optional hipEvent_t pair: when both are set, the call
+                                  records [0] before and [1] after its main attention
+                                  kernel on the same stream (timing hook)                   */
+} milo_attn_args;
+
+/* Workspace the given path needs for these arguments; 0 if the arguments are
+ * invalid or unsupported (shape fields only; pointers are not inspected). */
+size_t milo_attn_workspace_bytes(const milo_attn_args* args, int32_t path);
+
+/* Decode: q_len must be 1.  One query token per sequence attends over its
+ * listed blocks and its whole tail (tail_len[i] tokens).  Writes out and lse. */
+milo_status milo_attn_decode(const milo_attn_args* args, void* hip_stream);
+
+/* Chunked query: q_len = Q >= 1 new tokens per sequence, whose own keys and
+ * values are the last Q entries of the tail; query j sees every block token
+ * and tail tokens l <= tail_len[i] - Q + j.  Writes out and lse. */
+milo_status milo_attn_chunk(const milo_attn_args* args, void* hip_stream);
+
+/* Static description of a status code. */
+const char* milo_status_str(milo_status status);
+
+/* MILO_ABI_VERSION of the built library. */
+int32_t milo_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MILO_ATTN_H */

@@ -57,7 +57,13 @@ def _load():
         _lib = ctypes.CDLL(_LIB)
         _lib.milo_oracle_attend.argtypes = [ctypes.POINTER(_Args)]
         _lib.milo_oracle_attend.restype = ctypes.c_int
+        _lib.milo_oracle_threads.restype = ctypes.c_int
     return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle uses."""
+    return int(_load().milo_oracle_threads())
 
 
 def _f64(a: np.ndarray, dtype: str) -> np.ndarray:

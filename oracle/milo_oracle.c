@@ -28,6 +28,9 @@
  */
 #include <math.h>
 #include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdlib.h>
 #include <string.h>
 
@@ -175,4 +178,13 @@ int milo_oracle_attend(const milo_oracle_args* a) {
     }
   }
   return 0;
+}
+
+/* Threads the oracle's parallel regions use. */
+int milo_oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }

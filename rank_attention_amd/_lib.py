@@ -1,0 +1,71 @@
+"""ctypes view of the C ABI in include/milo_attn.h (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmilo_attn.so")
+
+MILO_OK, MILO_ERR_INVALID, MILO_ERR_UNSUPPORTED, MILO_ERR_WORKSPACE, MILO_ERR_DEVICE = range(5)
+MILO_F32, MILO_BF16 = 0, 1
+MILO_PATH_DECODE, MILO_PATH_CHUNK = 0, 1
+EXPORTS = ("milo_attn_workspace_bytes", "milo_attn_decode", "milo_attn_chunk",
+           "milo_status_str", "milo_abi_version")
+
+
+class MiloBlock(ctypes.Structure):
+    _fields_ = [("off", ctypes.c_int64), ("n_tok", ctypes.c_int32), ("ld_tok", ctypes.c_int32),
+                ("rank_k", ctypes.c_int32), ("rank_v", ctypes.c_int32)]
+
+
+class MiloAttnArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("q_len", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p),
+        ("pool", ctypes.c_void_p),
+        ("blocks", ctypes.c_void_p),
+        ("seq_blocks", ctypes.c_void_p),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("tail_cap", ctypes.c_int32),
+        ("k_tail", ctypes.c_void_p),
+        ("v_tail", ctypes.c_void_p),
+        ("tail_len", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("prof_events", ctypes.c_void_p * 2),
+    ]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the built HIP library; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build the HIP library first "
+                "(python -c 'import __graft_entry__ as g; g.build()')")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.milo_attn_workspace_bytes.argtypes = [ctypes.POINTER(MiloAttnArgs), ctypes.c_int32]
+        lib.milo_attn_workspace_bytes.restype = ctypes.c_size_t
+        for fn in (lib.milo_attn_decode, lib.milo_attn_chunk):
+            fn.argtypes = [ctypes.POINTER(MiloAttnArgs), ctypes.c_void_p]
+            fn.restype = ctypes.c_int
+        lib.milo_status_str.argtypes = [ctypes.c_int]
+        lib.milo_status_str.restype = ctypes.c_char_p
+        lib.milo_abi_version.argtypes = []
+        lib.milo_abi_version.restype = ctypes.c_int32
+        _lib = lib
+    return _lib

@@ -1,0 +1,623 @@
+// decode.hip -- gfx950 decode attention over a block-wise low-rank KV cache.
+//
+// MILO (summary at paperlayer.ai/abs/2609.29913v1) stores each block's keys
+// and values as separate low-rank factors, K_b ~= U_b W_b and V_b ~= U'_b W'_b
+// ("4.2 Block-wise Low-Rank Compression"), and at inference attends over the
+// selected blocks ("4.4 MILO Workflow").  This kernel evaluates that attention
+// in the absorbed order, which never forms K_b or V_b:
+//     p = scale*log2(e) * W_b q     s = U_b p     e = exp2(s - m)
+//     z = e^T U'_b                  o~ = z W'_b
+// and leaves per-unit partials (o~, m, l) for the merge kernel.
+//
+// Work unit = one wave (64 lanes) per (sequence, KV head, block slot), plus
+// one dense-tail unit per (sequence, KV head).  The G query heads of the KV
+// group share every factor load.  The block's token factors are streamed
+// once, rank-major, 16 bytes per lane:
+//   - scores: lane owns 16 tokens of a 1024-token tile (two 1 KB wave-wide
+//     row segments); rows 2m and 2m+1 of U^T are byte-permuted into rank
+//     pairs and met with packed bf16 pairs of p (v_dot2_f32_bf16);
+//   - values: the same lane/token ownership; e is packed to bf16 token pairs
+//     against rows of U'^T; per-lane partial z of up to 64 (row, head) slots
+//     are summed across the wave by one transposing butterfly.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace milo {
+
+namespace {
+
+constexpr int kLdsWords = 2048;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+template <int D, int G>
+struct Shape {
+  static constexpr int R = (64 / G < 12) ? 64 / G : 12;  // value rows per butterfly group
+  static constexpr int NG = (D + R - 1) / R;    // butterfly groups for rank <= D
+  static constexpr int JPL = D / 64;            // output columns per lane
+  static_assert(G >= 1 && G <= 8, "group size");
+  static_assert(NG * 64 <= 1024, "z staging fits its LDS region");
+};
+
+// ---------------------------------------------------------------------------
+// bf16 storage
+// ---------------------------------------------------------------------------
+
+// p = scale*log2(e) * W q for the G heads; lane k owns rows k and k+64.
+// Written to LDS as packed bf16 pairs: word [m*8 + h] = (p[h][2m], p[h][2m+1]).
+template <int D, int G>
+__device__ __forceinline__ void bf16_project_q(const uint16_t* W, const uint16_t* qh, int r,
+                                               float scale_log2, uint32_t* lds, int lane) {
+  float pa[G], pb[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) { pa[h] = 0.f; pb[h] = 0.f; }
+  const bool has_a = lane < r;
+  const bool has_b = (D > 64) && (lane + 64 < r);
+#pragma unroll 1
+  for (int jc = 0; jc < D / 8; ++jc) {
+    u32x4_t wa = {0, 0, 0, 0}, wb = {0, 0, 0, 0};
+    if (has_a) wa = ld16(W + (size_t)lane * D + jc * 8);
+    if (has_b) wb = ld16(W + (size_t)(lane + 64) * D + jc * 8);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const u32x4_t qv = ld16(qh + h * D + jc * 8);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        pa[h] = dot2bf(wa[w], qv[w], pa[h]);
+        if (D > 64) pb[h] = dot2bf(wb[w], qv[w], pb[h]);
+      }
+    }
+  }
+  uint16_t* p16 = reinterpret_cast<uint16_t*>(lds);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint32_t va = pack_bf16(pa[h] * scale_log2, 0.f) & 0xffffu;
+    p16[((lane >> 1) * 8 + h) * 2 + (lane & 1)] = (uint16_t)va;
+    if (D > 64) {
+      const uint32_t vb = pack_bf16(pb[h] * scale_log2, 0.f) & 0xffffu;
+      p16[(((lane + 64) >> 1) * 8 + h) * 2 + (lane & 1)] = (uint16_t)vb;
+    }
+  }
+}
+
+template <int D, int G, bool RAGGED>
+__device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* Upt, int ld, int T,
+                                           int r, int rv, const uint32_t* p2, float (&m_run)[G],
+                                           float (&l_run)[G], float* zl, int lane) {
+  using S = Shape<D, G>;
+  constexpr int R = S::R;
+  const int npair = (r + 1) >> 1;
+  for (int t0 = 0; t0 < T; t0 += 1024) {
+    const int tc0 = t0 + lane * 8, tc1 = t0 + 512 + lane * 8;
+    const bool ok0 = tc0 < T, ok1 = tc1 < T;
+
+    // ---- scores s[c*8+e][h] for token tc_c + e
+    float s[16][G];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[e][h] = 0.f;
+    for (int m = 0; m < npair; ++m) {
+      const uint16_t* r0 = Ut + (size_t)(2 * m) * ld;
+      const uint16_t* r1 = r0 + ld;
+      const bool has1 = 2 * m + 1 < r;
+      u32x4_t a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0}, b0 = {0, 0, 0, 0}, b1 = {0, 0, 0, 0};
+      if (ok0) {
+        a0 = ld16(r0 + tc0);
+        if (has1) a1 = ld16(r1 + tc0);
+      }
+      if (ok1) {
+        b0 = ld16(r0 + tc1);
+        if (has1) b1 = ld16(r1 + tc1);
+      }
+      const u32x4_t pq0 = *reinterpret_cast<const u32x4_t*>(p2 + m * 8);
+      const u32x4_t pq1 = *reinterpret_cast<const u32x4_t*>(p2 + m * 8 + 4);
+      uint32_t pp[8] = {pq0[0], pq0[1], pq0[2], pq0[3], pq1[0], pq1[1], pq1[2], pq1[3]};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t lo0 = perm_lo(a0[w], a1[w]), hi0 = perm_hi(a0[w], a1[w]);
+        const uint32_t lo1 = perm_lo(b0[w], b1[w]), hi1 = perm_hi(b0[w], b1[w]);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          s[2 * w][h] = dot2bf(lo0, pp[h], s[2 * w][h]);
+          s[2 * w + 1][h] = dot2bf(hi0, pp[h], s[2 * w + 1][h]);
+          s[8 + 2 * w][h] = dot2bf(lo1, pp[h], s[8 + 2 * w][h]);
+          s[8 + 2 * w + 1][h] = dot2bf(hi1, pp[h], s[8 + 2 * w + 1][h]);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int tok = (e < 8 ? tc0 : tc1) + (e & 7);
+      if (tok >= T) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) s[e][h] = kNegInf;
+      }
+    }
+
+    // ---- online softmax statistics; e packed to bf16 token pairs
+    uint32_t e2[2][4][G];
+    float alpha[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mx = s[0][h];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e][h]);
+      mx = wave_max(mx);
+      const float mn = fmaxf(m_run[h], mx);
+      alpha[h] = fast_exp2(m_run[h] - mn);
+      float sum = 0.f;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float x0 = fast_exp2(s[c * 8 + 2 * w][h] - mn);
+          const float x1 = fast_exp2(s[c * 8 + 2 * w + 1][h] - mn);
+          sum += x0 + x1;
+          e2[c][w][h] = pack_bf16(x0, x1);
+        }
+      l_run[h] = l_run[h] * alpha[h] + wave_sum(sum);
+      m_run[h] = mn;
+    }
+    {
+      const int hl = lane % G;
+      float al = alpha[0];
+#pragma unroll
+      for (int h = 1; h < G; ++h) al = (hl == h) ? alpha[h] : al;
+      for (int gi = 0; gi * R < rv; ++gi) zl[gi * 64 + lane] *= al;
+    }
+
+    // ---- z = e^T U'  (value factor), reduced per group of R rows
+    u32x4_t mask0 = {~0u, ~0u, ~0u, ~0u}, mask1 = {~0u, ~0u, ~0u, ~0u};
+    if (RAGGED) {
+      const int n0 = T - tc0, n1 = T - tc1;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        mask0[w] = (2 * w < n0 ? 0xffffu : 0u) | (2 * w + 1 < n0 ? 0xffff0000u : 0u);
+        mask1[w] = (2 * w < n1 ? 0xffffu : 0u) | (2 * w + 1 < n1 ? 0xffff0000u : 0u);
+      }
+    }
+#pragma unroll 1
+    for (int gi = 0; gi * R < rv; ++gi) {
+      {
+        float acc[64];
+#pragma unroll
+        for (int x = 0; x < 64; ++x) acc[x] = 0.f;
+#pragma unroll
+        for (int rho = 0; rho < R; ++rho) {
+          const int kp = gi * R + rho;
+          if (kp < rv) {
+            const uint16_t* row = Upt + (size_t)kp * ld;
+            u32x4_t u0 = {0, 0, 0, 0}, u1 = {0, 0, 0, 0};
+            if (ok0) u0 = ld16(row + tc0);
+            if (ok1) u1 = ld16(row + tc1);
+            if (RAGGED) { u0 &= mask0; u1 &= mask1; }
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+#pragma unroll
+              for (int h = 0; h < G; ++h) {
+                acc[rho * G + h] = dot2bf(u0[w], e2[0][w][h], acc[rho * G + h]);
+                acc[rho * G + h] = dot2bf(u1[w], e2[1][w][h], acc[rho * G + h]);
+              }
+          }
+        }
+        zl[gi * 64 + lane] += reduce_transpose64(acc, lane);
+      }
+    }
+  }
+}
+
+template <int D, int G>
+__device__ __forceinline__ void block_unit_bf16(const DecodeParams& p, int i, int g, int unit,
+                                                const milo_block& blk, uint32_t* lds) {
+  using S = Shape<D, G>;
+  constexpr int R = S::R, NG = S::NG, JPL = S::JPL;
+  const int lane = threadIdx.x;
+  const int T = max(blk.n_tok, 0);
+  const int ld = blk.ld_tok;
+  const int r = min(max(blk.rank_k, 0), D), rv = min(max(blk.rank_v, 0), D);
+  const uint16_t* Ut = reinterpret_cast<const uint16_t*>(p.pool) + blk.off +
+                       (int64_t)g * (r + rv) * (ld + D);
+  const uint16_t* W = Ut + (size_t)r * ld;
+  const uint16_t* Upt = W + (size_t)r * D;
+  const uint16_t* Wp = Upt + (size_t)rv * ld;
+  const uint16_t* qh = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)i * p.n_q_heads + g * G) * D;
+
+  bf16_project_q<D, G>(W, qh, r, p.scale_log2, lds, lane);
+  __syncthreads();
+
+  // z partial sums live in LDS: zl[gi*64 + l] = slot l of row group gi
+  float* zl = reinterpret_cast<float*>(lds + 1024);
+  float m_run[G], l_run[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) { m_run[h] = kNegInf; l_run[h] = 0.f; }
+  for (int gi = 0; gi < NG; ++gi) zl[gi * 64 + lane] = 0.f;
+
+  if (T & 7)
+    bf16_tiles<D, G, true>(Ut, Upt, ld, T, r, rv, lds, m_run, l_run, zl, lane);
+  else
+    bf16_tiles<D, G, false>(Ut, Upt, ld, T, r, rv, lds, m_run, l_run, zl, lane);
+
+  // ---- o~ = z W'
+  __syncthreads();
+  float o[G][JPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int jj = 0; jj < JPL; ++jj) o[h][jj] = 0.f;
+  for (int kp = 0; kp < rv; ++kp) {
+    const int gi = kp / R, rho = kp - gi * R;
+    const float* zp = zl + gi * 64 + rho * G;
+    float wv[JPL];
+    if (JPL == 2) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(Wp + (size_t)kp * D + 2 * lane);
+      wv[0] = bf_lo(w);
+      wv[JPL - 1] = bf_hi(w);
+    } else {
+      wv[0] = __uint_as_float((uint32_t)Wp[(size_t)kp * D + lane] << 16);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float z = zp[h];
+#pragma unroll
+      for (int jj = 0; jj < JPL; ++jj) o[h][jj] = fmaf(z, wv[jj], o[h][jj]);
+    }
+  }
+
+  float* po = p.part.o + (size_t)unit * G * D;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int jj = 0; jj < JPL; ++jj) po[h * D + lane * JPL + jj] = o[h][jj];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    if (lane == h) {
+      p.part.ml[((size_t)unit * G + h) * 2 + 0] = m_run[h];
+      p.part.ml[((size_t)unit * G + h) * 2 + 1] = l_run[h];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 storage (small workloads; same structure, plain FMA)
+// ---------------------------------------------------------------------------
+template <int D, int G, bool RAGGED>
+__device__ __forceinline__ void f32_tiles(const float* Ut, const float* Upt, int ld, int T, int r,
+                                          int rv, const float* pf, float (&m_run)[G],
+                                          float (&l_run)[G], float* zl, int lane) {
+  using S = Shape<D, G>;
+  constexpr int R = S::R;
+  for (int t0 = 0; t0 < T; t0 += 512) {
+    const int tc0 = t0 + lane * 4, tc1 = t0 + 256 + lane * 4;
+    const bool ok0 = tc0 < T, ok1 = tc1 < T;
+    float s[8][G];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[e][h] = 0.f;
+    for (int k = 0; k < r; ++k) {
+      const float* row = Ut + (size_t)k * ld;
+      f32x4_t u0 = {0.f, 0.f, 0.f, 0.f}, u1 = {0.f, 0.f, 0.f, 0.f};
+      if (ok0) u0 = ld16f(row + tc0);
+      if (ok1) u1 = ld16f(row + tc1);
+      const f32x4_t pq0 = *reinterpret_cast<const f32x4_t*>(pf + k * 8);
+      const f32x4_t pq1 = *reinterpret_cast<const f32x4_t*>(pf + k * 8 + 4);
+      const float pp[8] = {pq0[0], pq0[1], pq0[2], pq0[3], pq1[0], pq1[1], pq1[2], pq1[3]};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          s[e][h] = fmaf(u0[e], pp[h], s[e][h]);
+          s[4 + e][h] = fmaf(u1[e], pp[h], s[4 + e][h]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int tok = (e < 4 ? tc0 : tc1) + (e & 3);
+      if (tok >= T) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) s[e][h] = kNegInf;
+      }
+    }
+    float ex[8][G];
+    float alpha[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mx = s[0][h];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e][h]);
+      mx = wave_max(mx);
+      const float mn = fmaxf(m_run[h], mx);
+      alpha[h] = fast_exp2(m_run[h] - mn);
+      float sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ex[e][h] = fast_exp2(s[e][h] - mn);
+        sum += ex[e][h];
+      }
+      l_run[h] = l_run[h] * alpha[h] + wave_sum(sum);
+      m_run[h] = mn;
+    }
+    {
+      const int hl = lane % G;
+      float al = alpha[0];
+#pragma unroll
+      for (int h = 1; h < G; ++h) al = (hl == h) ? alpha[h] : al;
+      for (int gi = 0; gi * R < rv; ++gi) zl[gi * 64 + lane] *= al;
+    }
+#pragma unroll 1
+    for (int gi = 0; gi * R < rv; ++gi) {
+      {
+        float acc[64];
+#pragma unroll
+        for (int x = 0; x < 64; ++x) acc[x] = 0.f;
+#pragma unroll
+        for (int rho = 0; rho < R; ++rho) {
+          const int kp = gi * R + rho;
+          if (kp < rv) {
+            const float* row = Upt + (size_t)kp * ld;
+            f32x4_t u0 = {0.f, 0.f, 0.f, 0.f}, u1 = {0.f, 0.f, 0.f, 0.f};
+            if (ok0) u0 = ld16f(row + tc0);
+            if (ok1) u1 = ld16f(row + tc1);
+            if (RAGGED) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                u0[e] = (tc0 + e < T) ? u0[e] : 0.f;
+                u1[e] = (tc1 + e < T) ? u1[e] : 0.f;
+              }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+              for (int h = 0; h < G; ++h) {
+                acc[rho * G + h] = fmaf(u0[e], ex[e][h], acc[rho * G + h]);
+                acc[rho * G + h] = fmaf(u1[e], ex[4 + e][h], acc[rho * G + h]);
+              }
+          }
+        }
+        zl[gi * 64 + lane] += reduce_transpose64(acc, lane);
+      }
+    }
+  }
+}
+
+template <int D, int G>
+__device__ __forceinline__ void block_unit_f32(const DecodeParams& p, int i, int g, int unit,
+                                               const milo_block& blk, uint32_t* lds) {
+  using S = Shape<D, G>;
+  constexpr int R = S::R, NG = S::NG, JPL = S::JPL;
+  const int lane = threadIdx.x;
+  const int T = max(blk.n_tok, 0);
+  const int ld = blk.ld_tok;
+  const int r = min(max(blk.rank_k, 0), D), rv = min(max(blk.rank_v, 0), D);
+  const float* Ut = reinterpret_cast<const float*>(p.pool) + blk.off + (int64_t)g * (r + rv) * (ld + D);
+  const float* W = Ut + (size_t)r * ld;
+  const float* Upt = W + (size_t)r * D;
+  const float* Wp = Upt + (size_t)rv * ld;
+  const float* qh = reinterpret_cast<const float*>(p.q) + ((int64_t)i * p.n_q_heads + g * G) * D;
+
+  // p[k][h] (fp32) for rows k = lane, lane + 64
+  float* pf = reinterpret_cast<float*>(lds);
+  {
+    float pa[G], pb[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) { pa[h] = 0.f; pb[h] = 0.f; }
+    const bool has_a = lane < r, has_b = (D > 64) && (lane + 64 < r);
+    for (int jc = 0; jc < D / 4; ++jc) {
+      f32x4_t wa = {0.f, 0.f, 0.f, 0.f}, wb = {0.f, 0.f, 0.f, 0.f};
+      if (has_a) wa = ld16f(W + (size_t)lane * D + jc * 4);
+      if (has_b) wb = ld16f(W + (size_t)(lane + 64) * D + jc * 4);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const f32x4_t qv = ld16f(qh + h * D + jc * 4);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          pa[h] = fmaf(wa[w], qv[w], pa[h]);
+          pb[h] = fmaf(wb[w], qv[w], pb[h]);
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      pf[lane * 8 + h] = pa[h] * p.scale_log2;
+      if (D > 64) pf[(lane + 64) * 8 + h] = pb[h] * p.scale_log2;
+    }
+  }
+  __syncthreads();
+
+  float* zl = reinterpret_cast<float*>(lds + 1024);
+  float m_run[G], l_run[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) { m_run[h] = kNegInf; l_run[h] = 0.f; }
+  for (int gi = 0; gi < NG; ++gi) zl[gi * 64 + lane] = 0.f;
+  if (T & 3)
+    f32_tiles<D, G, true>(Ut, Upt, ld, T, r, rv, pf, m_run, l_run, zl, lane);
+  else
+    f32_tiles<D, G, false>(Ut, Upt, ld, T, r, rv, pf, m_run, l_run, zl, lane);
+
+  __syncthreads();
+  float o[G][JPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int jj = 0; jj < JPL; ++jj) o[h][jj] = 0.f;
+  for (int kp = 0; kp < rv; ++kp) {
+    const int gi = kp / R, rho = kp - gi * R;
+    const float* zp = zl + gi * 64 + rho * G;
+    float wv[JPL];
+#pragma unroll
+    for (int jj = 0; jj < JPL; ++jj) wv[jj] = Wp[(size_t)kp * D + lane * JPL + jj];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float z = zp[h];
+#pragma unroll
+      for (int jj = 0; jj < JPL; ++jj) o[h][jj] = fmaf(z, wv[jj], o[h][jj]);
+    }
+  }
+  float* po = p.part.o + (size_t)unit * G * D;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int jj = 0; jj < JPL; ++jj) po[h * D + lane * JPL + jj] = o[h][jj];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    if (lane == h) {
+      p.part.ml[((size_t)unit * G + h) * 2 + 0] = m_run[h];
+      p.part.ml[((size_t)unit * G + h) * 2 + 1] = l_run[h];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dense tail: K_t, V_t token-major [tail_cap][D]; every token < tail_len is
+// visible to the decode query.  Lane t scores token t of a 64-token tile.
+// ---------------------------------------------------------------------------
+template <int D, int G, int DT>
+__device__ __forceinline__ void tail_unit(const DecodeParams& p, int i, int g, int unit,
+                                          uint32_t* lds) {
+  constexpr int JPL = D / 64;
+  const int lane = threadIdx.x;
+  const int cap = p.tail_cap;
+  const int L = cap > 0 ? min(max(p.tail_len[i], 0), cap) : 0;
+  const size_t kv_off = ((size_t)i * p.n_kv_heads + g) * (size_t)cap * D;
+  float m_run[G], l_run[G], o[G][JPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m_run[h] = kNegInf;
+    l_run[h] = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < JPL; ++jj) o[h][jj] = 0.f;
+  }
+  float* el = reinterpret_cast<float*>(lds);   // [64 tokens][8 heads]
+  for (int t0 = 0; t0 < L; t0 += 64) {
+    const int t = t0 + lane;
+    const bool valid = t < L;
+    float s[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) s[h] = 0.f;
+    if (DT == MILO_BF16) {
+      const uint16_t* K = reinterpret_cast<const uint16_t*>(p.k_tail) + kv_off;
+      const uint16_t* qh = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)i * p.n_q_heads + g * G) * D;
+      for (int jc = 0; jc < D / 8; ++jc) {
+        u32x4_t kv = {0, 0, 0, 0};
+        if (valid) kv = ld16(K + (size_t)t * D + jc * 8);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const u32x4_t qv = ld16(qh + h * D + jc * 8);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) s[h] = dot2bf(kv[w], qv[w], s[h]);
+        }
+      }
+    } else {
+      const float* K = reinterpret_cast<const float*>(p.k_tail) + kv_off;
+      const float* qh = reinterpret_cast<const float*>(p.q) + ((int64_t)i * p.n_q_heads + g * G) * D;
+      for (int jc = 0; jc < D / 4; ++jc) {
+        f32x4_t kv = {0.f, 0.f, 0.f, 0.f};
+        if (valid) kv = ld16f(K + (size_t)t * D + jc * 4);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const f32x4_t qv = ld16f(qh + h * D + jc * 4);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) s[h] = fmaf(kv[w], qv[w], s[h]);
+        }
+      }
+    }
+    float alpha[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float sv = valid ? s[h] * p.scale_log2 : kNegInf;
+      const float mx = wave_max(sv);
+      const float mn = fmaxf(m_run[h], mx);
+      alpha[h] = fast_exp2(m_run[h] - mn);
+      const float ev = fast_exp2(sv - mn);
+      l_run[h] = l_run[h] * alpha[h] + wave_sum(ev);
+      m_run[h] = mn;
+      el[lane * 8 + h] = ev;
+#pragma unroll
+      for (int jj = 0; jj < JPL; ++jj) o[h][jj] *= alpha[h];
+    }
+    __syncthreads();
+    const int nt = min(64, L - t0);
+    for (int tt = 0; tt < nt; ++tt) {
+      float vv[JPL];
+      if (DT == MILO_BF16) {
+        const uint16_t* V = reinterpret_cast<const uint16_t*>(p.v_tail) + kv_off + (size_t)(t0 + tt) * D;
+        if (JPL == 2) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(V + 2 * lane);
+          vv[0] = bf_lo(w);
+          vv[JPL - 1] = bf_hi(w);
+        } else {
+          vv[0] = __uint_as_float((uint32_t)V[lane] << 16);
+        }
+      } else {
+        const float* V = reinterpret_cast<const float*>(p.v_tail) + kv_off + (size_t)(t0 + tt) * D;
+#pragma unroll
+        for (int jj = 0; jj < JPL; ++jj) vv[jj] = V[lane * JPL + jj];
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float ev = el[tt * 8 + h];
+#pragma unroll
+        for (int jj = 0; jj < JPL; ++jj) o[h][jj] = fmaf(ev, vv[jj], o[h][jj]);
+      }
+    }
+    __syncthreads();
+  }
+  float* po = p.part.o + (size_t)unit * G * D;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int jj = 0; jj < JPL; ++jj) po[h * D + lane * JPL + jj] = o[h][jj];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    if (lane == h) {
+      p.part.ml[((size_t)unit * G + h) * 2 + 0] = m_run[h];
+      p.part.ml[((size_t)unit * G + h) * 2 + 1] = l_run[h];
+    }
+}
+
+template <int D, int G, int DT>
+__global__ __launch_bounds__(64) void milo_decode_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
+  const int S = p.max_blocks + 1;
+  const int unit = blockIdx.x;
+  const int slot = unit % S;
+  const int ig = unit / S;
+  const int g = ig % p.n_kv_heads, i = ig / p.n_kv_heads;
+  if (slot == p.max_blocks) {
+    tail_unit<D, G, DT>(p, i, g, unit, lds);
+    return;
+  }
+  const int b0 = p.seq_blocks[i];
+  const int nb = min(max(p.seq_blocks[i + 1] - b0, 0), p.max_blocks);
+  if (slot >= nb) return;
+  const milo_block blk = p.blocks[b0 + slot];
+  if (DT == MILO_BF16)
+    block_unit_bf16<D, G>(p, i, g, unit, blk, lds);
+  else
+    block_unit_f32<D, G>(p, i, g, unit, blk, lds);
+}
+
+template <int D, int DT>
+hipError_t launch_decode_dg(const DecodeParams& p, int group, hipStream_t s) {
+  const int64_t units = decode_units(p.batch, p.n_kv_heads, p.max_blocks);
+  if (units == 0) return hipSuccess;
+  const dim3 grid((unsigned)units), block(64);
+  switch (group) {
+#define MILO_G(GG) \
+  case GG: hipLaunchKernelGGL((milo_decode_kernel<D, GG, DT>), grid, block, 0, s, p); break;
+    MILO_G(1) MILO_G(2) MILO_G(3) MILO_G(4) MILO_G(5) MILO_G(6) MILO_G(7) MILO_G(8)
+#undef MILO_G
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// One translation unit per (dtype, head_dim): compiled with
+// -DMILO_INST_DT=<0|1> -DMILO_INST_D=<64|128>.
+#define MILO_CAT2(a, b, c) launch_decode_##a##_##b##_##c
+#define MILO_CAT(a, b, c) MILO_CAT2(a, b, c)
+hipError_t MILO_CAT(dt, MILO_INST_DT, MILO_INST_D)(const DecodeParams& p, int group, hipStream_t s) {
+  return launch_decode_dg<MILO_INST_D, MILO_INST_DT>(p, group, s);
+}
+
+}  // namespace milo

@@ -1,0 +1,66 @@
+// kernels.h -- launch interface between the host library and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "milo_attn.h"
+
+namespace milo {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+// Partial results of one work unit for its rows: unnormalised output o~
+// ([rows][head_dim]) and the pair (m, l) per row, m in log2 units.
+struct Partials {
+  float* o;    // [n_units][rows_per_unit][head_dim]
+  float* ml;   // [n_units][rows_per_unit][2]
+};
+
+struct DecodeParams {
+  const void* q;
+  const void* pool;
+  const milo_block* blocks;
+  const int32_t* seq_blocks;
+  const void* k_tail;
+  const void* v_tail;
+  const int32_t* tail_len;
+  Partials part;
+  int32_t batch, n_q_heads, n_kv_heads, max_blocks, tail_cap;
+  float scale_log2;   // scale * log2(e)
+};
+
+struct MergeParams {
+  Partials part;
+  const int32_t* seq_blocks;
+  float* out;
+  float* lse;
+  int32_t batch, q_len, n_q_heads, n_kv_heads, max_blocks;
+  int32_t slots;          // work-unit slots per (sequence, KV head)
+  int32_t rows_per_unit;  // query rows stored per unit slot (q_len * group)
+  int32_t tail_slot;      // slot of the dense-tail unit
+};
+
+// Work units of the decode kernel: one per (sequence, KV head, block slot),
+// plus one dense-tail unit per (sequence, KV head).
+inline int64_t decode_units(int batch, int n_kv_heads, int max_blocks) {
+  return (int64_t)batch * n_kv_heads * (max_blocks + 1);
+}
+
+// One instantiation per (dtype, head_dim), each in its own translation unit.
+hipError_t launch_decode_dt_0_64(const DecodeParams& p, int group, hipStream_t s);
+hipError_t launch_decode_dt_0_128(const DecodeParams& p, int group, hipStream_t s);
+hipError_t launch_decode_dt_1_64(const DecodeParams& p, int group, hipStream_t s);
+hipError_t launch_decode_dt_1_128(const DecodeParams& p, int group, hipStream_t s);
+
+inline hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int group,
+                                hipStream_t s) {
+  if (dtype == MILO_F32 && head_dim == 64) return launch_decode_dt_0_64(p, group, s);
+  if (dtype == MILO_F32 && head_dim == 128) return launch_decode_dt_0_128(p, group, s);
+  if (dtype == MILO_BF16 && head_dim == 64) return launch_decode_dt_1_64(p, group, s);
+  if (dtype == MILO_BF16 && head_dim == 128) return launch_decode_dt_1_128(p, group, s);
+  return hipErrorInvalidValue;
+}
+hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t s);
+
+}  // namespace milo

@@ -1,0 +1,160 @@
+// milo_attn.cpp -- host side of the C ABI declared in include/milo_attn.h:
+// argument validation (before any HIP call), workspace sizing and kernel
+// launches on the caller's stream.  No allocation, no synchronisation, no
+// global mutable state.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kernels.h"
+#include "milo_attn.h"
+
+namespace {
+
+using milo::DecodeParams;
+using milo::MergeParams;
+using milo::Partials;
+
+constexpr size_t kWsAlign = 256;
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape-only checks shared by the workspace query and the entry points.
+milo_status check_shape(const milo_attn_args* a, int32_t path) {
+  if (!a) return MILO_ERR_INVALID;
+  if (a->struct_size != (int32_t)sizeof(milo_attn_args)) return MILO_ERR_INVALID;
+  if (path != MILO_PATH_DECODE && path != MILO_PATH_CHUNK) return MILO_ERR_INVALID;
+  if (a->dtype != MILO_F32 && a->dtype != MILO_BF16) return MILO_ERR_UNSUPPORTED;
+  if (a->batch < 0 || a->q_len < 1 || a->n_q_heads < 1 || a->n_kv_heads < 1) return MILO_ERR_INVALID;
+  if (a->n_q_heads % a->n_kv_heads != 0) return MILO_ERR_INVALID;
+  if (a->max_blocks_per_seq < 0 || a->tail_cap < 0) return MILO_ERR_INVALID;
+  if (!std::isfinite(a->scale)) return MILO_ERR_INVALID;
+  if (path == MILO_PATH_DECODE && a->q_len != 1) return MILO_ERR_INVALID;
+  if (path == MILO_PATH_CHUNK && a->tail_cap < a->q_len) return MILO_ERR_INVALID;
+  if (a->head_dim != 64 && a->head_dim != 128) return MILO_ERR_UNSUPPORTED;
+  const int group = a->n_q_heads / a->n_kv_heads;
+  if (group > 8) return MILO_ERR_UNSUPPORTED;
+  if (path == MILO_PATH_CHUNK) return MILO_ERR_UNSUPPORTED;  // chunk kernel not built yet
+  return MILO_OK;
+}
+
+struct Layout {
+  size_t o_bytes, ml_bytes, total;
+  int64_t units;
+  int32_t rows_per_unit;
+  int32_t slots;
+};
+
+Layout layout_of(const milo_attn_args* a) {
+  Layout L{};
+  const int group = a->n_q_heads / a->n_kv_heads;
+  L.slots = a->max_blocks_per_seq + 1;
+  L.rows_per_unit = a->q_len * group;
+  L.units = (int64_t)a->batch * a->n_kv_heads * L.slots;
+  L.o_bytes = round_up((size_t)L.units * L.rows_per_unit * a->head_dim * sizeof(float), kWsAlign);
+  L.ml_bytes = round_up((size_t)L.units * L.rows_per_unit * 2 * sizeof(float), kWsAlign);
+  L.total = L.o_bytes + L.ml_bytes;
+  return L;
+}
+
+milo_status check_pointers(const milo_attn_args* a, const Layout& L) {
+  if (a->batch == 0) return MILO_OK;
+  if (!a->q || !a->out || !a->seq_blocks) return MILO_ERR_INVALID;
+  if (!aligned(a->q, 16) || !aligned(a->out, 16)) return MILO_ERR_INVALID;
+  if (a->max_blocks_per_seq > 0) {
+    if (!a->blocks || !a->pool) return MILO_ERR_INVALID;
+    if (!aligned(a->pool, 16) || !aligned(a->blocks, 8)) return MILO_ERR_INVALID;
+  }
+  if ((a->tail_cap > 0) != (a->k_tail != nullptr) || (a->tail_cap > 0) != (a->v_tail != nullptr) ||
+      (a->tail_cap > 0) != (a->tail_len != nullptr))
+    return MILO_ERR_INVALID;
+  if (a->tail_cap > 0 && (!aligned(a->k_tail, 16) || !aligned(a->v_tail, 16))) return MILO_ERR_INVALID;
+  if (a->lse && !aligned(a->lse, 4)) return MILO_ERR_INVALID;
+  if (!a->workspace || a->workspace_bytes < L.total) return MILO_ERR_WORKSPACE;
+  if (!aligned(a->workspace, kWsAlign)) return MILO_ERR_WORKSPACE;
+  return MILO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t milo_attn_workspace_bytes(const milo_attn_args* a, int32_t path) {
+  if (check_shape(a, path) != MILO_OK) return 0;
+  return layout_of(a).total;
+}
+
+milo_status milo_attn_decode(const milo_attn_args* a, void* hip_stream) {
+  milo_status st = check_shape(a, MILO_PATH_DECODE);
+  if (st != MILO_OK) return st;
+  const Layout L = layout_of(a);
+  st = check_pointers(a, L);
+  if (st != MILO_OK) return st;
+  if (a->batch == 0) return MILO_OK;
+
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  const int group = a->n_q_heads / a->n_kv_heads;
+  char* ws = static_cast<char*>(a->workspace);
+  Partials part{reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + L.o_bytes)};
+
+  DecodeParams p{};
+  p.q = a->q;
+  p.pool = a->pool;
+  p.blocks = a->blocks;
+  p.seq_blocks = a->seq_blocks;
+  p.k_tail = a->k_tail;
+  p.v_tail = a->v_tail;
+  p.tail_len = a->tail_len;
+  p.part = part;
+  p.batch = a->batch;
+  p.n_q_heads = a->n_q_heads;
+  p.n_kv_heads = a->n_kv_heads;
+  p.max_blocks = a->max_blocks_per_seq;
+  p.tail_cap = a->tail_cap;
+  p.scale_log2 = a->scale * milo::kLog2eHost;
+
+  const bool timing = a->prof_events[0] && a->prof_events[1];
+  if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[0]), stream) != hipSuccess)
+    return MILO_ERR_DEVICE;
+  if (milo::launch_decode(p, a->dtype, a->head_dim, group, stream) != hipSuccess) return MILO_ERR_DEVICE;
+  if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[1]), stream) != hipSuccess)
+    return MILO_ERR_DEVICE;
+
+  MergeParams m{};
+  m.part = part;
+  m.seq_blocks = a->seq_blocks;
+  m.out = a->out;
+  m.lse = a->lse;
+  m.batch = a->batch;
+  m.q_len = a->q_len;
+  m.n_q_heads = a->n_q_heads;
+  m.n_kv_heads = a->n_kv_heads;
+  m.max_blocks = a->max_blocks_per_seq;
+  m.slots = L.slots;
+  m.rows_per_unit = L.rows_per_unit;
+  m.tail_slot = a->max_blocks_per_seq;
+  if (milo::launch_merge(m, a->head_dim, stream) != hipSuccess) return MILO_ERR_DEVICE;
+  return MILO_OK;
+}
+
+milo_status milo_attn_chunk(const milo_attn_args* a, void* hip_stream) {
+  (void)hip_stream;
+  return check_shape(a, MILO_PATH_CHUNK);
+}
+
+const char* milo_status_str(milo_status s) {
+  switch (s) {
+    case MILO_OK: return "ok";
+    case MILO_ERR_INVALID: return "invalid argument";
+    case MILO_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MILO_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MILO_ERR_DEVICE: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t milo_abi_version(void) { return MILO_ABI_VERSION; }
+
+}  // extern "C"

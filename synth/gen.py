@@ -33,6 +33,16 @@ VARIANTS = {"base": 0, "sharp": 1}
 _S_RANK, _S_Q, _S_BLOCK, _S_TAIL = 0, 1, 2, 3
 
 
+def _one_blas_thread():
+    """Keep BLAS single-threaded while the generator runs its own threads."""
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(1)
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        import contextlib
+        return contextlib.nullcontext()
+
+
 def _rng(*key: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(k) for k in key])))
 
@@ -64,16 +74,17 @@ def stored_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     return np.asarray(a, dtype=np.float64)
 
 
-def _orth_rows(rng: np.random.Generator, r: int, d: int) -> np.ndarray:
-    """diag(0.8^i) * Q^T with Q from the QR of a d x r Gaussian, sign-fixed."""
+def _orth_rows(rng: np.random.Generator, r: int, d: int, heads: int = 1) -> np.ndarray:
+    """[heads][r][d]: diag(0.8^i) * Q^T with Q from the QR of a d x r Gaussian,
+    column signs fixed so that diag(R) > 0."""
     if r == 0:
-        return np.zeros((0, d), np.float64)
-    g = rng.standard_normal((d, r))
+        return np.zeros((heads, 0, d), np.float64)
+    g = rng.standard_normal((heads, d, r))
     qm, rm = np.linalg.qr(g)
-    sgn = np.sign(np.diag(rm))
+    sgn = np.sign(np.diagonal(rm, axis1=1, axis2=2))
     sgn[sgn == 0] = 1.0
-    qm = qm * sgn[None, :]
-    return (0.8 ** np.arange(r))[:, None] * qm.T
+    qm = qm * sgn[:, None, :]
+    return (0.8 ** np.arange(r))[None, :, None] * np.swapaxes(qm, 1, 2)
 
 
 @dataclass
@@ -168,15 +179,10 @@ def _gen_block(cfg: Config, variant: str, seq: int, b: int, n_tok: int, rk: int,
                u_scale: float) -> LogicalBlock:
     rng = _rng(cfg.seed, VARIANTS[variant], _S_BLOCK, seq, b)
     d, h = cfg.head_dim, cfg.n_kv_heads
-    ut = np.empty((h, rk, n_tok), np.float32)
-    upt = np.empty((h, rv, n_tok), np.float32)
-    w = np.empty((h, rk, d), np.float32)
-    wp = np.empty((h, rv, d), np.float32)
-    for g in range(h):
-        ut[g] = rng.standard_normal((rk, n_tok), dtype=np.float32)
-        w[g] = _orth_rows(rng, rk, d)
-        upt[g] = rng.standard_normal((rv, n_tok), dtype=np.float32)
-        wp[g] = _orth_rows(rng, rv, d)
+    ut = rng.standard_normal((h, rk, n_tok), dtype=np.float32)
+    w = _orth_rows(rng, rk, d, h)
+    upt = rng.standard_normal((h, rv, n_tok), dtype=np.float32)
+    wp = _orth_rows(rng, rv, d, h)
     if u_scale != 1.0:
         ut *= np.float32(u_scale)
     if variant == "sharp":
@@ -227,7 +233,7 @@ def make_workload(cfg: Config, variant: str = "base", seqs: Optional[Sequence[in
             tasks.append((si, s, b, T, int(ranks[s][b, 0]), int(ranks[s][b, 1]), u_scale))
 
     nthr = threads or min(16, os.cpu_count() or 1)
-    with ThreadPoolExecutor(max_workers=nthr) as ex:
+    with _one_blas_thread(), ThreadPoolExecutor(max_workers=nthr) as ex:
         res = list(ex.map(lambda t: _gen_block(cfg, variant, t[1], t[2], t[3], t[4], t[5], t[6]), tasks))
     blocks: List[List[LogicalBlock]] = [[] for _ in seqs]
     for t, blk in zip(tasks, res):
@@ -239,18 +245,16 @@ def make_workload(cfg: Config, variant: str = "base", seqs: Optional[Sequence[in
     for si, s in enumerate(seqs):
         rq = _rng(cfg.seed, VARIANTS[variant], _S_Q, s)
         q[si] = rq.standard_normal((Q, hq, d), dtype=np.float32) * np.float32(q_mult)
-        rt = _rng(cfg.seed, VARIANTS[variant], _S_TAIL, s)
-        for g in range(hkv):
-            if cap == 0:
-                continue
-            uk = rt.standard_normal((cap, d))
-            wk = _orth_rows(rt, d, d)
-            uv = rt.standard_normal((cap, d))
-            wv = _orth_rows(rt, d, d)
-            kt[si, g] = (uk @ wk).astype(np.float32)
-            vt[si, g] = (uv @ wv).astype(np.float32)
+        if cap > 0:
+            rt = _rng(cfg.seed, VARIANTS[variant], _S_TAIL, s)
+            uk = rt.standard_normal((hkv, cap, d))
+            wk = _orth_rows(rt, d, d, hkv)
+            uv = rt.standard_normal((hkv, cap, d))
+            wv = _orth_rows(rt, d, d, hkv)
+            kt[si] = (uk @ wk).astype(np.float32)
+            vt[si] = (uv @ wv).astype(np.float32)
             if variant == "sharp":
-                vt[si, g] += np.float32(1.0)
+                vt[si] += np.float32(1.0)
     return Workload(cfg=cfg, variant=variant, seqs=seqs, q=_store(q, cfg.dtype), blocks=blocks,
                     k_tail=_store(kt, cfg.dtype), v_tail=_store(vt, cfg.dtype),
                     tail_len=tl[seqs].astype(np.int32), scale=cfg.scale)

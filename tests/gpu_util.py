@@ -1,0 +1,74 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and
+compare it with the fp64 oracle on the same seeded inputs."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+import rank_attention_amd as ra
+import synth
+from synth.gen import LogicalBlock, Workload
+
+# Official parity gate (elementwise, numpy isclose convention).
+ATOL, RTOL = 2e-3, 1e-2
+# Extra gates for workloads whose outputs are not tiny: relative L2 error per
+# query row and the log-sum-exp.
+REL_L2 = 1e-2
+LSE_ATOL, LSE_RTOL = 2e-3, 1e-2
+
+
+def note(msg: str) -> None:
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def run_hip(wl: Workload, path: str = "decode", repeat: int = 1, **packkw):
+    """Pack, upload, run the HIP path; returns (out, lse) float64 numpy arrays."""
+    import torch
+    pc = ra.pack(wl, **packkw)
+    dc = ra.DeviceCache(pc, scale=wl.scale)
+    note(f"{path} cfg={wl.cfg.name} variant={wl.variant} B={wl.batch} Q={wl.cfg.q_len} "
+         f"Hq={wl.cfg.n_q_heads} Hkv={wl.cfg.n_kv_heads} d={wl.cfg.head_dim} dtype={wl.dtype} "
+         f"max_blocks={pc.max_blocks} tail_cap={pc.k_tail.shape[2]}")
+    outs = []
+    for _ in range(repeat):
+        out, lse = dc.decode() if path == "decode" else dc.chunk()
+        torch.cuda.synchronize()
+        outs.append((out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)))
+    return outs if repeat > 1 else outs[0]
+
+
+def compare(out, lse, ref_o, ref_l, rows=None, sharp_gates=False, name=""):
+    """Assert the official gate (and the extra gates when asked) on the given
+    rows [(i, j, h)] or on every row."""
+    if rows is not None:
+        idx = tuple(np.array(rows).T)
+        out, lse, ref_o, ref_l = out[idx], lse[idx], ref_o[idx], ref_l[idx]
+    assert np.all(np.isfinite(out)), f"{name}: non-finite GPU output"
+    err = np.abs(out - ref_o)
+    bad = err > ATOL + RTOL * np.abs(ref_o)
+    assert not bad.any(), (f"{name}: {bad.sum()} of {bad.size} outputs outside atol {ATOL} + rtol {RTOL}; "
+                           f"max err {err.max():.3e}")
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(fin, np.isfinite(lse)), f"{name}: lse finiteness differs"
+    lerr = np.abs(lse[fin] - ref_l[fin])
+    assert np.all(lerr <= LSE_ATOL + LSE_RTOL * np.abs(ref_l[fin])), f"{name}: lse max err {lerr.max():.3e}"
+    if sharp_gates:
+        num = np.linalg.norm((out - ref_o).reshape(-1, out.shape[-1]), axis=-1)
+        den = np.linalg.norm(ref_o.reshape(-1, out.shape[-1]), axis=-1)
+        rel = num / np.maximum(den, 1e-30)
+        assert np.all(rel <= REL_L2), f"{name}: relative L2 error per row up to {rel.max():.3e}"
+    return float(err.max())
+
+
+def custom_workload(cfg, blocks, q, k_tail, v_tail, tail_len) -> Workload:
+    """A workload from explicit arrays (stored dtype of cfg)."""
+    return Workload(cfg=cfg, variant="custom", seqs=list(range(len(blocks))), q=q, blocks=blocks,
+                    k_tail=k_tail, v_tail=v_tail, tail_len=np.asarray(tail_len, np.int32),
+                    scale=cfg.scale)
+
+
+def bf16_bits(x):
+    return synth.gen.f32_to_bf16_bits(np.asarray(x, np.float32))

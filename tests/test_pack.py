@@ -1,0 +1,58 @@
+"""Host-side packing of logical factors into the pool layout of milo_attn.h."""
+import numpy as np
+
+import rank_attention_amd as ra
+import synth
+
+
+def unpack_block(pc, k, g):
+    b = pc.blocks[k]
+    off, T, ld, rk, rv = (int(b[f]) for f in ("off", "n_tok", "ld_tok", "rank_k", "rank_v"))
+    d = pc.head_dim
+    base = off + g * (rk + rv) * (ld + d)
+    ut = pc.pool[base:base + rk * ld].reshape(rk, ld)
+    w = pc.pool[base + rk * ld: base + rk * ld + rk * d].reshape(rk, d)
+    o = base + rk * (ld + d)
+    upt = pc.pool[o:o + rv * ld].reshape(rv, ld)
+    wp = pc.pool[o + rv * ld: o + rv * ld + rv * d].reshape(rv, d)
+    return ut, w, upt, wp, T
+
+
+def test_pool_roundtrip_and_poison():
+    cfg = synth.get_config("qwen05b_16k").with_(batch=3, n_blocks=3)
+    tokens = [[37, 512, 8], [1, 16, 100], [64, 65, 7]]
+    wl = synth.make_workload(cfg, tokens=tokens, n_blocks=[3, 3, 3], tail_len=[128, 0, 5])
+    pc = ra.pack(wl, shuffle_pool=5)
+    assert pc.pool.dtype == np.uint16
+    assert list(pc.seq_blocks) == [0, 3, 6, 9]
+    assert np.all(pc.blocks["off"] % 8 == 0) and np.all(pc.blocks["ld_tok"] % 8 == 0)
+    k = 0
+    for i in range(3):
+        for b in wl.blocks[i]:
+            for g in range(cfg.n_kv_heads):
+                ut, w, upt, wp, T = unpack_block(pc, k, g)
+                np.testing.assert_array_equal(ut[:, :T], b.ut[g])
+                np.testing.assert_array_equal(w, b.w[g])
+                np.testing.assert_array_equal(upt[:, :T], b.upt[g])
+                np.testing.assert_array_equal(wp, b.wp[g])
+                assert np.all(ut[:, T:] == 0x7FC0) and np.all(upt[:, T:] == 0x7FC0)
+            k += 1
+    # blocks do not overlap and the gaps hold NaN
+    spans = sorted((int(b["off"]), int(b["off"]) + cfg.n_kv_heads * (int(b["rank_k"]) + int(b["rank_v"])) *
+                    (int(b["ld_tok"]) + cfg.head_dim)) for b in pc.blocks)
+    for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
+        assert a1 < b0
+        assert np.all(pc.pool[a1:b0] == 0x7FC0)
+    # tail entries beyond tail_len are poisoned
+    assert np.all(pc.k_tail[1] == 0x7FC0)
+    assert np.all(pc.v_tail[2, :, 5:] == 0x7FC0)
+    np.testing.assert_array_equal(pc.k_tail[2, :, :5], wl.k_tail[2, :, :5])
+
+
+def test_f32_pool():
+    wl = synth.make_workload(synth.get_config("tiny"))
+    pc = ra.pack(wl)
+    assert pc.pool.dtype == np.float32
+    ut, w, upt, wp, T = unpack_block(pc, 3, 0)
+    np.testing.assert_array_equal(ut[:, :T], wl.blocks[0][3].ut[0])
+    assert pc.max_blocks == 4
