@@ -14,8 +14,8 @@
 // group share every factor load.  The block's token factors are streamed
 // once, rank-major, 16 bytes per lane:
 //   - scores: lane owns 16 tokens of a 1024-token tile (two 1 KB wave-wide
-//     row segments); rows 2m and 2m+1 of U^T are byte-permuted into rank
-//     pairs and met with packed bf16 pairs of p (v_dot2_f32_bf16);
+//     row segments); each row of U^T is unpacked to fp32 and met with fp32
+//     p held in LDS (broadcast reads), G FMAs per element;
 //   - values: the same lane/token ownership; e is packed to bf16 token pairs
 //     against rows of U'^T; per-lane partial z of up to 64 (row, head) slots
 //     are summed across the wave by one transposing butterfly.
@@ -42,11 +42,11 @@ struct Shape {
 // bf16 storage
 // ---------------------------------------------------------------------------
 
-// p = scale*log2(e) * W q for the G heads; lane k owns rows k and k+64.
-// Written to LDS as packed bf16 pairs: word [m*8 + h] = (p[h][2m], p[h][2m+1]).
+// p = scale*log2(e) * W q for the G heads, fp32; lane k owns rows k and k+64.
+// Written to LDS as pf[k*8 + h].  q and W are bf16, so dot2 products are exact.
 template <int D, int G>
 __device__ __forceinline__ void bf16_project_q(const uint16_t* W, const uint16_t* qh, int r,
-                                               float scale_log2, uint32_t* lds, int lane) {
+                                               float scale_log2, float* pf, int lane) {
   float pa[G], pb[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) { pa[h] = 0.f; pb[h] = 0.f; }
@@ -67,61 +67,48 @@ __device__ __forceinline__ void bf16_project_q(const uint16_t* W, const uint16_t
       }
     }
   }
-  uint16_t* p16 = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const uint32_t va = pack_bf16(pa[h] * scale_log2, 0.f) & 0xffffu;
-    p16[((lane >> 1) * 8 + h) * 2 + (lane & 1)] = (uint16_t)va;
-    if (D > 64) {
-      const uint32_t vb = pack_bf16(pb[h] * scale_log2, 0.f) & 0xffffu;
-      p16[(((lane + 64) >> 1) * 8 + h) * 2 + (lane & 1)] = (uint16_t)vb;
-    }
+    pf[lane * 8 + h] = pa[h] * scale_log2;
+    if (D > 64) pf[(lane + 64) * 8 + h] = pb[h] * scale_log2;
   }
 }
 
 template <int D, int G, bool RAGGED>
 __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* Upt, int ld, int T,
-                                           int r, int rv, const uint32_t* p2, float (&m_run)[G],
+                                           int r, int rv, const float* pf, float (&m_run)[G],
                                            float (&l_run)[G], float* zl, int lane) {
   using S = Shape<D, G>;
   constexpr int R = S::R;
-  const int npair = (r + 1) >> 1;
   for (int t0 = 0; t0 < T; t0 += 1024) {
     const int tc0 = t0 + lane * 8, tc1 = t0 + 512 + lane * 8;
     const bool ok0 = tc0 < T, ok1 = tc1 < T;
 
-    // ---- scores s[c*8+e][h] for token tc_c + e
+    // ---- scores s[c*8+e][h] for token tc_c + e: U rows unpacked to fp32
+    // and met with fp32 p (bf16 rounding of p would cost ~1% on sharp softmax)
     float s[16][G];
 #pragma unroll
     for (int e = 0; e < 16; ++e)
 #pragma unroll
       for (int h = 0; h < G; ++h) s[e][h] = 0.f;
-    for (int m = 0; m < npair; ++m) {
-      const uint16_t* r0 = Ut + (size_t)(2 * m) * ld;
-      const uint16_t* r1 = r0 + ld;
-      const bool has1 = 2 * m + 1 < r;
-      u32x4_t a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0}, b0 = {0, 0, 0, 0}, b1 = {0, 0, 0, 0};
-      if (ok0) {
-        a0 = ld16(r0 + tc0);
-        if (has1) a1 = ld16(r1 + tc0);
-      }
-      if (ok1) {
-        b0 = ld16(r0 + tc1);
-        if (has1) b1 = ld16(r1 + tc1);
-      }
-      const u32x4_t pq0 = *reinterpret_cast<const u32x4_t*>(p2 + m * 8);
-      const u32x4_t pq1 = *reinterpret_cast<const u32x4_t*>(p2 + m * 8 + 4);
-      uint32_t pp[8] = {pq0[0], pq0[1], pq0[2], pq0[3], pq1[0], pq1[1], pq1[2], pq1[3]};
+    for (int k = 0; k < r; ++k) {
+      const uint16_t* row = Ut + (size_t)k * ld;
+      u32x4_t a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+      if (ok0) a = ld16(row + tc0);
+      if (ok1) b = ld16(row + tc1);
+      const f32x4_t pq0 = *reinterpret_cast<const f32x4_t*>(pf + k * 8);
+      const f32x4_t pq1 = *reinterpret_cast<const f32x4_t*>(pf + k * 8 + 4);
+      const float pp[8] = {pq0[0], pq0[1], pq0[2], pq0[3], pq1[0], pq1[1], pq1[2], pq1[3]};
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t lo0 = perm_lo(a0[w], a1[w]), hi0 = perm_hi(a0[w], a1[w]);
-        const uint32_t lo1 = perm_lo(b0[w], b1[w]), hi1 = perm_hi(b0[w], b1[w]);
+        const float a0 = bf_lo(a[w]), a1 = bf_hi(a[w]);
+        const float b0 = bf_lo(b[w]), b1 = bf_hi(b[w]);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          s[2 * w][h] = dot2bf(lo0, pp[h], s[2 * w][h]);
-          s[2 * w + 1][h] = dot2bf(hi0, pp[h], s[2 * w + 1][h]);
-          s[8 + 2 * w][h] = dot2bf(lo1, pp[h], s[8 + 2 * w][h]);
-          s[8 + 2 * w + 1][h] = dot2bf(hi1, pp[h], s[8 + 2 * w + 1][h]);
+          s[2 * w][h] = fmaf(a0, pp[h], s[2 * w][h]);
+          s[2 * w + 1][h] = fmaf(a1, pp[h], s[2 * w + 1][h]);
+          s[8 + 2 * w][h] = fmaf(b0, pp[h], s[8 + 2 * w][h]);
+          s[8 + 2 * w + 1][h] = fmaf(b1, pp[h], s[8 + 2 * w + 1][h]);
         }
       }
     }
@@ -222,7 +209,8 @@ __device__ __forceinline__ void block_unit_bf16(const DecodeParams& p, int i, in
   const uint16_t* Wp = Upt + (size_t)rv * ld;
   const uint16_t* qh = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)i * p.n_q_heads + g * G) * D;
 
-  bf16_project_q<D, G>(W, qh, r, p.scale_log2, lds, lane);
+  float* pf = reinterpret_cast<float*>(lds);
+  bf16_project_q<D, G>(W, qh, r, p.scale_log2, pf, lane);
   __syncthreads();
 
   // z partial sums live in LDS: zl[gi*64 + l] = slot l of row group gi
@@ -233,9 +221,9 @@ __device__ __forceinline__ void block_unit_bf16(const DecodeParams& p, int i, in
   for (int gi = 0; gi < NG; ++gi) zl[gi * 64 + lane] = 0.f;
 
   if (T & 7)
-    bf16_tiles<D, G, true>(Ut, Upt, ld, T, r, rv, lds, m_run, l_run, zl, lane);
+    bf16_tiles<D, G, true>(Ut, Upt, ld, T, r, rv, pf, m_run, l_run, zl, lane);
   else
-    bf16_tiles<D, G, false>(Ut, Upt, ld, T, r, rv, lds, m_run, l_run, zl, lane);
+    bf16_tiles<D, G, false>(Ut, Upt, ld, T, r, rv, pf, m_run, l_run, zl, lane);
 
   // ---- o~ = z W'
   __syncthreads();
