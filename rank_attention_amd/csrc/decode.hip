@@ -44,19 +44,21 @@ struct Shape {
 
 // p = scale*log2(e) * W q for the G heads, fp32; lane k owns rows k and k+64.
 // Written to LDS as pf[k*8 + h].  q and W are bf16, so dot2 products are exact.
+// Loads are unconditional (row index clamped to r-1) so they can be issued
+// back to back; rows >= r are never read from pf.  Requires r >= 1.
 template <int D, int G>
 __device__ __forceinline__ void bf16_project_q(const uint16_t* W, const uint16_t* qh, int r,
                                                float scale_log2, float* pf, int lane) {
   float pa[G], pb[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) { pa[h] = 0.f; pb[h] = 0.f; }
-  const bool has_a = lane < r;
-  const bool has_b = (D > 64) && (lane + 64 < r);
-#pragma unroll 1
+  const uint16_t* wa_row = W + (size_t)min(lane, r - 1) * D;
+  const uint16_t* wb_row = W + (size_t)min(lane + 64, r - 1) * D;
+#pragma unroll 4
   for (int jc = 0; jc < D / 8; ++jc) {
-    u32x4_t wa = {0, 0, 0, 0}, wb = {0, 0, 0, 0};
-    if (has_a) wa = ld16(W + (size_t)lane * D + jc * 8);
-    if (has_b) wb = ld16(W + (size_t)(lane + 64) * D + jc * 8);
+    const u32x4_t wa = ld16(wa_row + jc * 8);
+    u32x4_t wb = {0, 0, 0, 0};
+    if (D > 64) wb = ld16(wb_row + jc * 8);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const u32x4_t qv = ld16(qh + h * D + jc * 8);
@@ -74,6 +76,46 @@ __device__ __forceinline__ void bf16_project_q(const uint16_t* W, const uint16_t
   }
 }
 
+constexpr int kRowsPerStep = 4;   // U^T rows per prefetch step of the score loop
+
+// Loads rows k0 .. k0+3 of U^T (clamped to r-1) at the lane's two chunks.
+__device__ __forceinline__ void load_rows4(const uint16_t* Ut, int ld, int k0, int r, int tq0,
+                                           int tq1, u32x4_t (&A)[kRowsPerStep],
+                                           u32x4_t (&B)[kRowsPerStep]) {
+#pragma unroll
+  for (int j = 0; j < kRowsPerStep; ++j) {
+    const uint16_t* row = Ut + (size_t)min(k0 + j, r - 1) * ld;
+    A[j] = ld16(row + tq0);
+    B[j] = ld16(row + tq1);
+  }
+}
+
+template <int G>
+__device__ __forceinline__ void score_rows4(const u32x4_t (&A)[kRowsPerStep],
+                                            const u32x4_t (&B)[kRowsPerStep], int k0, int r,
+                                            const float* pf, float (&s)[16][G]) {
+#pragma unroll
+  for (int j = 0; j < kRowsPerStep; ++j) {
+    if (k0 + j < r) {
+      const f32x4_t pq0 = *reinterpret_cast<const f32x4_t*>(pf + (k0 + j) * 8);
+      const f32x4_t pq1 = *reinterpret_cast<const f32x4_t*>(pf + (k0 + j) * 8 + 4);
+      const float pp[8] = {pq0[0], pq0[1], pq0[2], pq0[3], pq1[0], pq1[1], pq1[2], pq1[3]};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float a0 = bf_lo(A[j][w]), a1 = bf_hi(A[j][w]);
+        const float b0 = bf_lo(B[j][w]), b1 = bf_hi(B[j][w]);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          s[2 * w][h] = fmaf(a0, pp[h], s[2 * w][h]);
+          s[2 * w + 1][h] = fmaf(a1, pp[h], s[2 * w + 1][h]);
+          s[8 + 2 * w][h] = fmaf(b0, pp[h], s[8 + 2 * w][h]);
+          s[8 + 2 * w + 1][h] = fmaf(b1, pp[h], s[8 + 2 * w + 1][h]);
+        }
+      }
+    }
+  }
+}
+
 template <int D, int G, bool RAGGED>
 __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* Upt, int ld, int T,
                                            int r, int rv, const float* pf, float (&m_run)[G],
@@ -83,6 +125,9 @@ __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* U
   for (int t0 = 0; t0 < T; t0 += 1024) {
     const int tc0 = t0 + lane * 8, tc1 = t0 + 512 + lane * 8;
     const bool ok0 = tc0 < T, ok1 = tc1 < T;
+    // A lane whose chunk lies past the block end reads the tile's first
+    // chunk instead (always in bounds) and its tokens are masked below.
+    const int tq0 = ok0 ? tc0 : t0, tq1 = ok1 ? tc1 : t0;
 
     // ---- scores s[c*8+e][h] for token tc_c + e: U rows unpacked to fp32
     // and met with fp32 p (bf16 rounding of p would cost ~1% on sharp softmax)
@@ -91,25 +136,14 @@ __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* U
     for (int e = 0; e < 16; ++e)
 #pragma unroll
       for (int h = 0; h < G; ++h) s[e][h] = 0.f;
-    for (int k = 0; k < r; ++k) {
-      const uint16_t* row = Ut + (size_t)k * ld;
-      u32x4_t a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-      if (ok0) a = ld16(row + tc0);
-      if (ok1) b = ld16(row + tc1);
-      const f32x4_t pq0 = *reinterpret_cast<const f32x4_t*>(pf + k * 8);
-      const f32x4_t pq1 = *reinterpret_cast<const f32x4_t*>(pf + k * 8 + 4);
-      const float pp[8] = {pq0[0], pq0[1], pq0[2], pq0[3], pq1[0], pq1[1], pq1[2], pq1[3]};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float a0 = bf_lo(a[w]), a1 = bf_hi(a[w]);
-        const float b0 = bf_lo(b[w]), b1 = bf_hi(b[w]);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          s[2 * w][h] = fmaf(a0, pp[h], s[2 * w][h]);
-          s[2 * w + 1][h] = fmaf(a1, pp[h], s[2 * w + 1][h]);
-          s[8 + 2 * w][h] = fmaf(b0, pp[h], s[8 + 2 * w][h]);
-          s[8 + 2 * w + 1][h] = fmaf(b1, pp[h], s[8 + 2 * w + 1][h]);
-        }
+    if (r > 0) {
+      u32x4_t A0[kRowsPerStep], B0[kRowsPerStep], A1[kRowsPerStep], B1[kRowsPerStep];
+      load_rows4(Ut, ld, 0, r, tq0, tq1, A0, B0);
+      for (int k0 = 0; k0 < r; k0 += 2 * kRowsPerStep) {
+        if (k0 + kRowsPerStep < r) load_rows4(Ut, ld, k0 + kRowsPerStep, r, tq0, tq1, A1, B1);
+        score_rows4<G>(A0, B0, k0, r, pf, s);
+        if (k0 + 2 * kRowsPerStep < r) load_rows4(Ut, ld, k0 + 2 * kRowsPerStep, r, tq0, tq1, A0, B0);
+        if (k0 + kRowsPerStep < r) score_rows4<G>(A1, B1, k0 + kRowsPerStep, r, pf, s);
       }
     }
 #pragma unroll
@@ -153,10 +187,13 @@ __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* U
       for (int gi = 0; gi * R < rv; ++gi) zl[gi * 64 + lane] *= al;
     }
 
-    // ---- z = e^T U'  (value factor), reduced per group of R rows
+    // ---- z = e^T U'  (value factor), reduced per group of R rows.  Rows past
+    // rv are loaded clamped to rv-1 and land in slots that are never read.
+    // Masks zero the U' elements of tokens past the block end (padding may
+    // hold NaN); a lane with no valid token has e = 0 and a finite chunk.
     u32x4_t mask0 = {~0u, ~0u, ~0u, ~0u}, mask1 = {~0u, ~0u, ~0u, ~0u};
     if (RAGGED) {
-      const int n0 = T - tc0, n1 = T - tc1;
+      const int n0 = ok0 ? T - tc0 : 0, n1 = ok1 ? T - tc1 : 0;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         mask0[w] = (2 * w < n0 ? 0xffffu : 0u) | (2 * w + 1 < n0 ? 0xffff0000u : 0u);
@@ -165,30 +202,29 @@ __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* U
     }
 #pragma unroll 1
     for (int gi = 0; gi * R < rv; ++gi) {
-      {
-        float acc[64];
+      u32x4_t U0[R], U1[R];
 #pragma unroll
-        for (int x = 0; x < 64; ++x) acc[x] = 0.f;
-#pragma unroll
-        for (int rho = 0; rho < R; ++rho) {
-          const int kp = gi * R + rho;
-          if (kp < rv) {
-            const uint16_t* row = Upt + (size_t)kp * ld;
-            u32x4_t u0 = {0, 0, 0, 0}, u1 = {0, 0, 0, 0};
-            if (ok0) u0 = ld16(row + tc0);
-            if (ok1) u1 = ld16(row + tc1);
-            if (RAGGED) { u0 &= mask0; u1 &= mask1; }
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-#pragma unroll
-              for (int h = 0; h < G; ++h) {
-                acc[rho * G + h] = dot2bf(u0[w], e2[0][w][h], acc[rho * G + h]);
-                acc[rho * G + h] = dot2bf(u1[w], e2[1][w][h], acc[rho * G + h]);
-              }
-          }
-        }
-        zl[gi * 64 + lane] += reduce_transpose64(acc, lane);
+      for (int rho = 0; rho < R; ++rho) {
+        const uint16_t* row = Upt + (size_t)min(gi * R + rho, rv - 1) * ld;
+        U0[rho] = ld16(row + tq0);
+        U1[rho] = ld16(row + tq1);
       }
+      float acc[64];
+#pragma unroll
+      for (int x = 0; x < 64; ++x) acc[x] = 0.f;
+#pragma unroll
+      for (int rho = 0; rho < R; ++rho) {
+        u32x4_t u0 = U0[rho], u1 = U1[rho];
+        if (RAGGED) { u0 &= mask0; u1 &= mask1; }
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            acc[rho * G + h] = dot2bf(u0[w], e2[0][w][h], acc[rho * G + h]);
+            acc[rho * G + h] = dot2bf(u1[w], e2[1][w][h], acc[rho * G + h]);
+          }
+      }
+      zl[gi * 64 + lane] += reduce_transpose64(acc, lane);
     }
   }
 }
@@ -210,44 +246,50 @@ __device__ __forceinline__ void block_unit_bf16(const DecodeParams& p, int i, in
   const uint16_t* qh = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)i * p.n_q_heads + g * G) * D;
 
   float* pf = reinterpret_cast<float*>(lds);
-  bf16_project_q<D, G>(W, qh, r, p.scale_log2, pf, lane);
-  __syncthreads();
-
+  if (r > 0) bf16_project_q<D, G>(W, qh, r, p.scale_log2, pf, lane);
   // z partial sums live in LDS: zl[gi*64 + l] = slot l of row group gi
   float* zl = reinterpret_cast<float*>(lds + 1024);
+  for (int gi = 0; gi < NG; ++gi) zl[gi * 64 + lane] = 0.f;
+  __syncthreads();
+
   float m_run[G], l_run[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) { m_run[h] = kNegInf; l_run[h] = 0.f; }
-  for (int gi = 0; gi < NG; ++gi) zl[gi * 64 + lane] = 0.f;
 
   if (T & 7)
     bf16_tiles<D, G, true>(Ut, Upt, ld, T, r, rv, pf, m_run, l_run, zl, lane);
   else
     bf16_tiles<D, G, false>(Ut, Upt, ld, T, r, rv, pf, m_run, l_run, zl, lane);
 
-  // ---- o~ = z W'
+  // ---- o~ = z W'; eight rows of W' in flight per step
   __syncthreads();
   float o[G][JPL];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int jj = 0; jj < JPL; ++jj) o[h][jj] = 0.f;
-  for (int kp = 0; kp < rv; ++kp) {
-    const int gi = kp / R, rho = kp - gi * R;
-    const float* zp = zl + gi * 64 + rho * G;
-    float wv[JPL];
-    if (JPL == 2) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(Wp + (size_t)kp * D + 2 * lane);
-      wv[0] = bf_lo(w);
-      wv[JPL - 1] = bf_hi(w);
-    } else {
-      wv[0] = __uint_as_float((uint32_t)Wp[(size_t)kp * D + lane] << 16);
+  for (int k0 = 0; k0 < rv; k0 += 8) {
+    uint32_t wraw[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint16_t* wrow = Wp + (size_t)min(k0 + j, rv - 1) * D;
+      wraw[j] = (JPL == 2) ? *reinterpret_cast<const uint32_t*>(wrow + 2 * lane)
+                           : (uint32_t)wrow[lane] << 16;
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float z = zp[h];
+    for (int j = 0; j < 8; ++j) {
+      const int kp = k0 + j;
+      if (kp < rv) {
+        const int gi = kp / R, rho = kp - gi * R;
+        const float* zp = zl + gi * 64 + rho * G;
+        const float wv[2] = {bf_lo(wraw[j]), bf_hi(wraw[j])};
 #pragma unroll
-      for (int jj = 0; jj < JPL; ++jj) o[h][jj] = fmaf(z, wv[jj], o[h][jj]);
+        for (int h = 0; h < G; ++h) {
+          const float z = zp[h];
+#pragma unroll
+          for (int jj = 0; jj < JPL; ++jj) o[h][jj] = fmaf(z, wv[JPL == 2 ? jj : 1], o[h][jj]);
+        }
+      }
     }
   }
 
@@ -480,12 +522,13 @@ __device__ __forceinline__ void tail_unit(const DecodeParams& p, int i, int g, i
     float s[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) s[h] = 0.f;
+    const int tk = min(t, L - 1);   // lanes past the end re-read the last token (masked)
     if (DT == MILO_BF16) {
-      const uint16_t* K = reinterpret_cast<const uint16_t*>(p.k_tail) + kv_off;
+      const uint16_t* K = reinterpret_cast<const uint16_t*>(p.k_tail) + kv_off + (size_t)tk * D;
       const uint16_t* qh = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)i * p.n_q_heads + g * G) * D;
+#pragma unroll 4
       for (int jc = 0; jc < D / 8; ++jc) {
-        u32x4_t kv = {0, 0, 0, 0};
-        if (valid) kv = ld16(K + (size_t)t * D + jc * 8);
+        const u32x4_t kv = ld16(K + jc * 8);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           const u32x4_t qv = ld16(qh + h * D + jc * 8);
@@ -494,11 +537,11 @@ __device__ __forceinline__ void tail_unit(const DecodeParams& p, int i, int g, i
         }
       }
     } else {
-      const float* K = reinterpret_cast<const float*>(p.k_tail) + kv_off;
+      const float* K = reinterpret_cast<const float*>(p.k_tail) + kv_off + (size_t)tk * D;
       const float* qh = reinterpret_cast<const float*>(p.q) + ((int64_t)i * p.n_q_heads + g * G) * D;
+#pragma unroll 4
       for (int jc = 0; jc < D / 4; ++jc) {
-        f32x4_t kv = {0.f, 0.f, 0.f, 0.f};
-        if (valid) kv = ld16f(K + (size_t)t * D + jc * 4);
+        const f32x4_t kv = ld16f(K + jc * 4);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           const f32x4_t qv = ld16f(qh + h * D + jc * 4);
@@ -522,28 +565,38 @@ __device__ __forceinline__ void tail_unit(const DecodeParams& p, int i, int g, i
       for (int jj = 0; jj < JPL; ++jj) o[h][jj] *= alpha[h];
     }
     __syncthreads();
+    // o~ += e^T V over the tile, eight token rows of V in flight per step
     const int nt = min(64, L - t0);
-    for (int tt = 0; tt < nt; ++tt) {
-      float vv[JPL];
-      if (DT == MILO_BF16) {
-        const uint16_t* V = reinterpret_cast<const uint16_t*>(p.v_tail) + kv_off + (size_t)(t0 + tt) * D;
-        if (JPL == 2) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(V + 2 * lane);
-          vv[0] = bf_lo(w);
-          vv[JPL - 1] = bf_hi(w);
-        } else {
-          vv[0] = __uint_as_float((uint32_t)V[lane] << 16);
-        }
-      } else {
-        const float* V = reinterpret_cast<const float*>(p.v_tail) + kv_off + (size_t)(t0 + tt) * D;
+    for (int tt0 = 0; tt0 < nt; tt0 += 8) {
+      float vv[8][JPL];
 #pragma unroll
-        for (int jj = 0; jj < JPL; ++jj) vv[jj] = V[lane * JPL + jj];
+      for (int j = 0; j < 8; ++j) {
+        const size_t row = kv_off + (size_t)(t0 + min(tt0 + j, nt - 1)) * D;
+        if (DT == MILO_BF16) {
+          const uint16_t* V = reinterpret_cast<const uint16_t*>(p.v_tail) + row;
+          if (JPL == 2) {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(V + 2 * lane);
+            vv[j][0] = bf_lo(w);
+            vv[j][JPL - 1] = bf_hi(w);
+          } else {
+            vv[j][0] = __uint_as_float((uint32_t)V[lane] << 16);
+          }
+        } else {
+          const float* V = reinterpret_cast<const float*>(p.v_tail) + row;
+#pragma unroll
+          for (int jj = 0; jj < JPL; ++jj) vv[j][jj] = V[lane * JPL + jj];
+        }
       }
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float ev = el[tt * 8 + h];
+      for (int j = 0; j < 8; ++j) {
+        if (tt0 + j < nt) {
 #pragma unroll
-        for (int jj = 0; jj < JPL; ++jj) o[h][jj] = fmaf(ev, vv[jj], o[h][jj]);
+          for (int h = 0; h < G; ++h) {
+            const float ev = el[(tt0 + j) * 8 + h];
+#pragma unroll
+            for (int jj = 0; jj < JPL; ++jj) o[h][jj] = fmaf(ev, vv[j][jj], o[h][jj]);
+          }
+        }
       }
     }
     __syncthreads();
