@@ -103,9 +103,12 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen7b_64k")
     ap.add_argument("--variant", default="base")
+    ap.add_argument("--batch", type=int, default=0, help="override the workload's batch (sequences)")
+    ap.add_argument("--q-heads", type=int, default=0, help="override the query heads (group size)")
     ap.add_argument("--copies", type=int, default=2,
                     help="pool copies read in rotation so no step finds the last one's bytes in cache")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-plan", action="store_true", help="natural work-unit order (no schedule)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
@@ -138,6 +141,10 @@ def main(argv=None):
     lib = _lib.load()
 
     cfg = synth.get_config(args.workload)
+    if args.batch:
+        cfg = cfg.with_(batch=args.batch)
+    if args.q_heads:
+        cfg = cfg.with_(n_q_heads=args.q_heads)
     if cfg.path != "decode":
         raise SystemExit(f"{args.workload} is a {cfg.path} workload; bench.py times decode")
     t0 = time.time()
@@ -156,7 +163,7 @@ def main(argv=None):
     for pool in pools:
         a = ra.make_args(dc.q, pool, dc.blocks, dc.seq_blocks, dc.k_tail, dc.v_tail, dc.tail_len,
                          n_kv_heads=dc.n_kv_heads, scale=dc.scale, max_blocks=dc.max_blocks, out=out,
-                         lse=lse, workspace=ws)
+                         lse=lse, workspace=ws, unit_order=None if args.no_plan else dc.unit_order)
         argsets.append(a)
     stream = torch.cuda.current_stream().cuda_stream
     setup_s = time.time() - t0

@@ -117,6 +117,11 @@ typedef struct milo_attn_args {
   void* prof_events[2];        /* optional hipEvent_t pair: when both are set, the call
                                   records [0] before and [1] after its main attention
                                   kernel on the same stream (timing hook)                   */
+  const int32_t* unit_order;   /* optional device array: the order in which the decode
+                                  kernel takes its work units (see milo_attn_plan_decode);
+                                  NULL = natural order.  Must be a permutation of
+                                  [0, batch * n_kv_heads * (max_blocks_per_seq + 1)).
+                                  Only the decode path reads it.                            */
 } milo_attn_args;
 
 /* Workspace the given path needs for these arguments; 0 if the arguments are
@@ -131,6 +136,28 @@ milo_status milo_attn_decode(const milo_attn_args* args, void* hip_stream);
  * values are the last Q entries of the tail; query j sees every block token
  * and tail tokens l <= tail_len[i] - Q + j.  Writes out and lse. */
 milo_status milo_attn_chunk(const milo_attn_args* args, void* hip_stream);
+
+/*
+ * Host-side scheduler for the decode kernel.  Decode work unit
+ *     u = (i * n_kv_heads + g) * (max_blocks_per_seq + 1) + slot
+ * covers block slot `slot` of sequence i, KV head g (slot = max_blocks_per_seq
+ * is the dense tail).  Units differ in size by up to the ratio of their ranks,
+ * and one decode call runs about two units per wave slot of the GPU, so
+ * starting the largest first keeps the last units short (longest-processing-
+ * time-first).  The cost of a unit is its factor bytes, (r + r')(T + d), or
+ * 2 * tail_len * d for a tail unit.
+ *
+ * blocks, seq_blocks, tail_len are HOST copies of the device tables
+ * (tail_len may be NULL when tail_cap is 0);  order_out (host) receives
+ * batch * n_kv_heads * (max_blocks_per_seq + 1) unit indices, largest first,
+ * ties in natural order; empty slots come last.  The cache is static across
+ * decode steps, so the plan is computed once and copied to the device.
+ * Returns MILO_ERR_INVALID on null pointers or negative sizes.
+ */
+milo_status milo_attn_plan_decode(const milo_block* blocks, const int32_t* seq_blocks,
+                                  const int32_t* tail_len, int32_t batch, int32_t n_kv_heads,
+                                  int32_t max_blocks_per_seq, int32_t head_dim,
+                                  int32_t* order_out);
 
 /* Static description of a status code. */
 const char* milo_status_str(milo_status status);

@@ -52,7 +52,8 @@ def _ptr(t) -> Optional[int]:
 
 def make_args(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_kv_heads: int,
               scale: float, max_blocks: int, out=None, lse=None, workspace=None,
-              workspace_bytes: Optional[int] = None, prof_events=(None, None)) -> MiloAttnArgs:
+              workspace_bytes: Optional[int] = None, prof_events=(None, None),
+              unit_order=None) -> MiloAttnArgs:
     """Fill the C argument struct from device tensors (no checks: the library checks)."""
     B, Q, Hq, d = (int(x) for x in q.shape)
     cap = 0 if k_tail is None else int(k_tail.shape[2])
@@ -70,6 +71,7 @@ def make_args(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_kv_hea
                             (0 if workspace is None else workspace.numel() * workspace.element_size()))
     a.prof_events[0] = prof_events[0]
     a.prof_events[1] = prof_events[1]
+    a.unit_order = _ptr(unit_order)
     return a
 
 
@@ -79,7 +81,7 @@ def workspace_bytes(args: MiloAttnArgs, path: int) -> int:
 
 def _run(path: int, q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_kv_heads, scale,
          max_blocks, out=None, lse=None, workspace=None, stream=None, prof_events=(None, None),
-         want_lse=True) -> Tuple[object, object]:
+         unit_order=None, want_lse=True) -> Tuple[object, object]:
     import torch
     lib = _lib.load()
     B, Q, Hq, d = (int(x) for x in q.shape)
@@ -90,7 +92,7 @@ def _run(path: int, q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_
         lse = torch.empty((B, Q, Hq), dtype=torch.float32, device=dev)
     a = make_args(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, n_kv_heads=n_kv_heads,
                   scale=scale, max_blocks=max_blocks, out=out, lse=lse, workspace=workspace,
-                  prof_events=prof_events)
+                  prof_events=prof_events, unit_order=unit_order)
     if workspace is None:
         need = lib.milo_attn_workspace_bytes(ctypes.byref(a), path)
         if need == 0:
@@ -149,6 +151,7 @@ class DeviceCache:
         self.k_tail = dev(packed.k_tail, bf) if cap > 0 else None
         self.v_tail = dev(packed.v_tail, bf) if cap > 0 else None
         self.tail_len = dev(packed.tail_len) if cap > 0 else None
+        self.unit_order = dev(packed.unit_order) if packed.unit_order is not None else None
 
     def tensors(self):
         return (self.q, self.pool, self.blocks, self.seq_blocks, self.k_tail, self.v_tail,
@@ -156,6 +159,7 @@ class DeviceCache:
 
     def decode(self, **kw):
         kw.setdefault("scale", self.scale)
+        kw.setdefault("unit_order", self.unit_order)
         return decode(*self.tensors(), n_kv_heads=self.n_kv_heads, max_blocks=self.max_blocks, **kw)
 
     def chunk(self, **kw):

@@ -11,7 +11,7 @@ MILO_OK, MILO_ERR_INVALID, MILO_ERR_UNSUPPORTED, MILO_ERR_WORKSPACE, MILO_ERR_DE
 MILO_F32, MILO_BF16 = 0, 1
 MILO_PATH_DECODE, MILO_PATH_CHUNK = 0, 1
 EXPORTS = ("milo_attn_workspace_bytes", "milo_attn_decode", "milo_attn_chunk",
-           "milo_status_str", "milo_abi_version")
+           "milo_attn_plan_decode", "milo_status_str", "milo_abi_version")
 
 
 class MiloBlock(ctypes.Structure):
@@ -43,6 +43,7 @@ class MiloAttnArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("prof_events", ctypes.c_void_p * 2),
+        ("unit_order", ctypes.c_void_p),
     ]
 
 
@@ -63,6 +64,10 @@ def load() -> ctypes.CDLL:
         for fn in (lib.milo_attn_decode, lib.milo_attn_chunk):
             fn.argtypes = [ctypes.POINTER(MiloAttnArgs), ctypes.c_void_p]
             fn.restype = ctypes.c_int
+        lib.milo_attn_plan_decode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_void_p]
+        lib.milo_attn_plan_decode.restype = ctypes.c_int
         lib.milo_status_str.argtypes = [ctypes.c_int]
         lib.milo_status_str.restype = ctypes.c_char_p
         lib.milo_abi_version.argtypes = []

@@ -618,7 +618,8 @@ template <int D, int G, int DT>
 __global__ __launch_bounds__(64) void milo_decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
   const int S = p.max_blocks + 1;
-  const int unit = blockIdx.x;
+  const int unit = p.unit_order ? p.unit_order[blockIdx.x] : (int)blockIdx.x;
+  if ((unsigned)unit >= (unsigned)(p.batch * p.n_kv_heads * S)) return;   // not a unit index
   const int slot = unit % S;
   const int ig = unit / S;
   const int g = ig % p.n_kv_heads, i = ig / p.n_kv_heads;

@@ -26,6 +26,7 @@ struct DecodeParams {
   const void* v_tail;
   const int32_t* tail_len;
   Partials part;
+  const int32_t* unit_order;   // optional largest-first permutation of the units
   int32_t batch, n_q_heads, n_kv_heads, max_blocks, tail_cap;
   float scale_log2;   // scale * log2(e)
 };

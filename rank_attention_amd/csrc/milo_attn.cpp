@@ -4,8 +4,11 @@
 // global mutable state.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <numeric>
+#include <vector>
 
 #include "kernels.h"
 #include "milo_attn.h"
@@ -114,6 +117,7 @@ milo_status milo_attn_decode(const milo_attn_args* a, void* hip_stream) {
   p.max_blocks = a->max_blocks_per_seq;
   p.tail_cap = a->tail_cap;
   p.scale_log2 = a->scale * milo::kLog2eHost;
+  p.unit_order = a->unit_order;
 
   const bool timing = a->prof_events[0] && a->prof_events[1];
   if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[0]), stream) != hipSuccess)
@@ -142,6 +146,37 @@ milo_status milo_attn_decode(const milo_attn_args* a, void* hip_stream) {
 milo_status milo_attn_chunk(const milo_attn_args* a, void* hip_stream) {
   (void)hip_stream;
   return check_shape(a, MILO_PATH_CHUNK);
+}
+
+milo_status milo_attn_plan_decode(const milo_block* blocks, const int32_t* seq_blocks,
+                                  const int32_t* tail_len, int32_t batch, int32_t n_kv_heads,
+                                  int32_t max_blocks, int32_t head_dim, int32_t* order_out) {
+  if (batch < 0 || n_kv_heads < 1 || max_blocks < 0 || head_dim < 1) return MILO_ERR_INVALID;
+  if (batch > 0 && (!seq_blocks || !order_out)) return MILO_ERR_INVALID;
+  if (batch > 0 && max_blocks > 0 && !blocks) return MILO_ERR_INVALID;
+  const int64_t slots = (int64_t)max_blocks + 1;
+  const int64_t units = (int64_t)batch * n_kv_heads * slots;
+  std::vector<int64_t> cost((size_t)units, -1);   // -1: empty slot
+  for (int32_t i = 0; i < batch; ++i) {
+    const int32_t b0 = seq_blocks[i];
+    const int32_t nb = std::min(std::max(seq_blocks[i + 1] - b0, 0), max_blocks);
+    for (int32_t g = 0; g < n_kv_heads; ++g) {
+      const int64_t base = ((int64_t)i * n_kv_heads + g) * slots;
+      for (int32_t s = 0; s < nb; ++s) {
+        const milo_block& b = blocks[b0 + s];
+        const int64_t r = std::max(b.rank_k, 0) + std::max(b.rank_v, 0);
+        cost[(size_t)(base + s)] = r * ((int64_t)std::max(b.n_tok, 0) + head_dim);
+      }
+      const int64_t L = tail_len ? std::max(tail_len[i], 0) : 0;
+      cost[(size_t)(base + max_blocks)] = 2 * L * head_dim;
+    }
+  }
+  std::vector<int32_t> idx((size_t)units);
+  std::iota(idx.begin(), idx.end(), 0);
+  std::stable_sort(idx.begin(), idx.end(),
+                   [&](int32_t x, int32_t y) { return cost[(size_t)x] > cost[(size_t)y]; });
+  std::copy(idx.begin(), idx.end(), order_out);
+  return MILO_OK;
 }
 
 const char* milo_status_str(milo_status s) {

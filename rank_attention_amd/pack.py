@@ -33,6 +33,7 @@ class PackedCache:
     k_tail: np.ndarray         # [B][Hkv][cap][d]
     v_tail: np.ndarray
     tail_len: np.ndarray       # int32 [B]
+    unit_order: Optional[np.ndarray] = None   # int32 decode schedule (largest first)
 
 
 def _nan(dtype: str):
@@ -40,13 +41,15 @@ def _nan(dtype: str):
 
 
 def pack(wl, gap: int = 8, shuffle_pool: Optional[int] = None,
-         max_blocks: Optional[int] = None, poison_tail: bool = True) -> PackedCache:
+         max_blocks: Optional[int] = None, poison_tail: bool = True,
+         plan: bool = True) -> PackedCache:
     """Pack a ``synth`` workload.
 
     gap           NaN elements left between consecutive blocks (multiple of 8)
     shuffle_pool  seed: place blocks in the pool in a random order (the CSR
                   order is unchanged), to exercise arbitrary offsets
     max_blocks    host bound for the grid (default: the largest count)
+    plan          compute the largest-first decode schedule (unit_order)
     """
     assert gap % 8 == 0
     d, hkv = wl.cfg.head_dim, wl.cfg.n_kv_heads
@@ -95,6 +98,27 @@ def pack(wl, gap: int = 8, shuffle_pool: Optional[int] = None,
     if max_blocks is not None:
         assert max_blocks >= mb
         mb = max_blocks
+    tl = np.asarray(wl.tail_len, np.int32)
+    order = plan_decode(desc, seq_blocks, tl if kt.shape[2] > 0 else None, hkv, mb, d) if plan else None
     return PackedCache(dtype=wl.dtype, head_dim=d, n_kv_heads=hkv, pool=pool, blocks=desc,
                        seq_blocks=seq_blocks, max_blocks=mb, q=np.ascontiguousarray(wl.q),
-                       k_tail=kt, v_tail=vt, tail_len=np.asarray(wl.tail_len, np.int32))
+                       k_tail=kt, v_tail=vt, tail_len=tl, unit_order=order)
+
+
+def plan_decode(blocks: np.ndarray, seq_blocks: np.ndarray, tail_len, n_kv_heads: int,
+                max_blocks: int, head_dim: int) -> np.ndarray:
+    """Largest-first decode schedule from the library's host-side planner."""
+    import ctypes
+    from . import _lib
+    lib = _lib.load()
+    B = len(seq_blocks) - 1
+    out = np.empty(B * n_kv_heads * (max_blocks + 1), np.int32)
+    blocks = np.ascontiguousarray(blocks)
+    sb = np.ascontiguousarray(seq_blocks, np.int32)
+    tl = None if tail_len is None else np.ascontiguousarray(tail_len, np.int32)
+    rc = lib.milo_attn_plan_decode(blocks.ctypes.data if len(blocks) else None, sb.ctypes.data,
+                                   None if tl is None else tl.ctypes.data, B, n_kv_heads,
+                                   max_blocks, head_dim, out.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"milo_attn_plan_decode failed ({rc})")
+    return out

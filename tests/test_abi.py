@@ -32,9 +32,9 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_struct_size():
     assert ra.abi_version() == 1
-    # 7 int32 + float, 4 pointers, 2 int32, 6 pointers, size_t, 2 pointers; the
+    # 7 int32 + float, 4 pointers, 2 int32, 6 pointers, size_t, 3 pointers; the
     # C side agrees, or the batch-0 call below would fail its struct_size check
-    assert ctypes.sizeof(_lib.MiloAttnArgs) == 8 * 4 + 4 * 8 + 2 * 4 + 6 * 8 + 8 + 2 * 8
+    assert ctypes.sizeof(_lib.MiloAttnArgs) == 8 * 4 + 4 * 8 + 2 * 4 + 6 * 8 + 8 + 3 * 8
     assert ctypes.sizeof(_lib.MiloBlock) == 24 == ra.BLOCK_DTYPE.itemsize
 
 
@@ -135,3 +135,15 @@ def test_python_binding_raises_without_a_built_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load()
+
+
+def test_plan_rejects_bad_arguments():
+    lib = _lib.load()
+    out = (ctypes.c_int32 * 8)()
+    sb = (ctypes.c_int32 * 2)(0, 0)
+    assert lib.milo_attn_plan_decode(None, sb, None, -1, 1, 0, 64, out) == _lib.MILO_ERR_INVALID
+    assert lib.milo_attn_plan_decode(None, None, None, 1, 1, 0, 64, out) == _lib.MILO_ERR_INVALID
+    assert lib.milo_attn_plan_decode(None, sb, None, 1, 1, 2, 64, out) == _lib.MILO_ERR_INVALID
+    assert lib.milo_attn_plan_decode(None, sb, None, 1, 0, 0, 64, out) == _lib.MILO_ERR_INVALID
+    assert lib.milo_attn_plan_decode(None, sb, None, 1, 1, 0, 64, out) == _lib.MILO_OK
+    assert out[0] == 0

@@ -98,6 +98,15 @@ def test_full_and_extreme_ranks():
     compare(out, lse, ref_o, ref_l, sharp_gates=True, name="rank_extremes")
 
 
+def test_schedule_does_not_change_results():
+    """The largest-first unit order only changes when units run."""
+    cfg = synth.get_config("qwen7b_64k").with_(batch=3, n_blocks=6)
+    wl = synth.make_workload(cfg, variant="sharp", n_blocks=[6, 1, 4], tail_len=[256, 3, 0])
+    o1, l1 = run_hip(wl, plan=True)
+    o2, l2 = run_hip(wl, plan=False)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
 def test_deterministic_and_bounded_writes():
     import torch
     import rank_attention_amd as ra

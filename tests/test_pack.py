@@ -56,3 +56,32 @@ def test_f32_pool():
     ut, w, upt, wp, T = unpack_block(pc, 3, 0)
     np.testing.assert_array_equal(ut[:, :T], wl.blocks[0][3].ut[0])
     assert pc.max_blocks == 4
+
+
+def test_decode_plan_is_largest_first_permutation():
+    cfg = synth.get_config("qwen7b_64k").with_(batch=3, n_blocks=5)
+    wl = synth.make_workload(cfg, n_blocks=[5, 2, 0], tail_len=[256, 0, 17])
+    pc = ra.pack(wl, max_blocks=6)
+    order = pc.unit_order
+    S = pc.max_blocks + 1
+    units = cfg.batch * cfg.n_kv_heads * S
+    assert sorted(order.tolist()) == list(range(units))
+    d = cfg.head_dim
+
+    def cost(u):
+        i, rest = divmod(u, cfg.n_kv_heads * S)
+        g, slot = divmod(rest, S)
+        nb = int(pc.seq_blocks[i + 1] - pc.seq_blocks[i])
+        if slot == pc.max_blocks:
+            return 2 * int(pc.tail_len[i]) * d
+        if slot >= nb:
+            return -1
+        b = pc.blocks[pc.seq_blocks[i] + slot]
+        return (int(b["rank_k"]) + int(b["rank_v"])) * (int(b["n_tok"]) + d)
+
+    costs = [cost(int(u)) for u in order]
+    assert costs == sorted(costs, reverse=True)
+    # ties keep the natural order
+    for a, b in zip(order, order[1:]):
+        if cost(int(a)) == cost(int(b)):
+            assert a < b
