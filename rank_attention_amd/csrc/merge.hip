@@ -6,7 +6,7 @@
 // The softmax over the union of the units' tokens is then
 //   M = max_u m_u,  l = sum_u l_u 2^(m_u - M),  out = sum_u o~_u 2^(m_u - M) / l,
 //   lse = (M + log2 l) ln 2.
-// One wave per query row walks the row's units with that running rescale.
+// Each query row is folded by four waves with that running rescale.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -16,13 +16,19 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
-constexpr int kSlotChunk = 256;
+constexpr int kMergeWaves = 4;   // waves per query row
+constexpr int kMergeBatch = 8;   // slots whose loads one wave issues together
 
+// One workgroup of four waves per query row.  Wave w folds the slots
+// s = w, w+4, ... into a running (M, l, o) in batches of eight slots, all of
+// whose loads are issued before any is used; the four waves' results are
+// then combined through LDS.
 template <int D>
-__global__ __launch_bounds__(64) void milo_merge_kernel(MergeParams p) {
+__global__ __launch_bounds__(64 * kMergeWaves) void milo_merge_kernel(MergeParams p) {
   constexpr int JPL = D / 64;
-  __shared__ float wsh[kSlotChunk];
-  const int lane = threadIdx.x;
+  __shared__ float sh_m[kMergeWaves], sh_l[kMergeWaves];
+  __shared__ __attribute__((aligned(16))) float sh_o[kMergeWaves][D];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.x;  // (i * q_len + j) * n_q_heads + h
   const int h = row % p.n_q_heads;
   const int ij = row / p.n_q_heads;
@@ -33,63 +39,64 @@ __global__ __launch_bounds__(64) void milo_merge_kernel(MergeParams p) {
   const size_t rec0 = (size_t)(i * p.n_kv_heads + g) * p.slots * p.rows_per_unit + j * G + hl;
   const size_t rstride = p.rows_per_unit;
 
-  // pass 1: global max over the valid slots (lanes stride over slots)
-  float M = kNegInf;
-  for (int s = lane; s < p.slots; s += 64) {
-    const bool valid = (s == p.tail_slot) || (s < nb);
-    if (valid) {
-      const size_t rec = rec0 + (size_t)s * rstride;
-      const float lu = p.part.ml[rec * 2 + 1];
-      if (lu > 0.f) M = fmaxf(M, p.part.ml[rec * 2 + 0]);
-    }
-  }
-  M = wave_max(M);
-
-  // pass 2: weights 2^(m_u - M) per slot through LDS, then o = sum w_u o~_u
-  float l = 0.f, o[JPL];
+  float M = kNegInf, l = 0.f, o[JPL];
 #pragma unroll
   for (int jj = 0; jj < JPL; ++jj) o[jj] = 0.f;
-  for (int c0 = 0; c0 < p.slots; c0 += kSlotChunk) {
-    const int n = min(kSlotChunk, p.slots - c0);
-    for (int k = lane; k < n; k += 64) {
-      const int s = c0 + k;
-      float w = 0.f;
-      if ((s == p.tail_slot) || (s < nb)) {
-        const size_t rec = rec0 + (size_t)s * rstride;
-        const float lu = p.part.ml[rec * 2 + 1];
-        if (lu > 0.f) {
-          w = fast_exp2(p.part.ml[rec * 2 + 0] - M);
-          l += lu * w;
-        }
-      }
-      wsh[k] = w;
+  for (int s0 = wave; s0 < p.slots; s0 += kMergeWaves * kMergeBatch) {
+    float mu[kMergeBatch], lu[kMergeBatch], ou[kMergeBatch][JPL];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int s = s0 + u * kMergeWaves;
+      const bool valid = s < p.slots && ((s == p.tail_slot) || (s < nb));
+      const size_t rec = rec0 + (size_t)(valid ? s : 0) * rstride;
+      mu[u] = valid ? p.part.ml[rec * 2 + 0] : kNegInf;
+      lu[u] = valid ? p.part.ml[rec * 2 + 1] : 0.f;
+#pragma unroll
+      for (int jj = 0; jj < JPL; ++jj) ou[u][jj] = valid ? p.part.o[rec * D + lane * JPL + jj] : 0.f;
     }
-    __syncthreads();
-    for (int k0 = 0; k0 < n; k0 += 8) {
-      float ov[8][JPL];
+    float bm = M;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int k = min(k0 + u, n - 1);
-        const float* ou = p.part.o + (rec0 + (size_t)(c0 + k) * rstride) * D + lane * JPL;
-        const bool take = (k0 + u < n) && wsh[k] > 0.f;
+    for (int u = 0; u < kMergeBatch; ++u)
+      if (lu[u] > 0.f) bm = fmaxf(bm, mu[u]);
+    if (bm == kNegInf) continue;   // nothing valid yet
+    const float a = fast_exp2(M - bm);
+    l *= a;
 #pragma unroll
-        for (int jj = 0; jj < JPL; ++jj) ov[u][jj] = take ? ou[jj] : 0.f;
-      }
+    for (int jj = 0; jj < JPL; ++jj) o[jj] *= a;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float w = (k0 + u < n) ? wsh[min(k0 + u, n - 1)] : 0.f;
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const float w = lu[u] > 0.f ? fast_exp2(mu[u] - bm) : 0.f;
+      l += lu[u] * w;
 #pragma unroll
-        for (int jj = 0; jj < JPL; ++jj) o[jj] = fmaf(w, ov[u][jj], o[jj]);
-      }
+      for (int jj = 0; jj < JPL; ++jj) o[jj] = fmaf(w, ou[u][jj], o[jj]);
     }
-    __syncthreads();
+    M = bm;
   }
-  l = wave_sum(l);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (lane == 0) { sh_m[wave] = M; sh_l[wave] = l; }
+#pragma unroll
+  for (int jj = 0; jj < JPL; ++jj) sh_o[wave][lane * JPL + jj] = o[jj];
+  __syncthreads();
+  if (wave != 0) return;
+  float Mt = kNegInf;
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) Mt = fmaxf(Mt, sh_m[w]);
+  float lt = 0.f, ot[JPL];
+#pragma unroll
+  for (int jj = 0; jj < JPL; ++jj) ot[jj] = 0.f;
+  if (Mt != kNegInf) {
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) {
+      const float sc = fast_exp2(sh_m[w] - Mt);
+      lt += sh_l[w] * sc;
+#pragma unroll
+      for (int jj = 0; jj < JPL; ++jj) ot[jj] = fmaf(sc, sh_o[w][lane * JPL + jj], ot[jj]);
+    }
+  }
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
   float* op = p.out + (size_t)row * D + lane * JPL;
 #pragma unroll
-  for (int jj = 0; jj < JPL; ++jj) op[jj] = o[jj] * inv;
-  if (p.lse && lane == 0) p.lse[row] = l > 0.f ? (M + __log2f(l)) * kLn2 : kNegInf;
+  for (int jj = 0; jj < JPL; ++jj) op[jj] = ot[jj] * inv;
+  if (p.lse && lane == 0) p.lse[row] = lt > 0.f ? (Mt + __log2f(lt)) * kLn2 : kNegInf;
 }
 
 }  // namespace
@@ -97,7 +104,7 @@ __global__ __launch_bounds__(64) void milo_merge_kernel(MergeParams p) {
 hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t s) {
   const int64_t rows = (int64_t)p.batch * p.q_len * p.n_q_heads;
   if (rows == 0) return hipSuccess;
-  const dim3 grid((unsigned)rows), block(64);
+  const dim3 grid((unsigned)rows), block(64 * kMergeWaves);
   if (head_dim == 128)
     hipLaunchKernelGGL(milo_merge_kernel<128>, grid, block, 0, s, p);
   else if (head_dim == 64)
