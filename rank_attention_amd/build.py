@@ -31,6 +31,7 @@ UNITS = [
     ("decode.hip", ["-DMILO_INST_DT=1", "-DMILO_INST_D=64"], "decode_bf16_64.o"),
     ("decode.hip", ["-DMILO_INST_DT=1", "-DMILO_INST_D=128"], "decode_bf16_128.o"),
     ("merge.hip", [], "merge.o"),
+    ("chunk.hip", [], "chunk.o"),
     ("milo_attn.cpp", [], "milo_attn.o"),
 ]
 

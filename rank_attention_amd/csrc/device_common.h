@@ -22,6 +22,18 @@ __device__ __forceinline__ f32x4_t ld16f(const void* p) {
   return *reinterpret_cast<const f32x4_t*>(p);
 }
 
+// Raw buffer resource over [base, base + bytes): loads at offsets past the end
+// return zeros instead of faulting.  The third dword selects the 32-bit data
+// format required for untyped loads on this ISA.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16-byte load at byte offset voff (per lane) + soff (wave-uniform).
+__device__ __forceinline__ u32x4_t bld16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
 // d = a.lo*b.lo + a.hi*b.hi + c, bf16 pairs, fp32 accumulate (exact products).
 __device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),

@@ -31,15 +31,32 @@ struct DecodeParams {
   float scale_log2;   // scale * log2(e)
 };
 
+struct ChunkParams {
+  const void* q;
+  const void* pool;
+  const milo_block* blocks;
+  const int32_t* seq_blocks;
+  const void* k_tail;
+  const void* v_tail;
+  const int32_t* tail_len;
+  Partials part;
+  int32_t batch, q_len, n_q_heads, n_kv_heads, max_blocks, tail_cap;
+  int32_t n_qtiles;          // tiles of 128 query rows over q_len * group rows
+  int32_t n_ranges;          // block ranges per (sequence, KV head); slot n_ranges = tail
+  int32_t blocks_per_range;
+  float scale_log2;
+};
+
 struct MergeParams {
   Partials part;
   const int32_t* seq_blocks;
   float* out;
   float* lse;
   int32_t batch, q_len, n_q_heads, n_kv_heads, max_blocks;
-  int32_t slots;          // work-unit slots per (sequence, KV head)
-  int32_t rows_per_unit;  // query rows stored per unit slot (q_len * group)
-  int32_t tail_slot;      // slot of the dense-tail unit
+  int32_t slots;            // work-unit slots per (sequence, KV head)
+  int32_t rows_per_unit;    // query rows stored per unit slot (q_len * group)
+  int32_t tail_slot;        // slot of the dense-tail unit
+  int32_t blocks_per_slot;  // slot s < tail_slot holds blocks [s*bps, (s+1)*bps)
 };
 
 // Work units of the decode kernel: one per (sequence, KV head, block slot),
@@ -63,5 +80,6 @@ inline hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, 
   return hipErrorInvalidValue;
 }
 hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t s);
+hipError_t launch_chunk(const ChunkParams& p, int group, hipStream_t s);
 
 }  // namespace milo

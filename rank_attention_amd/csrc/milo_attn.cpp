@@ -39,8 +39,30 @@ milo_status check_shape(const milo_attn_args* a, int32_t path) {
   if (a->head_dim != 64 && a->head_dim != 128) return MILO_ERR_UNSUPPORTED;
   const int group = a->n_q_heads / a->n_kv_heads;
   if (group > 8) return MILO_ERR_UNSUPPORTED;
-  if (path == MILO_PATH_CHUNK) return MILO_ERR_UNSUPPORTED;  // chunk kernel not built yet
+  // the MFMA chunk kernel is built for bf16 storage and head_dim 128
+  if (path == MILO_PATH_CHUNK && (a->dtype != MILO_BF16 || a->head_dim != 128)) return MILO_ERR_UNSUPPORTED;
   return MILO_OK;
+}
+
+constexpr int kChunkRowsPerTile = 128;   // query rows per chunk workgroup
+constexpr int kChunkTargetUnits = 1024;  // aim for >= 4 workgroups per CU
+
+struct ChunkSplit {
+  int32_t n_qtiles, n_ranges, blocks_per_range;
+};
+
+// Split each (sequence, KV head) into 128-row query tiles and block ranges
+// so that the grid has about kChunkTargetUnits workgroups.
+ChunkSplit chunk_split(const milo_attn_args* a) {
+  ChunkSplit c{};
+  const int64_t rows = (int64_t)a->q_len * (a->n_q_heads / a->n_kv_heads);
+  c.n_qtiles = (int32_t)((rows + kChunkRowsPerTile - 1) / kChunkRowsPerTile);
+  const int64_t base = std::max<int64_t>(1, (int64_t)a->batch * a->n_kv_heads * c.n_qtiles);
+  const int32_t mb = std::max(a->max_blocks_per_seq, 1);
+  int32_t nr = (int32_t)std::min<int64_t>(mb, std::max<int64_t>(1, (kChunkTargetUnits + base - 1) / base));
+  c.blocks_per_range = (mb + nr - 1) / nr;
+  c.n_ranges = (mb + c.blocks_per_range - 1) / c.blocks_per_range;
+  return c;
 }
 
 struct Layout {
@@ -50,10 +72,10 @@ struct Layout {
   int32_t slots;
 };
 
-Layout layout_of(const milo_attn_args* a) {
+Layout layout_of(const milo_attn_args* a, int32_t path) {
   Layout L{};
   const int group = a->n_q_heads / a->n_kv_heads;
-  L.slots = a->max_blocks_per_seq + 1;
+  L.slots = path == MILO_PATH_CHUNK ? chunk_split(a).n_ranges + 1 : a->max_blocks_per_seq + 1;
   L.rows_per_unit = a->q_len * group;
   L.units = (int64_t)a->batch * a->n_kv_heads * L.slots;
   L.o_bytes = round_up((size_t)L.units * L.rows_per_unit * a->head_dim * sizeof(float), kWsAlign);
@@ -86,13 +108,13 @@ extern "C" {
 
 size_t milo_attn_workspace_bytes(const milo_attn_args* a, int32_t path) {
   if (check_shape(a, path) != MILO_OK) return 0;
-  return layout_of(a).total;
+  return layout_of(a, path).total;
 }
 
 milo_status milo_attn_decode(const milo_attn_args* a, void* hip_stream) {
   milo_status st = check_shape(a, MILO_PATH_DECODE);
   if (st != MILO_OK) return st;
-  const Layout L = layout_of(a);
+  const Layout L = layout_of(a, MILO_PATH_DECODE);
   st = check_pointers(a, L);
   if (st != MILO_OK) return st;
   if (a->batch == 0) return MILO_OK;
@@ -139,13 +161,68 @@ milo_status milo_attn_decode(const milo_attn_args* a, void* hip_stream) {
   m.slots = L.slots;
   m.rows_per_unit = L.rows_per_unit;
   m.tail_slot = a->max_blocks_per_seq;
+  m.blocks_per_slot = 1;
   if (milo::launch_merge(m, a->head_dim, stream) != hipSuccess) return MILO_ERR_DEVICE;
   return MILO_OK;
 }
 
 milo_status milo_attn_chunk(const milo_attn_args* a, void* hip_stream) {
-  (void)hip_stream;
-  return check_shape(a, MILO_PATH_CHUNK);
+  milo_status st = check_shape(a, MILO_PATH_CHUNK);
+  if (st != MILO_OK) return st;
+  const Layout L = layout_of(a, MILO_PATH_CHUNK);
+  st = check_pointers(a, L);
+  if (st != MILO_OK) return st;
+  if (a->batch == 0) return MILO_OK;
+
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  const int group = a->n_q_heads / a->n_kv_heads;
+  const ChunkSplit cs = chunk_split(a);
+  char* ws = static_cast<char*>(a->workspace);
+  Partials part{reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + L.o_bytes)};
+
+  milo::ChunkParams p{};
+  p.q = a->q;
+  p.pool = a->pool;
+  p.blocks = a->blocks;
+  p.seq_blocks = a->seq_blocks;
+  p.k_tail = a->k_tail;
+  p.v_tail = a->v_tail;
+  p.tail_len = a->tail_len;
+  p.part = part;
+  p.batch = a->batch;
+  p.q_len = a->q_len;
+  p.n_q_heads = a->n_q_heads;
+  p.n_kv_heads = a->n_kv_heads;
+  p.max_blocks = a->max_blocks_per_seq;
+  p.tail_cap = a->tail_cap;
+  p.n_qtiles = cs.n_qtiles;
+  p.n_ranges = cs.n_ranges;
+  p.blocks_per_range = cs.blocks_per_range;
+  p.scale_log2 = a->scale * milo::kLog2eHost;
+
+  const bool timing = a->prof_events[0] && a->prof_events[1];
+  if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[0]), stream) != hipSuccess)
+    return MILO_ERR_DEVICE;
+  if (milo::launch_chunk(p, group, stream) != hipSuccess) return MILO_ERR_DEVICE;
+  if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[1]), stream) != hipSuccess)
+    return MILO_ERR_DEVICE;
+
+  MergeParams m{};
+  m.part = part;
+  m.seq_blocks = a->seq_blocks;
+  m.out = a->out;
+  m.lse = a->lse;
+  m.batch = a->batch;
+  m.q_len = a->q_len;
+  m.n_q_heads = a->n_q_heads;
+  m.n_kv_heads = a->n_kv_heads;
+  m.max_blocks = a->max_blocks_per_seq;
+  m.slots = L.slots;
+  m.rows_per_unit = L.rows_per_unit;
+  m.tail_slot = cs.n_ranges;
+  m.blocks_per_slot = cs.blocks_per_range;
+  if (milo::launch_merge(m, a->head_dim, stream) != hipSuccess) return MILO_ERR_DEVICE;
+  return MILO_OK;
 }
 
 milo_status milo_attn_plan_decode(const milo_block* blocks, const int32_t* seq_blocks,
