@@ -1,11 +1,16 @@
 #!/usr/bin/env python3
-"""Decode-attention benchmark over a block-wise low-rank KV cache on one MI355X.
+"""Attention benchmark over a block-wise low-rank KV cache on one MI355X.
 
-One step = one decode call (split-K attention kernel + merge kernel) over the
-whole batch of one layer, inputs resident in HBM.  Prints one JSON line:
-context tokens/s for the step, the attention kernel's achieved HBM bandwidth
-on algorithmic bytes against the 8 TB/s peak (timed with HIP events on the
-launch stream), and the fp64 CPU oracle timed on a bounded sample.
+One step = one call of the attention path (split-K attention kernel + merge
+kernel) over the whole batch of one layer, inputs resident in HBM.  Prints one
+JSON line.
+
+Decode workloads (the default, qwen7b_64k): context tokens/s for the step and
+the attention kernel's achieved HBM bandwidth on algorithmic bytes against the
+8 TB/s peak.  Chunked-query workloads (qwen32b_chunk): query tokens/s and the
+kernel's algorithmic bf16 FLOP rate against the 2.5 PFLOP/s dense MFMA peak.
+Kernel time comes from HIP events recorded on the launch stream around the
+attention kernel alone; the fp64 CPU oracle is timed on a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen7b_64k]
 """
@@ -23,14 +28,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "low-rank-KV decode attn: context tokens/s and % of HBM peak (7B, 64k)"
+CHUNK_METRIC = "low-rank-KV chunked-query attn: query tokens/s and % of bf16 MFMA peak (32B, Q=256)"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["rank_attention_amd/csrc/decode.hip", "rank_attention_amd/csrc/device_common.h"]
+KERNEL_SOURCES = {
+    "decode": ["rank_attention_amd/csrc/decode.hip", "rank_attention_amd/csrc/device_common.h"],
+    "chunk": ["rank_attention_amd/csrc/chunk.hip", "rank_attention_amd/csrc/device_common.h"],
+}
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(path: str = "decode") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[path]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -65,16 +75,57 @@ class HipEvents:
         self.hip.hipEventDestroy(ctypes.c_void_p(ev))
 
 
-def traffic_from_profiles(workload: str):
+def traffic_from_profiles(workload: str, path: str = "decode"):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel sources; else None."""
-    path = os.path.join(PROFILES, f"decode_{workload}_traffic.json")
-    if not os.path.exists(path):
+    fn = os.path.join(PROFILES, f"{path}_{workload}_traffic.json")
+    if not os.path.exists(fn):
         return None
-    rec = json.load(open(path))
-    if rec.get("kernel_source_sha") != kernel_source_sha():
+    rec = json.load(open(fn))
+    if rec.get("kernel_source_sha") != kernel_source_sha(path):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def chunk_flops(wl) -> int:
+    """Algorithmic FLOPs of one chunked-query launch: per block and KV head
+    2*M*(r + r')*(T + d) for the four factor products (M = Q*G query rows),
+    and 4*d per visible (query row, tail token) pair of the causal tail."""
+    cfg = wl.cfg
+    G = cfg.n_q_heads // cfg.n_kv_heads
+    Q, d = cfg.q_len, cfg.head_dim
+    M = Q * G
+    total = 0
+    for i, seq in enumerate(wl.blocks):
+        for b in seq:
+            total += 2 * M * (b.rank_k + b.rank_v) * (b.n_tok + d) * cfg.n_kv_heads
+        L = int(wl.tail_len[i])
+        vis = sum(max(0, min(L, L - Q + j + 1)) for j in range(Q))
+        total += 4 * d * vis * G * cfg.n_kv_heads
+    return total
+
+
+def cpu_baseline_chunk(wl, seconds: float):
+    """fp64 oracle on sampled query positions (all heads) of sequence 0 of the
+    chunk workload, grown until `seconds` pass; reported per query token."""
+    import oracle
+    q, blocks, kt, vt, tl = oracle.logical_from_workload(wl, [0])
+    Q, Hq = wl.cfg.q_len, wl.cfg.n_q_heads
+    js, elapsed, n = [], 0.0, 1
+    order = [Q - 1 - (k * 37) % Q for k in range(Q)]
+    while elapsed < seconds and len(js) < Q:
+        new = order[len(js):len(js) + n]
+        sel = [(0, j, h) for j in new for h in range(Hq)]
+        t0 = time.perf_counter()
+        oracle.attend_logical(q, blocks, kt, vt, tl, wl.scale, sel=sel)
+        elapsed += time.perf_counter() - t0
+        js += new
+        n *= 2
+    return {"value": len(js) / elapsed, "unit": "query tokens/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{len(js)} of {Q} query positions x all {Hq} heads of sequence 0 "
+                      f"({sum(b.n_tok for b in wl.blocks[0]) + int(wl.tail_len[0])} context tokens), "
+                      f"fp64 reconstruct-then-attend, {elapsed:.1f} s"}
 
 
 def cpu_baseline(wl, seconds: float):
@@ -145,8 +196,9 @@ def main(argv=None):
         cfg = cfg.with_(batch=args.batch)
     if args.q_heads:
         cfg = cfg.with_(n_q_heads=args.q_heads)
-    if cfg.path != "decode":
-        raise SystemExit(f"{args.workload} is a {cfg.path} workload; bench.py times decode")
+    is_chunk = cfg.path == "chunk"
+    path_code = _lib.MILO_PATH_CHUNK if is_chunk else _lib.MILO_PATH_DECODE
+    entry = lib.milo_attn_chunk if is_chunk else lib.milo_attn_decode
     t0 = time.time()
     wl = synth.make_workload(cfg, variant=args.variant)
     pc = ra.pack(wl)
@@ -157,13 +209,14 @@ def main(argv=None):
     lse = torch.empty((B, Q, Hq), dtype=torch.float32, device="cuda:0")
     a0 = ra.make_args(*dc.tensors(), n_kv_heads=dc.n_kv_heads, scale=dc.scale, max_blocks=dc.max_blocks,
                       out=out, lse=lse)
-    need = lib.milo_attn_workspace_bytes(ctypes.byref(a0), _lib.MILO_PATH_DECODE)
+    need = lib.milo_attn_workspace_bytes(ctypes.byref(a0), path_code)
     ws = torch.empty(int(need), dtype=torch.uint8, device="cuda:0")
     argsets = []
     for pool in pools:
         a = ra.make_args(dc.q, pool, dc.blocks, dc.seq_blocks, dc.k_tail, dc.v_tail, dc.tail_len,
                          n_kv_heads=dc.n_kv_heads, scale=dc.scale, max_blocks=dc.max_blocks, out=out,
-                         lse=lse, workspace=ws, unit_order=None if args.no_plan else dc.unit_order)
+                         lse=lse, workspace=ws,
+                         unit_order=None if (args.no_plan or is_chunk) else dc.unit_order)
         argsets.append(a)
     stream = torch.cuda.current_stream().cuda_stream
     setup_s = time.time() - t0
@@ -176,9 +229,9 @@ def main(argv=None):
             a.prof_events[0], a.prof_events[1] = evs
         else:
             a.prof_events[0] = a.prof_events[1] = None
-        rc = lib.milo_attn_decode(ctypes.byref(a), ctypes.c_void_p(stream))
+        rc = entry(ctypes.byref(a), ctypes.c_void_p(stream))
         if rc != 0:
-            raise RuntimeError(f"milo_attn_decode failed: {ra.status_str(rc)}")
+            raise RuntimeError(f"milo_attn_{cfg.path} failed: {ra.status_str(rc)}")
 
     for k in range(args.warmup):
         step(k)
@@ -198,19 +251,33 @@ def main(argv=None):
         hip.destroy(b)
 
     ms_per_step = (t_end - t_start) * 1e3 / args.steps
-    ctx = wl.context_tokens()
-    alg_bytes = wl.factor_bytes() + wl.tail_bytes()
     kmean = sum(kern_ms) / len(kern_ms)
-    achieved = alg_bytes / (kmean * 1e-3) / 1e9
     kern_sorted = sorted(kern_ms)
-    print(f"[bench] attention kernel: mean {kmean * 1e3:.1f} us, median {kern_sorted[len(kern_sorted) // 2] * 1e3:.1f} us, "
-          f"min {kern_sorted[0] * 1e3:.1f} us; step {ms_per_step * 1e3:.1f} us; "
-          f"{achieved:.0f} GB/s on {alg_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
+    alg_bytes = wl.factor_bytes() + wl.tail_bytes()
+    if is_chunk:
+        flops = chunk_flops(wl)
+        achieved = flops / (kmean * 1e-3) / 1e12
+        peak, unit, bound = MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+        value, vunit, metric = B * Q / (ms_per_step * 1e-3), "query tokens/s", CHUNK_METRIC
+        kname = "milo_chunk_kernel"
+        print(f"[bench] attention kernel: mean {kmean * 1e3:.1f} us, median "
+              f"{kern_sorted[len(kern_sorted) // 2] * 1e3:.1f} us, min {kern_sorted[0] * 1e3:.1f} us; "
+              f"step {ms_per_step * 1e3:.1f} us; {achieved:.0f} TFLOP/s on {flops / 1e9:.1f} GFLOP, "
+              f"{alg_bytes / (kmean * 1e-3) / 1e9:.0f} GB/s of factor+tail bytes", file=sys.stderr, flush=True)
+    else:
+        achieved = alg_bytes / (kmean * 1e-3) / 1e9
+        peak, unit, bound = HBM_PEAK_GBS, "GB/s", "hbm"
+        value, vunit, metric = wl.context_tokens() / (ms_per_step * 1e-3), "context tokens/s", METRIC
+        kname = "milo_decode_kernel"
+        print(f"[bench] attention kernel: mean {kmean * 1e3:.1f} us, median "
+              f"{kern_sorted[len(kern_sorted) // 2] * 1e3:.1f} us, min {kern_sorted[0] * 1e3:.1f} us; "
+              f"step {ms_per_step * 1e3:.1f} us; {achieved:.0f} GB/s on {alg_bytes / 1e6:.1f} MB",
+              file=sys.stderr, flush=True)
 
     res = {
-        "metric": METRIC,
-        "value": ctx / (ms_per_step * 1e-3),
-        "unit": "context tokens/s",
+        "metric": metric,
+        "value": value,
+        "unit": vunit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -220,20 +287,23 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": cfg.name, "desc": cfg.desc, "batch": cfg.batch,
+        "config": {"workload": cfg.name, "desc": cfg.desc, "batch": cfg.batch, "q_len": cfg.q_len,
                    "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
                    "blocks_per_seq": cfg.n_blocks, "block_tokens": cfg.block_tokens,
-                   "tail_len": cfg.tail_len, "context_tokens_per_step": ctx,
+                   "tail_len": cfg.tail_len, "context_tokens_per_step": wl.context_tokens(),
                    "variant": args.variant, "pool_copies": len(pools)},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profiles(cfg.name),
-                     "kernel": "milo_decode_kernel", "kernel_us_mean": kmean * 1e3,
+        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak, "traffic": traffic_from_profiles(cfg.name, cfg.path),
+                     "kernel": kname, "kernel_us_mean": kmean * 1e3,
                      "algorithmic_bytes_per_launch": alg_bytes,
-                     "kernel_source_sha": kernel_source_sha()},
+                     "kernel_source_sha": kernel_source_sha(cfg.path)},
         "cpu_baseline": None,
     }
+    if is_chunk:
+        res["roofline"]["algorithmic_flops_per_launch"] = flops
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        res["cpu_baseline"] = (cpu_baseline_chunk(wl, args.cpu_seconds) if is_chunk
+                               else cpu_baseline(wl, args.cpu_seconds))
     print(json.dumps(res), flush=True)
     return 0
 
