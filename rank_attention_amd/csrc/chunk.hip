@@ -16,19 +16,33 @@
 // MFMA's operand straight from its accumulator registers: a 32x32 result
 // holds, in lane l, column l%32 and rows {8a + 4(l/32) + b}, which is exactly
 // an A/B operand whose K index runs over those rows.  The partner operand is
-// read with the same K permutation: rank-major U^T and row-major W' come from
-// LDS through ds_read_b64_tr_b16 (a 16-lane transpose read), U'^T rows are
-// read directly.  Every query row's softmax state lives in the lanes that own
+// read from LDS with the same K permutation: rank-major U^T and row-major W'
+// through ds_read_b64_tr_b16 (a 16-lane transpose read), U'^T rows with plain
+// 8-byte reads.  Every query row's softmax state lives in the lanes that own
 // its column, so rescaling is lane-local.
 //
-// Precision: P and Z are split into bf16 hi + lo parts (two MFMAs each), so
-// scores and the value projection keep ~16 mantissa bits; e = exp2(s - m) is
-// rounded to bf16 once (relative 2^-9 per weight, averaging out in the sum).
+// Work unit = one workgroup of four waves (one per SIMD): (sequence, KV head,
+// 128 query rows, block range); wave w owns rows 32w..32w+31 of the tile.
+// The last range slot is the dense causal tail.  Units write (o~, m, l)
+// partials that the merge kernel combines.  The query tiles that share a
+// block range are given consecutive workgroup slots on one XCD, so they run
+// together and read the range's factors from that XCD's L2.
 //
-// Work unit = one workgroup of four waves: (sequence, KV head, 128 query rows,
-// block range); wave w owns rows 32w..32w+31 of the tile.  The last range
-// slot is the dense causal tail.  Units write (o~, m, l) partials that the
-// merge kernel combines.
+// Per block: W and W' are staged in LDS and P^T is built from W and Q (Q
+// re-read from L2).  The block's token factors then pass through LDS in 64-token
+// tiles of U^T and U'^T, double buffered: the next tile's global loads are
+// issued before the current tile is computed and written to the other
+// buffer after it.  Within a tile both 32-token score tiles are issued on
+// the MFMA pipe before the first softmax, so exp2 work overlaps MFMA work.
+//
+// Softmax: the running max m enters the score MFMA as its initial
+// accumulator (-m), so the scores arrive relative to m.  m is raised only
+// when a score exceeds it by more than 2^8 (weights stay <= 256, exact
+// enough in fp32 and bf16); O, Z and l are rescaled only then.
+//
+// Precision: P is split into bf16 hi + lo parts (two MFMAs per score step),
+// so scores keep ~16 mantissa bits; e = exp2(s - m) and Z are rounded to
+// bf16 once each (relative 2^-9, averaging out over tokens and ranks).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -39,11 +53,18 @@ namespace {
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kD = 128;            // head_dim of this kernel
 constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 32;
-constexpr int kTT = 64;            // tokens per staged U^T tile
-constexpr int kUPitch = kTT + 8;   // LDS row pitch (elements) of the U^T tile
+constexpr int kTT = 64;            // tokens per staged tile
+constexpr int kUPitch = kTT + 8;   // LDS row pitch (elements) of the U^T tile (transposing reads)
+constexpr int kVPitch = kTT + 4;   // LDS row pitch of the U'^T tile (8-byte row reads)
 constexpr int kWPitch = kD + 8;    // LDS row pitch of W' and of the tail V tile
 constexpr int kMaxR = 128;
+constexpr int kChunksPerRow = kTT / 8;                             // 16-byte chunks per tile row
+constexpr int kStageSlots = 2 * kMaxR * kChunksPerRow / kThreads;  // chunks per thread per tile
+constexpr float kRescaleGap = 8.f; // log2 units: weights may reach 2^8 before m moves
+
+static_assert(kStageSlots * kThreads == 2 * kMaxR * kChunksPerRow, "tile staging split");
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -82,7 +103,8 @@ __device__ __forceinline__ bf16x8_t to_operand(const f32x16_t& acc, int c) {
 // Operand whose K index follows the accumulator row permutation, read from a
 // K-major LDS array X (row = K index, pitch in elements, columns contiguous):
 // slot s of lane l <- X[row0 + 4(l/32) + 8(s/4) + s%4][col0 + l%32].  Two
-// transposing 8-byte reads per lane.
+// transposing 8-byte reads per lane.  ds_read_b64_tr_b16 gives lane
+// B + 4a + b (B = 16*(l/16)) element j = mem[addr(lane B + a + 4j) + b].
 __device__ __forceinline__ bf16x8_t tr_operand(const uint16_t* X, int pitch, int row0, int col0,
                                                int lane) {
   const int kg = lane >> 5;
@@ -98,36 +120,111 @@ __device__ __forceinline__ bf16x8_t tr_operand(const uint16_t* X, int pitch, int
   return __builtin_bit_cast(bf16x8_t, w);
 }
 
+// Operand read along rows of an LDS array X (row = M index, columns = K):
+// slot s of lane l <- X[row0 + l%32][col0 + 4(l/32) + 8(s/4) + s%4], the
+// K permutation of an accumulator-sourced partner.  Two 8-byte reads.
+__device__ __forceinline__ bf16x8_t row_operand(const uint16_t* X, int pitch, int row0, int col0,
+                                                int lane) {
+  const uint16_t* src = X + (row0 + (lane & 31)) * pitch + col0 + 4 * (lane >> 5);
+  const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(src);
+  const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(src + 8);
+  const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
 struct LdsLayout {
+  uint16_t w[kMaxR * kWPitch];     // W (rank rows, zero-padded to a multiple of 32)
   uint16_t wp[kMaxR * kWPitch];    // W' (rank' rows, zero-padded to a multiple of 32)
-  uint16_t u[kMaxR * kUPitch];     // U^T token tile, or the tail V tile
+  uint16_t u[2][kMaxR * kUPitch];  // U^T token tiles (double buffer); the tail's V tile
+  uint16_t v[2][kMaxR * kVPitch];  // U'^T token tiles (double buffer)
 };
+
+// 16-byte load that yields zeros on lanes with !ok: their offset is pushed
+// past the resource's size, and out-of-range raw buffer reads return 0, so
+// no lane branches around the load.
+__device__ __forceinline__ u32x4_t bld16_or0(rsrc_t rs, uint32_t off, bool ok) {
+  return bld16(rs, ok ? off : 0x80000000u, 0);
+}
 
 // Stage rows [0, nrows_pad) x `chunks` 16-byte chunks of a row-major source
 // (row stride src_ld elements, starting at byte offset base) into LDS with
 // pitch `pitch`; rows >= nrows are written as zeros.
 __device__ __forceinline__ void stage_rows(rsrc_t rs, uint32_t base, int src_ld, int nrows,
-                                           int nrows_pad, int chunks, int col0, uint16_t* dst,
-                                           int pitch, int tid) {
-  for (int id = tid; id < nrows_pad * chunks; id += kWaves * 64) {
+                                           int nrows_pad, int chunks, uint16_t* dst, int pitch,
+                                           int tid) {
+  for (int id = tid; id < nrows_pad * chunks; id += kThreads) {
     const int row = id / chunks, ch = id - row * chunks;
-    u32x4_t v = {0, 0, 0, 0};
-    if (row < nrows) v = bld16(rs, (uint32_t)(row * src_ld + col0 + ch * 8) * 2, base);
+    const u32x4_t v = bld16_or0(rs, base + (uint32_t)(row * src_ld + ch * 8) * 2, row < nrows);
     *reinterpret_cast<u32x4_t*>(dst + row * pitch + ch * 8) = v;
   }
 }
 
+// One 64-token tile of a block: U^T rows [0, urows) then U'^T rows
+// [0, vrows), 8 chunks of 16 bytes per row; chunk slot tid + kThreads*k.
+// Rows past the rank are staged as zeros.
+struct TileShape {
+  int T, ld, r, rv, urows, vrows;
+  uint32_t v_off;   // byte offset of U'^T in the head's factors
+};
+
+__device__ __forceinline__ void load_tile(u32x4_t (&pf)[kStageSlots], rsrc_t rs, const TileShape& s,
+                                          int t0, int tid) {
+#pragma unroll
+  for (int k = 0; k < kStageSlots; ++k) {
+    const int id = tid + kThreads * k;
+    const bool is_u = id < s.urows * kChunksPerRow;
+    const int id2 = is_u ? id : id - s.urows * kChunksPerRow;
+    const int row = id2 / kChunksPerRow, tok = t0 + (id2 % kChunksPerRow) * 8;
+    const bool ok = tok < s.ld && (is_u ? row < s.r : (row < s.rv && id2 < s.vrows * kChunksPerRow));
+    pf[k] = bld16_or0(rs, (is_u ? 0u : s.v_off) + (uint32_t)(row * s.ld + tok) * 2, ok);
+  }
+}
+
+// Write a loaded tile to LDS.  U'^T tokens >= T are zeroed (the pool's row
+// padding may hold anything, and those columns meet e = 0 in the MFMA).
+__device__ __forceinline__ void store_tile(const u32x4_t (&pf)[kStageSlots], uint16_t* U, uint16_t* V,
+                                           const TileShape& s, int t0, int tid) {
+#pragma unroll
+  for (int k = 0; k < kStageSlots; ++k) {
+    const int id = tid + kThreads * k;
+    if (id < s.urows * kChunksPerRow) {
+      const int row = id / kChunksPerRow, ch = id % kChunksPerRow;
+      *reinterpret_cast<u32x4_t*>(U + row * kUPitch + ch * 8) = pf[k];
+    } else if (id < (s.urows + s.vrows) * kChunksPerRow) {
+      const int id2 = id - s.urows * kChunksPerRow;
+      const int row = id2 / kChunksPerRow, ch = id2 % kChunksPerRow;
+      u32x4_t v = pf[k];
+      const int tok = t0 + ch * 8;
+      if (tok + 8 > s.T) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          v[w] &= (tok + 2 * w < s.T ? 0xffffu : 0u) | (tok + 2 * w + 1 < s.T ? 0xffff0000u : 0u);
+      }
+      uint16_t* dst = V + row * kVPitch + ch * 8;
+      *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{v[0], v[1]};
+      *reinterpret_cast<u32x2_t*>(dst + 4) = u32x2_t{v[2], v[3]};
+    }
+  }
+}
+
 template <int G>
-__global__ __launch_bounds__(256) void milo_chunk_kernel(ChunkParams p) {
+__global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
   __shared__ __attribute__((aligned(16))) LdsLayout lds;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, kg = lane >> 5;
+
+  // workgroup -> (sequence, KV head, range slot, query tile).  The grid holds
+  // ceil(groups / 8) * 8 * n_qtiles workgroups, dispatched round-robin over
+  // the 8 XCDs: slot k of XCD x runs query tile k % n_qtiles of group
+  // (k / n_qtiles) * 8 + x.
   const int S = p.n_ranges + 1;
-  const int unit = blockIdx.x;
-  const int slot = unit % S;
-  int rest = unit / S;
-  const int qt = rest % p.n_qtiles;
-  rest /= p.n_qtiles;
-  const int g = rest % p.n_kv_heads, i = rest / p.n_kv_heads;
+  const int n_groups = p.batch * p.n_kv_heads * S;
+  const int xcd = blockIdx.x & 7, k8 = blockIdx.x >> 3;
+  const int group = (k8 / p.n_qtiles) * 8 + xcd;
+  const int qt = k8 % p.n_qtiles;
+  if (group >= n_groups) return;
+  const int slot = group % S;
+  const int g = (group / S) % p.n_kv_heads, i = group / (S * p.n_kv_heads);
+
   const int MQ = p.q_len * G;
   const int m0 = qt * (kWaves * kRowsPerWave) + wave * kRowsPerWave;
   const int m_l = m0 + (lane & 31);   // this lane's query row (column of every tile)
@@ -141,17 +238,16 @@ __global__ __launch_bounds__(256) void milo_chunk_kernel(ChunkParams p) {
   const bool tail = slot == p.n_ranges;
   if (!tail && blk_lo >= blk_hi) return;   // empty range: the merge skips it
 
-  // Q^T operand: qv[kk] = q[row m_l][16kk + 8kg .. +8]
-  u32x4_t qv[kD / 16];
-  {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
-                           (((int64_t)i * p.q_len + j_l) * p.n_q_heads + g * G + hl) * kD;
-#pragma unroll
-    for (int kk = 0; kk < kD / 16; ++kk) {
-      qv[kk] = u32x4_t{0, 0, 0, 0};
-      if (row_ok) qv[kk] = ld16(qrow + 16 * kk + 8 * kg);
-    }
-  }
+  // Q^T operand chunk kk: q[row m_l][16kk + 8kg .. +8], re-read (from L2)
+  // where it is needed rather than held in registers.
+  const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
+                         (((int64_t)i * p.q_len + (row_ok ? j_l : 0)) * p.n_q_heads + g * G +
+                          (row_ok ? hl : 0)) * kD + 8 * kg;
+  auto q_operand = [&](int kk) {
+    u32x4_t v = {0, 0, 0, 0};
+    if (row_ok) v = ld16(qrow + 16 * kk);
+    return __builtin_bit_cast(bf16x8_t, v);
+  };
 
   f32x16_t O[kD / 32];
 #pragma unroll
@@ -160,59 +256,100 @@ __global__ __launch_bounds__(256) void milo_chunk_kernel(ChunkParams p) {
     for (int v = 0; v < 16; ++v) O[dt][v] = 0.f;
   float m_run = kNegInf, l_run = 0.f;
 
-  // Online softmax of one 32-token x 32-row score tile (log2 units, masked
-  // entries -inf); rescales O (and Z when given) and returns e as operands.
-  auto softmax_tile = [&](f32x16_t& s, f32x16_t* Z, int nz, bf16x8_t (&eb)[2]) {
+  // Reference the next score tile is taken relative to: the running max, or
+  // 0 while this row has seen nothing.
+  auto score_ref = [&]() { return m_run == kNegInf ? 0.f : m_run; };
+
+  // Online softmax of one 32-token x 32-row score tile s whose entries are
+  // s_true - mref (masked entries -inf).  Raises m when a score exceeds it
+  // by more than kRescaleGap, rescaling O, Z and l, and returns
+  // e = exp2(s_true - m) as two bf16 operands.
+  auto softmax_tile = [&](f32x16_t& s, float mref, f32x16_t* Z, int nz, bf16x8_t (&eb)[2]) {
     float mx = s[0];
 #pragma unroll
     for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
-    {
-      float a = mx, b = mx;
+    const bool need = mx + mref > m_run + kRescaleGap;
+    if (__any(need)) {
+      float a = mx + mref, b = mx + mref;
       swap32(a, b);
-      mx = fmaxf(a, b);
+      const float m_new = fmaxf(m_run, fmaxf(a, b));
+      const float alpha = (m_run == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) O[dt][v] *= alpha;
+#pragma unroll
+        for (int zt = 0; zt < kMaxR / 32; ++zt)
+          if (zt < nz)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) Z[zt][v] *= alpha;
+        l_run *= alpha;
+      }
+      m_run = m_new;
     }
-    const float mn = fmaxf(m_run, mx);
-    const float alpha = (mn == kNegInf) ? 1.f : fast_exp2(m_run - mn);
-    if (__any(alpha != 1.f)) {
+    const float shift = (m_run == kNegInf) ? 0.f : mref - m_run;
+    if (__any(shift != 0.f)) {
 #pragma unroll
-      for (int dt = 0; dt < kD / 32; ++dt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) O[dt][v] *= alpha;
-#pragma unroll
-      for (int zt = 0; zt < kMaxR / 32; ++zt)
-        if (zt < nz)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) Z[zt][v] *= alpha;
+      for (int v = 0; v < 16; ++v) s[v] += shift;
     }
     float sum = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const float e = (mn == kNegInf) ? 0.f : fast_exp2(s[v] - mn);
+      const float e = fast_exp2(s[v]);
       s[v] = e;
       sum += e;
     }
-    l_run = l_run * alpha + sum;
-    m_run = mn;
+    l_run += sum;
     eb[0] = to_operand(s, 0);
     eb[1] = to_operand(s, 1);
   };
 
   if (!tail) {
     f32x16_t Z[kMaxR / 32];
+    u32x4_t pf[kStageSlots];
     for (int b = blk_lo; b < blk_hi; ++b) {
       const milo_block blk = p.blocks[b0 + b];
-      const int T = max(blk.n_tok, 0), ld = blk.ld_tok;
-      const int r = min(max(blk.rank_k, 0), kD), rv = min(max(blk.rank_v, 0), kD);
+      TileShape ts;
+      ts.T = max(blk.n_tok, 0);
+      ts.ld = blk.ld_tok;
+      ts.r = min(max(blk.rank_k, 0), kD);
+      ts.rv = min(max(blk.rank_v, 0), kD);
+      const int r = ts.r, rv = ts.rv, T = ts.T;
       const int nrt = (r + 31) / 32, nvt = (rv + 31) / 32;
+      ts.urows = nrt * 32;
+      ts.vrows = nvt * 32;
       const uint16_t* head = reinterpret_cast<const uint16_t*>(p.pool) + blk.off +
-                             (int64_t)g * (r + rv) * (ld + kD);
-      const rsrc_t rs = make_rsrc(head, (uint32_t)((r + rv) * (ld + kD)) * 2);
-      const uint32_t w_off = (uint32_t)(r * ld) * 2;
-      const uint32_t v_off = w_off + (uint32_t)(r * kD) * 2;
-      const uint32_t wp_off = v_off + (uint32_t)(rv * ld) * 2;
+                             (int64_t)g * (r + rv) * (ts.ld + kD);
+      const rsrc_t rs = make_rsrc(head, (uint32_t)((r + rv) * (ts.ld + kD)) * 2);
+      const uint32_t w_off = (uint32_t)(r * ts.ld) * 2;
+      ts.v_off = w_off + (uint32_t)(r * kD) * 2;
+      const uint32_t wp_off = ts.v_off + (uint32_t)(rv * ts.ld) * 2;
+      const int ntiles = (T + kTT - 1) / kTT;
 
-      __syncthreads();   // previous block's LDS reads are done
-      stage_rows(rs, wp_off, kD, rv, nvt * 32, kD / 8, 0, lds.wp, kWPitch, tid);
+      __syncthreads();   // the previous block's LDS reads are done
+      {
+        // W and W' rows [0, 32*ceil(rank/32)) to LDS, all loads in flight together
+        constexpr int kWSlots = kMaxR * (kD / 8) / kThreads;
+        u32x4_t wv[kWSlots], wpv[kWSlots];
+#pragma unroll
+        for (int k = 0; k < kWSlots; ++k) {
+          const int id = tid + kThreads * k, row = id / (kD / 8), ch = id % (kD / 8);
+          const uint32_t off = (uint32_t)(row * kD + ch * 8) * 2;
+          wv[k] = u32x4_t{0, 0, 0, 0};
+          wpv[k] = u32x4_t{0, 0, 0, 0};
+          if (row < ts.urows) wv[k] = bld16_or0(rs, w_off + off, row < r);
+          if (row < ts.vrows) wpv[k] = bld16_or0(rs, wp_off + off, row < rv);
+        }
+#pragma unroll
+        for (int k = 0; k < kWSlots; ++k) {
+          const int id = tid + kThreads * k, row = id / (kD / 8), ch = id % (kD / 8);
+          if (row < ts.urows) *reinterpret_cast<u32x4_t*>(lds.w + row * kWPitch + ch * 8) = wv[k];
+          if (row < ts.vrows) *reinterpret_cast<u32x4_t*>(lds.wp + row * kWPitch + ch * 8) = wpv[k];
+        }
+      }
+      if (ntiles > 0) load_tile(pf, rs, ts, 0, tid);
+      __syncthreads();
 
       // ---- P^T = W Q^T per 32-rank tile, scaled, split into hi/lo operands
       bf16x8_t ph[kMaxR / 32][2], pl[kMaxR / 32][2];
@@ -222,12 +359,11 @@ __global__ __launch_bounds__(256) void milo_chunk_kernel(ChunkParams p) {
           f32x16_t acc;
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-          const int wrow = 32 * rt + (lane & 31);
+          const uint16_t* wrow = lds.w + (32 * rt + (lane & 31)) * kWPitch + 8 * kg;
 #pragma unroll
           for (int kk = 0; kk < kD / 16; ++kk) {
-            u32x4_t wa = {0, 0, 0, 0};
-            if (wrow < r) wa = bld16(rs, (uint32_t)(wrow * kD + 16 * kk + 8 * kg) * 2, w_off);
-            acc = mfma(__builtin_bit_cast(bf16x8_t, wa), __builtin_bit_cast(bf16x8_t, qv[kk]), acc);
+            const u32x4_t wa = *reinterpret_cast<const u32x4_t*>(wrow + 16 * kk);
+            acc = mfma(__builtin_bit_cast(bf16x8_t, wa), q_operand(kk), acc);
           }
 #pragma unroll
           for (int v = 0; v < 16; ++v)
@@ -241,87 +377,79 @@ __global__ __launch_bounds__(256) void milo_chunk_kernel(ChunkParams p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) Z[zt][v] = 0.f;
 
-      for (int t0 = 0; t0 < T; t0 += kTT) {
-        __syncthreads();   // previous tile's reads of lds.u are done
-        stage_rows(rs, (uint32_t)t0 * 2, ld, r, nrt * 32, kTT / 8, 0, lds.u, kUPitch, tid);
-        __syncthreads();
+      if (ntiles > 0) store_tile(pf, lds.u[0], lds.v[0], ts, 0, tid);
+      __syncthreads();
+
+      for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        const int t0 = t * kTT;
+        if (t + 1 < ntiles) load_tile(pf, rs, ts, t0 + kTT, tid);
+        const uint16_t* U = lds.u[buf];
+        const uint16_t* V = lds.v[buf];
+
+        // ---- S^T = U P^T (hi + lo) for both 32-token halves, issued together;
+        // the accumulators start at -mref so scores arrive relative to it
+        const float mref = score_ref();
+        f32x16_t s[2];
 #pragma unroll
-        for (int st = 0; st < kTT / 32; ++st) {
-          const int tb = t0 + 32 * st;
-          if (tb >= T) break;
-          // U'^T operands for this sub-tile: rank' row 32vt + l%32, tokens
-          // tb + 16c + 4kg + {0..3} and + 8 (masked past the block end)
-          bf16x8_t ua[kMaxR / 32][2];
+        for (int st = 0; st < 2; ++st) {
 #pragma unroll
-          for (int vt = 0; vt < kMaxR / 32; ++vt) {
-            if (vt < nvt) {
-              const int vrow = 32 * vt + (lane & 31);
+          for (int v = 0; v < 16; ++v) s[st][v] = -mref;
+          if (t0 + 32 * st < T) {
 #pragma unroll
-              for (int c = 0; c < 2; ++c) {
-                const int tk = tb + 16 * c + 4 * kg;
-                u32x2_t lo2 = {0, 0}, hi2 = {0, 0};
-                if (vrow < rv) {
-                  const int off = (int)(v_off + (uint32_t)(vrow * ld + tk) * 2);
-                  lo2 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
-                  hi2 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, off + 16, 0, 0));
-                }
-                if (tb + 32 > T) {   // zero tokens past the block end (padding may be NaN)
+            for (int rt = 0; rt < kMaxR / 32; ++rt) {
+              if (rt < nrt) {
 #pragma unroll
-                  for (int h2 = 0; h2 < 2; ++h2) {
-                    const int ta = tk + 2 * h2, tb2 = tk + 8 + 2 * h2;
-                    lo2[h2] &= (ta < T ? 0xffffu : 0u) | (ta + 1 < T ? 0xffff0000u : 0u);
-                    hi2[h2] &= (tb2 < T ? 0xffffu : 0u) | (tb2 + 1 < T ? 0xffff0000u : 0u);
+                for (int c = 0; c < 2; ++c) {
+                  if (32 * rt + 16 * c < r) {
+                    const bf16x8_t a = tr_operand(U, kUPitch, 32 * rt + 16 * c, 32 * st, lane);
+                    s[st] = mfma(a, ph[rt][c], s[st]);
+                    s[st] = mfma(a, pl[rt][c], s[st]);
                   }
                 }
-                const u32x4_t w4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
-                ua[vt][c] = __builtin_bit_cast(bf16x8_t, w4);
               }
             }
           }
-          // ---- S^T = U P^T (hi + lo)
-          f32x16_t s;
+        }
 #pragma unroll
-          for (int v = 0; v < 16; ++v) s[v] = 0.f;
+        for (int st = 0; st < 2; ++st) {
+          const int tb = t0 + 32 * st;
+          if (tb >= T) break;
+          if (tb + 32 > T) {
 #pragma unroll
-          for (int rt = 0; rt < kMaxR / 32; ++rt) {
-            if (rt < nrt) {
-#pragma unroll
-              for (int c = 0; c < 2; ++c) {
-                const bf16x8_t a = tr_operand(lds.u, kUPitch, 32 * rt + 16 * c, 32 * st, lane);
-                s = mfma(a, ph[rt][c], s);
-                s = mfma(a, pl[rt][c], s);
-              }
-            }
+            for (int v = 0; v < 16; ++v)
+              if (tb + acc_row(v, kg) >= T) s[st][v] = kNegInf;
           }
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (tb + acc_row(v, kg) >= T) s[v] = kNegInf;
           bf16x8_t eb[2];
-          softmax_tile(s, Z, nvt, eb);
+          softmax_tile(s[st], mref, Z, nvt, eb);
           // ---- Z^T += U'^T E^T
 #pragma unroll
           for (int vt = 0; vt < kMaxR / 32; ++vt) {
             if (vt < nvt) {
-              Z[vt] = mfma(ua[vt][0], eb[0], Z[vt]);
-              Z[vt] = mfma(ua[vt][1], eb[1], Z[vt]);
+#pragma unroll
+              for (int c = 0; c < 2; ++c) {
+                const bf16x8_t a = row_operand(V, kVPitch, 32 * vt, 32 * st + 16 * c, lane);
+                Z[vt] = mfma(a, eb[c], Z[vt]);
+              }
             }
           }
         }
+        if (t + 1 < ntiles) store_tile(pf, lds.u[buf ^ 1], lds.v[buf ^ 1], ts, t0 + kTT, tid);
+        __syncthreads();
       }
-      // ---- O^T += W'^T Z^T (hi + lo)
-      __syncthreads();   // W' staged (and visible) before the transposing reads
+      // ---- O^T += W'^T Z^T (W' staged and visible since the barriers above)
 #pragma unroll
       for (int vt = 0; vt < kMaxR / 32; ++vt) {
         if (vt < nvt) {
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
-            bf16x8_t zh, zl;
-            split_operand(Z[vt], c, zh, zl);
+            if (32 * vt + 16 * c < rv) {
+              const bf16x8_t zb = to_operand(Z[vt], c);
 #pragma unroll
-            for (int dt = 0; dt < kD / 32; ++dt) {
-              const bf16x8_t a = tr_operand(lds.wp, kWPitch, 32 * vt + 16 * c, 32 * dt, lane);
-              O[dt] = mfma(a, zh, O[dt]);
-              O[dt] = mfma(a, zl, O[dt]);
+              for (int dt = 0; dt < kD / 32; ++dt) {
+                const bf16x8_t a = tr_operand(lds.wp, kWPitch, 32 * vt + 16 * c, 32 * dt, lane);
+                O[dt] = mfma(a, zb, O[dt]);
+              }
             }
           }
         }
@@ -338,32 +466,32 @@ __global__ __launch_bounds__(256) void milo_chunk_kernel(ChunkParams p) {
     const int vis = L - p.q_len + j_l;   // last visible tail token of this row
     for (int t0 = 0; t0 < L; t0 += 32) {
       __syncthreads();
-      stage_rows(rvv, (uint32_t)(t0 * kD) * 2, kD, min(32, L - t0), 32, kD / 8, 0, lds.u, kWPitch, tid);
+      stage_rows(rvv, (uint32_t)(t0 * kD) * 2, kD, min(32, L - t0), 32, kD / 8, lds.u[0], kWPitch, tid);
       __syncthreads();
-      // S^T = K_tail q^T, K = d
+      // S^T = K_tail q^T, K = d, taken relative to mref
+      const float mref = score_ref();
       f32x16_t s;
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[v] = 0.f;
       const int krow = t0 + (lane & 31);
 #pragma unroll
       for (int kk = 0; kk < kD / 16; ++kk) {
-        u32x4_t ka = {0, 0, 0, 0};
-        if (krow < L) ka = bld16(rk, (uint32_t)(krow * kD + 16 * kk + 8 * kg) * 2, 0);
-        s = mfma(__builtin_bit_cast(bf16x8_t, ka), __builtin_bit_cast(bf16x8_t, qv[kk]), s);
+        const u32x4_t ka = bld16_or0(rk, (uint32_t)(krow * kD + 16 * kk + 8 * kg) * 2, krow < L);
+        s = mfma(__builtin_bit_cast(bf16x8_t, ka), q_operand(kk), s);
       }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int t = t0 + acc_row(v, kg);
-        s[v] = (t < L && t <= vis) ? s[v] * p.scale_log2 : kNegInf;
+        s[v] = (t < L && t <= vis) ? s[v] * p.scale_log2 - mref : kNegInf;
       }
       bf16x8_t eb[2];
-      softmax_tile(s, nullptr, 0, eb);
+      softmax_tile(s, mref, nullptr, 0, eb);
       // O^T += V_tail^T E^T
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int dt = 0; dt < kD / 32; ++dt) {
-          const bf16x8_t a = tr_operand(lds.u, kWPitch, 16 * c, 32 * dt, lane);
+          const bf16x8_t a = tr_operand(lds.u[0], kWPitch, 16 * c, 32 * dt, lane);
           O[dt] = mfma(a, eb[c], O[dt]);
         }
     }
@@ -394,9 +522,10 @@ __global__ __launch_bounds__(256) void milo_chunk_kernel(ChunkParams p) {
 }  // namespace
 
 hipError_t launch_chunk(const ChunkParams& p, int group, hipStream_t s) {
-  const int64_t units = (int64_t)p.batch * p.n_kv_heads * p.n_qtiles * (p.n_ranges + 1);
-  if (units == 0) return hipSuccess;
-  const dim3 grid((unsigned)units), block(64 * kWaves);
+  const int64_t groups = (int64_t)p.batch * p.n_kv_heads * (p.n_ranges + 1);
+  if (groups == 0) return hipSuccess;
+  const int64_t wgs = (groups + 7) / 8 * 8 * p.n_qtiles;
+  const dim3 grid((unsigned)wgs), block(kThreads);
   switch (group) {
 #define MILO_G(GG) \
   case GG: hipLaunchKernelGGL((milo_chunk_kernel<GG>), grid, block, 0, s, p); break;
