@@ -44,6 +44,7 @@ struct ChunkParams {
   int32_t n_qtiles;          // tiles of 128 query rows over q_len * group rows
   int32_t n_ranges;          // block ranges per (sequence, KV head); slot n_ranges = tail
   int32_t blocks_per_range;
+  int32_t group;             // query heads per KV head (set by launch_chunk)
   float scale_log2;
 };
 
