@@ -59,9 +59,12 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 16;
 constexpr int kRowsPerTile = kWaves * kRowsPerWave;
 constexpr int kTT = 64;            // tokens per staged tile
-constexpr int kUPitch = kTT + 8;   // LDS row pitch (elements) of the U^T tile (transposing reads)
-constexpr int kVPitch = kTT + 4;   // LDS row pitch of the U'^T tile (8-byte row reads)
-constexpr int kWPitch = kD + 8;    // LDS row pitch of W, W' and the tail's K and V tiles
+// LDS row pitches (elements).  A transposing read touches 8 consecutive rows
+// per 32 lanes, 32 bytes each: a pitch of 40 (U^T) or 72 (W, W') 4-byte banks
+// modulo 64 puts those rows on disjoint banks.
+constexpr int kUPitch = kTT + 16;  // U^T tile
+constexpr int kVPitch = kTT + 8;   // U'^T tile (8-byte row reads: 36 banks keep 32 lanes disjoint)
+constexpr int kWPitch = kD + 16;   // W, W' and the tail's K and V tiles
 constexpr int kMaxR = 128;
 constexpr int kChunksPerRow = kTT / 8;                             // 16-byte chunks per tile row
 constexpr int kStageSlots = 2 * kMaxR * kChunksPerRow / kThreads;  // chunks per thread per tile
@@ -139,11 +142,14 @@ __device__ __forceinline__ u32x4_t row_operand(const uint16_t* X, int pitch, int
   return u32x4_t{a[0], a[1], b[0], b[1]};
 }
 
+struct TileBuf {
+  uint16_t u[kMaxR * kUPitch];     // U^T rows x 64 tokens
+  uint16_t v[kMaxR * kVPitch];     // U'^T rows x 64 tokens
+};
 struct LdsLayout {
   uint16_t w[kMaxR * kWPitch];     // W rows (zero-padded to a multiple of 16); the tail's K tile
   uint16_t wp[kMaxR * kWPitch];    // W' rows (zero-padded to a multiple of 16); the tail's V tile
-  uint16_t u[2][kMaxR * kUPitch];  // U^T token tiles (double buffer)
-  uint16_t v[2][kMaxR * kVPitch];  // U'^T token tiles (double buffer)
+  TileBuf tile[2];                 // token tiles, double buffered
 };
 
 // 16-byte load that yields zeros on lanes with !ok: their offset is pushed
@@ -154,50 +160,61 @@ __device__ __forceinline__ u32x4_t bld16_or0(rsrc_t rs, uint32_t off, bool ok) {
 }
 
 // One 64-token tile of a block: U^T rows [0, urows) then U'^T rows
-// [0, vrows), 8 chunks of 16 bytes per row; chunk slot tid + kThreads*k.
-// Rows past the rank are staged as zeros.
-struct TileShape {
-  int T, ld, r, rv, urows, vrows;
-  uint32_t v_off;   // byte offset of U'^T in the head's factors
+// [0, vrows), 8 chunks of 16 bytes per row; this thread moves chunks
+// tid + kThreads*k.  What does not change from tile to tile is worked out
+// once per block: the chunk's byte offset in the factors (at token 0), its
+// token offset, whether it is loaded at all (rows past the rank are staged
+// as zeros) and where it lands in a tile buffer (-1: not staged).
+struct StageSlots {
+  uint32_t goff[kStageSlots];
+  int tok[kStageSlots];
+  int lds[kStageSlots];            // byte offset in TileBuf, or -1
+  bool load[kStageSlots];
+  bool is_v[kStageSlots];
 };
 
-__device__ __forceinline__ void load_tile(u32x4_t (&pf)[kStageSlots], rsrc_t rs, const TileShape& s,
-                                          int t0, int tid) {
+__device__ __forceinline__ void plan_slots(StageSlots& ss, int tid, int r, int rv, int urows, int vrows,
+                                           int ld, uint32_t v_off) {
 #pragma unroll
   for (int k = 0; k < kStageSlots; ++k) {
     const int id = tid + kThreads * k;
-    const bool is_u = id < s.urows * kChunksPerRow;
-    const int id2 = is_u ? id : id - s.urows * kChunksPerRow;
-    const int row = id2 / kChunksPerRow, tok = t0 + (id2 % kChunksPerRow) * 8;
-    const bool ok = tok < s.ld && (is_u ? row < s.r : (row < s.rv && id2 < s.vrows * kChunksPerRow));
-    pf[k] = bld16_or0(rs, (is_u ? 0u : s.v_off) + (uint32_t)(row * s.ld + tok) * 2, ok);
+    const bool is_u = id < urows * kChunksPerRow;
+    const int id2 = is_u ? id : id - urows * kChunksPerRow;
+    const int row = id2 / kChunksPerRow, ch = id2 % kChunksPerRow;
+    const bool staged = is_u || id2 < vrows * kChunksPerRow;
+    ss.tok[k] = ch * 8;
+    ss.goff[k] = (is_u ? 0u : v_off) + (uint32_t)(row * ld + ch * 8) * 2;
+    ss.load[k] = is_u ? row < r : (staged && row < rv);
+    ss.is_v[k] = !is_u;
+    ss.lds[k] = !staged ? -1
+                        : (is_u ? (row * kUPitch + ch * 8) * 2
+                                : (int)offsetof(TileBuf, v) + (row * kVPitch + ch * 8) * 2);
   }
+}
+
+__device__ __forceinline__ void load_tile(u32x4_t (&pf)[kStageSlots], rsrc_t rs, const StageSlots& ss,
+                                          int ld, int t0) {
+#pragma unroll
+  for (int k = 0; k < kStageSlots; ++k)
+    pf[k] = bld16_or0(rs, ss.goff[k] + (uint32_t)t0 * 2, ss.load[k] && t0 + ss.tok[k] < ld);
 }
 
 // Write a loaded tile to LDS.  U'^T tokens >= T are zeroed (the pool's row
 // padding may hold anything, and those columns meet e = 0 in the MFMA).
-__device__ __forceinline__ void store_tile(const u32x4_t (&pf)[kStageSlots], uint16_t* U, uint16_t* V,
-                                           const TileShape& s, int t0, int tid) {
+__device__ __forceinline__ void store_tile(const u32x4_t (&pf)[kStageSlots], TileBuf* buf,
+                                           const StageSlots& ss, int T, int t0) {
+  char* base = reinterpret_cast<char*>(buf);
 #pragma unroll
   for (int k = 0; k < kStageSlots; ++k) {
-    const int id = tid + kThreads * k;
-    if (id < s.urows * kChunksPerRow) {
-      const int row = id / kChunksPerRow, ch = id % kChunksPerRow;
-      *reinterpret_cast<u32x4_t*>(U + row * kUPitch + ch * 8) = pf[k];
-    } else if (id < (s.urows + s.vrows) * kChunksPerRow) {
-      const int id2 = id - s.urows * kChunksPerRow;
-      const int row = id2 / kChunksPerRow, ch = id2 % kChunksPerRow;
-      u32x4_t v = pf[k];
-      const int tok = t0 + ch * 8;
-      if (tok + 8 > s.T) {
+    if (ss.lds[k] < 0) continue;
+    u32x4_t v = pf[k];
+    const int tok = t0 + ss.tok[k];
+    if (ss.is_v[k] && tok + 8 > T) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
-          v[w] &= (tok + 2 * w < s.T ? 0xffffu : 0u) | (tok + 2 * w + 1 < s.T ? 0xffff0000u : 0u);
-      }
-      uint16_t* dst = V + row * kVPitch + ch * 8;
-      *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{v[0], v[1]};
-      *reinterpret_cast<u32x2_t*>(dst + 4) = u32x2_t{v[2], v[3]};
+      for (int w = 0; w < 4; ++w)
+        v[w] &= (tok + 2 * w < T ? 0xffffu : 0u) | (tok + 2 * w + 1 < T ? 0xffff0000u : 0u);
     }
+    *reinterpret_cast<u32x4_t*>(base + ss.lds[k]) = v;
   }
 }
 
@@ -308,24 +325,21 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
     u32x4_t pf[kStageSlots];
     for (int b = blk_lo; b < blk_hi; ++b) {
       const milo_block blk = p.blocks[b0 + b];
-      TileShape ts;
-      ts.T = max(blk.n_tok, 0);
-      ts.ld = blk.ld_tok;
-      ts.r = min(max(blk.rank_k, 0), kD);
-      ts.rv = min(max(blk.rank_v, 0), kD);
-      const int r = ts.r, rv = ts.rv, T = ts.T;
+      const int T = max(blk.n_tok, 0), ld = blk.ld_tok;
+      const int r = min(max(blk.rank_k, 0), kD), rv = min(max(blk.rank_v, 0), kD);
       // 16-rank chunks: scores use at least one (a rank-0 block scores 0
       // against zero-padded factors); values use none for rank' 0
       const int nk = max(1, (r + 15) / 16), nv = (rv + 15) / 16;
-      ts.urows = nk * 16;
-      ts.vrows = nv * 16;
+      const int urows = nk * 16, vrows = nv * 16;
       const uint16_t* head = reinterpret_cast<const uint16_t*>(p.pool) + blk.off +
-                             (int64_t)g * (r + rv) * (ts.ld + kD);
-      const rsrc_t rs = make_rsrc(head, (uint32_t)((r + rv) * (ts.ld + kD)) * 2);
-      const uint32_t w_off = (uint32_t)(r * ts.ld) * 2;
-      ts.v_off = w_off + (uint32_t)(r * kD) * 2;
-      const uint32_t wp_off = ts.v_off + (uint32_t)(rv * ts.ld) * 2;
+                             (int64_t)g * (r + rv) * (ld + kD);
+      const rsrc_t rs = make_rsrc(head, (uint32_t)((r + rv) * (ld + kD)) * 2);
+      const uint32_t w_off = (uint32_t)(r * ld) * 2;
+      const uint32_t v_off = w_off + (uint32_t)(r * kD) * 2;
+      const uint32_t wp_off = v_off + (uint32_t)(rv * ld) * 2;
       const int ntiles = (T + kTT - 1) / kTT;
+      StageSlots ss;
+      plan_slots(ss, tid, r, rv, urows, vrows, ld, v_off);
 
       __syncthreads();   // the previous block's LDS reads are done
       {
@@ -341,13 +355,13 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
 #pragma unroll
         for (int k = 0; k < kWSlots; ++k) {
           const int id = tid + kThreads * k, row = id / (kD / 8), ch = id % (kD / 8);
-          if (row < ts.urows) *reinterpret_cast<u32x4_t*>(lds.w + row * kWPitch + ch * 8) = wv[k];
-          if (row < ts.vrows) *reinterpret_cast<u32x4_t*>(lds.wp + row * kWPitch + ch * 8) = wpv[k];
+          if (row < urows) *reinterpret_cast<u32x4_t*>(lds.w + row * kWPitch + ch * 8) = wv[k];
+          if (row < vrows) *reinterpret_cast<u32x4_t*>(lds.wp + row * kWPitch + ch * 8) = wpv[k];
         }
       }
       u32x4_t qv[kD / 32];
       load_q(qv);
-      if (ntiles > 0) load_tile(pf, rs, ts, 0, tid);
+      if (ntiles > 0) load_tile(pf, rs, ss, ld, 0);
       __syncthreads();
 #pragma unroll
       for (int zt = 0; zt < kMaxR / 16; ++zt) Z[zt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -380,15 +394,15 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
           if (REM) split_one(pt[NK - 1], ph16, pl16);
         }
 
-        if (ntiles > 0) store_tile(pf, lds.u[0], lds.v[0], ts, 0, tid);
+        if (ntiles > 0) store_tile(pf, &lds.tile[0], ss, T, 0);
         __syncthreads();
 
         for (int t = 0; t < ntiles; ++t) {
           const int buf = t & 1;
           const int t0 = t * kTT;
-          if (t + 1 < ntiles) load_tile(pf, rs, ts, t0 + kTT, tid);
-          const uint16_t* U = lds.u[buf];
-          const uint16_t* V = lds.v[buf];
+          if (t + 1 < ntiles) load_tile(pf, rs, ss, ld, t0 + kTT);
+          const uint16_t* U = lds.tile[buf].u;
+          const uint16_t* V = lds.tile[buf].v;
 
           // ---- S^T = U P^T (hi + lo) for the tile's four 16-token blocks;
           // the chains start from -mref, so scores arrive relative to it.
@@ -428,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
                 Z[vt] = mfma32(row_operand(V, kVPitch, 16 * vt, 32 * c, lane), eb[c], Z[vt]);
             }
           }
-          if (t + 1 < ntiles) store_tile(pf, lds.u[buf ^ 1], lds.v[buf ^ 1], ts, t0 + kTT, tid);
+          if (t + 1 < ntiles) store_tile(pf, &lds.tile[buf ^ 1], ss, T, t0 + kTT);
           __syncthreads();
         }
       };
