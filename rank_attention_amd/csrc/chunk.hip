@@ -408,20 +408,30 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
           // the chains start from -mref, so scores arrive relative to it.
           const float mref = score_ref();
           const f32x4_t bias = {-mref, -mref, -mref, -mref};
+          // Chunk-outer order: the four chains' operand reads for one rank
+          // chunk are in flight together before their MFMAs.
           f32x4_t s[4];
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            s[tt] = bias;
+          for (int tt = 0; tt < 4; ++tt) s[tt] = bias;
 #pragma unroll
-            for (int j = 0; j < NK2; ++j) {
-              const u32x4_t a = tr_operand(U, kUPitch, 32 * j, 16 * tt, lane);
-              s[tt] = mfma32(a, ph[j], s[tt]);
-              s[tt] = mfma32(a, pl[j], s[tt]);
+          for (int j = 0; j < NK2; ++j) {
+            u32x4_t a[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) a[tt] = tr_operand(U, kUPitch, 32 * j, 16 * tt, lane);
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+              s[tt] = mfma32(a[tt], ph[j], s[tt]);
+              s[tt] = mfma32(a[tt], pl[j], s[tt]);
             }
-            if (REM) {
-              const u32x2_t a = tr_operand16(U, kUPitch, 32 * NK2, 16 * tt, lane);
-              s[tt] = mfma16(a, ph16, s[tt]);
-              s[tt] = mfma16(a, pl16, s[tt]);
+          }
+          if (REM) {
+            u32x2_t a[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) a[tt] = tr_operand16(U, kUPitch, 32 * NK2, 16 * tt, lane);
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+              s[tt] = mfma16(a[tt], ph16, s[tt]);
+              s[tt] = mfma16(a[tt], pl16, s[tt]);
             }
           }
           if (t0 + kTT > T) {   // tokens past the block end
@@ -434,12 +444,22 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
           u32x4_t eb[2];
           softmax64(s, mref, nv, eb);
           // ---- Z^T += U'^T E^T
+          // pairs of rank' tiles, four operand reads in flight
 #pragma unroll
-          for (int vt = 0; vt < kMaxR / 16; ++vt) {
+          for (int vt = 0; vt < kMaxR / 16; vt += 2) {
             if (vt < nv) {
+              u32x4_t a[4];
 #pragma unroll
-              for (int c = 0; c < 2; ++c)
-                Z[vt] = mfma32(row_operand(V, kVPitch, 16 * vt, 32 * c, lane), eb[c], Z[vt]);
+              for (int c = 0; c < 2; ++c) {
+                a[c] = row_operand(V, kVPitch, 16 * vt, 32 * c, lane);
+                a[2 + c] = row_operand(V, kVPitch, 16 * vt + 16, 32 * c, lane);
+              }
+#pragma unroll
+              for (int c = 0; c < 2; ++c) Z[vt] = mfma32(a[c], eb[c], Z[vt]);
+              if (vt + 1 < nv) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c) Z[vt + 1] = mfma32(a[2 + c], eb[c], Z[vt + 1]);
+              }
             }
           }
           if (t + 1 < ntiles) store_tile(pf, &lds.tile[buf ^ 1], ss, T, t0 + kTT);
