@@ -144,13 +144,16 @@ milo_status milo_attn_chunk(const milo_attn_args* args, void* hip_stream);
  * is the dense tail).  Units differ in size by up to the ratio of their ranks,
  * and one decode call runs about two units per wave slot of the GPU, so
  * starting the largest first keeps the last units short (longest-processing-
- * time-first).  The cost of a unit is its factor bytes, (r + r')(T + d), or
- * 2 * tail_len * d for a tail unit.
+ * time-first).  The cost of a block unit is its factor bytes, (r + r')(T + d).
+ * Dense-tail units with tail_len > 0 are placed before every block unit: they
+ * are few and stream more slowly per byte, and started late they would be
+ * the last to finish.
  *
  * blocks, seq_blocks, tail_len are HOST copies of the device tables
  * (tail_len may be NULL when tail_cap is 0);  order_out (host) receives
- * batch * n_kv_heads * (max_blocks_per_seq + 1) unit indices, largest first,
- * ties in natural order; empty slots come last.  The cache is static across
+ * batch * n_kv_heads * (max_blocks_per_seq + 1) unit indices: non-empty
+ * tails (longest first), then block units (largest first), then empty slots
+ * and empty tails; ties in natural order.  The cache is static across
  * decode steps, so the plan is computed once and copied to the device.
  * Returns MILO_ERR_INVALID on null pointers or negative sizes.
  */

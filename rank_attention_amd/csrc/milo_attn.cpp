@@ -233,7 +233,11 @@ milo_status milo_attn_plan_decode(const milo_block* blocks, const int32_t* seq_b
   if (batch > 0 && max_blocks > 0 && !blocks) return MILO_ERR_INVALID;
   const int64_t slots = (int64_t)max_blocks + 1;
   const int64_t units = (int64_t)batch * n_kv_heads * slots;
-  std::vector<int64_t> cost((size_t)units, -1);   // -1: empty slot
+  // rank 0: dense-tail units (few, and per byte the slowest, so they go
+  // first and never finish last); rank 1: block units, largest first;
+  // rank 2: empty slots and empty tails
+  std::vector<int64_t> cost((size_t)units, 0);
+  std::vector<int8_t> rank((size_t)units, 2);
   for (int32_t i = 0; i < batch; ++i) {
     const int32_t b0 = seq_blocks[i];
     const int32_t nb = std::min(std::max(seq_blocks[i + 1] - b0, 0), max_blocks);
@@ -243,15 +247,19 @@ milo_status milo_attn_plan_decode(const milo_block* blocks, const int32_t* seq_b
         const milo_block& b = blocks[b0 + s];
         const int64_t r = std::max(b.rank_k, 0) + std::max(b.rank_v, 0);
         cost[(size_t)(base + s)] = r * ((int64_t)std::max(b.n_tok, 0) + head_dim);
+        rank[(size_t)(base + s)] = 1;
       }
       const int64_t L = tail_len ? std::max(tail_len[i], 0) : 0;
       cost[(size_t)(base + max_blocks)] = 2 * L * head_dim;
+      rank[(size_t)(base + max_blocks)] = L > 0 ? 0 : 2;
     }
   }
   std::vector<int32_t> idx((size_t)units);
   std::iota(idx.begin(), idx.end(), 0);
-  std::stable_sort(idx.begin(), idx.end(),
-                   [&](int32_t x, int32_t y) { return cost[(size_t)x] > cost[(size_t)y]; });
+  std::stable_sort(idx.begin(), idx.end(), [&](int32_t x, int32_t y) {
+    if (rank[(size_t)x] != rank[(size_t)y]) return rank[(size_t)x] < rank[(size_t)y];
+    return cost[(size_t)x] > cost[(size_t)y];
+  });
   std::copy(idx.begin(), idx.end(), order_out);
   return MILO_OK;
 }

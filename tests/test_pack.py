@@ -58,7 +58,7 @@ def test_f32_pool():
     assert pc.max_blocks == 4
 
 
-def test_decode_plan_is_largest_first_permutation():
+def test_decode_plan_tails_first_then_largest_first():
     cfg = synth.get_config("qwen7b_64k").with_(batch=3, n_blocks=5)
     wl = synth.make_workload(cfg, n_blocks=[5, 2, 0], tail_len=[256, 0, 17])
     pc = ra.pack(wl, max_blocks=6)
@@ -68,20 +68,24 @@ def test_decode_plan_is_largest_first_permutation():
     assert sorted(order.tolist()) == list(range(units))
     d = cfg.head_dim
 
-    def cost(u):
+    def key(u):
+        """(class, -cost): non-empty tails, then blocks by size, then empty slots."""
         i, rest = divmod(u, cfg.n_kv_heads * S)
         g, slot = divmod(rest, S)
         nb = int(pc.seq_blocks[i + 1] - pc.seq_blocks[i])
         if slot == pc.max_blocks:
-            return 2 * int(pc.tail_len[i]) * d
+            L = int(pc.tail_len[i])
+            return (0, -2 * L * d) if L > 0 else (2, 0)
         if slot >= nb:
-            return -1
+            return (2, 0)
         b = pc.blocks[pc.seq_blocks[i] + slot]
-        return (int(b["rank_k"]) + int(b["rank_v"])) * (int(b["n_tok"]) + d)
+        return (1, -(int(b["rank_k"]) + int(b["rank_v"])) * (int(b["n_tok"]) + d))
 
-    costs = [cost(int(u)) for u in order]
-    assert costs == sorted(costs, reverse=True)
+    keys = [key(int(u)) for u in order]
+    assert keys == sorted(keys)
+    n_tails = sum(1 for k in keys if k[0] == 0)
+    assert n_tails == 2 * cfg.n_kv_heads            # sequences 0 and 2 have a tail
     # ties keep the natural order
     for a, b in zip(order, order[1:]):
-        if cost(int(a)) == cost(int(b)):
+        if key(int(a)) == key(int(b)):
             assert a < b
