@@ -30,12 +30,17 @@
 // block range get consecutive workgroup slots on one XCD, so they run
 // together and read the range's factors from that XCD's L2.
 //
-// Per block: W and W' are staged in LDS and P^T is built from W and Q (Q
-// re-read from L2).  The block's token factors then pass through LDS in
-// 64-token tiles of U^T and U'^T, double buffered: the next tile's global
-// loads are issued before the current tile is computed and written to the
-// other buffer after it.  The score chain is compiled per count of 16-rank
-// chunks, so it is straight-line code.
+// Data movement: every factor byte goes from HBM straight into LDS with
+// buffer_load ... lds (16 bytes per lane; lanes out of range write zeros,
+// which pads ranks and token tiles).  The block's tokens pass in 64-token
+// tiles of U^T and U'^T through three LDS buffers, two tiles ahead of the
+// compute, across block boundaries; W of the next block is loaded during
+// the last tile of the current one and W' at the start of its own block.
+// LDS rows are unpadded; 16-byte chunks are XOR-swizzled per row so that
+// every read pattern below touches each bank once per 32 lanes.  Waits are
+// explicit (s_waitcnt vmcnt + s_barrier), so loads stay in flight across
+// barriers.  The score chain is compiled per count of 16-rank chunks, so it
+// is straight-line code.
 //
 // Softmax: the running max m enters the score MFMA as its initial
 // accumulator (-m), so scores arrive relative to m.  m is raised only when
@@ -59,25 +64,38 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 16;
 constexpr int kRowsPerTile = kWaves * kRowsPerWave;
 constexpr int kTT = 64;            // tokens per staged tile
-// LDS row pitches (elements).  A transposing read touches 8 consecutive rows
-// per 32 lanes, 32 bytes each: a pitch of 40 (U^T) or 72 (W, W') 4-byte banks
-// modulo 64 puts those rows on disjoint banks.
-constexpr int kUPitch = kTT + 16;  // U^T tile
-constexpr int kVPitch = kTT + 8;   // U'^T tile (8-byte row reads: 36 banks keep 32 lanes disjoint)
-constexpr int kWPitch = kD + 16;   // W, W' and the tail's K and V tiles
 constexpr int kMaxR = 128;
-constexpr int kChunksPerRow = kTT / 8;                             // 16-byte chunks per tile row
-constexpr int kStageSlots = 2 * kMaxR * kChunksPerRow / kThreads;  // chunks per thread per tile
-constexpr int kWSlots = kMaxR * (kD / 8) / kThreads;               // chunks per thread of W (or W')
+constexpr int kNBuf = 3;           // token-tile buffers: compute + two in flight
 constexpr float kRescaleGap = 8.f; // log2 units: weights may reach 2^8 before m moves
 
-static_assert(kStageSlots * kThreads == 2 * kMaxR * kChunksPerRow, "tile staging split");
-static_assert(kWSlots * kThreads == kMaxR * (kD / 8), "W staging split");
+// LDS byte layout: W and W' (128 rows x 256 B), then the token tiles, each
+// U^T (128 rows x 128 B) followed by U'^T (128 rows x 128 B).  The tail
+// unit stages K in the W region and V in the W' region.
+constexpr int kWBytes = kMaxR * kD * 2;
+constexpr int kOffW = 0;
+constexpr int kOffWp = kWBytes;
+constexpr int kHalfTile = kMaxR * kTT * 2;
+constexpr int kTileBytes = 2 * kHalfTile;
+constexpr int kOffTile = 2 * kWBytes;
+constexpr int kLdsBytes = kOffTile + kNBuf * kTileBytes;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 static_assert(kRowsPerTile == 128, "the host splits query rows in tiles of 128");
+
+// Swizzles (16-byte chunk index XOR a function of the row):
+//  W, tail K : 16 chunks per row, read 16 rows x one chunk per 16 lanes
+//  W', tail V: 16 chunks per row, transposing reads of 8 rows x 2 chunks
+//  U^T       :  8 chunks per row, transposing reads of 8 rows x 2 chunks
+//  U'^T      :  8 chunks per row, row reads of 16 rows x one chunk
+__device__ __forceinline__ int swz_w(int r) { return r & 15; }
+__device__ __forceinline__ int swz_wp(int r) { return (r & 7) << 1; }
+__device__ __forceinline__ int swz_u(int r) { return ((r >> 1) & 3) << 1; }
+__device__ __forceinline__ int swz_v(int r) { return (r >> 1) & 7; }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
 __device__ __forceinline__ f32x4_t mfma32(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -114,107 +132,159 @@ __device__ __forceinline__ u32x4_t pack_pair(const f32x4_t& x, const f32x4_t& y)
                  pack_bf16(y[2], y[3])};
 }
 
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-__device__ __forceinline__ u32x2_t tr_read(const uint16_t* p) {
+__device__ __forceinline__ u32x2_t tr_read(const char* p) {
   return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
 }
 
-// K = 32 operand from a K-major LDS array X (row = K index, columns = M):
-// slot s of lane l <- X[row0 + 4(l/16) + s%4 + 16(s/4)][col0 + l%16].
-__device__ __forceinline__ u32x4_t tr_operand(const uint16_t* X, int pitch, int row0, int col0, int lane) {
+// Operands read from a swizzled K-major LDS array (row = K index, columns =
+// M, `cpr` 16-byte chunks per row):
+//   K = 32: slot s of lane l <- X[row0 + 4(l/16) + s%4 + 16(s/4)][col0 + l%16]
+//   K = 16: slot s of lane l <- X[row0 + 4(l/16) + s][col0 + l%16]
+// Lane x addresses the 8 bytes at row row0 + 4(x/16) + (x%16)/4, columns
+// col0 + 4(x%4) .. +3 (col0 a multiple of 16); the swizzle of a row is the
+// same for that row + 16.
+template <int CPR, int (*SWZ)(int)>
+__device__ __forceinline__ int tr_addr(int row0, int col0, int lane) {
   const int r = row0 + 4 * (lane >> 4) + ((lane & 15) >> 2);
-  const int c = col0 + 4 * (lane & 3);
-  const u32x2_t a = tr_read(X + r * pitch + c), b = tr_read(X + (r + 16) * pitch + c);
-  return u32x4_t{a[0], a[1], b[0], b[1]};
+  const int chunk = (col0 >> 3) + ((lane & 3) >> 1);
+  return r * (CPR * 16) + ((chunk ^ SWZ(r)) << 4) + ((lane & 1) << 3);
 }
-// K = 16 operand: slot s of lane l <- X[row0 + 4(l/16) + s][col0 + l%16].
-__device__ __forceinline__ u32x2_t tr_operand16(const uint16_t* X, int pitch, int row0, int col0, int lane) {
-  const int r = row0 + 4 * (lane >> 4) + ((lane & 15) >> 2);
-  const int c = col0 + 4 * (lane & 3);
-  return tr_read(X + r * pitch + c);
+template <int CPR, int (*SWZ)(int)>
+__device__ __forceinline__ u32x4_t tr_operand(const char* X, int row0, int col0, int lane) {
+  const int a = tr_addr<CPR, SWZ>(row0, col0, lane);
+  const u32x2_t lo = tr_read(X + a), hi = tr_read(X + a + 16 * CPR * 16);
+  return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
 }
-// K = 32 operand read along rows of an LDS array X (row = M index, columns = K):
-// slot s of lane l <- X[row0 + l%16][col0 + 4(l/16) + s%4 + 16(s/4)].
-__device__ __forceinline__ u32x4_t row_operand(const uint16_t* X, int pitch, int row0, int col0, int lane) {
-  const uint16_t* src = X + (row0 + (lane & 15)) * pitch + col0 + 4 * (lane >> 4);
-  const u32x2_t a = *reinterpret_cast<const u32x2_t*>(src);
-  const u32x2_t b = *reinterpret_cast<const u32x2_t*>(src + 16);
-  return u32x4_t{a[0], a[1], b[0], b[1]};
+template <int CPR, int (*SWZ)(int)>
+__device__ __forceinline__ u32x2_t tr_operand16(const char* X, int row0, int col0, int lane) {
+  return tr_read(X + tr_addr<CPR, SWZ>(row0, col0, lane));
+}
+// K = 32 operand read along rows of the swizzled U'^T tile (row = M index,
+// 8 chunks per row, columns = K): slot s of lane l <-
+// X[row0 + l%16][col0 + 4(l/16) + s%4 + 16(s/4)], col0 a multiple of 32.
+__device__ __forceinline__ u32x4_t v_operand(const char* X, int row0, int col0, int lane) {
+  const int r = row0 + (lane & 15);
+  const int c0 = (col0 >> 3) + (lane >> 5), half = ((lane >> 4) & 1) << 3;
+  const int s = swz_v(r);
+  const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(X + r * 128 + ((c0 ^ s) << 4) + half);
+  const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(X + r * 128 + (((c0 + 2) ^ s) << 4) + half);
+  return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+}
+// A operand from a swizzled row-major 256-byte-row array (W, tail K): slot s
+// of lane l <- X[row0 + l%16][kc*32 + 8(l/16) + s].
+__device__ __forceinline__ u32x4_t w_operand(const char* X, int row0, int kc, int lane) {
+  const int r = row0 + (lane & 15);
+  const int chunk = 4 * kc + (lane >> 4);
+  return *reinterpret_cast<const u32x4_t*>(X + r * 256 + ((chunk ^ swz_w(r)) << 4));
 }
 
-struct TileBuf {
-  uint16_t u[kMaxR * kUPitch];     // U^T rows x 64 tokens
-  uint16_t v[kMaxR * kVPitch];     // U'^T rows x 64 tokens
+// Buffer resource words (base, no stride, `bytes` records, raw dword
+// format) of a wave-uniform range, for the LDS DMA below.
+__device__ __forceinline__ u32x4_t rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xffffu,
+                 (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+}
+// 16 bytes per lane from the buffer into LDS at lds + 16*lane (lds
+// wave-uniform, passed in M0).  Lanes with !ok read past the resource's
+// size and write zeros.  Issued from asm so that the compiler does not
+// track it: it cannot tell which LDS buffer the load writes and would wait
+// for every load in flight before each LDS read.  The waits are explicit
+// (wait_barrier) instead.  The compiler does not insert hazard wait states
+// for an asm statement's operands, so the asm holds them: a VMEM
+// instruction reading an SGPR that a VALU instruction wrote (the resource
+// words come from v_readfirstlane) needs 5 wait states, one reading M0
+// after an SALU write needs 1; s_nop 4 gives 5.
+__device__ __forceinline__ void dma16(const u32x4_t& rs, char* lds, uint32_t off, bool ok) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds));
+  const uint32_t voff = ok ? off : 0x80000000u;
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rs), "{m0}"(m0)
+               : "memory");
+}
+// x, hidden from the optimizer: per-lane LDS and DMA offsets derived from it
+// are recomputed where they are used instead of being hoisted out of the
+// loops and kept live (they would take ~40 registers for the whole unit).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+// vmcnt(N) (lgkmcnt(0), expcnt untouched), then a workgroup barrier.  No
+// memory fence: loads issued after the awaited ones stay in flight.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// A block's factor layout (wave-uniform).
+struct BlockInfo {
+  const uint16_t* head;   // this KV head's factors
+  uint32_t bytes;         // their size
+  int T, ld, r, rv, nk, nv, ntiles;
+  uint32_t w_off, v_off, wp_off;
 };
-struct LdsLayout {
-  uint16_t w[kMaxR * kWPitch];     // W rows (zero-padded to a multiple of 16); the tail's K tile
-  uint16_t wp[kMaxR * kWPitch];    // W' rows (zero-padded to a multiple of 16); the tail's V tile
-  TileBuf tile[2];                 // token tiles, double buffered
-};
 
-// 16-byte load that yields zeros on lanes with !ok: their offset is pushed
-// past the resource's size, and out-of-range raw buffer reads return 0, so
-// no lane branches around the load.
-__device__ __forceinline__ u32x4_t bld16_or0(rsrc_t rs, uint32_t off, bool ok) {
-  return bld16(rs, ok ? off : 0x80000000u, 0);
+// Buffer resource of a block's factors.
+__device__ __forceinline__ u32x4_t rsrc_of(const BlockInfo& io) { return rsrc_words(io.head, io.bytes); }
+
+// The block table is read through the constant address space: it does not
+// change during the kernel, so its (wave-uniform) reads stay scalar loads
+// even though the DMA asm counts as a memory clobber.
+typedef __attribute__((address_space(4))) const milo_block const_milo_block;
+
+__device__ __forceinline__ void block_info(BlockInfo& io, const ChunkParams& p, int gblk, int g) {
+  const_milo_block* blk = (const_milo_block*)p.blocks + gblk;
+  io.T = max(blk->n_tok, 0);
+  io.ld = blk->ld_tok;
+  io.r = min(max(blk->rank_k, 0), kD);
+  io.rv = min(max(blk->rank_v, 0), kD);
+  // 16-rank chunks: scores use at least one (a rank-0 block scores 0
+  // against zero-padded factors); values use none for rank' 0
+  io.nk = max(1, (io.r + 15) / 16);
+  io.nv = (io.rv + 15) / 16;
+  io.ntiles = max(1, (io.T + kTT - 1) / kTT);
+  io.head = reinterpret_cast<const uint16_t*>(p.pool) + blk->off +
+            (int64_t)g * (io.r + io.rv) * (io.ld + kD);
+  io.bytes = (uint32_t)((io.r + io.rv) * (io.ld + kD)) * 2;
+  io.w_off = (uint32_t)(io.r * io.ld) * 2;
+  io.v_off = io.w_off + (uint32_t)(io.r * kD) * 2;
+  io.wp_off = io.v_off + (uint32_t)(io.rv * io.ld) * 2;
 }
 
-// One 64-token tile of a block: U^T rows [0, urows) then U'^T rows
-// [0, vrows), 8 chunks of 16 bytes per row; this thread moves chunks
-// tid + kThreads*k.  What does not change from tile to tile is worked out
-// once per block: the chunk's byte offset in the factors (at token 0), its
-// token offset, whether it is loaded at all (rows past the rank are staged
-// as zeros) and where it lands in a tile buffer (-1: not staged).
-struct StageSlots {
-  uint32_t goff[kStageSlots];
-  int tok[kStageSlots];
-  int lds[kStageSlots];            // byte offset in TileBuf, or -1
-  bool load[kStageSlots];
-  bool is_v[kStageSlots];
-};
-
-__device__ __forceinline__ void plan_slots(StageSlots& ss, int tid, int r, int rv, int urows, int vrows,
-                                           int ld, uint32_t v_off) {
+// Token tile starting at t0 into tile buffer `buf` (4 loads per wave): load
+// k of wave w moves 8 rows (row block 8k + w of the 32 row blocks: U^T
+// 0-15, U'^T 16-31) x 8 chunks, lane l taking row (l/8) of the row block
+// and LDS chunk position l%8.  Rows past the rank and chunks past the
+// block's padded length load zeros.
+__device__ __forceinline__ void issue_tile(const BlockInfo& io, char* buf, int t0, int lane, int wave) {
+  const u32x4_t rs = rsrc_of(io);
 #pragma unroll
-  for (int k = 0; k < kStageSlots; ++k) {
-    const int id = tid + kThreads * k;
-    const bool is_u = id < urows * kChunksPerRow;
-    const int id2 = is_u ? id : id - urows * kChunksPerRow;
-    const int row = id2 / kChunksPerRow, ch = id2 % kChunksPerRow;
-    const bool staged = is_u || id2 < vrows * kChunksPerRow;
-    ss.tok[k] = ch * 8;
-    ss.goff[k] = (is_u ? 0u : v_off) + (uint32_t)(row * ld + ch * 8) * 2;
-    ss.load[k] = is_u ? row < r : (staged && row < rv);
-    ss.is_v[k] = !is_u;
-    ss.lds[k] = !staged ? -1
-                        : (is_u ? (row * kUPitch + ch * 8) * 2
-                                : (int)offsetof(TileBuf, v) + (row * kVPitch + ch * 8) * 2);
+  for (int k = 0; k < 4; ++k) {
+    const bool is_v = k >= 2;
+    const int rb = (k & 1) * 8 + wave;
+    const int row = rb * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ (is_v ? swz_v(row) : swz_u(row));
+    const uint32_t off = (is_v ? io.v_off : 0u) + (uint32_t)(row * io.ld + t0 + chunk * 8) * 2;
+    const bool ok = row < (is_v ? io.rv : io.r) && t0 + chunk * 8 < io.ld;
+    dma16(rs, buf + (is_v ? kHalfTile : 0) + rb * 1024, off, ok);
   }
 }
-
-__device__ __forceinline__ void load_tile(u32x4_t (&pf)[kStageSlots], rsrc_t rs, const StageSlots& ss,
-                                          int ld, int t0) {
+// W (wp = false) or W' rows of a block into their LDS region (4 loads per
+// wave: row block 8k + w of 32, 4 rows x 16 chunks each).
+__device__ __forceinline__ void issue_w(const BlockInfo& io, char* region, bool wp, int lane, int wave) {
+  const u32x4_t rs = rsrc_of(io);
 #pragma unroll
-  for (int k = 0; k < kStageSlots; ++k)
-    pf[k] = bld16_or0(rs, ss.goff[k] + (uint32_t)t0 * 2, ss.load[k] && t0 + ss.tok[k] < ld);
-}
-
-// Write a loaded tile to LDS.  U'^T tokens >= T are zeroed (the pool's row
-// padding may hold anything, and those columns meet e = 0 in the MFMA).
-__device__ __forceinline__ void store_tile(const u32x4_t (&pf)[kStageSlots], TileBuf* buf,
-                                           const StageSlots& ss, int T, int t0) {
-  char* base = reinterpret_cast<char*>(buf);
-#pragma unroll
-  for (int k = 0; k < kStageSlots; ++k) {
-    if (ss.lds[k] < 0) continue;
-    u32x4_t v = pf[k];
-    const int tok = t0 + ss.tok[k];
-    if (ss.is_v[k] && tok + 8 > T) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        v[w] &= (tok + 2 * w < T ? 0xffffu : 0u) | (tok + 2 * w + 1 < T ? 0xffff0000u : 0u);
-    }
-    *reinterpret_cast<u32x4_t*>(base + ss.lds[k]) = v;
+  for (int k = 0; k < 4; ++k) {
+    const int rb = 8 * k + wave;
+    const int row = rb * 4 + (lane >> 4);
+    const int chunk = (lane & 15) ^ (wp ? swz_wp(row) : swz_w(row));
+    const uint32_t off = (wp ? io.wp_off : io.w_off) + (uint32_t)(row * kD + chunk * 8) * 2;
+    dma16(rs, region + rb * 1024, off, row < (wp ? io.rv : io.r));
   }
 }
 
@@ -224,9 +294,13 @@ struct IntC {
 };
 
 __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
-  __shared__ __attribute__((aligned(16))) LdsLayout lds;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q4 = lane >> 4;
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  const int tid = threadIdx.x, lane = tid & 63, q4 = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.group;
+  char* const ldsW = lds + kOffW;
+  char* const ldsWp = lds + kOffWp;
+  auto tile_buf = [&](int k) { return lds + kOffTile + (k % kNBuf) * kTileBytes; };
 
   // workgroup -> (sequence, KV head, range slot, query tile).  The grid holds
   // ceil(groups / 8) * 8 * n_qtiles workgroups, dispatched round-robin over
@@ -253,15 +327,19 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
   const bool tail = slot == p.n_ranges;
   if (!tail && blk_lo >= blk_hi) return;   // empty range: the merge skips it
 
-  // Q^T operand chunks qv[kk] = q[row m_l][32kk + 8(l/16) .. +8], re-read
-  // (from L2) where needed rather than held in registers.  Lanes past the
-  // last row read row 0 instead: their columns are never written out.
-  const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
-                         (((int64_t)i * p.q_len + (row_ok ? j_l : 0)) * p.n_q_heads + g * G +
-                          (row_ok ? hl : 0)) * kD + 8 * q4;
-  auto load_q = [&](u32x4_t (&qv)[kD / 32]) {
+  // Q^T operand chunks qv[kk] = q[row m_l][32kk + 8(l/16) .. +8], held for
+  // the whole unit.  Lanes past the last row read row 0: their columns are
+  // never written out.  Loaded after the unit's first DMA loads and awaited
+  // at once (vmcnt(0)): a wait left to the compiler would sit in the block
+  // loop and also drain the prefetched tiles at every block.
+  u32x4_t qv[kD / 32];
+  auto load_q = [&]() {
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
+                           (((int64_t)i * p.q_len + (row_ok ? j_l : 0)) * p.n_q_heads + g * G +
+                            (row_ok ? hl : 0)) * kD + 8 * q4;
 #pragma unroll
     for (int kk = 0; kk < kD / 32; ++kk) qv[kk] = ld16(qrow + 32 * kk);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   };
 
   f32x4_t O[kD / 16];
@@ -276,9 +354,9 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
 
   // Online softmax of four 16-token x 16-row score tiles s (64 tokens)
   // whose entries are s_true - mref (masked entries -inf).  Raises m when a
-  // score exceeds it by more than kRescaleGap, rescaling O, Z[0..nz) and l,
-  // and returns e = exp2(s_true - m) as two K = 32 bf16 operands.
-  auto softmax64 = [&](f32x4_t (&s)[4], float mref, int nz, u32x4_t (&eb)[2]) {
+  // score exceeds it by more than kRescaleGap, rescaling O, Z and l, and
+  // returns e = exp2(s_true - m) as two K = 32 bf16 operands.
+  auto softmax64 = [&](f32x4_t (&s)[4], float mref, u32x4_t (&eb)[2]) {
     float mx = kNegInf;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
@@ -296,8 +374,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
 #pragma unroll
         for (int dt = 0; dt < kD / 16; ++dt) O[dt] *= alpha;
 #pragma unroll
-        for (int zt = 0; zt < kMaxR / 16; ++zt)
-          if (zt < nz) Z[zt] *= alpha;
+        for (int zt = 0; zt < kMaxR / 16; ++zt) Z[zt] *= alpha;
         l_run *= alpha;
       }
       m_run = m_new;
@@ -322,47 +399,41 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
   };
 
   if (!tail) {
-    u32x4_t pf[kStageSlots];
-    for (int b = blk_lo; b < blk_hi; ++b) {
-      const milo_block blk = p.blocks[b0 + b];
-      const int T = max(blk.n_tok, 0), ld = blk.ld_tok;
-      const int r = min(max(blk.rank_k, 0), kD), rv = min(max(blk.rank_v, 0), kD);
-      // 16-rank chunks: scores use at least one (a rank-0 block scores 0
-      // against zero-padded factors); values use none for rank' 0
-      const int nk = max(1, (r + 15) / 16), nv = (rv + 15) / 16;
-      const int urows = nk * 16, vrows = nv * 16;
-      const uint16_t* head = reinterpret_cast<const uint16_t*>(p.pool) + blk.off +
-                             (int64_t)g * (r + rv) * (ld + kD);
-      const rsrc_t rs = make_rsrc(head, (uint32_t)((r + rv) * (ld + kD)) * 2);
-      const uint32_t w_off = (uint32_t)(r * ld) * 2;
-      const uint32_t v_off = w_off + (uint32_t)(r * kD) * 2;
-      const uint32_t wp_off = v_off + (uint32_t)(rv * ld) * 2;
-      const int ntiles = (T + kTT - 1) / kTT;
-      StageSlots ss;
-      plan_slots(ss, tid, r, rv, urows, vrows, ld, v_off);
-
-      __syncthreads();   // the previous block's LDS reads are done
-      {
-        // W and W' rows to LDS, all loads in flight together
-        u32x4_t wv[kWSlots], wpv[kWSlots];
-#pragma unroll
-        for (int k = 0; k < kWSlots; ++k) {
-          const int id = tid + kThreads * k, row = id / (kD / 8), ch = id % (kD / 8);
-          const uint32_t off = (uint32_t)(row * kD + ch * 8) * 2;
-          wv[k] = bld16_or0(rs, w_off + off, row < r);
-          wpv[k] = bld16_or0(rs, wp_off + off, row < rv);
-        }
-#pragma unroll
-        for (int k = 0; k < kWSlots; ++k) {
-          const int id = tid + kThreads * k, row = id / (kD / 8), ch = id % (kD / 8);
-          if (row < urows) *reinterpret_cast<u32x4_t*>(lds.w + row * kWPitch + ch * 8) = wv[k];
-          if (row < vrows) *reinterpret_cast<u32x4_t*>(lds.wp + row * kWPitch + ch * 8) = wpv[k];
-        }
+    // Pipeline over the unit's tiles k = 0, 1, ...: tile k + 2 is issued at
+    // step k, after the step's barrier (its buffer was last read at step
+    // k - 1).  Every step waits with vmcnt(4): all loads but the newest tile
+    // (issued at step k - 1, after any W / W' loads of that step) are done.
+    BlockInfo cb, pb;                     // compute block, prefetch block
+    block_info(cb, p, b0 + blk_lo, g);
+    pb = cb;
+    int pblk = blk_lo, pt = 0;            // next tile to issue: block pblk, tile pt
+    int kpre = 0;                         // global index of that tile
+    auto advance_pre = [&]() {
+      ++kpre;
+      if (++pt >= pb.ntiles) {
+        pt = 0;
+        if (++pblk < blk_hi) {
+          block_info(pb, p, b0 + pblk, g);
+              }
       }
-      u32x4_t qv[kD / 32];
-      load_q(qv);
-      if (ntiles > 0) load_tile(pf, rs, ss, ld, 0);
-      __syncthreads();
+    };
+    auto issue_next = [&](int ln) -> bool {
+      if (pblk >= blk_hi) return false;
+      issue_tile(pb, tile_buf(kpre), pt * kTT, ln, wave);
+      advance_pre();
+      return true;
+    };
+    issue_w(cb, ldsW, false, lane, wave);
+    issue_w(cb, ldsWp, true, lane, wave);
+    issue_next(lane);
+    bool newest = issue_next(lane);           // was a tile issued at the previous step?
+    load_q();
+    int k = 0;                            // global index of the tile computed now
+
+    for (int b = blk_lo; b < blk_hi; ++b) {
+      if (b > blk_lo) block_info(cb, p, b0 + b, g);
+      const int T = cb.T, r = cb.r, nv = cb.nv, ntiles = cb.ntiles;
+      const bool has_next = b + 1 < blk_hi;
 #pragma unroll
       for (int zt = 0; zt < kMaxR / 16; ++zt) Z[zt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -372,44 +443,62 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
         constexpr int NK = decltype(nk_c)::value;
         constexpr int NK2 = NK / 2;           // K = 32 chunks
         constexpr bool REM = (NK & 1) != 0;   // trailing K = 16 chunk
-        // ---- P^T = W Q^T per 16-rank tile, scaled, split into hi/lo operands
         u32x4_t ph[NK2 > 0 ? NK2 : 1], pl[NK2 > 0 ? NK2 : 1];
         u32x2_t ph16, pl16;
-        {
-          f32x4_t pt[NK];
-#pragma unroll
-          for (int rt = 0; rt < NK; ++rt) {
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-            const uint16_t* wrow = lds.w + (16 * rt + (lane & 15)) * kWPitch + 8 * q4;
-#pragma unroll
-            for (int kk = 0; kk < kD / 32; ++kk)
-              acc = mfma32(*reinterpret_cast<const u32x4_t*>(wrow + 32 * kk), qv[kk], acc);
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              acc[v] = (16 * rt + 4 * q4 + v < r) ? acc[v] * p.scale_log2 : 0.f;
-            pt[rt] = acc;
-          }
-#pragma unroll
-          for (int j = 0; j < NK2; ++j) split_pair(pt[2 * j], pt[2 * j + 1], ph[j], pl[j]);
-          if (REM) split_one(pt[NK - 1], ph16, pl16);
-        }
-
-        if (ntiles > 0) store_tile(pf, &lds.tile[0], ss, T, 0);
-        __syncthreads();
-
-        for (int t = 0; t < ntiles; ++t) {
-          const int buf = t & 1;
+        for (int t = 0; t < ntiles; ++t, ++k) {
+          if (newest) wait_barrier<4>(); else wait_barrier<0>();
+          const int ln = opaque(lane);
+          const char* U = tile_buf(k);
+          const char* V = U + kHalfTile;
           const int t0 = t * kTT;
-          if (t + 1 < ntiles) load_tile(pf, rs, ss, ld, t0 + kTT);
-          const uint16_t* U = lds.tile[buf].u;
-          const uint16_t* V = lds.tile[buf].v;
+          if (t == 0) {
+            if (b > blk_lo) issue_w(cb, ldsWp, true, ln, wave);   // W' of this block
+            // ---- P^T = W Q^T per 16-rank tile, scaled, split into hi/lo operands
+            f32x4_t pt[NK];
+#pragma unroll
+            for (int rt = 0; rt < NK; ++rt) {
+              f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int kk = 0; kk < kD / 32; ++kk)
+                acc = mfma32(w_operand(ldsW, 16 * rt, kk, ln), qv[kk], acc);
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+                acc[v] = (16 * rt + 4 * q4 + v < r) ? acc[v] * p.scale_log2 : 0.f;
+              pt[rt] = acc;
+            }
+#pragma unroll
+            for (int j = 0; j < NK2; ++j) split_pair(pt[2 * j], pt[2 * j + 1], ph[j], pl[j]);
+            if (REM) split_one(pt[NK - 1], ph16, pl16);
+            if (ntiles == 1 && has_next) {   // W is read: the next block's may land
+              wait_barrier<63>();
+              issue_w(pb, ldsW, false, ln, wave);
+            }
+          } else if (t == ntiles - 1 && has_next) {
+            issue_w(pb, ldsW, false, ln, wave);   // W of the next block
+          }
+          newest = issue_next(ln);
+          if (t0 + kTT > T && (T & 7)) {
+            // U'^T tokens past the block end in the tile's last partial chunk
+            // (row padding) are zeroed: they meet e = 0 in the MFMA.
+            if (tid < kMaxR) {
+              const int c = (T - t0) >> 3, n = (T - t0) & 7;
+              u32x4_t* pv = reinterpret_cast<u32x4_t*>(const_cast<char*>(V) + tid * 128 +
+                                                       ((c ^ swz_v(tid)) << 4));
+              u32x4_t v = *pv;
+#pragma unroll
+              for (int w = 0; w < 4; ++w)
+                v[w] &= (2 * w < n ? 0xffffu : 0u) | (2 * w + 1 < n ? 0xffff0000u : 0u);
+              *pv = v;
+            }
+            wait_barrier<63>();
+          }
 
-          // ---- S^T = U P^T (hi + lo) for the tile's four 16-token blocks;
-          // the chains start from -mref, so scores arrive relative to it.
+          // ---- S^T = U P^T (hi + lo) for the tile's four 16-token blocks,
+          // chunk-outer so that the four chains' reads are in flight
+          // together; the chains start from -mref, so scores arrive
+          // relative to it.
           const float mref = score_ref();
           const f32x4_t bias = {-mref, -mref, -mref, -mref};
-          // Chunk-outer order: the four chains' operand reads for one rank
-          // chunk are in flight together before their MFMAs.
           f32x4_t s[4];
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) s[tt] = bias;
@@ -417,7 +506,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
           for (int j = 0; j < NK2; ++j) {
             u32x4_t a[4];
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) a[tt] = tr_operand(U, kUPitch, 32 * j, 16 * tt, lane);
+            for (int tt = 0; tt < 4; ++tt) a[tt] = tr_operand<8, swz_u>(U, 32 * j, 16 * tt, ln);
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
               s[tt] = mfma32(a[tt], ph[j], s[tt]);
@@ -427,7 +516,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
           if (REM) {
             u32x2_t a[4];
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) a[tt] = tr_operand16(U, kUPitch, 32 * NK2, 16 * tt, lane);
+            for (int tt = 0; tt < 4; ++tt) a[tt] = tr_operand16<8, swz_u>(U, 32 * NK2, 16 * tt, ln);
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
               s[tt] = mfma16(a[tt], ph16, s[tt]);
@@ -442,17 +531,16 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
                 if (t0 + 16 * tt + 4 * q4 + v >= T) s[tt][v] = kNegInf;
           }
           u32x4_t eb[2];
-          softmax64(s, mref, nv, eb);
-          // ---- Z^T += U'^T E^T
-          // pairs of rank' tiles, four operand reads in flight
+          softmax64(s, mref, eb);
+          // ---- Z^T += U'^T E^T, pairs of rank' tiles, four reads in flight
 #pragma unroll
           for (int vt = 0; vt < kMaxR / 16; vt += 2) {
             if (vt < nv) {
               u32x4_t a[4];
 #pragma unroll
               for (int c = 0; c < 2; ++c) {
-                a[c] = row_operand(V, kVPitch, 16 * vt, 32 * c, lane);
-                a[2 + c] = row_operand(V, kVPitch, 16 * vt + 16, 32 * c, lane);
+                a[c] = v_operand(V, 16 * vt, 32 * c, ln);
+                a[2 + c] = v_operand(V, 16 * vt + 16, 32 * c, ln);
               }
 #pragma unroll
               for (int c = 0; c < 2; ++c) Z[vt] = mfma32(a[c], eb[c], Z[vt]);
@@ -462,11 +550,9 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
               }
             }
           }
-          if (t + 1 < ntiles) store_tile(pf, &lds.tile[buf ^ 1], ss, T, t0 + kTT);
-          __syncthreads();
         }
       };
-      switch (nk) {
+      switch (cb.nk) {
         case 1: body(IntC<1>{}); break;
         case 2: body(IntC<2>{}); break;
         case 3: body(IntC<3>{}); break;
@@ -477,8 +563,11 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
         default: body(IntC<8>{}); break;
       }
 
-      // ---- O^T += W'^T Z^T (W' staged and visible since the barriers above;
-      // its rows past rank' are zero, as are Z's)
+      // ---- O^T += W'^T Z^T.  W' was issued at this block's first step; a
+      // single-tile block waits for it here.  Its rows past rank' are zero,
+      // as are Z's.
+      if (ntiles == 1) wait_barrier<0>();
+      const int ln = opaque(lane);
 #pragma unroll
       for (int j = 0; j < kMaxR / 32; ++j) {
         if (2 * j + 1 < nv) {
@@ -486,7 +575,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
           split_pair(Z[2 * j], Z[2 * j + 1], zh, zl);
 #pragma unroll
           for (int dt = 0; dt < kD / 16; ++dt) {
-            const u32x4_t a = tr_operand(lds.wp, kWPitch, 32 * j, 16 * dt, lane);
+            const u32x4_t a = tr_operand<16, swz_wp>(ldsWp, 32 * j, 16 * dt, ln);
             O[dt] = mfma32(a, zh, O[dt]);
             O[dt] = mfma32(a, zl, O[dt]);
           }
@@ -495,55 +584,46 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
           split_one(Z[2 * j], zh, zl);
 #pragma unroll
           for (int dt = 0; dt < kD / 16; ++dt) {
-            const u32x2_t a = tr_operand16(lds.wp, kWPitch, 32 * j, 16 * dt, lane);
+            const u32x2_t a = tr_operand16<16, swz_wp>(ldsWp, 32 * j, 16 * dt, ln);
             O[dt] = mfma16(a, zh, O[dt]);
             O[dt] = mfma16(a, zl, O[dt]);
           }
         }
       }
     }
+    // no load of this unit is left in flight (the last steps issued none)
+    __builtin_amdgcn_s_waitcnt(0);
   } else {
     // ---- dense causal tail: token l is visible to query j iff l <= L - Q + j.
-    // 64-token tiles of K and V are staged in LDS (the W and W' regions).
+    // 64-token tiles of K (W region) and V (W' region), one at a time.
     const int cap = p.tail_cap;
     const int L = min(max(p.tail_len[i], 0), cap);
     const uint16_t* kt = reinterpret_cast<const uint16_t*>(p.k_tail) + ((size_t)i * p.n_kv_heads + g) * cap * kD;
     const uint16_t* vtp = reinterpret_cast<const uint16_t*>(p.v_tail) + ((size_t)i * p.n_kv_heads + g) * cap * kD;
-    const rsrc_t rk = make_rsrc(kt, (uint32_t)(cap * kD) * 2);
-    const rsrc_t rvv = make_rsrc(vtp, (uint32_t)(cap * kD) * 2);
+    const u32x4_t rk = rsrc_words(kt, (uint32_t)(cap * kD) * 2);
+    const u32x4_t rvv = rsrc_words(vtp, (uint32_t)(cap * kD) * 2);
     const int vis = L - p.q_len + j_l;   // last visible tail token of this row
-    u32x4_t qv[kD / 32];
-    load_q(qv);
-    constexpr int kTailSlots = kTT * (kD / 8) / kThreads;
+    load_q();
     for (int t0 = 0; t0 < L; t0 += kTT) {
-      __syncthreads();
-      {
-        u32x4_t kv[kTailSlots], vv[kTailSlots];
+      wait_barrier<0>();   // the previous tile's reads are done
+      const int ln = opaque(lane);
 #pragma unroll
-        for (int k = 0; k < kTailSlots; ++k) {
-          const int id = tid + kThreads * k, row = id / (kD / 8), ch = id % (kD / 8);
-          const uint32_t off = (uint32_t)((t0 + row) * kD + ch * 8) * 2;
-          kv[k] = bld16_or0(rk, off, t0 + row < L);
-          vv[k] = bld16_or0(rvv, off, t0 + row < L);
-        }
-#pragma unroll
-        for (int k = 0; k < kTailSlots; ++k) {
-          const int id = tid + kThreads * k, row = id / (kD / 8), ch = id % (kD / 8);
-          *reinterpret_cast<u32x4_t*>(lds.w + row * kWPitch + ch * 8) = kv[k];
-          *reinterpret_cast<u32x4_t*>(lds.wp + row * kWPitch + ch * 8) = vv[k];
-        }
+      for (int k = 0; k < 2; ++k) {
+        const int rb = 8 * k + wave;
+        const int row = rb * 4 + (ln >> 4);
+        const bool ok = t0 + row < L;
+        dma16(rk, ldsW + rb * 1024, (uint32_t)((t0 + row) * kD + ((ln & 15) ^ swz_w(row)) * 8) * 2, ok);
+        dma16(rvv, ldsWp + rb * 1024, (uint32_t)((t0 + row) * kD + ((ln & 15) ^ swz_wp(row)) * 8) * 2, ok);
       }
-      __syncthreads();
+      wait_barrier<0>();
       // S^T = K_tail q^T (K = d), scaled, relative to mref, causally masked
       const float mref = score_ref();
       f32x4_t s[4];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        const uint16_t* krow = lds.w + (16 * tt + (lane & 15)) * kWPitch + 8 * q4;
 #pragma unroll
-        for (int kk = 0; kk < kD / 32; ++kk)
-          acc = mfma32(*reinterpret_cast<const u32x4_t*>(krow + 32 * kk), qv[kk], acc);
+        for (int kk = 0; kk < kD / 32; ++kk) acc = mfma32(w_operand(ldsW, 16 * tt, kk, ln), qv[kk], acc);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int tok = t0 + 16 * tt + 4 * q4 + v;
@@ -552,13 +632,13 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
         s[tt] = acc;
       }
       u32x4_t eb[2];
-      softmax64(s, mref, 0, eb);
+      softmax64(s, mref, eb);
       // O^T += V_tail^T E^T
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int dt = 0; dt < kD / 16; ++dt)
-          O[dt] = mfma32(tr_operand(lds.wp, kWPitch, 32 * c, 16 * dt, lane), eb[c], O[dt]);
+          O[dt] = mfma32(tr_operand<16, swz_wp>(ldsWp, 32 * c, 16 * dt, ln), eb[c], O[dt]);
     }
   }
 
