@@ -19,6 +19,12 @@
 //   - values: the same lane/token ownership; e is packed to bf16 token pairs
 //     against rows of U'^T; per-lane partial z of up to 64 (row, head) slots
 //     are summed across the wave by one transposing butterfly.
+// The U^T and U'^T streams are read once and wave-coalesced, so they are
+// loaded non-temporally.  W and W' are read lane-per-row (W) or in short
+// rows (W'), with all of a unit's rows of W in flight at once (one memory
+// round trip) and W' in batches of 32 rows.  A unit is one wave, so LDS
+// hand-offs between its lanes need no barrier (a barrier would also wait
+// for every load in flight).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -26,7 +32,7 @@ namespace milo {
 
 namespace {
 
-constexpr int kLdsWords = 2048;
+constexpr int kLdsWords = 2560;   // p (4 KB) | z partials (4 KB) | q of the group (2 KB)
 constexpr float kNegInf = -__builtin_huge_valf();
 
 template <int D, int G>
@@ -42,37 +48,62 @@ struct Shape {
 // bf16 storage
 // ---------------------------------------------------------------------------
 
-// p = scale*log2(e) * W q for the G heads, fp32; lane k owns rows k and k+64.
-// Written to LDS as pf[k*8 + h].  q and W are bf16, so dot2 products are exact.
-// Loads are unconditional (row index clamped to r-1) so they can be issued
-// back to back; rows >= r are never read from pf.  Requires r >= 1.
+// Orders this wave's LDS writes before its later LDS reads for the
+// compiler.  A unit is one wave, and the LDS executes one wave's requests
+// in order, so no barrier (which would also wait for every load in flight)
+// is needed.
+__device__ __forceinline__ void wave_lds_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
+
+// p = scale*log2(e) * W q for the G heads, fp32; lane k owns rows k and k+64
+// (the second only when r > 64).  q is staged in LDS (ql) and read back as
+// broadcasts; every W load of the lane is issued before the first product,
+// so the projection costs one memory round trip.  q and W are bf16, so the
+// dot2 products are exact.  Rows are clamped to r-1; rows >= r are never
+// read from pf.  Requires r >= 1.
 template <int D, int G>
 __device__ __forceinline__ void bf16_project_q(const uint16_t* W, const uint16_t* qh, int r,
-                                               float scale_log2, float* pf, int lane) {
+                                               float scale_log2, float* pf, uint16_t* ql, int lane) {
+  constexpr int NC = D / 8, NQ = G * NC;   // 16-byte chunks per row; q chunks of the group
+  u32x4_t q0 = {0u, 0u, 0u, 0u}, q1 = {0u, 0u, 0u, 0u};
+  if (lane < NQ) q0 = ld16(qh + lane * 8);
+  if (lane + 64 < NQ) q1 = ld16(qh + (lane + 64) * 8);
+  const bool two = D > 64 && r > 64;
+  u32x4_t wa[NC], wb[NC];
+  const uint16_t* wa_row = W + (size_t)min(lane, r - 1) * D;
+  const uint16_t* wb_row = W + (size_t)min(lane + 64, r - 1) * D;
+#pragma unroll
+  for (int jc = 0; jc < NC; ++jc) wa[jc] = ld16(wa_row + jc * 8);
+  if (two) {
+#pragma unroll
+    for (int jc = 0; jc < NC; ++jc) wb[jc] = ld16(wb_row + jc * 8);
+  }
+  if (lane < NQ) *reinterpret_cast<u32x4_t*>(ql + lane * 8) = q0;
+  if (lane + 64 < NQ) *reinterpret_cast<u32x4_t*>(ql + (lane + 64) * 8) = q1;
+  wave_lds_fence();
   float pa[G], pb[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) { pa[h] = 0.f; pb[h] = 0.f; }
-  const uint16_t* wa_row = W + (size_t)min(lane, r - 1) * D;
-  const uint16_t* wb_row = W + (size_t)min(lane + 64, r - 1) * D;
-#pragma unroll 4
-  for (int jc = 0; jc < D / 8; ++jc) {
-    const u32x4_t wa = ld16(wa_row + jc * 8);
-    u32x4_t wb = {0, 0, 0, 0};
-    if (D > 64) wb = ld16(wb_row + jc * 8);
+#pragma unroll
+  for (int jc = 0; jc < NC; ++jc)
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const u32x4_t qv = ld16(qh + h * D + jc * 8);
+      const u32x4_t qv = *reinterpret_cast<const u32x4_t*>(ql + h * D + jc * 8);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        pa[h] = dot2bf(wa[w], qv[w], pa[h]);
-        if (D > 64) pb[h] = dot2bf(wb[w], qv[w], pb[h]);
-      }
+      for (int w = 0; w < 4; ++w) pa[h] = dot2bf(wa[jc][w], qv[w], pa[h]);
     }
-  }
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    pf[lane * 8 + h] = pa[h] * scale_log2;
-    if (D > 64) pf[(lane + 64) * 8 + h] = pb[h] * scale_log2;
+  for (int h = 0; h < G; ++h) pf[lane * 8 + h] = pa[h] * scale_log2;
+  if (two) {
+#pragma unroll
+    for (int jc = 0; jc < NC; ++jc)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const u32x4_t qv = *reinterpret_cast<const u32x4_t*>(ql + h * D + jc * 8);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) pb[h] = dot2bf(wb[jc][w], qv[w], pb[h]);
+      }
+#pragma unroll
+    for (int h = 0; h < G; ++h) pf[(lane + 64) * 8 + h] = pb[h] * scale_log2;
   }
 }
 
@@ -85,8 +116,8 @@ __device__ __forceinline__ void load_rows4(const uint16_t* Ut, int ld, int k0, i
 #pragma unroll
   for (int j = 0; j < kRowsPerStep; ++j) {
     const uint16_t* row = Ut + (size_t)min(k0 + j, r - 1) * ld;
-    A[j] = ld16(row + tq0);
-    B[j] = ld16(row + tq1);
+    A[j] = ld16_stream(row + tq0);
+    B[j] = ld16_stream(row + tq1);
   }
 }
 
@@ -206,8 +237,8 @@ __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* U
 #pragma unroll
       for (int rho = 0; rho < R; ++rho) {
         const uint16_t* row = Upt + (size_t)min(gi * R + rho, rv - 1) * ld;
-        U0[rho] = ld16(row + tq0);
-        U1[rho] = ld16(row + tq1);
+        U0[rho] = ld16_stream(row + tq0);
+        U1[rho] = ld16_stream(row + tq1);
       }
       float acc[64];
 #pragma unroll
@@ -246,11 +277,11 @@ __device__ __forceinline__ void block_unit_bf16(const DecodeParams& p, int i, in
   const uint16_t* qh = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)i * p.n_q_heads + g * G) * D;
 
   float* pf = reinterpret_cast<float*>(lds);
-  if (r > 0) bf16_project_q<D, G>(W, qh, r, p.scale_log2, pf, lane);
+  if (r > 0) bf16_project_q<D, G>(W, qh, r, p.scale_log2, pf, reinterpret_cast<uint16_t*>(lds + 2048), lane);
   // z partial sums live in LDS: zl[gi*64 + l] = slot l of row group gi
   float* zl = reinterpret_cast<float*>(lds + 1024);
   for (int gi = 0; gi < NG; ++gi) zl[gi * 64 + lane] = 0.f;
-  __syncthreads();
+  wave_lds_fence();
 
   float m_run[G], l_run[G];
 #pragma unroll
@@ -261,23 +292,25 @@ __device__ __forceinline__ void block_unit_bf16(const DecodeParams& p, int i, in
   else
     bf16_tiles<D, G, false>(Ut, Upt, ld, T, r, rv, pf, m_run, l_run, zl, lane);
 
-  // ---- o~ = z W'; eight rows of W' in flight per step
-  __syncthreads();
+  // ---- o~ = z W'; lane owns output columns JPL*lane .. +JPL-1; 32 rows of
+  // W' in flight per step
+  wave_lds_fence();
+  constexpr int kWpRows = 32;
   float o[G][JPL];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int jj = 0; jj < JPL; ++jj) o[h][jj] = 0.f;
-  for (int k0 = 0; k0 < rv; k0 += 8) {
-    uint32_t wraw[8];
+  for (int k0 = 0; k0 < rv; k0 += kWpRows) {
+    uint32_t wraw[kWpRows];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kWpRows; ++j) {
       const uint16_t* wrow = Wp + (size_t)min(k0 + j, rv - 1) * D;
       wraw[j] = (JPL == 2) ? *reinterpret_cast<const uint32_t*>(wrow + 2 * lane)
                            : (uint32_t)wrow[lane] << 16;
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kWpRows; ++j) {
       const int kp = k0 + j;
       if (kp < rv) {
         const int gi = kp / R, rho = kp - gi * R;
@@ -516,6 +549,15 @@ __device__ __forceinline__ void tail_unit(const DecodeParams& p, int i, int g, i
     for (int jj = 0; jj < JPL; ++jj) o[h][jj] = 0.f;
   }
   float* el = reinterpret_cast<float*>(lds);   // [64 tokens][8 heads]
+  // bf16: q of the group staged in LDS (read back as broadcasts)
+  uint16_t* ql = reinterpret_cast<uint16_t*>(lds + 2048);
+  if (DT == MILO_BF16 && L > 0) {
+    constexpr int NQ = G * D / 8;
+    const uint16_t* qh = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)i * p.n_q_heads + g * G) * D;
+    if (lane < NQ) *reinterpret_cast<u32x4_t*>(ql + lane * 8) = ld16(qh + lane * 8);
+    if (lane + 64 < NQ) *reinterpret_cast<u32x4_t*>(ql + (lane + 64) * 8) = ld16(qh + (lane + 64) * 8);
+    wave_lds_fence();
+  }
   for (int t0 = 0; t0 < L; t0 += 64) {
     const int t = t0 + lane;
     const bool valid = t < L;
@@ -524,18 +566,19 @@ __device__ __forceinline__ void tail_unit(const DecodeParams& p, int i, int g, i
     for (int h = 0; h < G; ++h) s[h] = 0.f;
     const int tk = min(t, L - 1);   // lanes past the end re-read the last token (masked)
     if (DT == MILO_BF16) {
+      // the whole key row of the lane's token in flight at once
       const uint16_t* K = reinterpret_cast<const uint16_t*>(p.k_tail) + kv_off + (size_t)tk * D;
-      const uint16_t* qh = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)i * p.n_q_heads + g * G) * D;
-#pragma unroll 4
-      for (int jc = 0; jc < D / 8; ++jc) {
-        const u32x4_t kv = ld16(K + jc * 8);
+      u32x4_t kv[D / 8];
+#pragma unroll
+      for (int jc = 0; jc < D / 8; ++jc) kv[jc] = ld16(K + jc * 8);
+#pragma unroll
+      for (int jc = 0; jc < D / 8; ++jc)
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const u32x4_t qv = ld16(qh + h * D + jc * 8);
+          const u32x4_t qv = *reinterpret_cast<const u32x4_t*>(ql + h * D + jc * 8);
 #pragma unroll
-          for (int w = 0; w < 4; ++w) s[h] = dot2bf(kv[w], qv[w], s[h]);
+          for (int w = 0; w < 4; ++w) s[h] = dot2bf(kv[jc][w], qv[w], s[h]);
         }
-      }
     } else {
       const float* K = reinterpret_cast<const float*>(p.k_tail) + kv_off + (size_t)tk * D;
       const float* qh = reinterpret_cast<const float*>(p.q) + ((int64_t)i * p.n_q_heads + g * G) * D;
@@ -564,13 +607,14 @@ __device__ __forceinline__ void tail_unit(const DecodeParams& p, int i, int g, i
 #pragma unroll
       for (int jj = 0; jj < JPL; ++jj) o[h][jj] *= alpha[h];
     }
-    __syncthreads();
+    wave_lds_fence();
     // o~ += e^T V over the tile, eight token rows of V in flight per step
+    constexpr int kVRows = 8;
     const int nt = min(64, L - t0);
-    for (int tt0 = 0; tt0 < nt; tt0 += 8) {
-      float vv[8][JPL];
+    for (int tt0 = 0; tt0 < nt; tt0 += kVRows) {
+      float vv[kVRows][JPL];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < kVRows; ++j) {
         const size_t row = kv_off + (size_t)(t0 + min(tt0 + j, nt - 1)) * D;
         if (DT == MILO_BF16) {
           const uint16_t* V = reinterpret_cast<const uint16_t*>(p.v_tail) + row;
@@ -588,7 +632,7 @@ __device__ __forceinline__ void tail_unit(const DecodeParams& p, int i, int g, i
         }
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < kVRows; ++j) {
         if (tt0 + j < nt) {
 #pragma unroll
           for (int h = 0; h < G; ++h) {
@@ -599,7 +643,7 @@ __device__ __forceinline__ void tail_unit(const DecodeParams& p, int i, int g, i
         }
       }
     }
-    __syncthreads();
+    wave_lds_fence();
   }
   float* po = p.part.o + (size_t)unit * G * D;
 #pragma unroll

@@ -21,6 +21,13 @@ __device__ __forceinline__ u32x4_t ld16(const void* p) {
 __device__ __forceinline__ f32x4_t ld16f(const void* p) {
   return *reinterpret_cast<const f32x4_t*>(p);
 }
+// 16-byte load of data read once per launch, wave-coalesced (a wave's lanes
+// cover whole cache lines): marked non-temporal, so the stream does not
+// displace cached data.  Not for lane-strided reads, whose lines are
+// reused by the lane's next loads.
+__device__ __forceinline__ u32x4_t ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
 
 // Raw buffer resource over [base, base + bytes): loads at offsets past the end
 // return zeros instead of faulting.  The third dword selects the 32-bit data
