@@ -161,6 +161,7 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-plan", action="store_true", help="natural work-unit order (no schedule)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dump-steps", action="store_true", help="print each timed step's kernel time")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -246,6 +247,9 @@ def main(argv=None):
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     kern_ms = [hip.elapsed_ms(a, b) for a, b in evs]
+    if args.dump_steps:
+        print("[bench] kernel us per step: " + " ".join(f"{x * 1e3:.1f}" for x in kern_ms),
+              file=sys.stderr, flush=True)
     for a, b in evs:
         hip.destroy(a)
         hip.destroy(b)

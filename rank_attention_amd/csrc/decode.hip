@@ -19,10 +19,12 @@
 //   - values: the same lane/token ownership; e is packed to bf16 token pairs
 //     against rows of U'^T; per-lane partial z of up to 64 (row, head) slots
 //     are summed across the wave by one transposing butterfly.
+//   - o~ += z W' is applied per row group as soon as the group's z is
+//     reduced; the group's W' rows load with its U'^T rows, so no memory
+//     round trip is left after the last group.
 // The U^T and U'^T streams are read once and wave-coalesced, so they are
-// loaded non-temporally.  W and W' are read lane-per-row (W) or in short
-// rows (W'), with all of a unit's rows of W in flight at once (one memory
-// round trip) and W' in batches of 32 rows.  A unit is one wave, so LDS
+// loaded non-temporally.  W is read lane-per-row, all of the unit's rows in
+// flight at once (one memory round trip).  A unit is one wave, so LDS
 // hand-offs between its lanes need no barrier (a barrier would also wait
 // for every load in flight).
 #include "device_common.h"
@@ -147,12 +149,17 @@ __device__ __forceinline__ void score_rows4(const u32x4_t (&A)[kRowsPerStep],
   }
 }
 
+// One 1024-token tile at a time: scores, online softmax, then per group of
+// R rows of U'^T the group's z = e^T U' and at once o~ += z W' for those
+// rows (W' rows load with the group), so no pass over W' is left at the end.
+// o~ is rescaled with the softmax like l.
 template <int D, int G, bool RAGGED>
-__device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* Upt, int ld, int T,
-                                           int r, int rv, const float* pf, float (&m_run)[G],
-                                           float (&l_run)[G], float* zl, int lane) {
+__device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* Upt,
+                                           const uint16_t* Wp, int ld, int T, int r, int rv,
+                                           const float* pf, float (&m_run)[G], float (&l_run)[G],
+                                           float (&o)[G][D / 64], float* zs, int lane) {
   using S = Shape<D, G>;
-  constexpr int R = S::R;
+  constexpr int R = S::R, JPL = S::JPL;
   for (int t0 = 0; t0 < T; t0 += 1024) {
     const int tc0 = t0 + lane * 8, tc1 = t0 + 512 + lane * 8;
     const bool ok0 = tc0 < T, ok1 = tc1 < T;
@@ -210,16 +217,14 @@ __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* U
       l_run[h] = l_run[h] * alpha[h] + wave_sum(sum);
       m_run[h] = mn;
     }
-    {
-      const int hl = lane % G;
-      float al = alpha[0];
 #pragma unroll
-      for (int h = 1; h < G; ++h) al = (hl == h) ? alpha[h] : al;
-      for (int gi = 0; gi * R < rv; ++gi) zl[gi * 64 + lane] *= al;
-    }
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int jj = 0; jj < JPL; ++jj) o[h][jj] *= alpha[h];
 
-    // ---- z = e^T U'  (value factor), reduced per group of R rows.  Rows past
-    // rv are loaded clamped to rv-1 and land in slots that are never read.
+    // ---- z = e^T U'  (value factor), reduced per group of R rows, then
+    // o~ += z W' for the group.  Rows past rv are loaded clamped to rv-1 and
+    // land in slots that are never read.
     // Masks zero the U' elements of tokens past the block end (padding may
     // hold NaN); a lane with no valid token has e = 0 and a finite chunk.
     u32x4_t mask0 = {~0u, ~0u, ~0u, ~0u}, mask1 = {~0u, ~0u, ~0u, ~0u};
@@ -234,11 +239,19 @@ __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* U
 #pragma unroll 1
     for (int gi = 0; gi * R < rv; ++gi) {
       u32x4_t U0[R], U1[R];
+      uint32_t wr[R];   // the lane's JPL columns of the group's W' rows
 #pragma unroll
       for (int rho = 0; rho < R; ++rho) {
-        const uint16_t* row = Upt + (size_t)min(gi * R + rho, rv - 1) * ld;
+        const int k = min(gi * R + rho, rv - 1);
+        const uint16_t* row = Upt + (size_t)k * ld;
         U0[rho] = ld16_stream(row + tq0);
         U1[rho] = ld16_stream(row + tq1);
+      }
+#pragma unroll
+      for (int rho = 0; rho < R; ++rho) {
+        const uint16_t* wrow = Wp + (size_t)min(gi * R + rho, rv - 1) * D;
+        wr[rho] = (JPL == 2) ? *reinterpret_cast<const uint32_t*>(wrow + 2 * lane)
+                             : (uint32_t)wrow[lane] << 16;
       }
       float acc[64];
 #pragma unroll
@@ -255,7 +268,25 @@ __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* U
             acc[rho * G + h] = dot2bf(u1[w], e2[1][w][h], acc[rho * G + h]);
           }
       }
-      zl[gi * 64 + lane] += reduce_transpose64(acc, lane);
+      // lane l ends with z of slot l = (row rho, head h); staged in LDS as
+      // zs[rho*8 + h] and read back as broadcasts
+      const float zg = reduce_transpose64(acc, lane);
+      if (lane < R * G) zs[(lane / G) * 8 + lane % G] = zg;
+      wave_lds_fence();
+#pragma unroll
+      for (int rho = 0; rho < R; ++rho) {
+        if (gi * R + rho < rv) {
+          const f32x4_t z0 = *reinterpret_cast<const f32x4_t*>(zs + rho * 8);
+          const f32x4_t z1 = *reinterpret_cast<const f32x4_t*>(zs + rho * 8 + 4);
+          const float zz[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
+          const float wv[2] = {bf_lo(wr[rho]), bf_hi(wr[rho])};
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int jj = 0; jj < JPL; ++jj) o[h][jj] = fmaf(zz[h], wv[JPL == 2 ? jj : 1], o[h][jj]);
+        }
+      }
+      wave_lds_fence();
     }
   }
 }
@@ -264,7 +295,7 @@ template <int D, int G>
 __device__ __forceinline__ void block_unit_bf16(const DecodeParams& p, int i, int g, int unit,
                                                 const milo_block& blk, uint32_t* lds) {
   using S = Shape<D, G>;
-  constexpr int R = S::R, NG = S::NG, JPL = S::JPL;
+  constexpr int JPL = S::JPL;
   const int lane = threadIdx.x;
   const int T = max(blk.n_tok, 0);
   const int ld = blk.ld_tok;
@@ -278,53 +309,23 @@ __device__ __forceinline__ void block_unit_bf16(const DecodeParams& p, int i, in
 
   float* pf = reinterpret_cast<float*>(lds);
   if (r > 0) bf16_project_q<D, G>(W, qh, r, p.scale_log2, pf, reinterpret_cast<uint16_t*>(lds + 2048), lane);
-  // z partial sums live in LDS: zl[gi*64 + l] = slot l of row group gi
-  float* zl = reinterpret_cast<float*>(lds + 1024);
-  for (int gi = 0; gi < NG; ++gi) zl[gi * 64 + lane] = 0.f;
-  wave_lds_fence();
+  // z of one row group, staged for broadcast reads: zs[rho*8 + h]
+  float* zs = reinterpret_cast<float*>(lds + 1024);
 
-  float m_run[G], l_run[G];
+  float m_run[G], l_run[G], o[G][JPL];
 #pragma unroll
-  for (int h = 0; h < G; ++h) { m_run[h] = kNegInf; l_run[h] = 0.f; }
-
-  if (T & 7)
-    bf16_tiles<D, G, true>(Ut, Upt, ld, T, r, rv, pf, m_run, l_run, zl, lane);
-  else
-    bf16_tiles<D, G, false>(Ut, Upt, ld, T, r, rv, pf, m_run, l_run, zl, lane);
-
-  // ---- o~ = z W'; lane owns output columns JPL*lane .. +JPL-1; 32 rows of
-  // W' in flight per step
-  wave_lds_fence();
-  constexpr int kWpRows = 32;
-  float o[G][JPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int h = 0; h < G; ++h) {
+    m_run[h] = kNegInf;
+    l_run[h] = 0.f;
 #pragma unroll
     for (int jj = 0; jj < JPL; ++jj) o[h][jj] = 0.f;
-  for (int k0 = 0; k0 < rv; k0 += kWpRows) {
-    uint32_t wraw[kWpRows];
-#pragma unroll
-    for (int j = 0; j < kWpRows; ++j) {
-      const uint16_t* wrow = Wp + (size_t)min(k0 + j, rv - 1) * D;
-      wraw[j] = (JPL == 2) ? *reinterpret_cast<const uint32_t*>(wrow + 2 * lane)
-                           : (uint32_t)wrow[lane] << 16;
-    }
-#pragma unroll
-    for (int j = 0; j < kWpRows; ++j) {
-      const int kp = k0 + j;
-      if (kp < rv) {
-        const int gi = kp / R, rho = kp - gi * R;
-        const float* zp = zl + gi * 64 + rho * G;
-        const float wv[2] = {bf_lo(wraw[j]), bf_hi(wraw[j])};
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float z = zp[h];
-#pragma unroll
-          for (int jj = 0; jj < JPL; ++jj) o[h][jj] = fmaf(z, wv[JPL == 2 ? jj : 1], o[h][jj]);
-        }
-      }
-    }
   }
+  wave_lds_fence();
+
+  if (T & 7)
+    bf16_tiles<D, G, true>(Ut, Upt, Wp, ld, T, r, rv, pf, m_run, l_run, o, zs, lane);
+  else
+    bf16_tiles<D, G, false>(Ut, Upt, Wp, ld, T, r, rv, pf, m_run, l_run, o, zs, lane);
 
   float* po = p.part.o + (size_t)unit * G * D;
 #pragma unroll
