@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MILO_ABI_VERSION 1
+#define MILO_ABI_VERSION 2
 
 typedef enum milo_status {
   MILO_OK = 0,
@@ -69,7 +69,8 @@ typedef enum milo_dtype {
 
 typedef enum milo_path {
   MILO_PATH_DECODE = 0,      /* one new query token per sequence                         */
-  MILO_PATH_CHUNK = 1        /* q_len new query tokens per sequence                      */
+  MILO_PATH_CHUNK = 1,       /* q_len new query tokens per sequence                      */
+  MILO_PATH_SHARED = 2       /* one query token per sequence, one context for the batch  */
 } milo_path;
 
 /*
@@ -136,6 +137,19 @@ milo_status milo_attn_decode(const milo_attn_args* args, void* hip_stream);
  * values are the last Q entries of the tail; query j sees every block token
  * and tail tokens l <= tail_len[i] - Q + j.  Writes out and lse. */
 milo_status milo_attn_chunk(const milo_attn_args* args, void* hip_stream);
+
+/* Decode over one compressed context shared by the whole batch: the
+ * pre-encoded many-shot cache of one demonstration set ("1. Introduction")
+ * serving many test queries.  Same arguments and result as milo_attn_decode
+ * (q_len must be 1), except that every sequence attends to the blocks listed
+ * for sequence 0 (blocks[seq_blocks[0] .. seq_blocks[1]-1]; the other
+ * sequences' lists are not read) plus its own tail.  The shared factors are
+ * read once for all batch * group query rows of a KV head: the blocks are
+ * evaluated as dense contractions on the MFMA path, so this entry point
+ * needs bf16 storage and head_dim 128 (MILO_ERR_UNSUPPORTED otherwise).
+ * Workspace: milo_attn_workspace_bytes(args, MILO_PATH_SHARED).
+ * prof_events bracket the block and tail kernels together. */
+milo_status milo_attn_decode_shared(const milo_attn_args* args, void* hip_stream);
 
 /*
  * Host-side scheduler for the decode kernel.  Decode work unit

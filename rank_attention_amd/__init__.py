@@ -13,11 +13,11 @@ from typing import Optional, Tuple
 import numpy as np
 
 from . import _lib
-from ._lib import (MILO_BF16, MILO_F32, MILO_PATH_CHUNK, MILO_PATH_DECODE, MiloAttnArgs,
+from ._lib import (MILO_BF16, MILO_F32, MILO_PATH_CHUNK, MILO_PATH_DECODE, MILO_PATH_SHARED, MiloAttnArgs,
                    MILO_OK, MILO_ERR_DEVICE)
 from .pack import BLOCK_DTYPE, PackedCache, pack  # noqa: F401
 
-__all__ = ["decode", "chunk", "workspace_bytes", "abi_version", "status_str", "DeviceCache",
+__all__ = ["decode", "chunk", "decode_shared", "workspace_bytes", "abi_version", "status_str", "DeviceCache",
            "pack", "PackedCache", "MiloError", "library_path"]
 
 library_path = _lib.LIB_PATH
@@ -93,17 +93,17 @@ def _run(path: int, q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_
     a = make_args(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, n_kv_heads=n_kv_heads,
                   scale=scale, max_blocks=max_blocks, out=out, lse=lse, workspace=workspace,
                   prof_events=prof_events, unit_order=unit_order)
+    fn = {MILO_PATH_DECODE: lib.milo_attn_decode, MILO_PATH_CHUNK: lib.milo_attn_chunk,
+          MILO_PATH_SHARED: lib.milo_attn_decode_shared}[path]
     if workspace is None:
         need = lib.milo_attn_workspace_bytes(ctypes.byref(a), path)
         if need == 0:
-            rc = (lib.milo_attn_decode if path == MILO_PATH_DECODE else lib.milo_attn_chunk)(
-                ctypes.byref(a), None)
+            rc = fn(ctypes.byref(a), None)
             raise MiloError(rc, status_str(rc))
         workspace = torch.empty(int(need), dtype=torch.uint8, device=dev)
         a.workspace, a.workspace_bytes = workspace.data_ptr(), int(need)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
-    fn = lib.milo_attn_decode if path == MILO_PATH_DECODE else lib.milo_attn_chunk
     rc = fn(ctypes.byref(a), ctypes.c_void_p(int(stream)))
     if rc != MILO_OK:
         if rc == MILO_ERR_DEVICE:
@@ -123,6 +123,15 @@ def chunk(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_kv_heads: 
           max_blocks: int, **kw):
     """Chunked-query attention (q_len = Q, bottom-right causal over the tail)."""
     return _run(MILO_PATH_CHUNK, q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len,
+                n_kv_heads=n_kv_heads, scale=scale, max_blocks=max_blocks, **kw)
+
+
+def decode_shared(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_kv_heads: int,
+                  scale: float, max_blocks: int, **kw):
+    """Decode (q_len = 1) with the blocks of sequence 0 shared by every
+    sequence; each sequence keeps its own tail.  Same result layout as decode."""
+    kw.pop("unit_order", None)
+    return _run(MILO_PATH_SHARED, q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len,
                 n_kv_heads=n_kv_heads, scale=scale, max_blocks=max_blocks, **kw)
 
 
@@ -165,3 +174,7 @@ class DeviceCache:
     def chunk(self, **kw):
         kw.setdefault("scale", self.scale)
         return chunk(*self.tensors(), n_kv_heads=self.n_kv_heads, max_blocks=self.max_blocks, **kw)
+
+    def decode_shared(self, **kw):
+        kw.setdefault("scale", self.scale)
+        return decode_shared(*self.tensors(), n_kv_heads=self.n_kv_heads, max_blocks=self.max_blocks, **kw)

@@ -9,8 +9,8 @@ LIB_PATH = os.path.join(HERE, "libmilo_attn.so")
 
 MILO_OK, MILO_ERR_INVALID, MILO_ERR_UNSUPPORTED, MILO_ERR_WORKSPACE, MILO_ERR_DEVICE = range(5)
 MILO_F32, MILO_BF16 = 0, 1
-MILO_PATH_DECODE, MILO_PATH_CHUNK = 0, 1
-EXPORTS = ("milo_attn_workspace_bytes", "milo_attn_decode", "milo_attn_chunk",
+MILO_PATH_DECODE, MILO_PATH_CHUNK, MILO_PATH_SHARED = 0, 1, 2
+EXPORTS = ("milo_attn_workspace_bytes", "milo_attn_decode", "milo_attn_chunk", "milo_attn_decode_shared",
            "milo_attn_plan_decode", "milo_status_str", "milo_abi_version")
 
 
@@ -61,7 +61,7 @@ def load() -> ctypes.CDLL:
         lib = ctypes.CDLL(LIB_PATH)
         lib.milo_attn_workspace_bytes.argtypes = [ctypes.POINTER(MiloAttnArgs), ctypes.c_int32]
         lib.milo_attn_workspace_bytes.restype = ctypes.c_size_t
-        for fn in (lib.milo_attn_decode, lib.milo_attn_chunk):
+        for fn in (lib.milo_attn_decode, lib.milo_attn_chunk, lib.milo_attn_decode_shared):
             fn.argtypes = [ctypes.POINTER(MiloAttnArgs), ctypes.c_void_p]
             fn.restype = ctypes.c_int
         lib.milo_attn_plan_decode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,

@@ -326,6 +326,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
   const int blk_hi = min(nb, blk_lo + p.blocks_per_range);
   const bool tail = slot == p.n_ranges;
   if (!tail && blk_lo >= blk_hi) return;   // empty range: the merge skips it
+  if (tail && p.no_tail) return;
 
   // Q^T operand chunks qv[kk] = q[row m_l][32kk + 8(l/16) .. +8], held for
   // the whole unit.  Lanes past the last row read row 0: their columns are
@@ -651,7 +652,8 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
     l_run = c + d;
   }
   if (row_ok) {
-    const size_t rec = ((size_t)((i * p.n_kv_heads + g) * S + slot)) * MQ + m_l;
+    const int si = i + m_l / p.part_rows, ml = m_l % p.part_rows;
+    const size_t rec = ((size_t)((si * p.n_kv_heads + g) * S + slot)) * p.part_rows + ml;
     float* po = p.part.o + rec * kD;
 #pragma unroll
     for (int dt = 0; dt < kD / 16; ++dt)

@@ -28,6 +28,7 @@ struct DecodeParams {
   Partials part;
   const int32_t* unit_order;   // optional largest-first permutation of the units
   int32_t batch, n_q_heads, n_kv_heads, max_blocks, tail_cap;
+  int32_t tail_only;  // launch only the dense-tail unit of each (sequence, KV head)
   float scale_log2;   // scale * log2(e)
 };
 
@@ -45,6 +46,12 @@ struct ChunkParams {
   int32_t n_ranges;          // block ranges per (sequence, KV head); slot n_ranges = tail
   int32_t blocks_per_range;
   int32_t group;             // query heads per KV head (set by launch_chunk)
+  // Partial records: query row m of a unit of sequence i goes to sequence
+  // i + m / part_rows, row m % part_rows of that sequence's unit slot
+  // (part_rows = q_len * group, or group when the query rows of a shared
+  // context stack the batch's sequences).
+  int32_t part_rows;
+  int32_t no_tail;           // skip the tail slot (its partials come from elsewhere)
   float scale_log2;
 };
 
@@ -58,6 +65,7 @@ struct MergeParams {
   int32_t rows_per_unit;    // query rows stored per unit slot (q_len * group)
   int32_t tail_slot;        // slot of the dense-tail unit
   int32_t blocks_per_slot;  // slot s < tail_slot holds blocks [s*bps, (s+1)*bps)
+  int32_t seq_stride;       // sequence i's block count is read at seq_blocks[i * seq_stride]
 };
 
 // Work units of the decode kernel: one per (sequence, KV head, block slot),

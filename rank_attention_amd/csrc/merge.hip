@@ -35,7 +35,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void milo_merge_kernel(MergeParam
   const int j = ij % p.q_len, i = ij / p.q_len;
   const int G = p.n_q_heads / p.n_kv_heads;
   const int g = h / G, hl = h - g * G;
-  const int nb = min(max(p.seq_blocks[i + 1] - p.seq_blocks[i], 0), p.max_blocks);
+  const int si = i * p.seq_stride;
+  const int nb = min(max(p.seq_blocks[si + 1] - p.seq_blocks[si], 0), p.max_blocks);
   const size_t rec0 = (size_t)(i * p.n_kv_heads + g) * p.slots * p.rows_per_unit + j * G + hl;
   const size_t rstride = p.rows_per_unit;
 

@@ -28,19 +28,19 @@ inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_
 milo_status check_shape(const milo_attn_args* a, int32_t path) {
   if (!a) return MILO_ERR_INVALID;
   if (a->struct_size != (int32_t)sizeof(milo_attn_args)) return MILO_ERR_INVALID;
-  if (path != MILO_PATH_DECODE && path != MILO_PATH_CHUNK) return MILO_ERR_INVALID;
+  if (path != MILO_PATH_DECODE && path != MILO_PATH_CHUNK && path != MILO_PATH_SHARED) return MILO_ERR_INVALID;
   if (a->dtype != MILO_F32 && a->dtype != MILO_BF16) return MILO_ERR_UNSUPPORTED;
   if (a->batch < 0 || a->q_len < 1 || a->n_q_heads < 1 || a->n_kv_heads < 1) return MILO_ERR_INVALID;
   if (a->n_q_heads % a->n_kv_heads != 0) return MILO_ERR_INVALID;
   if (a->max_blocks_per_seq < 0 || a->tail_cap < 0) return MILO_ERR_INVALID;
   if (!std::isfinite(a->scale)) return MILO_ERR_INVALID;
-  if (path == MILO_PATH_DECODE && a->q_len != 1) return MILO_ERR_INVALID;
+  if ((path == MILO_PATH_DECODE || path == MILO_PATH_SHARED) && a->q_len != 1) return MILO_ERR_INVALID;
   if (path == MILO_PATH_CHUNK && a->tail_cap < a->q_len) return MILO_ERR_INVALID;
   if (a->head_dim != 64 && a->head_dim != 128) return MILO_ERR_UNSUPPORTED;
   const int group = a->n_q_heads / a->n_kv_heads;
   if (group > 8) return MILO_ERR_UNSUPPORTED;
-  // the MFMA chunk kernel is built for bf16 storage and head_dim 128
-  if (path == MILO_PATH_CHUNK && (a->dtype != MILO_BF16 || a->head_dim != 128)) return MILO_ERR_UNSUPPORTED;
+  // the MFMA chunk kernel (chunk and shared paths) is built for bf16 storage and head_dim 128
+  if (path != MILO_PATH_DECODE && (a->dtype != MILO_BF16 || a->head_dim != 128)) return MILO_ERR_UNSUPPORTED;
   return MILO_OK;
 }
 
@@ -52,12 +52,13 @@ struct ChunkSplit {
 };
 
 // Split each (sequence, KV head) into 128-row query tiles and block ranges
-// so that the grid has about kChunkTargetUnits workgroups.
-ChunkSplit chunk_split(const milo_attn_args* a) {
+// so that the grid has about kChunkTargetUnits workgroups.  With a shared
+// context the batch's query rows form one sequence of batch * group rows.
+ChunkSplit chunk_split(const milo_attn_args* a, bool shared = false) {
   ChunkSplit c{};
-  const int64_t rows = (int64_t)a->q_len * (a->n_q_heads / a->n_kv_heads);
+  const int64_t rows = (int64_t)(shared ? a->batch : a->q_len) * (a->n_q_heads / a->n_kv_heads);
   c.n_qtiles = (int32_t)((rows + kChunkRowsPerTile - 1) / kChunkRowsPerTile);
-  const int64_t base = std::max<int64_t>(1, (int64_t)a->batch * a->n_kv_heads * c.n_qtiles);
+  const int64_t base = std::max<int64_t>(1, (int64_t)(shared ? 1 : a->batch) * a->n_kv_heads * c.n_qtiles);
   const int32_t mb = std::max(a->max_blocks_per_seq, 1);
   int32_t nr = (int32_t)std::min<int64_t>(mb, std::max<int64_t>(1, (kChunkTargetUnits + base - 1) / base));
   c.blocks_per_range = (mb + nr - 1) / nr;
@@ -75,7 +76,9 @@ struct Layout {
 Layout layout_of(const milo_attn_args* a, int32_t path) {
   Layout L{};
   const int group = a->n_q_heads / a->n_kv_heads;
-  L.slots = path == MILO_PATH_CHUNK ? chunk_split(a).n_ranges + 1 : a->max_blocks_per_seq + 1;
+  L.slots = path == MILO_PATH_CHUNK    ? chunk_split(a).n_ranges + 1
+            : path == MILO_PATH_SHARED ? chunk_split(a, true).n_ranges + 1
+                                       : a->max_blocks_per_seq + 1;
   L.rows_per_unit = a->q_len * group;
   L.units = (int64_t)a->batch * a->n_kv_heads * L.slots;
   L.o_bytes = round_up((size_t)L.units * L.rows_per_unit * a->head_dim * sizeof(float), kWsAlign);
@@ -162,6 +165,7 @@ milo_status milo_attn_decode(const milo_attn_args* a, void* hip_stream) {
   m.rows_per_unit = L.rows_per_unit;
   m.tail_slot = a->max_blocks_per_seq;
   m.blocks_per_slot = 1;
+  m.seq_stride = 1;
   if (milo::launch_merge(m, a->head_dim, stream) != hipSuccess) return MILO_ERR_DEVICE;
   return MILO_OK;
 }
@@ -198,6 +202,8 @@ milo_status milo_attn_chunk(const milo_attn_args* a, void* hip_stream) {
   p.n_qtiles = cs.n_qtiles;
   p.n_ranges = cs.n_ranges;
   p.blocks_per_range = cs.blocks_per_range;
+  p.part_rows = a->q_len * group;
+  p.no_tail = 0;
   p.scale_log2 = a->scale * milo::kLog2eHost;
 
   const bool timing = a->prof_events[0] && a->prof_events[1];
@@ -221,6 +227,93 @@ milo_status milo_attn_chunk(const milo_attn_args* a, void* hip_stream) {
   m.rows_per_unit = L.rows_per_unit;
   m.tail_slot = cs.n_ranges;
   m.blocks_per_slot = cs.blocks_per_range;
+  m.seq_stride = 1;
+  if (milo::launch_merge(m, a->head_dim, stream) != hipSuccess) return MILO_ERR_DEVICE;
+  return MILO_OK;
+}
+
+milo_status milo_attn_decode_shared(const milo_attn_args* a, void* hip_stream) {
+  milo_status st = check_shape(a, MILO_PATH_SHARED);
+  if (st != MILO_OK) return st;
+  const Layout L = layout_of(a, MILO_PATH_SHARED);
+  st = check_pointers(a, L);
+  if (st != MILO_OK) return st;
+  if (a->batch == 0) return MILO_OK;
+
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  const int group = a->n_q_heads / a->n_kv_heads;
+  const ChunkSplit cs = chunk_split(a, true);
+  char* ws = static_cast<char*>(a->workspace);
+  Partials part{reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + L.o_bytes)};
+
+  // Blocks: the MFMA kernel over one "sequence" whose batch * group query
+  // rows are the batch's queries (q is [batch][1][n_q_heads][d], the same
+  // memory as [1][batch][n_q_heads][d]); block list of sequence 0; its
+  // partials land in every sequence's own unit slots (part_rows = group).
+  milo::ChunkParams p{};
+  p.q = a->q;
+  p.pool = a->pool;
+  p.blocks = a->blocks;
+  p.seq_blocks = a->seq_blocks;
+  p.k_tail = a->k_tail;
+  p.v_tail = a->v_tail;
+  p.tail_len = a->tail_len;
+  p.part = part;
+  p.batch = 1;
+  p.q_len = a->batch;
+  p.n_q_heads = a->n_q_heads;
+  p.n_kv_heads = a->n_kv_heads;
+  p.max_blocks = a->max_blocks_per_seq;
+  p.tail_cap = a->tail_cap;
+  p.n_qtiles = cs.n_qtiles;
+  p.n_ranges = cs.n_ranges;
+  p.blocks_per_range = cs.blocks_per_range;
+  p.part_rows = group;
+  p.no_tail = 1;
+  p.scale_log2 = a->scale * milo::kLog2eHost;
+
+  // Tails: the decode kernel's dense-tail unit of every (sequence, KV head),
+  // written to slot n_ranges of that sequence's units.
+  DecodeParams t{};
+  t.q = a->q;
+  t.pool = a->pool;
+  t.blocks = a->blocks;
+  t.seq_blocks = a->seq_blocks;
+  t.k_tail = a->k_tail;
+  t.v_tail = a->v_tail;
+  t.tail_len = a->tail_len;
+  t.part = part;
+  t.batch = a->batch;
+  t.n_q_heads = a->n_q_heads;
+  t.n_kv_heads = a->n_kv_heads;
+  t.max_blocks = cs.n_ranges;
+  t.tail_cap = a->tail_cap;
+  t.tail_only = 1;
+  t.scale_log2 = a->scale * milo::kLog2eHost;
+
+  const bool timing = a->prof_events[0] && a->prof_events[1];
+  if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[0]), stream) != hipSuccess)
+    return MILO_ERR_DEVICE;
+  if (milo::launch_chunk(p, group, stream) != hipSuccess) return MILO_ERR_DEVICE;
+  if (milo::launch_decode(t, a->dtype, a->head_dim, group, stream) != hipSuccess) return MILO_ERR_DEVICE;
+  if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[1]), stream) != hipSuccess)
+    return MILO_ERR_DEVICE;
+
+  MergeParams m{};
+  m.part = part;
+  m.seq_blocks = a->seq_blocks;
+  m.out = a->out;
+  m.lse = a->lse;
+  m.batch = a->batch;
+  m.q_len = 1;
+  m.n_q_heads = a->n_q_heads;
+  m.n_kv_heads = a->n_kv_heads;
+  m.max_blocks = a->max_blocks_per_seq;
+  m.slots = L.slots;
+  m.rows_per_unit = L.rows_per_unit;
+  m.tail_slot = cs.n_ranges;
+  m.blocks_per_slot = cs.blocks_per_range;
+  m.seq_stride = 0;                   // every sequence uses sequence 0's block count
   if (milo::launch_merge(m, a->head_dim, stream) != hipSuccess) return MILO_ERR_DEVICE;
   return MILO_OK;
 }

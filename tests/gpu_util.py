@@ -34,7 +34,7 @@ def run_hip(wl: Workload, path: str = "decode", repeat: int = 1, **packkw):
          f"max_blocks={pc.max_blocks} tail_cap={pc.k_tail.shape[2]}")
     outs = []
     for _ in range(repeat):
-        out, lse = dc.decode() if path == "decode" else dc.chunk()
+        out, lse = {"decode": dc.decode, "chunk": dc.chunk, "shared": dc.decode_shared}[path]()
         torch.cuda.synchronize()
         outs.append((out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)))
     return outs if repeat > 1 else outs[0]

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_struct_size():
-    assert ra.abi_version() == 1
+    assert ra.abi_version() == 2
     # 7 int32 + float, 4 pointers, 2 int32, 6 pointers, size_t, 3 pointers; the
     # C side agrees, or the batch-0 call below would fail its struct_size check
     assert ctypes.sizeof(_lib.MiloAttnArgs) == 8 * 4 + 4 * 8 + 2 * 4 + 6 * 8 + 8 + 3 * 8
@@ -112,6 +112,36 @@ def test_decode_rejects_before_any_hip_call(over, code):
     lib = _lib.load()
     a.workspace_bytes = 1 << 30
     assert call(a) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"dtype": _lib.MILO_F32}, _lib.MILO_ERR_UNSUPPORTED),   # the MFMA path is bf16 only
+    ({"head_dim": 64}, _lib.MILO_ERR_UNSUPPORTED),           # and head_dim 128 only
+    ({"q_len": 2}, _lib.MILO_ERR_INVALID),                  # one query token per sequence
+    ({"n_q_heads": 32, "n_kv_heads": 2}, _lib.MILO_ERR_UNSUPPORTED),
+    ({"workspace": None}, _lib.MILO_ERR_WORKSPACE),
+])
+def test_shared_rejects_before_any_hip_call(over, code):
+    lib = _lib.load()
+    a = good_args(**{"head_dim": 128, **over})
+    a.workspace_bytes = 1 << 30
+    assert lib.milo_attn_decode_shared(ctypes.byref(a), None) == code
+    assert lib.milo_attn_decode_shared(None, None) == _lib.MILO_ERR_INVALID
+
+
+def test_shared_workspace_query():
+    """Shared path: the batch's B * G query rows form one tile set per KV head;
+    slots = block ranges + 1 tail slot per (sequence, KV head), G rows each."""
+    lib = _lib.load()
+    a = good_args(head_dim=128, batch=16, n_q_heads=28, n_kv_heads=4, max_blocks_per_seq=64)
+    need = lib.milo_attn_workspace_bytes(ctypes.byref(a), _lib.MILO_PATH_SHARED)
+    # 16 * 7 = 112 rows -> one 128-row tile; 4 KV heads -> base 4 workgroups;
+    # ranges = min(64, ceil(1024 / 4)) = 64 of one block each
+    units, rows = 16 * 4 * (64 + 1), 7
+    exp_o = -(-units * rows * 128 * 4 // 256) * 256
+    exp_ml = -(-units * rows * 2 * 4 // 256) * 256
+    assert need == exp_o + exp_ml
+    assert lib.milo_attn_workspace_bytes(ctypes.byref(good_args(head_dim=64)), _lib.MILO_PATH_SHARED) == 0
 
 
 def test_small_workspace_is_rejected():
