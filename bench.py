@@ -9,10 +9,16 @@ Decode workloads (the default, qwen7b_64k): context tokens/s for the step and
 the attention kernel's achieved HBM bandwidth on algorithmic bytes against the
 8 TB/s peak.  Chunked-query workloads (qwen32b_chunk): query tokens/s and the
 kernel's algorithmic bf16 FLOP rate against the 2.5 PFLOP/s dense MFMA peak.
+Shared-context decode (--shared, on a decode workload): every sequence of the
+batch attends to sequence 0's compressed context plus its own tail; context
+tokens/s counts each sequence's full context, and the roofline is that of the
+MFMA kernel, which reads the shared factors once and each sequence's tail
+(HBM-bound while the batch's query rows per KV head stay under the 312
+FLOP/byte ridge).
 Kernel time comes from HIP events recorded on the launch stream around the
 attention kernel alone; the fp64 CPU oracle is timed on a bounded sample.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen7b_64k]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen7b_64k] [--shared]
 """
 from __future__ import annotations
 
@@ -28,9 +34,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "low-rank-KV decode attn: context tokens/s and % of HBM peak (7B, 64k)"
+SHARED_METRIC = "low-rank-KV shared-context decode attn: context tokens/s (7B, 64k context shared by the batch)"
 CHUNK_METRIC = "low-rank-KV chunked-query attn: query tokens/s and % of bf16 MFMA peak (32B, Q=256)"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+LAST_LEVEL_CACHE_BYTES = 256 << 20   # MI355X Infinity Cache
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "decode": ["rank_attention_amd/csrc/decode.hip", "rank_attention_amd/csrc/device_common.h"],
@@ -87,15 +95,20 @@ def traffic_from_profiles(workload: str, path: str = "decode"):
     return rec.get("hbm_bytes_per_launch")
 
 
-def chunk_flops(wl) -> int:
+def chunk_flops(wl, shared: bool = False) -> int:
     """Algorithmic FLOPs of one chunked-query launch: per block and KV head
     2*M*(r + r')*(T + d) for the four factor products (M = Q*G query rows),
-    and 4*d per visible (query row, tail token) pair of the causal tail."""
+    and 4*d per visible (query row, tail token) pair of the causal tail.
+    Shared context: M = batch*G rows over sequence 0's blocks, plus each
+    sequence's G rows over its own tail."""
     cfg = wl.cfg
     G = cfg.n_q_heads // cfg.n_kv_heads
     Q, d = cfg.q_len, cfg.head_dim
     M = Q * G
     total = 0
+    if shared:
+        return (sum(2 * wl.batch * G * (b.rank_k + b.rank_v) * (b.n_tok + d) * cfg.n_kv_heads
+                    for b in wl.blocks[0]) + 4 * d * G * cfg.n_kv_heads * int(wl.tail_len.sum()))
     for i, seq in enumerate(wl.blocks):
         for b in seq:
             total += 2 * M * (b.rank_k + b.rank_v) * (b.n_tok + d) * cfg.n_kv_heads
@@ -156,6 +169,8 @@ def main(argv=None):
     ap.add_argument("--variant", default="base")
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch (sequences)")
     ap.add_argument("--q-heads", type=int, default=0, help="override the query heads (group size)")
+    ap.add_argument("--shared", action="store_true",
+                    help="shared-context decode: the batch attends to sequence 0's context")
     ap.add_argument("--copies", type=int, default=2,
                     help="pool copies read in rotation so no step finds the last one's bytes in cache")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -194,17 +209,39 @@ def main(argv=None):
 
     cfg = synth.get_config(args.workload)
     if args.batch:
-        cfg = cfg.with_(batch=args.batch)
+        cfg = cfg.with_(batch=args.batch, desc=f"{cfg.desc}; batch set to {args.batch}")
     if args.q_heads:
-        cfg = cfg.with_(n_q_heads=args.q_heads)
+        cfg = cfg.with_(n_q_heads=args.q_heads, desc=f"{cfg.desc}; {args.q_heads} query heads")
     is_chunk = cfg.path == "chunk"
-    path_code = _lib.MILO_PATH_CHUNK if is_chunk else _lib.MILO_PATH_DECODE
-    entry = lib.milo_attn_chunk if is_chunk else lib.milo_attn_decode
+    shared = args.shared
+    if shared and is_chunk:
+        print("--shared needs a decode workload", file=sys.stderr)
+        return 2
+    path_code = (_lib.MILO_PATH_CHUNK if is_chunk else
+                 _lib.MILO_PATH_SHARED if shared else _lib.MILO_PATH_DECODE)
+    entry = (lib.milo_attn_chunk if is_chunk else
+             lib.milo_attn_decode_shared if shared else lib.milo_attn_decode)
     t0 = time.time()
-    wl = synth.make_workload(cfg, variant=args.variant)
+    if shared:
+        # only sequence 0's blocks are packed: the shared path reads no other list
+        wl = synth.make_workload(cfg, variant=args.variant, n_blocks=[cfg.n_blocks] + [0] * (cfg.batch - 1))
+    else:
+        wl = synth.make_workload(cfg, variant=args.variant)
     pc = ra.pack(wl)
     dc = ra.DeviceCache(pc, device="cuda:0", scale=wl.scale)
-    pools = [dc.pool] + [dc.pool.clone() for _ in range(max(0, args.copies - 1))]
+    copies = args.copies
+    if shared:
+        # the shared factors and the tails are small: rotate enough copies of
+        # both that a step never finds the previous steps' bytes in the
+        # last-level cache
+        step_bytes = dc.pool.numel() * dc.pool.element_size()
+        if dc.k_tail is not None:
+            step_bytes += 2 * dc.k_tail.numel() * dc.k_tail.element_size()
+        copies = max(copies, -(-3 * LAST_LEVEL_CACHE_BYTES // max(1, step_bytes)))
+    pools = [dc.pool] + [dc.pool.clone() for _ in range(max(0, copies - 1))]
+    tails = [(dc.k_tail, dc.v_tail)] * len(pools)
+    if shared and dc.k_tail is not None:
+        tails = [(dc.k_tail, dc.v_tail)] + [(dc.k_tail.clone(), dc.v_tail.clone()) for _ in pools[1:]]
     B, Q, Hq, d = (int(x) for x in dc.q.shape)
     out = torch.empty((B, Q, Hq, d), dtype=torch.float32, device="cuda:0")
     lse = torch.empty((B, Q, Hq), dtype=torch.float32, device="cuda:0")
@@ -213,14 +250,17 @@ def main(argv=None):
     need = lib.milo_attn_workspace_bytes(ctypes.byref(a0), path_code)
     ws = torch.empty(int(need), dtype=torch.uint8, device="cuda:0")
     argsets = []
-    for pool in pools:
-        a = ra.make_args(dc.q, pool, dc.blocks, dc.seq_blocks, dc.k_tail, dc.v_tail, dc.tail_len,
+    for pool, (kt, vt) in zip(pools, tails):
+        a = ra.make_args(dc.q, pool, dc.blocks, dc.seq_blocks, kt, vt, dc.tail_len,
                          n_kv_heads=dc.n_kv_heads, scale=dc.scale, max_blocks=dc.max_blocks, out=out,
                          lse=lse, workspace=ws,
-                         unit_order=None if (args.no_plan or is_chunk) else dc.unit_order)
+                         unit_order=None if (args.no_plan or is_chunk or shared) else dc.unit_order)
         argsets.append(a)
     stream = torch.cuda.current_stream().cuda_stream
     setup_s = time.time() - t0
+    shared_factor_bytes = wl.factor_bytes()
+    if shared:
+        wl.blocks = [wl.blocks[0] for _ in range(wl.batch)]   # what every sequence attends to
     print(f"[bench] {cfg.desc}: factor {wl.factor_bytes() / 1e6:.1f} MB, tail {wl.tail_bytes() / 1e6:.1f} MB, "
           f"setup {setup_s:.1f} s", file=sys.stderr, flush=True)
 
@@ -232,7 +272,8 @@ def main(argv=None):
             a.prof_events[0] = a.prof_events[1] = None
         rc = entry(ctypes.byref(a), ctypes.c_void_p(stream))
         if rc != 0:
-            raise RuntimeError(f"milo_attn_{cfg.path} failed: {ra.status_str(rc)}")
+            raise RuntimeError(f"{'milo_attn_decode_shared' if shared else 'milo_attn_' + cfg.path} "
+                               f"failed: {ra.status_str(rc)}")
 
     for k in range(args.warmup):
         step(k)
@@ -258,7 +299,26 @@ def main(argv=None):
     kmean = sum(kern_ms) / len(kern_ms)
     kern_sorted = sorted(kern_ms)
     alg_bytes = wl.factor_bytes() + wl.tail_bytes()
-    if is_chunk:
+    prof_key = (cfg.name + "_shared", "chunk") if shared else (cfg.name, cfg.path)
+    if shared:
+        flops = chunk_flops(wl, shared=True)
+        alg_bytes = shared_factor_bytes + wl.tail_bytes()
+        t_hbm, t_mfma = alg_bytes / HBM_PEAK_GBS / 1e9, flops / MFMA_BF16_PEAK_TFLOPS / 1e12
+        if t_mfma > t_hbm:
+            achieved = flops / (kmean * 1e-3) / 1e12
+            peak, unit, bound = MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+        else:
+            achieved = alg_bytes / (kmean * 1e-3) / 1e9
+            peak, unit, bound = HBM_PEAK_GBS, "GB/s", "hbm"
+        value, vunit, metric = wl.context_tokens() / (ms_per_step * 1e-3), "context tokens/s", SHARED_METRIC
+        kname = "milo_chunk_kernel"
+        print(f"[bench] shared-context block kernel: mean {kmean * 1e3:.1f} us, median "
+              f"{kern_sorted[len(kern_sorted) // 2] * 1e3:.1f} us, min {kern_sorted[0] * 1e3:.1f} us; "
+              f"step {ms_per_step * 1e3:.1f} us; {flops / (kmean * 1e-3) / 1e12:.0f} TFLOP/s on "
+              f"{flops / 1e9:.2f} GFLOP, {alg_bytes / (kmean * 1e-3) / 1e9:.0f} GB/s on "
+              f"{alg_bytes / 1e6:.1f} MB shared factors + tails ({flops / max(1, alg_bytes):.0f} FLOP/B); "
+              f"{copies} pool copies", file=sys.stderr, flush=True)
+    elif is_chunk:
         flops = chunk_flops(wl)
         achieved = flops / (kmean * 1e-3) / 1e12
         peak, unit, bound = MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
@@ -295,15 +355,15 @@ def main(argv=None):
                    "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
                    "blocks_per_seq": cfg.n_blocks, "block_tokens": cfg.block_tokens,
                    "tail_len": cfg.tail_len, "context_tokens_per_step": wl.context_tokens(),
-                   "variant": args.variant, "pool_copies": len(pools)},
+                   "variant": args.variant, "pool_copies": len(pools), "shared_context": shared},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-                     "frac": achieved / peak, "traffic": traffic_from_profiles(cfg.name, cfg.path),
+                     "frac": achieved / peak, "traffic": traffic_from_profiles(*prof_key),
                      "kernel": kname, "kernel_us_mean": kmean * 1e3,
                      "algorithmic_bytes_per_launch": alg_bytes,
-                     "kernel_source_sha": kernel_source_sha(cfg.path)},
+                     "kernel_source_sha": kernel_source_sha(prof_key[1])},
         "cpu_baseline": None,
     }
-    if is_chunk:
+    if is_chunk or shared:
         res["roofline"]["algorithmic_flops_per_launch"] = flops
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = (cpu_baseline_chunk(wl, args.cpu_seconds) if is_chunk

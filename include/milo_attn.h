@@ -147,8 +147,8 @@ milo_status milo_attn_chunk(const milo_attn_args* args, void* hip_stream);
  * read once for all batch * group query rows of a KV head: the blocks are
  * evaluated as dense contractions on the MFMA path, so this entry point
  * needs bf16 storage and head_dim 128 (MILO_ERR_UNSUPPORTED otherwise).
- * Workspace: milo_attn_workspace_bytes(args, MILO_PATH_SHARED).
- * prof_events bracket the block and tail kernels together. */
+ * The sequences' own tails are evaluated in the same kernel launch.
+ * Workspace: milo_attn_workspace_bytes(args, MILO_PATH_SHARED). */
 milo_status milo_attn_decode_shared(const milo_attn_args* args, void* hip_stream);
 
 /*

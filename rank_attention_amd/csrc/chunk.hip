@@ -69,8 +69,8 @@ constexpr int kNBuf = 3;           // token-tile buffers: compute + two in fligh
 constexpr float kRescaleGap = 8.f; // log2 units: weights may reach 2^8 before m moves
 
 // LDS byte layout: W and W' (128 rows x 256 B), then the token tiles, each
-// U^T (128 rows x 128 B) followed by U'^T (128 rows x 128 B).  The tail
-// unit stages K in the W region and V in the W' region.
+// U^T (128 rows x 128 B) followed by U'^T (128 rows x 128 B).  A tail unit
+// uses the whole LDS as its own stages.
 constexpr int kWBytes = kMaxR * kD * 2;
 constexpr int kOffW = 0;
 constexpr int kOffWp = kWBytes;
@@ -79,6 +79,11 @@ constexpr int kTileBytes = 2 * kHalfTile;
 constexpr int kOffTile = 2 * kWBytes;
 constexpr int kLdsBytes = kOffTile + kNBuf * kTileBytes;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+// A tail unit's LDS: stages of one 64-token tile, K (64 rows x 256 B) then V.
+constexpr int kTailHalf = kTT * kD * 2;
+constexpr int kTailStageBytes = 2 * kTailHalf;
+constexpr int kTailStages = kLdsBytes / kTailStageBytes;
+static_assert(kTailStages == 5, "the tail loop's waits assume 4 tiles in flight");
 static_assert(kRowsPerTile == 128, "the host splits query rows in tiles of 128");
 
 // Swizzles (16-byte chunk index XOR a function of the row):
@@ -302,31 +307,51 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
   char* const ldsWp = lds + kOffWp;
   auto tile_buf = [&](int k) { return lds + kOffTile + (k % kNBuf) * kTileBytes; };
 
-  // workgroup -> (sequence, KV head, range slot, query tile).  The grid holds
+  // workgroup -> (sequence, KV head, range slot, query tile).  A shared-
+  // context launch first has ceil(tail_units / 8) * 8 workgroups for the
+  // per-sequence dense tails (sequence i, KV head g, one query token).  Then
   // ceil(groups / 8) * 8 * n_qtiles workgroups, dispatched round-robin over
   // the 8 XCDs: slot k of XCD x runs query tile k % n_qtiles of group
   // (k / n_qtiles) * 8 + x.
   const int S = p.n_ranges + 1;
-  const int n_groups = p.batch * p.n_kv_heads * S;
-  const int xcd = blockIdx.x & 7, k8 = blockIdx.x >> 3;
-  const int group = (k8 / p.n_qtiles) * 8 + xcd;
-  const int qt = k8 % p.n_qtiles;
-  if (group >= n_groups) return;
-  const int slot = group % S;
-  const int g = (group / S) % p.n_kv_heads, i = group / (S * p.n_kv_heads);
+  const int n_lead = (p.tail_units + 7) & ~7;
+  const bool lead = (int)blockIdx.x < n_lead;
+  int i, g, slot, qt, qlen;
+  if (lead) {
+    if ((int)blockIdx.x >= p.tail_units) return;
+    i = blockIdx.x / p.n_kv_heads;
+    g = blockIdx.x % p.n_kv_heads;
+    slot = p.n_ranges;
+    qt = 0;
+    qlen = 1;
+  } else {
+    const int n_groups = p.batch * p.n_kv_heads * S;
+    const int bid = blockIdx.x - n_lead;   // n_lead is a multiple of 8: same XCD
+    const int xcd = bid & 7, k8 = bid >> 3;
+    const int group = (k8 / p.n_qtiles) * 8 + xcd;
+    if (group >= n_groups) return;
+    qt = k8 % p.n_qtiles;
+    slot = group % S;
+    g = (group / S) % p.n_kv_heads;
+    i = group / (S * p.n_kv_heads);
+    qlen = p.q_len;
+  }
 
-  const int MQ = p.q_len * G;
+  const int MQ = qlen * G;
   const int m_l = qt * kRowsPerTile + wave * kRowsPerWave + (lane & 15);  // this lane's column
   const bool row_ok = m_l < MQ;
   const int j_l = m_l / G, hl = m_l - j_l * G;
 
-  const int b0 = p.seq_blocks[i];
-  const int nb = min(max(p.seq_blocks[i + 1] - b0, 0), p.max_blocks);
-  const int blk_lo = slot * p.blocks_per_range;
-  const int blk_hi = min(nb, blk_lo + p.blocks_per_range);
   const bool tail = slot == p.n_ranges;
-  if (!tail && blk_lo >= blk_hi) return;   // empty range: the merge skips it
-  if (tail && p.no_tail) return;
+  if (tail && p.no_tail && !lead) return;
+  int b0 = 0, blk_lo = 0, blk_hi = 0;
+  if (!tail) {
+    b0 = p.seq_blocks[i];
+    const int nb = min(max(p.seq_blocks[i + 1] - b0, 0), p.max_blocks);
+    blk_lo = slot * p.blocks_per_range;
+    blk_hi = min(nb, blk_lo + p.blocks_per_range);
+    if (blk_lo >= blk_hi) return;   // empty range: the merge skips it
+  }
 
   // Q^T operand chunks qv[kk] = q[row m_l][32kk + 8(l/16) .. +8], held for
   // the whole unit.  Lanes past the last row read row 0: their columns are
@@ -336,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
   u32x4_t qv[kD / 32];
   auto load_q = [&]() {
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
-                           (((int64_t)i * p.q_len + (row_ok ? j_l : 0)) * p.n_q_heads + g * G +
+                           (((int64_t)i * qlen + (row_ok ? j_l : 0)) * p.n_q_heads + g * G +
                             (row_ok ? hl : 0)) * kD + 8 * q4;
 #pragma unroll
     for (int kk = 0; kk < kD / 32; ++kk) qv[kk] = ld16(qrow + 32 * kk);
@@ -596,27 +621,45 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
     __builtin_amdgcn_s_waitcnt(0);
   } else {
     // ---- dense causal tail: token l is visible to query j iff l <= L - Q + j.
-    // 64-token tiles of K (W region) and V (W' region), one at a time.
+    // 64-token tiles of K and V through kTailStages LDS stages of 32 KB (the
+    // unit uses no other LDS), up to kTailStages - 1 tiles in flight.  Every
+    // lane issues 4 loads per tile, so tile t is in LDS once at most 4 * n
+    // loads are pending, n = tiles issued after it.
     const int cap = p.tail_cap;
-    const int L = min(max(p.tail_len[i], 0), cap);
+    const int L = cap > 0 ? min(max(p.tail_len[i], 0), cap) : 0;   // tail_len may be NULL if cap is 0
     const uint16_t* kt = reinterpret_cast<const uint16_t*>(p.k_tail) + ((size_t)i * p.n_kv_heads + g) * cap * kD;
     const uint16_t* vtp = reinterpret_cast<const uint16_t*>(p.v_tail) + ((size_t)i * p.n_kv_heads + g) * cap * kD;
     const u32x4_t rk = rsrc_words(kt, (uint32_t)(cap * kD) * 2);
     const u32x4_t rvv = rsrc_words(vtp, (uint32_t)(cap * kD) * 2);
-    const int vis = L - p.q_len + j_l;   // last visible tail token of this row
-    load_q();
-    for (int t0 = 0; t0 < L; t0 += kTT) {
-      wait_barrier<0>();   // the previous tile's reads are done
+    const int vis = L - qlen + j_l;   // last visible tail token of this row
+    const int nt = (L + kTT - 1) / kTT;
+    auto stage = [&](int t) { return lds + (t % kTailStages) * kTailStageBytes; };
+    auto issue_tail = [&](int t) {
       const int ln = opaque(lane);
+      char* const sk = stage(t);
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int rb = 8 * k + wave;
         const int row = rb * 4 + (ln >> 4);
-        const bool ok = t0 + row < L;
-        dma16(rk, ldsW + rb * 1024, (uint32_t)((t0 + row) * kD + ((ln & 15) ^ swz_w(row)) * 8) * 2, ok);
-        dma16(rvv, ldsWp + rb * 1024, (uint32_t)((t0 + row) * kD + ((ln & 15) ^ swz_wp(row)) * 8) * 2, ok);
+        const bool ok = t * kTT + row < L;
+        dma16(rk, sk + rb * 1024, (uint32_t)((t * kTT + row) * kD + ((ln & 15) ^ swz_w(row)) * 8) * 2, ok);
+        dma16(rvv, sk + kTailHalf + rb * 1024,
+              (uint32_t)((t * kTT + row) * kD + ((ln & 15) ^ swz_wp(row)) * 8) * 2, ok);
       }
-      wait_barrier<0>();
+    };
+    for (int t = 0; t < min(nt, kTailStages - 1); ++t) issue_tail(t);
+    load_q();   // also waits for this lane's tile loads
+    for (int t = 0; t < nt; ++t) {
+      // tile t complete in every wave; stage (t + 4) % 5, read at step t - 1, is free
+      switch (min(nt - 1, t + kTailStages - 2) - t) {
+        case 3: wait_barrier<12>(); break;
+        case 2: wait_barrier<8>(); break;
+        case 1: wait_barrier<4>(); break;
+        default: wait_barrier<0>(); break;
+      }
+      if (t + kTailStages - 1 < nt) issue_tail(t + kTailStages - 1);
+      const int ln = opaque(lane);
+      char* const sk = stage(t);
       // S^T = K_tail q^T (K = d), scaled, relative to mref, causally masked
       const float mref = score_ref();
       f32x4_t s[4];
@@ -624,10 +667,10 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
       for (int tt = 0; tt < 4; ++tt) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < kD / 32; ++kk) acc = mfma32(w_operand(ldsW, 16 * tt, kk, ln), qv[kk], acc);
+        for (int kk = 0; kk < kD / 32; ++kk) acc = mfma32(w_operand(sk, 16 * tt, kk, ln), qv[kk], acc);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int tok = t0 + 16 * tt + 4 * q4 + v;
+          const int tok = t * kTT + 16 * tt + 4 * q4 + v;
           acc[v] = (tok < L && tok <= vis) ? acc[v] * p.scale_log2 - mref : kNegInf;
         }
         s[tt] = acc;
@@ -639,7 +682,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int dt = 0; dt < kD / 16; ++dt)
-          O[dt] = mfma32(tr_operand<16, swz_wp>(ldsWp, 32 * c, 16 * dt, ln), eb[c], O[dt]);
+          O[dt] = mfma32(tr_operand<16, swz_wp>(sk + kTailHalf, 32 * c, 16 * dt, ln), eb[c], O[dt]);
     }
   }
 
@@ -671,7 +714,7 @@ hipError_t launch_chunk(const ChunkParams& p, int group, hipStream_t s) {
   const int64_t groups = (int64_t)p.batch * p.n_kv_heads * (p.n_ranges + 1);
   if (groups == 0) return hipSuccess;
   if (group < 1 || group > 8) return hipErrorInvalidValue;
-  const int64_t wgs = (groups + 7) / 8 * 8 * p.n_qtiles;
+  const int64_t wgs = (p.tail_units + 7) / 8 * 8 + (groups + 7) / 8 * 8 * p.n_qtiles;
   ChunkParams q = p;
   q.group = group;
   hipLaunchKernelGGL(milo_chunk_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, s, q);

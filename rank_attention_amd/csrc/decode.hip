@@ -663,8 +663,7 @@ template <int D, int G, int DT>
 __global__ __launch_bounds__(64) void milo_decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
   const int S = p.max_blocks + 1;
-  const int unit = p.tail_only ? (int)blockIdx.x * S + p.max_blocks
-                               : (p.unit_order ? p.unit_order[blockIdx.x] : (int)blockIdx.x);
+  const int unit = p.unit_order ? p.unit_order[blockIdx.x] : (int)blockIdx.x;
   if ((unsigned)unit >= (unsigned)(p.batch * p.n_kv_heads * S)) return;   // not a unit index
   const int slot = unit % S;
   const int ig = unit / S;
@@ -685,8 +684,7 @@ __global__ __launch_bounds__(64) void milo_decode_kernel(DecodeParams p) {
 
 template <int D, int DT>
 hipError_t launch_decode_dg(const DecodeParams& p, int group, hipStream_t s) {
-  const int64_t units = p.tail_only ? (int64_t)p.batch * p.n_kv_heads
-                                    : decode_units(p.batch, p.n_kv_heads, p.max_blocks);
+  const int64_t units = decode_units(p.batch, p.n_kv_heads, p.max_blocks);
   if (units == 0) return hipSuccess;
   const dim3 grid((unsigned)units), block(64);
   switch (group) {

@@ -28,7 +28,6 @@ struct DecodeParams {
   Partials part;
   const int32_t* unit_order;   // optional largest-first permutation of the units
   int32_t batch, n_q_heads, n_kv_heads, max_blocks, tail_cap;
-  int32_t tail_only;  // launch only the dense-tail unit of each (sequence, KV head)
   float scale_log2;   // scale * log2(e)
 };
 
@@ -51,7 +50,12 @@ struct ChunkParams {
   // (part_rows = q_len * group, or group when the query rows of a shared
   // context stack the batch's sequences).
   int32_t part_rows;
-  int32_t no_tail;           // skip the tail slot (its partials come from elsewhere)
+  int32_t no_tail;           // skip the tail slots of the range groups
+  // Shared context: the launch starts with one workgroup per (sequence,
+  // KV head) of the shared batch, tail_units = batch * n_kv_heads of them,
+  // each the dense tail of that sequence's own G query rows (q_len 1); 0
+  // otherwise.
+  int32_t tail_units;
   float scale_log2;
 };
 

@@ -39,6 +39,9 @@ milo_status check_shape(const milo_attn_args* a, int32_t path) {
   if (a->head_dim != 64 && a->head_dim != 128) return MILO_ERR_UNSUPPORTED;
   const int group = a->n_q_heads / a->n_kv_heads;
   if (group > 8) return MILO_ERR_UNSUPPORTED;
+  // partial records (query rows x unit slots) are indexed in 32 bits on the device
+  if ((int64_t)a->batch * a->q_len * a->n_q_heads * ((int64_t)a->max_blocks_per_seq + 1) > INT32_MAX)
+    return MILO_ERR_UNSUPPORTED;
   // the MFMA chunk kernel (chunk and shared paths) is built for bf16 storage and head_dim 128
   if (path != MILO_PATH_DECODE && (a->dtype != MILO_BF16 || a->head_dim != 128)) return MILO_ERR_UNSUPPORTED;
   return MILO_OK;
@@ -246,10 +249,12 @@ milo_status milo_attn_decode_shared(const milo_attn_args* a, void* hip_stream) {
   char* ws = static_cast<char*>(a->workspace);
   Partials part{reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + L.o_bytes)};
 
-  // Blocks: the MFMA kernel over one "sequence" whose batch * group query
-  // rows are the batch's queries (q is [batch][1][n_q_heads][d], the same
-  // memory as [1][batch][n_q_heads][d]); block list of sequence 0; its
-  // partials land in every sequence's own unit slots (part_rows = group).
+  // One MFMA kernel launch.  Blocks: one "sequence" whose batch * group
+  // query rows are the batch's queries (q is [batch][1][n_q_heads][d], the
+  // same memory as [1][batch][n_q_heads][d]) over sequence 0's block list;
+  // its partials land in every sequence's own unit slots (part_rows =
+  // group).  Tails: batch * n_kv_heads leading workgroups, each sequence's
+  // own tail for its G rows, written to slot n_ranges of its units.
   milo::ChunkParams p{};
   p.q = a->q;
   p.pool = a->pool;
@@ -270,32 +275,13 @@ milo_status milo_attn_decode_shared(const milo_attn_args* a, void* hip_stream) {
   p.blocks_per_range = cs.blocks_per_range;
   p.part_rows = group;
   p.no_tail = 1;
+  p.tail_units = a->batch * a->n_kv_heads;
   p.scale_log2 = a->scale * milo::kLog2eHost;
-
-  // Tails: the decode kernel's dense-tail unit of every (sequence, KV head),
-  // written to slot n_ranges of that sequence's units.
-  DecodeParams t{};
-  t.q = a->q;
-  t.pool = a->pool;
-  t.blocks = a->blocks;
-  t.seq_blocks = a->seq_blocks;
-  t.k_tail = a->k_tail;
-  t.v_tail = a->v_tail;
-  t.tail_len = a->tail_len;
-  t.part = part;
-  t.batch = a->batch;
-  t.n_q_heads = a->n_q_heads;
-  t.n_kv_heads = a->n_kv_heads;
-  t.max_blocks = cs.n_ranges;
-  t.tail_cap = a->tail_cap;
-  t.tail_only = 1;
-  t.scale_log2 = a->scale * milo::kLog2eHost;
 
   const bool timing = a->prof_events[0] && a->prof_events[1];
   if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[0]), stream) != hipSuccess)
     return MILO_ERR_DEVICE;
   if (milo::launch_chunk(p, group, stream) != hipSuccess) return MILO_ERR_DEVICE;
-  if (milo::launch_decode(t, a->dtype, a->head_dim, group, stream) != hipSuccess) return MILO_ERR_DEVICE;
   if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[1]), stream) != hipSuccess)
     return MILO_ERR_DEVICE;
 

@@ -94,6 +94,7 @@ def test_workspace_query():
     ({"batch": -1}, _lib.MILO_ERR_INVALID),
     ({"n_kv_heads": 0}, _lib.MILO_ERR_INVALID),
     ({"max_blocks_per_seq": -1}, _lib.MILO_ERR_INVALID),
+    ({"batch": 1 << 20, "max_blocks_per_seq": 1 << 10}, _lib.MILO_ERR_UNSUPPORTED),  # 32-bit indices
     ({"q": None}, _lib.MILO_ERR_INVALID),
     ({"out": None}, _lib.MILO_ERR_INVALID),
     ({"seq_blocks": None}, _lib.MILO_ERR_INVALID),

@@ -45,6 +45,16 @@ def test_chunk_ragged(hq, hkv, q_len):
     compare(out, lse, ref_o, ref_l, sharp_gates=True, name=cfg.name)
 
 
+
+def test_chunk_long_tails():
+    """Tails of up to 11 tiles of 64 tokens: the tail loop's LDS stages wrap
+    and refill while loads are in flight; lengths off the tile grid."""
+    cfg = small_chunk_cfg(name="chunk_long_tails", batch=3, q_len=20, tail_len=700, n_blocks=2, seed=23)
+    wl = synth.make_workload(cfg, variant="sharp", tail_len=[700, 20, 321])
+    out, lse = run_hip(wl, path="chunk")
+    ref_o, ref_l = oracle.attend(wl)
+    compare(out, lse, ref_o, ref_l, sharp_gates=True, name=cfg.name)
+
 def test_chunk_causal_planted_token():
     """A tail token whose key matches every query strongly may only reach the
     queries at or after its position."""

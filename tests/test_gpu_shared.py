@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 
 import oracle
+import rank_attention_amd as ra
 import synth
 from tests.gpu_util import compare, note, run_hip
 
@@ -94,3 +95,13 @@ def test_shared_qwen7b_64k_sampled():
     # every row against the regular decode path over per-sequence copies
     od, ld = run_hip(wl, path="decode")
     compare(out, lse, od, ld, sharp_gates=True, name="qwen7b_64k_shared_vs_decode")
+
+
+def test_shared_without_tails():
+    """tail_cap 0: no tail tensors at all (NULL tail pointers)."""
+    cfg = synth.get_config("qwen7b_64k").with_(name="shared_no_tail", batch=9, n_blocks=3, tail_len=0)
+    wl = shared(synth.make_workload(cfg, variant="sharp"))
+    assert ra.pack(wl).k_tail.shape[2] == 0
+    out, lse = run_hip(wl, path="shared")
+    ref_o, ref_l = oracle.attend(wl)
+    compare(out, lse, ref_o, ref_l, sharp_gates=True, name="shared_no_tail")
