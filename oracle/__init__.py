@@ -7,7 +7,8 @@ drawn by ``synth`` (token-major U, row-major W), never the packed pool.
 
 The arithmetic lives in ``milo_oracle.c`` (reconstruct K = U W, V = U' W',
 then plain two-pass softmax attention in double precision); this module only
-builds that file and marshals arrays into it.
+builds that file and marshals arrays into it.  ``oracle.encode`` is the
+encode step's oracle (per-block truncated SVD in numpy float64).
 """
 from __future__ import annotations
 

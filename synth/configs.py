@@ -108,3 +108,58 @@ CONFIG_ORDER = ["tiny", "qwen05b_16k", "qwen7b_64k", "qwen7b_128k", "qwen32b_chu
 
 def get_config(name: str) -> Config:
     return CONFIGS[name]
+
+
+# ---------------------------------------------------------------------------
+# Encode workloads: dense keys and values of a demonstration context, split
+# into blocks, to be factorised per block (MILO summary, "4.2 Block-wise
+# Low-Rank Compression" and "4.4 MILO Workflow").  Per block, KV head and K/V
+# the dense matrix is A diag(rho^i) Q^T (A ~ N(0,1), Q orthonormal), the same
+# model as the decode workloads' factors, with a decay rho drawn per matrix
+# so that blocks differ in how fast their spectra fall (what rank allocation,
+# "4.3 Dynamic Rank Allocation", responds to).
+# ---------------------------------------------------------------------------
+@dataclass(frozen=True)
+class EncodeConfig:
+    name: str
+    n_blocks: int
+    block_tokens: int
+    n_kv_heads: int
+    head_dim: int
+    decay_lo: float          # rho ~ U[decay_lo, decay_hi] per (block, head, K/V)
+    decay_hi: float
+    ranks: RankDist          # target (r_b, r'_b) when ranks are given
+    dtype: str
+    seed: int
+    planted_rank: int = 0    # variant "planted": scale 1 for i < planted_rank, 0 after
+    desc: str = ""
+
+    def with_(self, **kw) -> "EncodeConfig":
+        return replace(self, **kw)
+
+
+ENCODE_CONFIGS = {
+    "enc_small": EncodeConfig(
+        name="enc_small", n_blocks=5, block_tokens=256, n_kv_heads=2, head_dim=128,
+        decay_lo=0.6, decay_hi=0.97, ranks=RankDist("uniform", lo=0, hi=128), dtype="bf16",
+        seed=40, planted_rank=24,
+        desc="5 blocks x 256 tokens, 2 KV heads, d128, rho~U[0.6,0.97], r~U{0..128}"),
+    # One pre-encoded demonstration context at the headline decode shape:
+    # 64 blocks of 1024 tokens, Qwen2.5-7B-like KV heads.
+    "enc_qwen7b_64k": EncodeConfig(
+        name="enc_qwen7b_64k", n_blocks=64, block_tokens=1024, n_kv_heads=4, head_dim=128,
+        decay_lo=0.7, decay_hi=0.97,
+        ranks=RankDist("lognormal", median=48.0, sigma=0.5, lo=16, hi=96), dtype="bf16",
+        seed=41, planted_rank=48,
+        desc="one 64k context: 64 blocks x 1024 tokens, 4 KV heads, d128, rho~U[0.7,0.97], "
+             "r~clip(lognormal(48))"),
+    "enc_d64_f32": EncodeConfig(
+        name="enc_d64_f32", n_blocks=3, block_tokens=512, n_kv_heads=2, head_dim=64,
+        decay_lo=0.6, decay_hi=0.95, ranks=RankDist("uniform", lo=0, hi=64), dtype="f32",
+        seed=42, planted_rank=12,
+        desc="3 blocks x 512 tokens, 2 KV heads, d64, fp32, r~U{0..64}"),
+}
+
+
+def get_encode_config(name: str) -> EncodeConfig:
+    return ENCODE_CONFIGS[name]

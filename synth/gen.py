@@ -25,12 +25,12 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from .configs import Config
+from .configs import Config, EncodeConfig
 
 VARIANTS = {"base": 0, "sharp": 1}
 
 # stream ids
-_S_RANK, _S_Q, _S_BLOCK, _S_TAIL = 0, 1, 2, 3
+_S_RANK, _S_Q, _S_BLOCK, _S_TAIL, _S_DENSE = 0, 1, 2, 3, 4
 
 
 def _one_blas_thread():
@@ -258,3 +258,80 @@ def make_workload(cfg: Config, variant: str = "base", seqs: Optional[Sequence[in
     return Workload(cfg=cfg, variant=variant, seqs=seqs, q=_store(q, cfg.dtype), blocks=blocks,
                     k_tail=_store(kt, cfg.dtype), v_tail=_store(vt, cfg.dtype),
                     tail_len=tl[seqs].astype(np.int32), scale=cfg.scale)
+
+
+# ---------------------------------------------------------------------------
+# Dense contexts for the encode step
+# ---------------------------------------------------------------------------
+ENCODE_VARIANTS = {"base": 0, "planted": 1}
+
+
+@dataclass
+class DenseContext:
+    """Dense keys and values of one context, split into blocks.
+
+    k, v       [Hkv][N][d] in the stored dtype, N = sum of the block sizes
+    tok_start  int64 [n_blocks]: block b covers tokens tok_start[b] .. + n_tok[b] - 1
+    n_tok      int32 [n_blocks]
+    ranks      int64 [n_blocks][2]: target (r_b, r'_b) drawn from the config
+    decay      float64 [n_blocks][Hkv][2]: the rho each (block, head, K/V) was drawn with
+    """
+    cfg: EncodeConfig
+    variant: str
+    k: np.ndarray
+    v: np.ndarray
+    tok_start: np.ndarray
+    n_tok: np.ndarray
+    ranks: np.ndarray
+    decay: np.ndarray
+
+    def dense_f64(self, kv: int, b: int, g: int) -> np.ndarray:
+        """Exact stored values of block b, KV head g, keys (kv 0) or values (kv 1)."""
+        a = self.k if kv == 0 else self.v
+        s, n = int(self.tok_start[b]), int(self.n_tok[b])
+        return stored_to_f64(a[g, s:s + n], self.cfg.dtype)
+
+
+def _dense_block(cfg: EncodeConfig, variant: str, b: int, T: int):
+    """[Hkv][2][T][d] float32 and the drawn decays [Hkv][2]."""
+    rng = _rng(cfg.seed, ENCODE_VARIANTS[variant], _S_DENSE, b)
+    d, h = cfg.head_dim, cfg.n_kv_heads
+    out = np.empty((h, 2, T, d), np.float32)
+    rho = rng.uniform(cfg.decay_lo, cfg.decay_hi, size=(h, 2))
+    for g in range(h):
+        for kv in range(2):
+            a = rng.standard_normal((T, d))
+            qm, rm = np.linalg.qr(rng.standard_normal((d, d)))
+            scale = rho[g, kv] ** np.arange(d)
+            if variant == "planted":   # exactly rank planted_rank (before rounding), flat spectrum
+                scale = (np.arange(d) < cfg.planted_rank).astype(np.float64)
+            out[g, kv] = ((a * scale[None, :]) @ qm.T).astype(np.float32)
+    return out, rho
+
+
+def make_dense_context(cfg: EncodeConfig, variant: str = "base",
+                       tokens: Optional[Sequence[int]] = None) -> DenseContext:
+    """Draw one context's dense K and V (tokens: per-block sizes, default
+    cfg.block_tokens each)."""
+    toks = [int(t) for t in tokens] if tokens is not None else [cfg.block_tokens] * cfg.n_blocks
+    nb = len(toks)
+    starts = np.concatenate([[0], np.cumsum(toks)[:-1]]).astype(np.int64) if nb else np.zeros(0, np.int64)
+    N = int(sum(toks))
+    d, h = cfg.head_dim, cfg.n_kv_heads
+    k = np.empty((h, N, d), np.float32)
+    v = np.empty((h, N, d), np.float32)
+    decay = np.empty((nb, h, 2))
+    with _one_blas_thread(), ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        res = list(ex.map(lambda b: _dense_block(cfg, variant, b, toks[b]), range(nb)))
+    for b, (x, rho) in enumerate(res):
+        s = starts[b]
+        k[:, s:s + toks[b]] = x[:, 0]
+        v[:, s:s + toks[b]] = x[:, 1]
+        decay[b] = rho
+    # target ranks: the decode workloads' rank model on a one-sequence draw
+    rcfg = Config(name=cfg.name, batch=1, q_len=1, n_q_heads=h, n_kv_heads=h, head_dim=d,
+                  n_blocks=nb, block_tokens=cfg.block_tokens, ranks=cfg.ranks, tail_len=0,
+                  dtype=cfg.dtype, path="decode", seed=cfg.seed)
+    ranks = draw_ranks(rcfg, "base", [nb])[0]
+    return DenseContext(cfg=cfg, variant=variant, k=_store(k, cfg.dtype), v=_store(v, cfg.dtype),
+                        tok_start=starts, n_tok=np.array(toks, np.int32), ranks=ranks, decay=decay)
