@@ -1,0 +1,95 @@
+/*
+ * milo_encode.h -- C ABI of the encode step that produces the factors
+ * milo_attn.h attends over, for AMD Instinct MI355X (gfx950).
+ *
+ * MILO (summary at paperlayer.ai/abs/2609.29913v1) pre-encodes a many-shot
+ * demonstration context, splits its cache into blocks ("4.4 MILO Workflow":
+ * partition, analyse, store) and keeps each block's keys and values as
+ * separate low-rank factors ("4.2 Block-wise Low-Rank Compression") at
+ * block-specific ranks ("4.3 Dynamic Rank Allocation").  The factorisation
+ * is the truncated SVD: for a block X (T x d) of keys or values,
+ *     W = the r right singular vectors of the largest singular values (rows)
+ *     U = X W^T
+ * so U W is the best rank-r approximation of X in Frobenius norm.
+ *
+ * Two calls, so that ranks can be chosen from the spectra in between:
+ *   milo_encode_spectrum   singular values of every (block, KV head, K/V),
+ *                          and the sorted singular vectors kept in the
+ *                          workspace;
+ *   milo_encode_factors    U^T, W, U'^T, W' of every block written into the
+ *                          pool at the descriptors' offsets and ranks.
+ * milo_encode_layout (host) places blocks of given sizes and ranks in a pool.
+ *
+ * Conventions are those of milo_attn.h: device pointers except the args
+ * struct, asynchronous on the given stream, no allocation, host-checkable
+ * faults reported before any HIP call, device tables are the caller's
+ * contract (tok_start[b] >= 0 and tok_start[b] + n_tok <= n_tokens; token
+ * ranges are clamped on the device).  Inputs must be finite.
+ */
+#ifndef MILO_ENCODE_H
+#define MILO_ENCODE_H
+
+#include "milo_attn.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct milo_encode_args {
+  int32_t struct_size;         /* sizeof(milo_encode_args)                                  */
+  int32_t dtype;               /* milo_dtype of k, v and the factors written                */
+  int32_t n_blocks;            /* >= 0                                                      */
+  int32_t n_kv_heads;          /* >= 1                                                      */
+  int32_t head_dim;            /* 64 or 128                                                 */
+  int32_t n_tokens;            /* tokens per KV head in k and v, >= 0                       */
+  const void* k;               /* [n_kv_heads][n_tokens][head_dim] dense keys, 16-B aligned */
+  const void* v;               /* same shape: dense values                                  */
+  const int64_t* tok_start;    /* [n_blocks]: block b covers tokens tok_start[b] ..
+                                  tok_start[b] + blocks[b].n_tok - 1                        */
+  const milo_block* blocks;    /* [n_blocks] descriptors.  Spectrum call: n_tok.  Factors
+                                  call: also off, ld_tok, rank_k, rank_v (pool layout of
+                                  milo_attn.h)                                              */
+  float* sigma;                /* [n_blocks][n_kv_heads][2][head_dim] singular values,
+                                  descending, K then V; written by the spectrum call; may
+                                  be NULL                                                   */
+  int32_t* sweeps;             /* [n_blocks][n_kv_heads][2] Jacobi sweeps used by the
+                                  spectrum call (negative: stopped at the limit of 16
+                                  before converging); may be NULL                           */
+  void* pool;                  /* factor pool written by the factors call, 16-B aligned     */
+  void* workspace;             /* milo_encode_workspace_bytes() bytes, 256-B aligned: the
+                                  spectrum call writes it, the factors call reads it        */
+  size_t workspace_bytes;
+} milo_encode_args;
+
+/* Workspace both calls need (singular vectors of every matrix: 4 * head_dim^2
+ * bytes each); 0 if the shape fields are invalid or unsupported. */
+size_t milo_encode_workspace_bytes(const milo_encode_args* args);
+
+/* Spectra: per (block, KV head, K/V) the Gram matrix X^T X (fp32 sums of
+ * exact products) and its eigen-decomposition by cyclic Jacobi rotations
+ * (fp32).  sigma_i = sqrt(max(lambda_i, 0)).  Writes sigma, sweeps and the
+ * workspace. */
+milo_status milo_encode_spectrum(const milo_encode_args* args, void* hip_stream);
+
+/* Factors: for every block, KV head and K/V, W = the first rank rows of the
+ * sorted singular vectors and U^T = W X^T (fp32 sums), stored in dtype
+ * (bf16: round to nearest even); U^T rows are zero past n_tok up to ld_tok.
+ * Needs the workspace of a spectrum call on the same k, v, tok_start and
+ * blocks[].n_tok. */
+milo_status milo_encode_factors(const milo_encode_args* args, void* hip_stream);
+
+/* Host-side layout: descriptors for blocks of n_tok[b] tokens and ranks
+ * (rank_k[b], rank_v[b]) placed back to back in a pool (ld_tok =
+ * n_tok rounded up to 8; every offset a multiple of 8 elements).  All
+ * pointers are HOST arrays; blocks_out receives n_blocks descriptors and
+ * *pool_elems the pool size in elements.  MILO_ERR_INVALID on null pointers,
+ * negative sizes or ranks outside [0, head_dim]. */
+milo_status milo_encode_layout(const int32_t* n_tok, const int32_t* rank_k, const int32_t* rank_v,
+                               int32_t n_blocks, int32_t n_kv_heads, int32_t head_dim,
+                               milo_block* blocks_out, int64_t* pool_elems);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MILO_ENCODE_H */

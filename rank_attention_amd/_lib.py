@@ -1,4 +1,5 @@
-"""ctypes view of the C ABI in include/milo_attn.h (argument marshalling only)."""
+"""ctypes view of the C ABI in include/milo_attn.h and include/milo_encode.h
+(argument marshalling only)."""
 from __future__ import annotations
 
 import ctypes
@@ -11,7 +12,8 @@ MILO_OK, MILO_ERR_INVALID, MILO_ERR_UNSUPPORTED, MILO_ERR_WORKSPACE, MILO_ERR_DE
 MILO_F32, MILO_BF16 = 0, 1
 MILO_PATH_DECODE, MILO_PATH_CHUNK, MILO_PATH_SHARED = 0, 1, 2
 EXPORTS = ("milo_attn_workspace_bytes", "milo_attn_decode", "milo_attn_chunk", "milo_attn_decode_shared",
-           "milo_attn_plan_decode", "milo_status_str", "milo_abi_version")
+           "milo_attn_plan_decode", "milo_status_str", "milo_abi_version",
+           "milo_encode_workspace_bytes", "milo_encode_spectrum", "milo_encode_factors", "milo_encode_layout")
 
 
 class MiloBlock(ctypes.Structure):
@@ -47,6 +49,26 @@ class MiloAttnArgs(ctypes.Structure):
     ]
 
 
+class MiloEncodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("n_blocks", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("n_tokens", ctypes.c_int32),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("tok_start", ctypes.c_void_p),
+        ("blocks", ctypes.c_void_p),
+        ("sigma", ctypes.c_void_p),
+        ("sweeps", ctypes.c_void_p),
+        ("pool", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 _lib = None
 
 
@@ -70,6 +92,15 @@ def load() -> ctypes.CDLL:
         lib.milo_attn_plan_decode.restype = ctypes.c_int
         lib.milo_status_str.argtypes = [ctypes.c_int]
         lib.milo_status_str.restype = ctypes.c_char_p
+        lib.milo_encode_workspace_bytes.argtypes = [ctypes.POINTER(MiloEncodeArgs)]
+        lib.milo_encode_workspace_bytes.restype = ctypes.c_size_t
+        for fn in (lib.milo_encode_spectrum, lib.milo_encode_factors):
+            fn.argtypes = [ctypes.POINTER(MiloEncodeArgs), ctypes.c_void_p]
+            fn.restype = ctypes.c_int
+        lib.milo_encode_layout.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                           ctypes.POINTER(ctypes.c_int64)]
+        lib.milo_encode_layout.restype = ctypes.c_int
         lib.milo_abi_version.argtypes = []
         lib.milo_abi_version.restype = ctypes.c_int32
         _lib = lib

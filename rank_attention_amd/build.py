@@ -32,7 +32,9 @@ UNITS = [
     ("decode.hip", ["-DMILO_INST_DT=1", "-DMILO_INST_D=128"], "decode_bf16_128.o"),
     ("merge.hip", [], "merge.o"),
     ("chunk.hip", [], "chunk.o"),
+    ("encode.hip", [], "encode.o"),
     ("milo_attn.cpp", [], "milo_attn.o"),
+    ("milo_encode.cpp", [], "milo_encode.o"),
 ]
 
 

@@ -72,6 +72,21 @@ struct MergeParams {
   int32_t seq_stride;       // sequence i's block count is read at seq_blocks[i * seq_stride]
 };
 
+// Encode step: one workgroup per matrix m = (b * n_kv_heads + g) * 2 + kv.
+struct EncodeParams {
+  const void* k;               // [n_kv_heads][n_tokens][head_dim]
+  const void* v;
+  const int64_t* tok_start;    // [n_blocks]
+  const milo_block* blocks;    // [n_blocks]
+  float* sigma;                // [n_mats][head_dim] descending, or null
+  int32_t* sweeps;             // [n_mats] Jacobi sweeps (negative: not converged), or null
+  float* vecs;                 // [n_mats][head_dim][head_dim] eigenvector rows, descending
+  void* pool;
+  int32_t n_blocks, n_kv_heads, n_tokens;
+};
+hipError_t launch_encode_spectrum(const EncodeParams& p, int dtype, int head_dim, hipStream_t s);
+hipError_t launch_encode_factors(const EncodeParams& p, int dtype, int head_dim, hipStream_t s);
+
 // Work units of the decode kernel: one per (sequence, KV head, block slot),
 // plus one dense-tail unit per (sequence, KV head).
 inline int64_t decode_units(int batch, int n_kv_heads, int max_blocks) {

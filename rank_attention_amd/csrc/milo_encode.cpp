@@ -1,0 +1,121 @@
+// milo_encode.cpp -- host side of the encode ABI declared in
+// include/milo_encode.h: argument validation (before any HIP call),
+// workspace sizing, the host-side pool layout and kernel launches on the
+// caller's stream.  No allocation, no synchronisation, no global state.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.h"
+#include "milo_encode.h"
+
+namespace {
+
+constexpr size_t kEncWsAlign = 256;
+
+inline size_t enc_round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline bool enc_aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t n_mats(const milo_encode_args* a) { return (int64_t)a->n_blocks * a->n_kv_heads * 2; }
+
+milo_status check_shape(const milo_encode_args* a) {
+  if (!a) return MILO_ERR_INVALID;
+  if (a->struct_size != (int32_t)sizeof(milo_encode_args)) return MILO_ERR_INVALID;
+  if (a->dtype != MILO_F32 && a->dtype != MILO_BF16) return MILO_ERR_UNSUPPORTED;
+  if (a->n_blocks < 0 || a->n_kv_heads < 1 || a->n_tokens < 0) return MILO_ERR_INVALID;
+  if (a->head_dim != 64 && a->head_dim != 128) return MILO_ERR_UNSUPPORTED;
+  if (n_mats(a) > INT32_MAX) return MILO_ERR_UNSUPPORTED;   // one workgroup per matrix
+  if ((int64_t)a->n_kv_heads * a->n_tokens * a->head_dim > INT64_MAX / 4) return MILO_ERR_UNSUPPORTED;
+  return MILO_OK;
+}
+
+size_t workspace_of(const milo_encode_args* a) {
+  return enc_round_up((size_t)n_mats(a) * a->head_dim * a->head_dim * sizeof(float), kEncWsAlign);
+}
+
+milo_status check_common(const milo_encode_args* a) {
+  milo_status st = check_shape(a);
+  if (st != MILO_OK || a->n_blocks == 0) return st;
+  if (!a->tok_start || !a->blocks) return MILO_ERR_INVALID;
+  if (!enc_aligned(a->tok_start, 8) || !enc_aligned(a->blocks, 8)) return MILO_ERR_INVALID;
+  if (a->n_tokens > 0 && (!a->k || !a->v)) return MILO_ERR_INVALID;
+  if ((a->k && !enc_aligned(a->k, 16)) || (a->v && !enc_aligned(a->v, 16))) return MILO_ERR_INVALID;
+  if (!a->workspace || a->workspace_bytes < workspace_of(a)) return MILO_ERR_WORKSPACE;
+  if (!enc_aligned(a->workspace, kEncWsAlign)) return MILO_ERR_WORKSPACE;
+  return MILO_OK;
+}
+
+milo::EncodeParams params_of(const milo_encode_args* a) {
+  milo::EncodeParams p{};
+  p.k = a->k;
+  p.v = a->v;
+  p.tok_start = a->tok_start;
+  p.blocks = a->blocks;
+  p.sigma = a->sigma;
+  p.sweeps = a->sweeps;
+  p.vecs = static_cast<float*>(a->workspace);
+  p.pool = a->pool;
+  p.n_blocks = a->n_blocks;
+  p.n_kv_heads = a->n_kv_heads;
+  p.n_tokens = a->n_tokens;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t milo_encode_workspace_bytes(const milo_encode_args* a) {
+  if (check_shape(a) != MILO_OK) return 0;
+  return workspace_of(a);
+}
+
+milo_status milo_encode_spectrum(const milo_encode_args* a, void* hip_stream) {
+  milo_status st = check_common(a);
+  if (st != MILO_OK) return st;
+  if (a->n_blocks == 0) return MILO_OK;
+  if ((a->sigma && !enc_aligned(a->sigma, 4)) || (a->sweeps && !enc_aligned(a->sweeps, 4)))
+    return MILO_ERR_INVALID;
+  const milo::EncodeParams p = params_of(a);
+  if (milo::launch_encode_spectrum(p, a->dtype, a->head_dim, reinterpret_cast<hipStream_t>(hip_stream)) !=
+      hipSuccess)
+    return MILO_ERR_DEVICE;
+  return MILO_OK;
+}
+
+milo_status milo_encode_factors(const milo_encode_args* a, void* hip_stream) {
+  milo_status st = check_common(a);
+  if (st != MILO_OK) return st;
+  if (a->n_blocks == 0) return MILO_OK;
+  if (!a->pool || !enc_aligned(a->pool, 16)) return MILO_ERR_INVALID;
+  const milo::EncodeParams p = params_of(a);
+  if (milo::launch_encode_factors(p, a->dtype, a->head_dim, reinterpret_cast<hipStream_t>(hip_stream)) !=
+      hipSuccess)
+    return MILO_ERR_DEVICE;
+  return MILO_OK;
+}
+
+milo_status milo_encode_layout(const int32_t* n_tok, const int32_t* rank_k, const int32_t* rank_v,
+                               int32_t n_blocks, int32_t n_kv_heads, int32_t head_dim,
+                               milo_block* blocks_out, int64_t* pool_elems) {
+  if (n_blocks < 0 || n_kv_heads < 1 || head_dim < 1 || head_dim % 8 != 0 || !pool_elems)
+    return MILO_ERR_INVALID;
+  if (n_blocks > 0 && (!n_tok || !rank_k || !rank_v || !blocks_out)) return MILO_ERR_INVALID;
+  int64_t off = 0;
+  for (int32_t b = 0; b < n_blocks; ++b) {
+    if (n_tok[b] < 0 || n_tok[b] > INT32_MAX - 7) return MILO_ERR_INVALID;
+    if (rank_k[b] < 0 || rank_k[b] > head_dim || rank_v[b] < 0 || rank_v[b] > head_dim)
+      return MILO_ERR_INVALID;
+    const int32_t ld = (n_tok[b] + 7) / 8 * 8;
+    blocks_out[b].off = off;
+    blocks_out[b].n_tok = n_tok[b];
+    blocks_out[b].ld_tok = ld;
+    blocks_out[b].rank_k = rank_k[b];
+    blocks_out[b].rank_v = rank_v[b];
+    off += (int64_t)n_kv_heads * (rank_k[b] + rank_v[b]) * ((int64_t)ld + head_dim);
+  }
+  *pool_elems = off;
+  return MILO_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+"""Binding of the encode step (include/milo_encode.h): dense keys and values
+of a context to per-block low-rank factors in a pool that the attention
+entry points read.  Argument marshalling only: the spectra and the factors
+are computed by the HIP kernels of ``libmilo_attn.so``."""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import _lib
+from ._lib import MILO_BF16, MILO_F32, MILO_OK, MILO_ERR_DEVICE, MiloEncodeArgs
+from .pack import BLOCK_DTYPE
+
+
+def layout(n_tok: Sequence[int], rank_k: Sequence[int], rank_v: Sequence[int], n_kv_heads: int,
+           head_dim: int) -> Tuple[np.ndarray, int]:
+    """Descriptors (BLOCK_DTYPE) and pool size in elements for blocks of the
+    given sizes and ranks, placed back to back (milo_encode_layout)."""
+    from . import MiloError, status_str
+    nt = np.ascontiguousarray(n_tok, np.int32)
+    rk = np.ascontiguousarray(rank_k, np.int32)
+    rv = np.ascontiguousarray(rank_v, np.int32)
+    nb = len(nt)
+    if len(rk) != nb or len(rv) != nb:
+        raise ValueError("n_tok, rank_k and rank_v must have one entry per block")
+    blocks = np.zeros(nb, BLOCK_DTYPE)
+    elems = ctypes.c_int64(0)
+    rc = _lib.load().milo_encode_layout(nt.ctypes.data, rk.ctypes.data, rv.ctypes.data, nb, int(n_kv_heads),
+                                        int(head_dim), blocks.ctypes.data, ctypes.byref(elems))
+    if rc != MILO_OK:
+        raise MiloError(rc, status_str(rc))
+    return blocks, int(elems.value)
+
+
+class DeviceContext:
+    """Dense keys and values of one context ([Hkv][N][d], stored dtype: bf16
+    bit patterns as uint16, or float32) in device memory, split into blocks
+    at tok_start / n_tok, with the two encode calls on them."""
+
+    def __init__(self, k: np.ndarray, v: np.ndarray, tok_start, n_tok, dtype: str = "bf16",
+                 device="cuda"):
+        import torch
+
+        def dev(a, raw16=False):
+            a = np.ascontiguousarray(a)
+            if raw16:
+                a = a.view(np.int16)
+            return torch.from_numpy(a).to(device)
+
+        if k.shape != v.shape or k.ndim != 3:
+            raise ValueError("k and v must both be [n_kv_heads][n_tokens][head_dim]")
+        self.dtype = dtype
+        self.code = MILO_BF16 if dtype == "bf16" else MILO_F32
+        self.n_kv_heads, self.n_tokens, self.head_dim = (int(x) for x in k.shape)
+        self.k = dev(k, dtype == "bf16")
+        self.v = dev(v, dtype == "bf16")
+        self.n_tok = np.ascontiguousarray(n_tok, np.int32)
+        self.tok_start = dev(np.ascontiguousarray(tok_start, np.int64))
+        self.n_blocks = len(self.n_tok)
+        self.device = device
+        self.workspace = None
+        self._spectrum_blocks = None
+
+    def _args(self, blocks_dev, pool=None, sigma=None, sweeps=None) -> MiloEncodeArgs:
+        a = MiloEncodeArgs()
+        a.struct_size = ctypes.sizeof(MiloEncodeArgs)
+        a.dtype = self.code
+        a.n_blocks, a.n_kv_heads, a.head_dim, a.n_tokens = (self.n_blocks, self.n_kv_heads, self.head_dim,
+                                                            self.n_tokens)
+        a.k, a.v = self.k.data_ptr(), self.v.data_ptr()
+        a.tok_start = self.tok_start.data_ptr()
+        a.blocks = blocks_dev.data_ptr()
+        a.sigma = None if sigma is None else sigma.data_ptr()
+        a.sweeps = None if sweeps is None else sweeps.data_ptr()
+        a.pool = None if pool is None else pool.data_ptr()
+        if self.workspace is not None:
+            a.workspace, a.workspace_bytes = self.workspace.data_ptr(), self.workspace.numel()
+        return a
+
+    def _call(self, fn, a, stream):
+        import torch
+        from . import MiloError, status_str
+        if stream is None:
+            stream = torch.cuda.current_stream(self.k.device).cuda_stream
+        rc = fn(ctypes.byref(a), ctypes.c_void_p(int(stream)))
+        if rc != MILO_OK:
+            if rc == MILO_ERR_DEVICE:
+                raise RuntimeError(f"milo_encode: {status_str(rc)}")
+            raise MiloError(rc, status_str(rc))
+
+    def spectrum(self, stream=None):
+        """Singular values [n_blocks][Hkv][2][d] (fp32, descending; K then V)
+        and Jacobi sweep counts [n_blocks][Hkv][2]; keeps the singular
+        vectors in this context's workspace for factors()."""
+        import torch
+        lib = _lib.load()
+        blocks, _ = layout(self.n_tok, np.zeros(self.n_blocks, np.int32), np.zeros(self.n_blocks, np.int32),
+                           self.n_kv_heads, self.head_dim)
+        self._spectrum_blocks = torch.from_numpy(blocks.view(np.uint8)).to(self.device)
+        sigma = torch.empty((self.n_blocks, self.n_kv_heads, 2, self.head_dim), dtype=torch.float32,
+                            device=self.device)
+        sweeps = torch.empty((self.n_blocks, self.n_kv_heads, 2), dtype=torch.int32, device=self.device)
+        a = self._args(self._spectrum_blocks, sigma=sigma, sweeps=sweeps)
+        need = lib.milo_encode_workspace_bytes(ctypes.byref(a))
+        if need and (self.workspace is None or self.workspace.numel() < need):
+            self.workspace = torch.empty(int(need), dtype=torch.uint8, device=self.device)
+        a = self._args(self._spectrum_blocks, sigma=sigma, sweeps=sweeps)
+        self._call(lib.milo_encode_spectrum, a, stream)
+        return sigma, sweeps
+
+    def factors(self, rank_k, rank_v, stream=None):
+        """Factors at the given per-block ranks (after spectrum()): returns
+        (pool, blocks_dev, blocks_host) where pool is in the stored dtype
+        (int16 views of bf16) and the descriptors follow include/milo_attn.h."""
+        import torch
+        if self.workspace is None and self.n_blocks:
+            raise RuntimeError("factors() needs the singular vectors of a spectrum() call")
+        lib = _lib.load()
+        blocks, elems = layout(self.n_tok, rank_k, rank_v, self.n_kv_heads, self.head_dim)
+        bdev = torch.from_numpy(blocks.view(np.uint8).copy()).to(self.device)
+        tdt = torch.int16 if self.dtype == "bf16" else torch.float32
+        pool = torch.empty(max(elems, 8), dtype=tdt, device=self.device)
+        self._call(lib.milo_encode_factors, self._args(bdev, pool=pool), stream)
+        return pool, bdev, blocks

@@ -11,15 +11,18 @@ import rank_attention_amd as ra
 from rank_attention_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "milo_attn.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 FAKE = 0x10000  # 64 KiB-aligned non-null address; never dereferenced by these calls
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(milo_[a-z_0-9]+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(milo_[a-z_0-9]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -178,3 +181,77 @@ def test_plan_rejects_bad_arguments():
     assert lib.milo_attn_plan_decode(None, sb, None, 1, 0, 0, 64, out) == _lib.MILO_ERR_INVALID
     assert lib.milo_attn_plan_decode(None, sb, None, 1, 1, 0, 64, out) == _lib.MILO_OK
     assert out[0] == 0
+
+
+# --------------------------------------------------------------------------
+# encode ABI (include/milo_encode.h)
+# --------------------------------------------------------------------------
+def enc_args(**over):
+    a = _lib.MiloEncodeArgs()
+    a.struct_size = ctypes.sizeof(_lib.MiloEncodeArgs)
+    a.dtype = _lib.MILO_BF16
+    a.n_blocks, a.n_kv_heads, a.head_dim, a.n_tokens = 3, 2, 128, 1000
+    a.k = a.v = a.tok_start = a.blocks = a.pool = FAKE
+    a.sigma = a.sweeps = FAKE
+    a.workspace, a.workspace_bytes = FAKE, 1 << 30
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_encode_struct_size_and_workspace():
+    assert ctypes.sizeof(_lib.MiloEncodeArgs) == 6 * 4 + 8 * 8 + 8
+    lib = _lib.load()
+    # 3 blocks x 2 heads x (K, V) matrices of 128 x 128 fp32 singular vectors
+    assert lib.milo_encode_workspace_bytes(ctypes.byref(enc_args())) == 12 * 128 * 128 * 4
+    assert lib.milo_encode_workspace_bytes(ctypes.byref(enc_args(head_dim=96))) == 0
+    assert lib.milo_encode_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"struct_size": 8}, _lib.MILO_ERR_INVALID),
+    ({"dtype": 5}, _lib.MILO_ERR_UNSUPPORTED),
+    ({"head_dim": 96}, _lib.MILO_ERR_UNSUPPORTED),
+    ({"n_blocks": -1}, _lib.MILO_ERR_INVALID),
+    ({"n_kv_heads": 0}, _lib.MILO_ERR_INVALID),
+    ({"n_tokens": -5}, _lib.MILO_ERR_INVALID),
+    ({"k": None}, _lib.MILO_ERR_INVALID),
+    ({"k": FAKE + 8}, _lib.MILO_ERR_INVALID),
+    ({"tok_start": None}, _lib.MILO_ERR_INVALID),
+    ({"blocks": FAKE + 4}, _lib.MILO_ERR_INVALID),
+    ({"workspace": None}, _lib.MILO_ERR_WORKSPACE),
+    ({"workspace_bytes": 100}, _lib.MILO_ERR_WORKSPACE),
+    ({"workspace": FAKE + 64}, _lib.MILO_ERR_WORKSPACE),
+    ({"n_blocks": 1 << 30}, _lib.MILO_ERR_UNSUPPORTED),   # more matrices than one grid holds
+])
+def test_encode_rejects_before_any_hip_call(over, code):
+    lib = _lib.load()
+    a = enc_args(**over)
+    assert lib.milo_encode_spectrum(ctypes.byref(a), None) == code
+    assert lib.milo_encode_factors(ctypes.byref(a), None) == code
+
+
+def test_encode_specific_pointer_checks():
+    lib = _lib.load()
+    assert lib.milo_encode_spectrum(ctypes.byref(enc_args(sigma=FAKE + 2)), None) == _lib.MILO_ERR_INVALID
+    assert lib.milo_encode_factors(ctypes.byref(enc_args(pool=None)), None) == _lib.MILO_ERR_INVALID
+    assert lib.milo_encode_factors(ctypes.byref(enc_args(pool=FAKE + 8)), None) == _lib.MILO_ERR_INVALID
+    assert lib.milo_encode_spectrum(None, None) == _lib.MILO_ERR_INVALID
+    # nothing to encode: no pointer is needed and nothing is launched
+    empty = enc_args(n_blocks=0, k=None, v=None, tok_start=None, blocks=None, workspace=None, pool=None)
+    assert lib.milo_encode_spectrum(ctypes.byref(empty), None) == _lib.MILO_OK
+    assert lib.milo_encode_factors(ctypes.byref(empty), None) == _lib.MILO_OK
+
+
+def test_encode_layout():
+    from rank_attention_amd import encode as enc
+    blocks, elems = enc.layout([37, 1024, 0], [5, 128, 0], [3, 1, 7], n_kv_heads=2, head_dim=128)
+    assert list(blocks["ld_tok"]) == [40, 1024, 0]
+    assert list(blocks["off"]) == [0, 2 * 8 * (40 + 128), 2 * 8 * (40 + 128) + 2 * 129 * (1024 + 128)]
+    assert elems == blocks["off"][2] + 2 * 7 * 128
+    assert all(o % 8 == 0 for o in blocks["off"])
+    for bad in ([[1], [129], [0]], [[-1], [0], [0]], [[4], [0], [-2]]):
+        with pytest.raises(ra.MiloError):
+            enc.layout(*bad, n_kv_heads=1, head_dim=128)
+    lib = _lib.load()
+    assert lib.milo_encode_layout(None, None, None, 1, 1, 128, None, None) == _lib.MILO_ERR_INVALID
