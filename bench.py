@@ -18,7 +18,13 @@ FLOP/byte ridge).
 Kernel time comes from HIP events recorded on the launch stream around the
 attention kernel alone; the fp64 CPU oracle is timed on a bounded sample.
 
+Encode (--encode, workload enc_qwen7b_64k): one step factorises the dense
+keys and values of one 64k-token context (spectrum kernel + factors kernel
+at the workload's target ranks); context tokens/s, and the spectrum
+kernel's algorithmic fp32 rate against the 157.3 TFLOP/s vector peak.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen7b_64k] [--shared]
+    python bench.py --encode [--workload enc_qwen7b_64k]
 """
 from __future__ import annotations
 
@@ -33,6 +39,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+ENCODE_METRIC = "low-rank-KV encode: context tokens/s factorised (dense K/V -> per-block truncated SVD factors)"
+FP32_VECTOR_PEAK_TFLOPS = 157.3
 METRIC = "low-rank-KV decode attn: context tokens/s and % of HBM peak (7B, 64k)"
 SHARED_METRIC = "low-rank-KV shared-context decode attn: context tokens/s (7B, 64k context shared by the batch)"
 CHUNK_METRIC = "low-rank-KV chunked-query attn: query tokens/s and % of bf16 MFMA peak (32B, Q=256)"
@@ -43,6 +51,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "decode": ["rank_attention_amd/csrc/decode.hip", "rank_attention_amd/csrc/device_common.h"],
     "chunk": ["rank_attention_amd/csrc/chunk.hip", "rank_attention_amd/csrc/device_common.h"],
+    "encode": ["rank_attention_amd/csrc/encode.hip", "rank_attention_amd/csrc/device_common.h"],
 }
 
 
@@ -118,6 +127,137 @@ def chunk_flops(wl, shared: bool = False) -> int:
     return total
 
 
+def encode_flops(ctx) -> int:
+    """Algorithmic FLOPs of encoding a context: per (block, head, K/V)
+    matrix of T tokens at rank r, the Gram matrix (2 T d^2), a symmetric
+    eigen-decomposition with vectors at the textbook count (9 d^3:
+    tridiagonalisation plus implicit QR with accumulated rotations) and the
+    projection U = X W^T (2 T d r)."""
+    d, h = ctx.cfg.head_dim, ctx.cfg.n_kv_heads
+    total = 0
+    for b in range(len(ctx.n_tok)):
+        T = int(ctx.n_tok[b])
+        for kv in range(2):
+            total += h * (2 * T * d * d + 9 * d ** 3 + 2 * T * d * int(ctx.ranks[b][kv]))
+    return total
+
+
+def cpu_baseline_encode(ctx, seconds: float):
+    """fp64 SVD oracle on whole blocks of the context until `seconds` pass."""
+    from oracle import encode as oenc
+    toks, elapsed, done = 0, 0.0, 0
+    for b in range(len(ctx.n_tok)):
+        t0 = time.perf_counter()
+        for g in range(ctx.cfg.n_kv_heads):
+            for kv in range(2):
+                oenc.encode_block(ctx.dense_f64(kv, b, g), int(ctx.ranks[b][kv]))
+        elapsed += time.perf_counter() - t0
+        toks += int(ctx.n_tok[b])
+        done += 1
+        if elapsed >= seconds:
+            break
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = 1
+    return {"value": toks / elapsed, "unit": "context tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {len(ctx.n_tok)} blocks (all {ctx.cfg.n_kv_heads} KV heads, K and V), "
+                      f"numpy fp64 SVD, {elapsed:.1f} s"}
+
+
+def run_encode(args) -> int:
+    import torch
+    import rank_attention_amd as ra
+    import synth
+    from rank_attention_amd import _lib
+    from rank_attention_amd.encode import DeviceContext
+
+    if not os.path.exists(ra.library_path):
+        import __graft_entry__
+        __graft_entry__.build()
+    lib = _lib.load()
+    name = args.workload if args.workload.startswith("enc_") else "enc_qwen7b_64k"
+    cfg = synth.get_encode_config(name)
+    t0 = time.time()
+    ctx = synth.make_dense_context(cfg)
+    dc = DeviceContext(ctx.k, ctx.v, ctx.tok_start, ctx.n_tok, dtype=cfg.dtype, device="cuda:0")
+    dense_bytes = 2 * dc.k.numel() * dc.k.element_size()
+    copies = max(args.copies, -(-3 * LAST_LEVEL_CACHE_BYTES // max(1, dense_bytes)))
+    kvs = [(dc.k, dc.v)] + [(dc.k.clone(), dc.v.clone()) for _ in range(copies - 1)]
+    sigma, sweeps = dc.spectrum()           # sizes the workspace
+    rk, rv = ctx.ranks[:, 0], ctx.ranks[:, 1]
+    pool, bdev, _ = dc.factors(rk, rv)
+    torch.cuda.synchronize()
+    sw = sweeps.cpu().numpy()
+    spec_blocks = dc._spectrum_blocks
+    stream = torch.cuda.current_stream().cuda_stream
+    argsets = []
+    for k, v in kvs:
+        dc.k, dc.v = k, v
+        argsets.append((dc._args(spec_blocks, sigma=sigma, sweeps=sweeps), dc._args(bdev, pool=pool)))
+    print(f"[bench] {cfg.desc}: dense K/V {dense_bytes / 1e6:.1f} MB, {copies} copies, Jacobi sweeps "
+          f"{sw.min()}..{sw.max()} (mean {sw.mean():.1f}), setup {time.time() - t0:.1f} s",
+          file=sys.stderr, flush=True)
+
+    def step(k, evs=None):
+        a_s, a_f = argsets[k % len(argsets)]
+        if evs is not None:
+            evs[0].record()
+        rc = lib.milo_encode_spectrum(ctypes.byref(a_s), ctypes.c_void_p(stream))
+        if evs is not None:
+            evs[1].record()
+        rc = rc or lib.milo_encode_factors(ctypes.byref(a_f), ctypes.c_void_p(stream))
+        if evs is not None:
+            evs[2].record()
+        if rc != 0:
+            raise RuntimeError(f"milo_encode failed: {ra.status_str(rc)}")
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(k, evs[k])
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    spec_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    fac_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_per_step = (t_end - t_start) * 1e3 / args.steps
+    kmean = sum(spec_ms) / len(spec_ms)
+    fmean = sum(fac_ms) / len(fac_ms)
+    flops = encode_flops(ctx)
+    d = cfg.head_dim
+    spec_flops = sum(cfg.n_kv_heads * 2 * (2 * int(T) * d * d + 9 * d ** 3) for T in ctx.n_tok)
+    achieved = spec_flops / (kmean * 1e-3) / 1e12
+    tokens = int(ctx.n_tok.sum())
+    print(f"[bench] spectrum kernel mean {kmean * 1e3:.1f} us, factors kernel mean {fmean * 1e3:.1f} us, "
+          f"step {ms_per_step * 1e3:.1f} us; {achieved:.2f} TFLOP/s algorithmic in the spectrum kernel; "
+          f"{flops / 1e9:.1f} GFLOP per step", file=sys.stderr, flush=True)
+    res = {
+        "metric": ENCODE_METRIC, "value": tokens / (ms_per_step * 1e-3), "unit": "context tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "desc": cfg.desc, "n_blocks": len(ctx.n_tok),
+                   "block_tokens": cfg.block_tokens, "n_kv_heads": cfg.n_kv_heads, "head_dim": d,
+                   "context_tokens_per_step": tokens, "copies": copies,
+                   "jacobi_sweeps_mean": float(sw.mean())},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
+                     "traffic": traffic_from_profiles(cfg.name, "encode"),
+                     "kernel": "milo_encode_spectrum_kernel", "kernel_us_mean": kmean * 1e3,
+                     "factors_kernel_us_mean": fmean * 1e3,
+                     "algorithmic_flops_per_launch": spec_flops,
+                     "algorithmic_bytes_per_launch": dense_bytes,
+                     "kernel_source_sha": kernel_source_sha("encode")},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_encode(ctx, args.cpu_seconds),
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def cpu_baseline_chunk(wl, seconds: float):
     """fp64 oracle on sampled query positions (all heads) of sequence 0 of the
     chunk workload, grown until `seconds` pass; reported per query token."""
@@ -169,6 +309,8 @@ def main(argv=None):
     ap.add_argument("--variant", default="base")
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch (sequences)")
     ap.add_argument("--q-heads", type=int, default=0, help="override the query heads (group size)")
+    ap.add_argument("--encode", action="store_true",
+                    help="encode step: factorise the dense K/V of one context (enc_* workloads)")
     ap.add_argument("--shared", action="store_true",
                     help="shared-context decode: the batch attends to sequence 0's context")
     ap.add_argument("--copies", type=int, default=2,
@@ -187,6 +329,9 @@ def main(argv=None):
         return 2
 
     import torch
+
+    if args.encode or args.workload.startswith("enc_"):
+        return run_encode(args)
 
     if args.copy_probe:
         n = args.copy_probe << 20

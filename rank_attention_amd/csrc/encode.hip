@@ -14,7 +14,8 @@
 //            every round applies d/2 disjoint plane rotations chosen by the
 //            round-robin (circle) pairing, so a sweep of d-1 rounds meets
 //            every index pair once.  A rotation's 2x2 blocks of G are
-//            owned by single threads, so a round is two barriers.  Sweeps
+//            owned by single threads, so a round is two barriers; each
+//            thread reads all of its blocks before writing any.  Sweeps
 //            stop after one without rotations.  Output: sigma_i =
 //            sqrt(max(lambda_i, 0)) descending and the eigenvectors as
 //            rows, sorted the same way (workspace).
@@ -47,7 +48,8 @@ struct EncSmem {
   int pp[D / 2], pq[D / 2];
   int rank[D];
   float trace;
-  int nrot;
+  int nrot;              // rotations in the current sweep
+  int nrot_round[2];     // rotations in the current round (alternating by round parity)
 };
 
 // 8 consecutive elements of a dense array as fp32 (16-byte aligned).
@@ -117,6 +119,10 @@ __global__ __launch_bounds__(kEncThreads) void milo_encode_spectrum_kernel(Encod
   __shared__ __attribute__((aligned(16))) EncSmem<D> sm;
   constexpr int S = EncSmem<D>::S;
   constexpr int H = D / 2;
+  constexpr int KS = kEncThreads / H;   // rows of blocks (and of V) between a thread's items
+  constexpr int NB = H * H / kEncThreads;   // 2x2 blocks of G per thread per round
+  constexpr int NV = D * H / kEncThreads;   // (row, pair) items of V per thread per round
+  static_assert(kEncThreads % H == 0 && NB * kEncThreads == H * H && NV * kEncThreads == D * H, "work split");
   const int tid = threadIdx.x;
   const int m = blockIdx.x;
   const EncMat e = enc_mat(p, m, D);
@@ -168,7 +174,10 @@ __global__ __launch_bounds__(kEncThreads) void milo_encode_spectrum_kernel(Encod
     const int i = q / D, j = q % D;
     sm.v[i * S + j] = (i == j) ? 1.f : 0.f;
   }
-  if (tid == 0) sm.nrot = 0;
+  if (tid == 0) {
+    sm.nrot = 0;
+    sm.nrot_round[0] = sm.nrot_round[1] = 0;
+  }
   __syncthreads();
   if (tid < 64) {
     float s = 0.f;
@@ -180,12 +189,15 @@ __global__ __launch_bounds__(kEncThreads) void milo_encode_spectrum_kernel(Encod
   const float tol_abs = kEncTolAbs * fabsf(sm.trace);
 
   // ---- cyclic Jacobi sweeps
-  int sweeps = 0;
+  int sweeps = 0, rounds = 0;   // rounds: over all sweeps (parity of the round counter)
   bool converged = false;
   while (sweeps < kEncMaxSweeps) {
     ++sweeps;
-    for (int rnd = 0; rnd < D - 1; ++rnd) {
+    for (int rnd = 0; rnd < D - 1; ++rnd, ++rounds) {
       __syncthreads();   // the previous round's updates are visible
+      // the previous round's counter was read before the barrier above; it
+      // is the one the next round uses, so clear it now
+      if (tid == 0) sm.nrot_round[(rounds + 1) & 1] = 0;
       if (tid < H) {
         // circle pairing: position 0 holds index 0, position k > 0 holds
         // 1 + (k - 1 + rnd) mod (D - 1); pair = positions (tid, D - 1 - tid)
@@ -202,6 +214,7 @@ __global__ __launch_bounds__(kEncThreads) void milo_encode_spectrum_kernel(Encod
           c = 1.f / sqrtf(fmaf(t, t, 1.f));
           s = t * c;
           atomicAdd(&sm.nrot, 1);
+          atomicAdd(&sm.nrot_round[rounds & 1], 1);
         }
         sm.pp[tid] = pi;
         sm.pq[tid] = qi;
@@ -210,42 +223,64 @@ __global__ __launch_bounds__(kEncThreads) void milo_encode_spectrum_kernel(Encod
         sm.pt[tid] = t;
       }
       __syncthreads();
+      if (sm.nrot_round[rounds & 1] == 0) continue;   // no rotation in this round (uniform)
       // G <- J^T G J, J = the round's rotations ([[c, s], [-s, c]] on (p, q)):
-      // 2x2 block (k, l) of G becomes R_k^T B R_l; one thread per block
-      for (int q = tid; q < H * H; q += kEncThreads) {
-        const int k = q / H, l = q % H;
-        const float sk = sm.ps[k], sl = sm.ps[l];
-        if (sk == 0.f && sl == 0.f) continue;
-        const int pk = sm.pp[k], qk = sm.pq[k];
-        if (k == l) {
-          const float t = sm.pt[k], gpq = sm.g[pk * S + qk];
-          sm.g[pk * S + pk] -= t * gpq;
-          sm.g[qk * S + qk] += t * gpq;
-          sm.g[pk * S + qk] = 0.f;
-          sm.g[qk * S + pk] = 0.f;
-        } else {
-          const int pl = sm.pp[l], ql = sm.pq[l];
-          const float ck = sm.pc[k], cl = sm.pc[l];
-          const float b00 = sm.g[pk * S + pl], b01 = sm.g[pk * S + ql];
-          const float b10 = sm.g[qk * S + pl], b11 = sm.g[qk * S + ql];
-          const float m00 = ck * b00 - sk * b10, m01 = ck * b01 - sk * b11;
-          const float m10 = sk * b00 + ck * b10, m11 = sk * b01 + ck * b11;
-          sm.g[pk * S + pl] = cl * m00 - sl * m01;
-          sm.g[pk * S + ql] = sl * m00 + cl * m01;
-          sm.g[qk * S + pl] = cl * m10 - sl * m11;
-          sm.g[qk * S + ql] = sl * m10 + cl * m11;
-        }
-      }
-      // V <- V J: columns p_l, q_l of every row
-      for (int q = tid; q < D * H; q += kEncThreads) {
-        const int i = q / H, l = q % H;
-        const float sl = sm.ps[l];
-        if (sl == 0.f) continue;
+      // 2x2 block (k, l) of G becomes R_k^T B R_l.  Thread tid owns the
+      // blocks l = tid % H, k = tid / H + KS * i: it reads all of them, then
+      // rotates, then writes (the blocks are disjoint, and an identity
+      // rotation reproduces its block exactly, so no block is skipped).
+      {
+        const int l = tid % H, kb = tid / H;
         const int pl = sm.pp[l], ql = sm.pq[l];
-        const float cl = sm.pc[l];
-        const float a = sm.v[i * S + pl], b = sm.v[i * S + ql];
-        sm.v[i * S + pl] = cl * a - sl * b;
-        sm.v[i * S + ql] = sl * a + cl * b;
+        const float cl = sm.pc[l], sl = sm.ps[l];
+        float b[NB][4];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const int k = kb + KS * i;
+          const int pk = sm.pp[k], qk = sm.pq[k];
+          b[i][0] = sm.g[pk * S + pl];
+          b[i][1] = sm.g[pk * S + ql];
+          b[i][2] = sm.g[qk * S + pl];
+          b[i][3] = sm.g[qk * S + ql];
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const int k = kb + KS * i;
+          const int pk = sm.pp[k], qk = sm.pq[k];
+          if (k == l) {
+            // diagonal block: closed form, a rotated coupling becomes exactly 0
+            const float t = sm.pt[k];
+            const bool rot = sl != 0.f;
+            sm.g[pk * S + pk] = b[i][0] - t * b[i][1];
+            sm.g[qk * S + qk] = b[i][3] + t * b[i][1];
+            sm.g[pk * S + qk] = rot ? 0.f : b[i][1];
+            sm.g[qk * S + pk] = rot ? 0.f : b[i][2];
+          } else {
+            const float ck = sm.pc[k], sk = sm.ps[k];
+            const float m00 = ck * b[i][0] - sk * b[i][2], m01 = ck * b[i][1] - sk * b[i][3];
+            const float m10 = sk * b[i][0] + ck * b[i][2], m11 = sk * b[i][1] + ck * b[i][3];
+            sm.g[pk * S + pl] = cl * m00 - sl * m01;
+            sm.g[pk * S + ql] = sl * m00 + cl * m01;
+            sm.g[qk * S + pl] = cl * m10 - sl * m11;
+            sm.g[qk * S + ql] = sl * m10 + cl * m11;
+          }
+        }
+        // V <- V J: columns p_l, q_l of rows tid / H + KS * i
+        if (sl != 0.f) {
+          float va[NV], vb[NV];
+#pragma unroll
+          for (int i = 0; i < NV; ++i) {
+            const int row = kb + KS * i;
+            va[i] = sm.v[row * S + pl];
+            vb[i] = sm.v[row * S + ql];
+          }
+#pragma unroll
+          for (int i = 0; i < NV; ++i) {
+            const int row = kb + KS * i;
+            sm.v[row * S + pl] = cl * va[i] - sl * vb[i];
+            sm.v[row * S + ql] = sl * va[i] + cl * vb[i];
+          }
+        }
       }
     }
     __syncthreads();
