@@ -7,4 +7,4 @@ so both the fp64 oracle and the HIP path can consume its output.
 from .configs import CONFIGS, Config, get_config  # noqa: F401
 from .configs import ENCODE_CONFIGS, EncodeConfig, get_encode_config  # noqa: F401
 from .gen import Workload, LogicalBlock, make_workload, bf16_bits_to_f32  # noqa: F401
-from .gen import DenseContext, make_dense_context  # noqa: F401
+from .gen import DenseContext, make_dense_context, make_spectra  # noqa: F401

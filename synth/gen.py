@@ -335,3 +335,25 @@ def make_dense_context(cfg: EncodeConfig, variant: str = "base",
     ranks = draw_ranks(rcfg, "base", [nb])[0]
     return DenseContext(cfg=cfg, variant=variant, k=_store(k, cfg.dtype), v=_store(v, cfg.dtype),
                         tok_start=starts, n_tok=np.array(toks, np.int32), ranks=ranks, decay=decay)
+
+
+_S_SPECTRA = 5
+
+
+def make_spectra(n_blocks: int, n_kv_heads: int, head_dim: int, seed: int,
+                 decay_lo: float = 0.6, decay_hi: float = 0.98) -> np.ndarray:
+    """Seeded singular-value spectra float32 [n_blocks][Hkv][2][head_dim],
+    descending: sigma_i = a * rho^i with rho ~ U[decay_lo, decay_hi] per
+    (block, head, K/V) and a ~ lognormal.  Block 1 (if present) has a
+    planted rank of head_dim // 4, block 2 is all zero, block 3 is flat."""
+    rng = _rng(seed, _S_SPECTRA)
+    rho = rng.uniform(decay_lo, decay_hi, size=(n_blocks, n_kv_heads, 2))
+    amp = np.exp(rng.standard_normal((n_blocks, n_kv_heads, 2)))
+    s = amp[..., None] * rho[..., None] ** np.arange(head_dim)
+    if n_blocks > 1:
+        s[1, ..., head_dim // 4:] = 0.0
+    if n_blocks > 2:
+        s[2] = 0.0
+    if n_blocks > 3:
+        s[3] = amp[3][..., None]
+    return s.astype(np.float32)
