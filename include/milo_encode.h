@@ -88,6 +88,47 @@ milo_status milo_encode_layout(const int32_t* n_tok, const int32_t* rank_k, cons
                                int32_t n_blocks, int32_t n_kv_heads, int32_t head_dim,
                                milo_block* blocks_out, int64_t* pool_elems);
 
+/*
+ * Rank allocation ("4.3 Dynamic Rank Allocation"): under a fixed total
+ * budget, every block starts at r_min and the remaining rank units of size
+ * `unit` go one at a time to the block whose next unit has the largest
+ * marginal gain; keys and values have separate budgets ("4.4 MILO
+ * Workflow").  The pages leave the entropy and the gain open; the readings:
+ *   p     = the block's normalised energy sigma_i^2 / sum_j sigma_j^2 per KV
+ *           head, averaged over its heads and renormalised (heads without
+ *           energy contribute nothing);
+ *   H     = -sum p_i ln p_i, high for slowly decaying spectra;
+ *   gain of the unit raising rank r to r + unit = H * (p_r + .. + p_{r+unit-1});
+ *   ties go to the lowest block index.
+ * The result is exactly that greedy's (gains are non-increasing within a
+ * block, so its picks are the K largest gains), computed without a
+ * sequential loop.  Ranks never exceed r_min + unit * floor((head_dim -
+ * r_min) / unit).
+ */
+typedef struct milo_rank_args {
+  int32_t struct_size;         /* sizeof(milo_rank_args)                                    */
+  int32_t n_blocks;            /* >= 0                                                      */
+  int32_t n_kv_heads;          /* >= 1                                                      */
+  int32_t head_dim;            /* 64 or 128                                                 */
+  int32_t budget_k;            /* sum of the key ranks over all blocks                      */
+  int32_t budget_v;            /* sum of the value ranks                                    */
+  int32_t r_min;               /* minimum rank per block, 0 <= r_min <= head_dim            */
+  int32_t unit;                /* rank granularity >= 1; each budget must be n_blocks *
+                                  r_min plus a whole number of units that fit               */
+  const float* sigma;          /* [n_blocks][n_kv_heads][2][head_dim] singular values,
+                                  finite, descending per head (milo_encode_spectrum)        */
+  int32_t* ranks;              /* out: [n_blocks][2] (rank_k, rank_v)                        */
+  float* entropy;              /* out: [n_blocks][2] H of keys and values; may be NULL      */
+  void* workspace;             /* milo_rank_workspace_bytes() bytes, 256-B aligned          */
+  size_t workspace_bytes;
+} milo_rank_args;
+
+/* Workspace (the unit gains); 0 if the arguments are invalid. */
+size_t milo_rank_workspace_bytes(const milo_rank_args* args);
+
+/* Ranks of every block for keys and values (two kernels on the stream). */
+milo_status milo_rank_allocate(const milo_rank_args* args, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,7 +13,8 @@ MILO_F32, MILO_BF16 = 0, 1
 MILO_PATH_DECODE, MILO_PATH_CHUNK, MILO_PATH_SHARED = 0, 1, 2
 EXPORTS = ("milo_attn_workspace_bytes", "milo_attn_decode", "milo_attn_chunk", "milo_attn_decode_shared",
            "milo_attn_plan_decode", "milo_status_str", "milo_abi_version",
-           "milo_encode_workspace_bytes", "milo_encode_spectrum", "milo_encode_factors", "milo_encode_layout")
+           "milo_encode_workspace_bytes", "milo_encode_spectrum", "milo_encode_factors", "milo_encode_layout",
+           "milo_rank_workspace_bytes", "milo_rank_allocate")
 
 
 class MiloBlock(ctypes.Structure):
@@ -69,6 +70,24 @@ class MiloEncodeArgs(ctypes.Structure):
     ]
 
 
+class MiloRankArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_int32),
+        ("n_blocks", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("budget_k", ctypes.c_int32),
+        ("budget_v", ctypes.c_int32),
+        ("r_min", ctypes.c_int32),
+        ("unit", ctypes.c_int32),
+        ("sigma", ctypes.c_void_p),
+        ("ranks", ctypes.c_void_p),
+        ("entropy", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 _lib = None
 
 
@@ -101,6 +120,10 @@ def load() -> ctypes.CDLL:
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                            ctypes.POINTER(ctypes.c_int64)]
         lib.milo_encode_layout.restype = ctypes.c_int
+        lib.milo_rank_workspace_bytes.argtypes = [ctypes.POINTER(MiloRankArgs)]
+        lib.milo_rank_workspace_bytes.restype = ctypes.c_size_t
+        lib.milo_rank_allocate.argtypes = [ctypes.POINTER(MiloRankArgs), ctypes.c_void_p]
+        lib.milo_rank_allocate.restype = ctypes.c_int
         lib.milo_abi_version.argtypes = []
         lib.milo_abi_version.restype = ctypes.c_int32
         _lib = lib

@@ -33,6 +33,7 @@ UNITS = [
     ("merge.hip", [], "merge.o"),
     ("chunk.hip", [], "chunk.o"),
     ("encode.hip", [], "encode.o"),
+    ("rank.hip", [], "rank.o"),
     ("milo_attn.cpp", [], "milo_attn.o"),
     ("milo_encode.cpp", [], "milo_encode.o"),
 ]

@@ -87,6 +87,18 @@ struct EncodeParams {
 hipError_t launch_encode_spectrum(const EncodeParams& p, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_encode_factors(const EncodeParams& p, int dtype, int head_dim, hipStream_t s);
 
+// Rank allocation: unit gains per (K/V, block) in the workspace, then one
+// selection per K/V.
+struct RankParams {
+  const float* sigma;          // [n_blocks][n_kv_heads][2][head_dim]
+  float* gains;                // [2][n_blocks][n_units]
+  int32_t* ranks;              // [n_blocks][2]
+  float* entropy;              // [n_blocks][2] or null
+  int32_t n_blocks, n_kv_heads, n_units, r_min, unit;
+  int64_t k_units_k, k_units_v;   // units to hand out above r_min
+};
+hipError_t launch_rank(const RankParams& p, int head_dim, hipStream_t s);
+
 // Work units of the decode kernel: one per (sequence, KV head, block slot),
 // plus one dense-tail unit per (sequence, KV head).
 inline int64_t decode_units(int batch, int n_kv_heads, int max_blocks) {

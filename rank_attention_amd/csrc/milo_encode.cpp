@@ -4,6 +4,7 @@
 // caller's stream.  No allocation, no synchronisation, no global state.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "kernels.h"
@@ -61,9 +62,60 @@ milo::EncodeParams params_of(const milo_encode_args* a) {
   return p;
 }
 
+int32_t rank_units(const milo_rank_args* a) { return (a->head_dim - a->r_min) / a->unit; }
+
+milo_status check_rank(const milo_rank_args* a) {
+  if (!a) return MILO_ERR_INVALID;
+  if (a->struct_size != (int32_t)sizeof(milo_rank_args)) return MILO_ERR_INVALID;
+  if (a->n_blocks < 0 || a->n_kv_heads < 1 || a->unit < 1) return MILO_ERR_INVALID;
+  if (a->head_dim != 64 && a->head_dim != 128) return MILO_ERR_UNSUPPORTED;
+  if (a->r_min < 0 || a->r_min > a->head_dim) return MILO_ERR_INVALID;
+  if ((int64_t)a->n_blocks * 2 * (rank_units(a) + 1) > INT32_MAX) return MILO_ERR_UNSUPPORTED;
+  for (int32_t budget : {a->budget_k, a->budget_v}) {
+    const int64_t extra = (int64_t)budget - (int64_t)a->n_blocks * a->r_min;
+    if (extra < 0 || extra % a->unit != 0 || extra / a->unit > (int64_t)a->n_blocks * rank_units(a))
+      return MILO_ERR_INVALID;
+  }
+  return MILO_OK;
+}
+
+size_t rank_workspace_of(const milo_rank_args* a) {
+  return enc_round_up((size_t)2 * a->n_blocks * std::max(rank_units(a), 1) * sizeof(float), kEncWsAlign);
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t milo_rank_workspace_bytes(const milo_rank_args* a) {
+  if (check_rank(a) != MILO_OK) return 0;
+  return rank_workspace_of(a);
+}
+
+milo_status milo_rank_allocate(const milo_rank_args* a, void* hip_stream) {
+  milo_status st = check_rank(a);
+  if (st != MILO_OK) return st;
+  if (a->n_blocks == 0) return MILO_OK;
+  if (!a->sigma || !a->ranks || !enc_aligned(a->sigma, 4) || !enc_aligned(a->ranks, 4)) return MILO_ERR_INVALID;
+  if (a->entropy && !enc_aligned(a->entropy, 4)) return MILO_ERR_INVALID;
+  if (!a->workspace || a->workspace_bytes < rank_workspace_of(a) || !enc_aligned(a->workspace, kEncWsAlign))
+    return MILO_ERR_WORKSPACE;
+  milo::RankParams p{};
+  p.sigma = a->sigma;
+  p.gains = static_cast<float*>(a->workspace);
+  p.ranks = a->ranks;
+  p.entropy = a->entropy;
+  p.n_blocks = a->n_blocks;
+  p.n_kv_heads = a->n_kv_heads;
+  p.n_units = rank_units(a);
+  p.r_min = a->r_min;
+  p.unit = a->unit;
+  p.k_units_k = ((int64_t)a->budget_k - (int64_t)a->n_blocks * a->r_min) / a->unit;
+  p.k_units_v = ((int64_t)a->budget_v - (int64_t)a->n_blocks * a->r_min) / a->unit;
+  if (milo::launch_rank(p, a->head_dim, reinterpret_cast<hipStream_t>(hip_stream)) != hipSuccess)
+    return MILO_ERR_DEVICE;
+  return MILO_OK;
+}
 
 size_t milo_encode_workspace_bytes(const milo_encode_args* a) {
   if (check_shape(a) != MILO_OK) return 0;

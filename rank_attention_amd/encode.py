@@ -10,7 +10,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 from . import _lib
-from ._lib import MILO_BF16, MILO_F32, MILO_OK, MILO_ERR_DEVICE, MiloEncodeArgs
+from ._lib import MILO_BF16, MILO_F32, MILO_OK, MILO_ERR_DEVICE, MiloEncodeArgs, MiloRankArgs
 from .pack import BLOCK_DTYPE
 
 
@@ -32,6 +32,39 @@ def layout(n_tok: Sequence[int], rank_k: Sequence[int], rank_v: Sequence[int], n
     if rc != MILO_OK:
         raise MiloError(rc, status_str(rc))
     return blocks, int(elems.value)
+
+
+def allocate_ranks(sigma, budget_k: int, budget_v: int, r_min: int, unit: int = 1, stream=None):
+    """Entropy-driven ranks (milo_rank_allocate) from device spectra sigma
+    [n_blocks][Hkv][2][d] (fp32, descending per head).  Returns (ranks int32
+    [n_blocks][2], entropy fp32 [n_blocks][2]) on the device."""
+    import torch
+    from . import MiloError, status_str
+    nb, h, two, d = (int(x) for x in sigma.shape)
+    if two != 2 or sigma.dtype != torch.float32:
+        raise ValueError("sigma must be float32 [n_blocks][n_kv_heads][2][head_dim]")
+    lib = _lib.load()
+    ranks = torch.empty((nb, 2), dtype=torch.int32, device=sigma.device)
+    ent = torch.empty((nb, 2), dtype=torch.float32, device=sigma.device)
+    a = MiloRankArgs()
+    a.struct_size = ctypes.sizeof(MiloRankArgs)
+    a.n_blocks, a.n_kv_heads, a.head_dim = nb, h, d
+    a.budget_k, a.budget_v, a.r_min, a.unit = int(budget_k), int(budget_v), int(r_min), int(unit)
+    a.sigma, a.ranks, a.entropy = sigma.data_ptr(), ranks.data_ptr(), ent.data_ptr()
+    need = lib.milo_rank_workspace_bytes(ctypes.byref(a))
+    if need == 0:
+        rc = lib.milo_rank_allocate(ctypes.byref(a), None)
+        raise MiloError(rc, status_str(rc))
+    ws = torch.empty(int(need), dtype=torch.uint8, device=sigma.device)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), int(need)
+    if stream is None:
+        stream = torch.cuda.current_stream(sigma.device).cuda_stream
+    rc = lib.milo_rank_allocate(ctypes.byref(a), ctypes.c_void_p(int(stream)))
+    if rc != MILO_OK:
+        if rc == MILO_ERR_DEVICE:
+            raise RuntimeError(f"milo_rank_allocate: {status_str(rc)}")
+        raise MiloError(rc, status_str(rc))
+    return ranks, ent
 
 
 class DeviceContext:

@@ -255,3 +255,49 @@ def test_encode_layout():
             enc.layout(*bad, n_kv_heads=1, head_dim=128)
     lib = _lib.load()
     assert lib.milo_encode_layout(None, None, None, 1, 1, 128, None, None) == _lib.MILO_ERR_INVALID
+
+
+def rank_args(**over):
+    a = _lib.MiloRankArgs()
+    a.struct_size = ctypes.sizeof(_lib.MiloRankArgs)
+    a.n_blocks, a.n_kv_heads, a.head_dim = 10, 2, 128
+    a.budget_k, a.budget_v, a.r_min, a.unit = 10 * 8 + 320, 10 * 8 + 160, 8, 1
+    a.sigma = a.ranks = a.entropy = FAKE
+    a.workspace, a.workspace_bytes = FAKE, 1 << 20
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_rank_struct_and_workspace():
+    assert ctypes.sizeof(_lib.MiloRankArgs) == 8 * 4 + 5 * 8
+    lib = _lib.load()
+    # 2 x 10 blocks x 120 units of fp32 gains
+    assert lib.milo_rank_workspace_bytes(ctypes.byref(rank_args())) == -(-2 * 10 * 120 * 4 // 256) * 256
+    assert lib.milo_rank_workspace_bytes(ctypes.byref(rank_args(unit=16))) == -(-2 * 10 * 7 * 4 // 256) * 256
+    assert lib.milo_rank_workspace_bytes(ctypes.byref(rank_args(budget_k=5))) == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"struct_size": 4}, _lib.MILO_ERR_INVALID),
+    ({"head_dim": 96}, _lib.MILO_ERR_UNSUPPORTED),
+    ({"unit": 0}, _lib.MILO_ERR_INVALID),
+    ({"r_min": 129}, _lib.MILO_ERR_INVALID),
+    ({"r_min": -1}, _lib.MILO_ERR_INVALID),
+    ({"budget_k": 79}, _lib.MILO_ERR_INVALID),              # below n_blocks * r_min
+    ({"budget_v": 10 * 128 + 1}, _lib.MILO_ERR_INVALID),    # more than every block at full rank
+    ({"unit": 16, "budget_k": 80 + 17}, _lib.MILO_ERR_INVALID),   # not whole units
+    ({"sigma": None}, _lib.MILO_ERR_INVALID),
+    ({"ranks": FAKE + 2}, _lib.MILO_ERR_INVALID),
+    ({"workspace": None}, _lib.MILO_ERR_WORKSPACE),
+    ({"workspace_bytes": 16}, _lib.MILO_ERR_WORKSPACE),
+])
+def test_rank_rejects_before_any_hip_call(over, code):
+    assert _lib.load().milo_rank_allocate(ctypes.byref(rank_args(**over)), None) == code
+
+
+def test_rank_empty_and_null():
+    lib = _lib.load()
+    assert lib.milo_rank_allocate(None, None) == _lib.MILO_ERR_INVALID
+    empty = rank_args(n_blocks=0, budget_k=0, budget_v=0, sigma=None, ranks=None, workspace=None)
+    assert lib.milo_rank_allocate(ctypes.byref(empty), None) == _lib.MILO_OK
