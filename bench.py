@@ -18,10 +18,11 @@ FLOP/byte ridge).
 Kernel time comes from HIP events recorded on the launch stream around the
 attention kernel alone; the fp64 CPU oracle is timed on a bounded sample.
 
-Encode (--encode, workload enc_qwen7b_64k): one step factorises the dense
-keys and values of one 64k-token context (spectrum kernel + factors kernel
-at the workload's target ranks); context tokens/s, and the spectrum
-kernel's algorithmic fp32 rate against the 157.3 TFLOP/s vector peak.
+Encode (--encode, workload enc_qwen7b_64k): one step runs the encode
+workflow over the dense keys and values of one 64k-token context (spectra,
+entropy-driven ranks at a 50% budget, host layout, factors); context
+tokens/s, and the spectrum kernel's algorithmic fp32 rate against the 157.3
+TFLOP/s vector peak.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen7b_64k] [--shared]
     python bench.py --encode [--workload enc_qwen7b_64k]
@@ -167,11 +168,15 @@ def cpu_baseline_encode(ctx, seconds: float):
 
 
 def run_encode(args) -> int:
+    """The encode workflow per step: spectra (Gram + Jacobi), entropy-driven
+    ranks at a 50% rank budget for keys and for values (r_min 8), the pool
+    layout on the host, then the factors at those ranks."""
+    import numpy as np
     import torch
     import rank_attention_amd as ra
     import synth
     from rank_attention_amd import _lib
-    from rank_attention_amd.encode import DeviceContext
+    from rank_attention_amd.encode import DeviceContext, allocate_ranks, layout
 
     if not os.path.exists(ra.library_path):
         import __graft_entry__
@@ -181,74 +186,81 @@ def run_encode(args) -> int:
     cfg = synth.get_encode_config(name)
     t0 = time.time()
     ctx = synth.make_dense_context(cfg)
+    nb, d, h = len(ctx.n_tok), cfg.head_dim, cfg.n_kv_heads
+    r_min, frac = 8, 0.5
+    budget = int(nb * d * frac)
     dc = DeviceContext(ctx.k, ctx.v, ctx.tok_start, ctx.n_tok, dtype=cfg.dtype, device="cuda:0")
     dense_bytes = 2 * dc.k.numel() * dc.k.element_size()
     copies = max(args.copies, -(-3 * LAST_LEVEL_CACHE_BYTES // max(1, dense_bytes)))
     kvs = [(dc.k, dc.v)] + [(dc.k.clone(), dc.v.clone()) for _ in range(copies - 1)]
     sigma, sweeps = dc.spectrum()           # sizes the workspace
-    rk, rv = ctx.ranks[:, 0], ctx.ranks[:, 1]
-    pool, bdev, _ = dc.factors(rk, rv)
+    _, full_elems = layout(ctx.n_tok, [d] * nb, [d] * nb, h, d)
+    pool = torch.empty(full_elems, dtype=torch.int16 if cfg.dtype == "bf16" else torch.float32, device="cuda:0")
     torch.cuda.synchronize()
     sw = sweeps.cpu().numpy()
     spec_blocks = dc._spectrum_blocks
-    stream = torch.cuda.current_stream().cuda_stream
-    argsets = []
-    for k, v in kvs:
-        dc.k, dc.v = k, v
-        argsets.append((dc._args(spec_blocks, sigma=sigma, sweeps=sweeps), dc._args(bdev, pool=pool)))
     print(f"[bench] {cfg.desc}: dense K/V {dense_bytes / 1e6:.1f} MB, {copies} copies, Jacobi sweeps "
-          f"{sw.min()}..{sw.max()} (mean {sw.mean():.1f}), setup {time.time() - t0:.1f} s",
-          file=sys.stderr, flush=True)
+          f"{sw.min()}..{sw.max()} (mean {sw.mean():.1f}), rank budget {budget} per K/V (50%), r_min {r_min}, "
+          f"setup {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
     def step(k, evs=None):
-        a_s, a_f = argsets[k % len(argsets)]
-        if evs is not None:
-            evs[0].record()
-        rc = lib.milo_encode_spectrum(ctypes.byref(a_s), ctypes.c_void_p(stream))
-        if evs is not None:
-            evs[1].record()
-        rc = rc or lib.milo_encode_factors(ctypes.byref(a_f), ctypes.c_void_p(stream))
-        if evs is not None:
-            evs[2].record()
+        dc.k, dc.v = kvs[k % len(kvs)]
+        rec = (lambda i: evs[i].record()) if evs is not None else (lambda i: None)
+        rec(0)
+        rc = lib.milo_encode_spectrum(ctypes.byref(dc._args(spec_blocks, sigma=sigma, sweeps=sweeps)),
+                                      ctypes.c_void_p(stream))
         if rc != 0:
-            raise RuntimeError(f"milo_encode failed: {ra.status_str(rc)}")
+            raise RuntimeError(f"milo_encode_spectrum failed: {ra.status_str(rc)}")
+        rec(1)
+        ranks, _ = allocate_ranks(sigma, budget, budget, r_min, 1)
+        rec(2)
+        rk = ranks.cpu().numpy()                 # the pool layout is a host step
+        blocks, _ = layout(ctx.n_tok, rk[:, 0], rk[:, 1], h, d)
+        bdev = torch.from_numpy(blocks.view(np.uint8).copy()).to("cuda:0", non_blocking=False)
+        rec(3)
+        rc = lib.milo_encode_factors(ctypes.byref(dc._args(bdev, pool=pool)), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"milo_encode_factors failed: {ra.status_str(rc)}")
+        rec(4)
+        return rk
 
+    stream = torch.cuda.current_stream().cuda_stream
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t_start = time.perf_counter()
     for k in range(args.steps):
-        step(k, evs[k])
+        rk = step(k, evs[k])
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     spec_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    fac_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    alloc_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    fac_ms = [e[3].elapsed_time(e[4]) for e in evs]
     ms_per_step = (t_end - t_start) * 1e3 / args.steps
     kmean = sum(spec_ms) / len(spec_ms)
+    amean = sum(alloc_ms) / len(alloc_ms)
     fmean = sum(fac_ms) / len(fac_ms)
-    flops = encode_flops(ctx)
-    d = cfg.head_dim
-    spec_flops = sum(cfg.n_kv_heads * 2 * (2 * int(T) * d * d + 9 * d ** 3) for T in ctx.n_tok)
+    spec_flops = sum(h * 2 * (2 * int(T) * d * d + 9 * d ** 3) for T in ctx.n_tok)
     achieved = spec_flops / (kmean * 1e-3) / 1e12
     tokens = int(ctx.n_tok.sum())
-    print(f"[bench] spectrum kernel mean {kmean * 1e3:.1f} us, factors kernel mean {fmean * 1e3:.1f} us, "
-          f"step {ms_per_step * 1e3:.1f} us; {achieved:.2f} TFLOP/s algorithmic in the spectrum kernel; "
-          f"{flops / 1e9:.1f} GFLOP per step", file=sys.stderr, flush=True)
+    print(f"[bench] spectrum kernel mean {kmean * 1e3:.1f} us, rank allocation {amean * 1e3:.1f} us, factors "
+          f"kernel mean {fmean * 1e3:.1f} us, step {ms_per_step * 1e3:.1f} us; {achieved:.2f} TFLOP/s "
+          f"algorithmic in the spectrum kernel; allocated ranks K {rk[:, 0].min()}..{rk[:, 0].max()}, "
+          f"V {rk[:, 1].min()}..{rk[:, 1].max()}", file=sys.stderr, flush=True)
     res = {
         "metric": ENCODE_METRIC, "value": tokens / (ms_per_step * 1e-3), "unit": "context tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": cfg.name, "desc": cfg.desc, "n_blocks": len(ctx.n_tok),
-                   "block_tokens": cfg.block_tokens, "n_kv_heads": cfg.n_kv_heads, "head_dim": d,
-                   "context_tokens_per_step": tokens, "copies": copies,
-                   "jacobi_sweeps_mean": float(sw.mean())},
+        "config": {"workload": cfg.name, "desc": cfg.desc, "n_blocks": nb, "block_tokens": cfg.block_tokens,
+                   "n_kv_heads": h, "head_dim": d, "context_tokens_per_step": tokens, "copies": copies,
+                   "rank_budget": budget, "r_min": r_min, "jacobi_sweeps_mean": float(sw.mean())},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
                      "traffic": traffic_from_profiles(cfg.name, "encode"),
                      "kernel": "milo_encode_spectrum_kernel", "kernel_us_mean": kmean * 1e3,
-                     "factors_kernel_us_mean": fmean * 1e3,
+                     "rank_allocation_us_mean": amean * 1e3, "factors_kernel_us_mean": fmean * 1e3,
                      "algorithmic_flops_per_launch": spec_flops,
                      "algorithmic_bytes_per_launch": dense_bytes,
                      "kernel_source_sha": kernel_source_sha("encode")},
