@@ -176,6 +176,35 @@ milo_status milo_attn_plan_decode(const milo_block* blocks, const int32_t* seq_b
                                   int32_t max_blocks_per_seq, int32_t head_dim,
                                   int32_t* order_out);
 
+/*
+ * Device-side check of the tables a call reads, for debugging callers: the
+ * kernels clamp counts and lengths but trust offsets and ranks.  Reads only
+ * blocks[0 .. n_descriptors), seq_blocks and tail_len (never the pool), in
+ * two kernels on the stream, and writes *status (device, 8 bytes):
+ *     UINT64_MAX                          every rule holds;
+ *     ((uint64_t)rule << 32) | index     otherwise, the smallest violated
+ *                                         milo_table_rule and, for it, the
+ *                                         smallest offending index (sequence
+ *                                         for rules 1, 2, 7; descriptor else).
+ * With path MILO_PATH_SHARED only sequence 0's list is checked (the other
+ * lists are not read by that path).  pool_elems is the pool size in
+ * elements.  Host-checkable faults return a status as for the other entry
+ * points (status must be 8-byte aligned).
+ */
+typedef enum milo_table_rule {
+  MILO_TABLE_SEQ_RANGE = 1,        /* seq_blocks[i] < 0, decreasing, or past n_descriptors        */
+  MILO_TABLE_TOO_MANY_BLOCKS = 2,  /* seq_blocks[i+1] - seq_blocks[i] > max_blocks_per_seq        */
+  MILO_TABLE_RANK = 3,             /* rank_k or rank_v outside [0, head_dim]                      */
+  MILO_TABLE_TOKENS = 4,           /* n_tok < 0, ld_tok < n_tok, or ld_tok not a multiple of 8    */
+  MILO_TABLE_OFFSET = 5,           /* off < 0 or not a multiple of 8                              */
+  MILO_TABLE_POOL_BOUNDS = 6,      /* the block's factors end past pool_elems                     */
+  MILO_TABLE_TAIL_LEN = 7          /* tail_len[i] outside [0, tail_cap] (decode, shared) or
+                                      [q_len, tail_cap] (chunk)                                   */
+} milo_table_rule;
+
+milo_status milo_attn_validate(const milo_attn_args* args, int32_t path, int32_t n_descriptors,
+                               int64_t pool_elems, uint64_t* status, void* hip_stream);
+
 /* Static description of a status code. */
 const char* milo_status_str(milo_status status);
 

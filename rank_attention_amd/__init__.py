@@ -17,7 +17,7 @@ from ._lib import (MILO_BF16, MILO_F32, MILO_PATH_CHUNK, MILO_PATH_DECODE, MILO_
                    MILO_OK, MILO_ERR_DEVICE)
 from .pack import BLOCK_DTYPE, PackedCache, pack  # noqa: F401
 
-__all__ = ["decode", "chunk", "decode_shared", "workspace_bytes", "abi_version", "status_str", "DeviceCache",
+__all__ = ["decode", "chunk", "decode_shared", "validate_tables", "workspace_bytes", "abi_version", "status_str", "DeviceCache",
            "pack", "PackedCache", "MiloError", "library_path"]
 
 library_path = _lib.LIB_PATH
@@ -135,6 +135,29 @@ def decode_shared(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_kv
                 n_kv_heads=n_kv_heads, scale=scale, max_blocks=max_blocks, **kw)
 
 
+def validate_tables(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_kv_heads: int,
+                    max_blocks: int, path: int = MILO_PATH_DECODE, scale: float = 1.0):
+    """Check the device tables against the contract (milo_attn_validate) and
+    wait for the result: None if every rule holds, else (rule name, index)."""
+    import torch
+    lib = _lib.load()
+    status = torch.empty(1, dtype=torch.int64, device=q.device)
+    a = make_args(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, n_kv_heads=n_kv_heads, scale=scale,
+                  max_blocks=max_blocks)
+    n_desc = int(blocks.numel() * blocks.element_size()) // BLOCK_DTYPE.itemsize
+    pool_elems = int(pool.numel()) if pool is not None else 0
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib.milo_attn_validate(ctypes.byref(a), int(path), n_desc, pool_elems, status.data_ptr(),
+                                ctypes.c_void_p(int(stream)))
+    if rc != MILO_OK:
+        raise MiloError(rc, status_str(rc))
+    torch.cuda.synchronize(q.device)
+    v = int(status.cpu().numpy().view(np.uint64)[0])
+    if v == 0xFFFFFFFFFFFFFFFF:
+        return None
+    return _lib.TABLE_RULES.get(v >> 32, str(v >> 32)), int(v & 0xFFFFFFFF)
+
+
 class DeviceCache:
     """A packed cache and its query moved to device memory (torch tensors)."""
 
@@ -174,6 +197,9 @@ class DeviceCache:
     def chunk(self, **kw):
         kw.setdefault("scale", self.scale)
         return chunk(*self.tensors(), n_kv_heads=self.n_kv_heads, max_blocks=self.max_blocks, **kw)
+
+    def validate(self, path: int = MILO_PATH_DECODE):
+        return validate_tables(*self.tensors(), n_kv_heads=self.n_kv_heads, max_blocks=self.max_blocks, path=path)
 
     def decode_shared(self, **kw):
         kw.setdefault("scale", self.scale)

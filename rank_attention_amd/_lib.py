@@ -14,7 +14,9 @@ MILO_PATH_DECODE, MILO_PATH_CHUNK, MILO_PATH_SHARED = 0, 1, 2
 EXPORTS = ("milo_attn_workspace_bytes", "milo_attn_decode", "milo_attn_chunk", "milo_attn_decode_shared",
            "milo_attn_plan_decode", "milo_status_str", "milo_abi_version",
            "milo_encode_workspace_bytes", "milo_encode_spectrum", "milo_encode_factors", "milo_encode_layout",
-           "milo_rank_workspace_bytes", "milo_rank_allocate")
+           "milo_rank_workspace_bytes", "milo_rank_allocate", "milo_attn_validate")
+TABLE_RULES = {1: "seq_range", 2: "too_many_blocks", 3: "rank", 4: "tokens", 5: "offset", 6: "pool_bounds",
+               7: "tail_len"}
 
 
 class MiloBlock(ctypes.Structure):
@@ -105,6 +107,9 @@ def load() -> ctypes.CDLL:
         for fn in (lib.milo_attn_decode, lib.milo_attn_chunk, lib.milo_attn_decode_shared):
             fn.argtypes = [ctypes.POINTER(MiloAttnArgs), ctypes.c_void_p]
             fn.restype = ctypes.c_int
+        lib.milo_attn_validate.argtypes = [ctypes.POINTER(MiloAttnArgs), ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        lib.milo_attn_validate.restype = ctypes.c_int
         lib.milo_attn_plan_decode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_void_p]

@@ -34,6 +34,7 @@ UNITS = [
     ("chunk.hip", [], "chunk.o"),
     ("encode.hip", [], "encode.o"),
     ("rank.hip", [], "rank.o"),
+    ("validate.hip", [], "validate.o"),
     ("milo_attn.cpp", [], "milo_attn.o"),
     ("milo_encode.cpp", [], "milo_encode.o"),
 ]

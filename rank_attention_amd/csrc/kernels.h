@@ -99,6 +99,17 @@ struct RankParams {
 };
 hipError_t launch_rank(const RankParams& p, int head_dim, hipStream_t s);
 
+// Device table check (milo_attn_validate).
+struct ValidateParams {
+  const milo_block* blocks;
+  const int32_t* seq_blocks;
+  const int32_t* tail_len;
+  unsigned long long* status;
+  int64_t pool_elems;
+  int32_t n_descriptors, n_seqs_checked, batch, max_blocks, n_kv_heads, head_dim, tail_cap, tail_min;
+};
+hipError_t launch_validate(const ValidateParams& p, hipStream_t s);
+
 // Work units of the decode kernel: one per (sequence, KV head, block slot),
 // plus one dense-tail unit per (sequence, KV head).
 inline int64_t decode_units(int batch, int n_kv_heads, int max_blocks) {

@@ -304,6 +304,32 @@ milo_status milo_attn_decode_shared(const milo_attn_args* a, void* hip_stream) {
   return MILO_OK;
 }
 
+milo_status milo_attn_validate(const milo_attn_args* a, int32_t path, int32_t n_descriptors,
+                               int64_t pool_elems, uint64_t* status, void* hip_stream) {
+  milo_status st = check_shape(a, path);
+  if (st != MILO_OK) return st;
+  if (n_descriptors < 0 || pool_elems < 0 || !status || !aligned(status, 8)) return MILO_ERR_INVALID;
+  if (a->batch > 0 && !a->seq_blocks) return MILO_ERR_INVALID;
+  if (n_descriptors > 0 && (!a->blocks || !aligned(a->blocks, 8))) return MILO_ERR_INVALID;
+  if (a->tail_cap > 0 && !a->tail_len) return MILO_ERR_INVALID;
+  milo::ValidateParams p{};
+  p.blocks = a->blocks;
+  p.seq_blocks = a->seq_blocks;
+  p.tail_len = a->tail_len;
+  p.status = reinterpret_cast<unsigned long long*>(status);
+  p.pool_elems = pool_elems;
+  p.n_descriptors = n_descriptors;
+  p.n_seqs_checked = a->batch == 0 ? 0 : (path == MILO_PATH_SHARED ? 1 : a->batch);
+  p.batch = a->batch;
+  p.max_blocks = a->max_blocks_per_seq;
+  p.n_kv_heads = a->n_kv_heads;
+  p.head_dim = a->head_dim;
+  p.tail_cap = a->tail_cap;
+  p.tail_min = path == MILO_PATH_CHUNK ? a->q_len : 0;
+  if (milo::launch_validate(p, reinterpret_cast<hipStream_t>(hip_stream)) != hipSuccess) return MILO_ERR_DEVICE;
+  return MILO_OK;
+}
+
 milo_status milo_attn_plan_decode(const milo_block* blocks, const int32_t* seq_blocks,
                                   const int32_t* tail_len, int32_t batch, int32_t n_kv_heads,
                                   int32_t max_blocks, int32_t head_dim, int32_t* order_out) {

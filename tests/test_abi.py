@@ -301,3 +301,17 @@ def test_rank_empty_and_null():
     assert lib.milo_rank_allocate(None, None) == _lib.MILO_ERR_INVALID
     empty = rank_args(n_blocks=0, budget_k=0, budget_v=0, sigma=None, ranks=None, workspace=None)
     assert lib.milo_rank_allocate(ctypes.byref(empty), None) == _lib.MILO_OK
+
+
+def test_validate_rejects_bad_host_arguments():
+    lib = _lib.load()
+    a = good_args()
+    assert lib.milo_attn_validate(ctypes.byref(a), _lib.MILO_PATH_DECODE, 4, 1000, None, None) == _lib.MILO_ERR_INVALID
+    assert lib.milo_attn_validate(ctypes.byref(a), _lib.MILO_PATH_DECODE, 4, 1000, FAKE + 4, None) == _lib.MILO_ERR_INVALID
+    assert lib.milo_attn_validate(ctypes.byref(a), _lib.MILO_PATH_DECODE, -1, 1000, FAKE, None) == _lib.MILO_ERR_INVALID
+    assert lib.milo_attn_validate(ctypes.byref(a), _lib.MILO_PATH_DECODE, 4, -5, FAKE, None) == _lib.MILO_ERR_INVALID
+    b = good_args(seq_blocks=None)
+    assert lib.milo_attn_validate(ctypes.byref(b), _lib.MILO_PATH_DECODE, 4, 1000, FAKE, None) == _lib.MILO_ERR_INVALID
+    c = good_args(head_dim=96)
+    assert lib.milo_attn_validate(ctypes.byref(c), _lib.MILO_PATH_DECODE, 4, 1000, FAKE, None) == _lib.MILO_ERR_UNSUPPORTED
+    assert lib.milo_attn_validate(None, _lib.MILO_PATH_DECODE, 4, 1000, FAKE, None) == _lib.MILO_ERR_INVALID
