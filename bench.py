@@ -105,6 +105,38 @@ def traffic_from_profiles(workload: str, path: str = "decode"):
     return rec.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def read_ceiling_gbs(lib, torch, gib: int = 2, reps: int = 5) -> float:
+    """HBM read rate of the library's streaming-read probe (the decode
+    kernel's load form) over a fresh `gib` GiB buffer, mean of `reps` runs."""
+    n = gib << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):
+        lib.milo_read_probe(buf.data_ptr(), n, sink.data_ptr(), 4096, ctypes.c_void_p(stream))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        rc = lib.milo_read_probe(buf.data_ptr(), n, sink.data_ptr(), 4096, ctypes.c_void_p(stream))
+        b.record()
+        if rc != 0:
+            raise RuntimeError("milo_read_probe failed")
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / reps
+    del buf
+    return n / (ms * 1e-3) / 1e9
+
+
 def chunk_flops(wl, shared: bool = False) -> int:
     """Algorithmic FLOPs of one chunked-query launch: per block and KV head
     2*M*(r + r')*(T + d) for the four factor products (M = Q*G query rows),
@@ -162,7 +194,7 @@ def cpu_baseline_encode(ctx, seconds: float):
         cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         cores = 1
-    return {"value": toks / elapsed, "unit": "context tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": toks / elapsed, "unit": "context tokens/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{done} of {len(ctx.n_tok)} blocks (all {ctx.cfg.n_kv_heads} KV heads, K and V), "
                       f"numpy fp64 SVD, {elapsed:.1f} s"}
 
@@ -287,7 +319,7 @@ def cpu_baseline_chunk(wl, seconds: float):
         js += new
         n *= 2
     return {"value": len(js) / elapsed, "unit": "query tokens/s", "cores": oracle.threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{len(js)} of {Q} query positions x all {Hq} heads of sequence 0 "
                       f"({sum(b.n_tok for b in wl.blocks[0]) + int(wl.tail_len[0])} context tokens), "
                       f"fp64 reconstruct-then-attend, {elapsed:.1f} s"}
@@ -307,7 +339,7 @@ def cpu_baseline(wl, seconds: float):
         if elapsed >= seconds:
             break
     return {"value": toks / elapsed, "unit": "context tokens/s", "cores": oracle.threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{done} of {wl.batch} sequences ({toks} context tokens, all {wl.cfg.n_q_heads} "
                       f"query heads), fp64 reconstruct-then-attend, {elapsed:.1f} s"}
 
@@ -330,6 +362,7 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-plan", action="store_true", help="natural work-unit order (no schedule)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-probe", action="store_true", help="skip the measured read-ceiling probe")
     ap.add_argument("--dump-steps", action="store_true", help="print each timed step's kernel time")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
@@ -455,7 +488,15 @@ def main(argv=None):
     ms_per_step = (t_end - t_start) * 1e3 / args.steps
     kmean = sum(kern_ms) / len(kern_ms)
     kern_sorted = sorted(kern_ms)
+
+    def pct(q):
+        return kern_sorted[min(len(kern_sorted) - 1, int(q * (len(kern_sorted) - 1) + 0.5))] * 1e3
+
     alg_bytes = wl.factor_bytes() + wl.tail_bytes()
+    es = 2 if cfg.dtype == "bf16" else 4
+    # every byte a step moves: factors + tails + q, partials written and read, out and lse
+    all_bytes = (wl.factor_bytes() + wl.tail_bytes() + B * Q * Hq * d * es + 2 * int(need)
+                 + B * Q * Hq * (d + 1) * 4)
     prof_key = (cfg.name + "_shared", "chunk") if shared else (cfg.name, cfg.path)
     if shared:
         flops = chunk_flops(wl, shared=True)
@@ -516,12 +557,19 @@ def main(argv=None):
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic_from_profiles(*prof_key),
                      "kernel": kname, "kernel_us_mean": kmean * 1e3,
-                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "kernel_us_p10": pct(0.1), "kernel_us_median": pct(0.5), "kernel_us_p90": pct(0.9),
+                     "algorithmic_bytes_per_launch": alg_bytes, "all_bytes_per_step": all_bytes,
                      "kernel_source_sha": kernel_source_sha(prof_key[1])},
         "cpu_baseline": None,
     }
     if is_chunk or shared:
         res["roofline"]["algorithmic_flops_per_launch"] = flops
+    if bound == "hbm" and not args.no_read_probe:
+        ceil = read_ceiling_gbs(lib, torch)
+        res["roofline"]["measured_read_ceiling_gbs"] = ceil
+        res["roofline"]["frac_of_measured_ceiling"] = achieved / ceil
+        print(f"[bench] streaming-read probe: {ceil:.0f} GB/s; kernel at {100 * achieved / ceil:.1f}% of it",
+              file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = (cpu_baseline_chunk(wl, args.cpu_seconds) if is_chunk
                                else cpu_baseline(wl, args.cpu_seconds))

@@ -205,6 +205,16 @@ typedef enum milo_table_rule {
 milo_status milo_attn_validate(const milo_attn_args* args, int32_t path, int32_t n_descriptors,
                                int64_t pool_elems, uint64_t* status, void* hip_stream);
 
+/* Measurement helper: streams `bytes` (a multiple of 16, 16-B aligned) of
+ * device memory once with the decode kernel's load form (16-byte
+ * non-temporal loads, a contiguous slice per wave; n_workgroups of 256
+ * threads, e.g. 4096) and discards the data.  `sink` (device, n_workgroups
+ * uint32) is written only if an improbable checksum occurs.  Timing it with
+ * events gives the read rate this device reaches, a ceiling beside the
+ * published HBM peak. */
+milo_status milo_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t n_workgroups,
+                            void* hip_stream);
+
 /* Static description of a status code. */
 const char* milo_status_str(milo_status status);
 

@@ -14,7 +14,7 @@ MILO_PATH_DECODE, MILO_PATH_CHUNK, MILO_PATH_SHARED = 0, 1, 2
 EXPORTS = ("milo_attn_workspace_bytes", "milo_attn_decode", "milo_attn_chunk", "milo_attn_decode_shared",
            "milo_attn_plan_decode", "milo_status_str", "milo_abi_version",
            "milo_encode_workspace_bytes", "milo_encode_spectrum", "milo_encode_factors", "milo_encode_layout",
-           "milo_rank_workspace_bytes", "milo_rank_allocate", "milo_attn_validate")
+           "milo_rank_workspace_bytes", "milo_rank_allocate", "milo_attn_validate", "milo_read_probe")
 TABLE_RULES = {1: "seq_range", 2: "too_many_blocks", 3: "rank", 4: "tokens", 5: "offset", 6: "pool_bounds",
                7: "tail_len"}
 
@@ -110,6 +110,9 @@ def load() -> ctypes.CDLL:
         lib.milo_attn_validate.argtypes = [ctypes.POINTER(MiloAttnArgs), ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
         lib.milo_attn_validate.restype = ctypes.c_int
+        lib.milo_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32,
+                                        ctypes.c_void_p]
+        lib.milo_read_probe.restype = ctypes.c_int
         lib.milo_attn_plan_decode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_void_p]

@@ -35,6 +35,7 @@ UNITS = [
     ("encode.hip", [], "encode.o"),
     ("rank.hip", [], "rank.o"),
     ("validate.hip", [], "validate.o"),
+    ("probe.hip", [], "probe.o"),
     ("milo_attn.cpp", [], "milo_attn.o"),
     ("milo_encode.cpp", [], "milo_encode.o"),
 ]

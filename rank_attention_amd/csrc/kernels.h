@@ -110,6 +110,8 @@ struct ValidateParams {
 };
 hipError_t launch_validate(const ValidateParams& p, hipStream_t s);
 
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int n_wg, hipStream_t s);
+
 // Work units of the decode kernel: one per (sequence, KV head, block slot),
 // plus one dense-tail unit per (sequence, KV head).
 inline int64_t decode_units(int batch, int n_kv_heads, int max_blocks) {

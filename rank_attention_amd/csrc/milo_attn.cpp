@@ -330,6 +330,16 @@ milo_status milo_attn_validate(const milo_attn_args* a, int32_t path, int32_t n_
   return MILO_OK;
 }
 
+milo_status milo_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t n_workgroups,
+                            void* hip_stream) {
+  if (!buf || !sink || bytes % 16 != 0 || !aligned(buf, 16) || n_workgroups < 1) return MILO_ERR_INVALID;
+  if (bytes == 0) return MILO_OK;
+  if (milo::launch_read_probe(buf, bytes, sink, n_workgroups, reinterpret_cast<hipStream_t>(hip_stream)) !=
+      hipSuccess)
+    return MILO_ERR_DEVICE;
+  return MILO_OK;
+}
+
 milo_status milo_attn_plan_decode(const milo_block* blocks, const int32_t* seq_blocks,
                                   const int32_t* tail_len, int32_t batch, int32_t n_kv_heads,
                                   int32_t max_blocks, int32_t head_dim, int32_t* order_out) {
