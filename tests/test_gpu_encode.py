@@ -199,3 +199,39 @@ def test_encode_then_decode(rank_mode):
         zero = np.zeros((1, h, 0, d))
         ref_o, ref_l = oracle.attend_logical(q64, [bl], zero, zero, np.array([0]), scale)
     compare(out, lse, ref_o, ref_l, sharp_gates=True, name=f"encode_then_decode/{rank_mode}")
+
+
+def test_clamped_ranges_zero_block_and_empty_context():
+    """Token ranges past the dense arrays are clamped on the device (the
+    block is encoded over the tokens that exist); an all-zero block has a
+    zero spectrum after one sweep and zero factors; a context with no tokens
+    at all is all-zero."""
+    import torch
+    from rank_attention_amd.encode import DeviceContext
+    cfg = synth.get_encode_config("enc_small").with_(n_blocks=3, block_tokens=100, seed=47)
+    ctx = synth.make_dense_context(cfg)
+    k = ctx.k.copy()
+    k[:, 100:200] = 0                                   # block 1 of the keys is all zero
+    tok_start = np.array([0, 100, 250], np.int64)      # block 2 claims 100 tokens but only 50 exist
+    dc = DeviceContext(k, ctx.v, tok_start, ctx.n_tok, dtype=cfg.dtype)
+    sigma, sweeps = dc.spectrum()
+    torch.cuda.synchronize()
+    sig = sigma.cpu().numpy().astype(np.float64)
+    assert np.all(sig[1, :, 0] == 0) and np.all(sweeps.cpu().numpy()[1, :, 0] == 1)
+    x2 = bf16_bits_to_f32(ctx.v[1, 250:300]).astype(np.float64)   # the 50 tokens of block 2 that exist
+    ref = oenc.block_spectrum(x2)[0]
+    assert np.all(np.abs(sig[2, 1, 1] - ref) <= 2e-3 * (ref[0] + ref))
+    pool, _, blocks = dc.factors(np.full(3, 5), np.full(3, 5))
+    torch.cuda.synchronize()
+    poolf = pool_f64(pool, "bf16")
+    ut, w = factors_of(poolf, blocks[1], 0, 0, cfg.n_kv_heads, 128)
+    assert np.all(ut == 0)
+    ut, w = factors_of(poolf, blocks[2], 1, 1, cfg.n_kv_heads, 128)
+    assert np.all(ut[:, 50:] == 0)                      # tokens past the dense arrays encode as zeros
+    assert np.linalg.norm(ut[:, :50].T @ w - oenc.approx(x2, 5)) <= 1e-2 * np.linalg.norm(x2)
+    # no tokens at all
+    z = np.zeros((2, 0, 128), np.uint16)
+    dz = DeviceContext(z, z, np.zeros(2, np.int64), np.zeros(2, np.int32), dtype="bf16")
+    s0, w0 = dz.spectrum()
+    torch.cuda.synchronize()
+    assert np.all(s0.cpu().numpy() == 0) and np.all(w0.cpu().numpy() == 1)
