@@ -307,26 +307,27 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
   char* const ldsWp = lds + kOffWp;
   auto tile_buf = [&](int k) { return lds + kOffTile + (k % kNBuf) * kTileBytes; };
 
-  // workgroup -> (sequence, KV head, range slot, query tile).  A shared-
-  // context launch first has ceil(tail_units / 8) * 8 workgroups for the
-  // per-sequence dense tails (sequence i, KV head g, one query token).  Then
-  // ceil(groups / 8) * 8 * n_qtiles workgroups, dispatched round-robin over
-  // the 8 XCDs: slot k of XCD x runs query tile k % n_qtiles of group
-  // (k / n_qtiles) * 8 + x.
+  // workgroup -> (sequence, KV head, range slot, query tile).  The first
+  // ceil(groups / 8) * 8 * n_qtiles workgroups are dispatched round-robin
+  // over the 8 XCDs: slot k of XCD x runs query tile k % n_qtiles of group
+  // (k / n_qtiles) * 8 + x.  A shared-context launch then has tail_units
+  // more, each the dense tail of one (sequence i, KV head g) for its one
+  // query token; placed last, they take the CUs that finish first.
   const int S = p.n_ranges + 1;
-  const int n_lead = (p.tail_units + 7) & ~7;
-  const bool lead = (int)blockIdx.x < n_lead;
+  const int n_groups = p.batch * p.n_kv_heads * S;
+  const int n_block_wgs = (n_groups + 7) / 8 * 8 * p.n_qtiles;
+  const bool extra = (int)blockIdx.x >= n_block_wgs;
   int i, g, slot, qt, qlen;
-  if (lead) {
-    if ((int)blockIdx.x >= p.tail_units) return;
-    i = blockIdx.x / p.n_kv_heads;
-    g = blockIdx.x % p.n_kv_heads;
+  if (extra) {
+    const int u = (int)blockIdx.x - n_block_wgs;
+    if (u >= p.tail_units) return;
+    i = u / p.n_kv_heads;
+    g = u % p.n_kv_heads;
     slot = p.n_ranges;
     qt = 0;
     qlen = 1;
   } else {
-    const int n_groups = p.batch * p.n_kv_heads * S;
-    const int bid = blockIdx.x - n_lead;   // n_lead is a multiple of 8: same XCD
+    const int bid = blockIdx.x;
     const int xcd = bid & 7, k8 = bid >> 3;
     const int group = (k8 / p.n_qtiles) * 8 + xcd;
     if (group >= n_groups) return;
@@ -340,10 +341,14 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
   const int MQ = qlen * G;
   const int m_l = qt * kRowsPerTile + wave * kRowsPerWave + (lane & 15);  // this lane's column
   const bool row_ok = m_l < MQ;
+  // A wave whose 16 rows all lie past the last query row skips the MFMA and
+  // softmax work (it still issues its share of every load and joins every
+  // barrier), leaving its SIMD to the other wave.
+  const bool wave_live = qt * kRowsPerTile + wave * kRowsPerWave < MQ;
   const int j_l = m_l / G, hl = m_l - j_l * G;
 
   const bool tail = slot == p.n_ranges;
-  if (tail && p.no_tail && !lead) return;
+  if (tail && p.no_tail && !extra) return;
   int b0 = 0, blk_lo = 0, blk_hi = 0;
   if (!tail) {
     b0 = p.seq_blocks[i];
@@ -481,6 +486,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
             if (b > blk_lo) issue_w(cb, ldsWp, true, ln, wave);   // W' of this block
             // ---- P^T = W Q^T per 16-rank tile, scaled, split into hi/lo operands
             f32x4_t pt[NK];
+            if (wave_live) {
 #pragma unroll
             for (int rt = 0; rt < NK; ++rt) {
               f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -495,6 +501,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
 #pragma unroll
             for (int j = 0; j < NK2; ++j) split_pair(pt[2 * j], pt[2 * j + 1], ph[j], pl[j]);
             if (REM) split_one(pt[NK - 1], ph16, pl16);
+            }
             if (ntiles == 1 && has_next) {   // W is read: the next block's may land
               wait_barrier<63>();
               issue_w(pb, ldsW, false, ln, wave);
@@ -519,6 +526,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
             wait_barrier<63>();
           }
 
+          if (!wave_live) continue;   // no query rows in this wave
           // ---- S^T = U P^T (hi + lo) for the tile's four 16-token blocks,
           // chunk-outer so that the four chains' reads are in flight
           // together; the chains start from -mref, so scores arrive
@@ -596,6 +604,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
       const int ln = opaque(lane);
 #pragma unroll
       for (int j = 0; j < kMaxR / 32; ++j) {
+        if (!wave_live) break;
         if (2 * j + 1 < nv) {
           u32x4_t zh, zl;
           split_pair(Z[2 * j], Z[2 * j + 1], zh, zl);
@@ -658,6 +667,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
         default: wait_barrier<0>(); break;
       }
       if (t + kTailStages - 1 < nt) issue_tail(t + kTailStages - 1);
+      if (!wave_live) continue;   // no query rows in this wave
       const int ln = opaque(lane);
       char* const sk = stage(t);
       // S^T = K_tail q^T (K = d), scaled, relative to mref, causally masked

@@ -51,10 +51,10 @@ struct ChunkParams {
   // context stack the batch's sequences).
   int32_t part_rows;
   int32_t no_tail;           // skip the tail slots of the range groups
-  // Shared context: the launch starts with one workgroup per (sequence,
-  // KV head) of the shared batch, tail_units = batch * n_kv_heads of them,
-  // each the dense tail of that sequence's own G query rows (q_len 1); 0
-  // otherwise.
+  // Shared context: after the block workgroups the launch has one
+  // workgroup per (sequence, KV head) of the shared batch, tail_units =
+  // batch * n_kv_heads of them, each the dense tail of that sequence's own
+  // G query rows (q_len 1); 0 otherwise.
   int32_t tail_units;
   float scale_log2;
 };

@@ -253,7 +253,7 @@ milo_status milo_attn_decode_shared(const milo_attn_args* a, void* hip_stream) {
   // query rows are the batch's queries (q is [batch][1][n_q_heads][d], the
   // same memory as [1][batch][n_q_heads][d]) over sequence 0's block list;
   // its partials land in every sequence's own unit slots (part_rows =
-  // group).  Tails: batch * n_kv_heads leading workgroups, each sequence's
+  // group).  Tails: batch * n_kv_heads trailing workgroups, each sequence's
   // own tail for its G rows, written to slot n_ranges of its units.
   milo::ChunkParams p{};
   p.q = a->q;
