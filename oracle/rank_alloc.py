@@ -66,18 +66,22 @@ def allocate(sigma: np.ndarray, budget: int, r_min: int, unit: int = 1) -> np.nd
     extra = budget - nb * r_min
     if extra < 0 or extra % unit or extra // unit > nb * per_block:
         raise ValueError("budget must be n_blocks*r_min plus a whole number of units that fit")
-    dist = [block_distribution(sigma[b]) for b in range(nb)]
-    r = [r_min] * nb
+    # gains[b][j]: the gain of block b's unit raising rank r_min + j*unit
+    gains = []
+    for b in range(nb):
+        H, p = block_distribution(sigma[b])
+        gains.append([unit_gain(H, p, r_min + j * unit, unit) for j in range(per_block)])
+    taken = [0] * nb
     for _ in range(extra // unit):
         best, best_g = -1, -1.0
         for b in range(nb):
-            if r[b] + unit > d:
+            if taken[b] == per_block:
                 continue
-            g = unit_gain(dist[b][0], dist[b][1], r[b], unit)
+            g = gains[b][taken[b]]
             if g > best_g:
                 best, best_g = b, g
-        r[best] += unit
-    return np.array(r, dtype=np.int64)
+        taken[best] += 1
+    return np.array([r_min + unit * t for t in taken], dtype=np.int64)
 
 
 def objective(sigma: np.ndarray, ranks, r_min: int, unit: int = 1) -> float:
