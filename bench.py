@@ -18,13 +18,18 @@ FLOP/byte ridge).
 Kernel time comes from HIP events recorded on the launch stream around the
 attention kernel alone; the fp64 CPU oracle is timed on a bounded sample.
 
+8-bit token factors (--q8, on a decode workload): the bf16 pool is quantised
+once (milo_quantize_factors, outside the timed region) and the decode path
+reads the 8-bit pool; algorithmic bytes are the codes, the bf16 W/W' and the
+per-row (scale, bias) pairs plus the tails.
+
 Encode (--encode, workload enc_qwen7b_64k): one step runs the encode
 workflow over the dense keys and values of one 64k-token context (spectra,
 entropy-driven ranks at a 50% budget, host layout, factors); context
 tokens/s, and the spectrum kernel's algorithmic fp32 rate against the 157.3
 TFLOP/s vector peak.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen7b_64k] [--shared]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen7b_64k] [--shared | --q8]
     python bench.py --encode [--workload enc_qwen7b_64k]
 """
 from __future__ import annotations
@@ -43,6 +48,7 @@ sys.path.insert(0, ROOT)
 ENCODE_METRIC = "low-rank-KV encode: context tokens/s factorised (dense K/V -> per-block truncated SVD factors)"
 FP32_VECTOR_PEAK_TFLOPS = 157.3
 METRIC = "low-rank-KV decode attn: context tokens/s and % of HBM peak (7B, 64k)"
+Q8_METRIC = "low-rank-KV decode attn, 8-bit token factors: context tokens/s and % of HBM peak (7B, 64k)"
 SHARED_METRIC = "low-rank-KV shared-context decode attn: context tokens/s (7B, 64k context shared by the batch)"
 CHUNK_METRIC = "low-rank-KV chunked-query attn: query tokens/s and % of bf16 MFMA peak (32B, Q=256)"
 HBM_PEAK_GBS = 8000.0
@@ -325,13 +331,18 @@ def cpu_baseline_chunk(wl, seconds: float):
                       f"fp64 reconstruct-then-attend, {elapsed:.1f} s"}
 
 
-def cpu_baseline(wl, seconds: float):
-    """fp64 oracle on whole sequences of the same workload until `seconds` pass."""
+def cpu_baseline(wl, seconds: float, q8: bool = False):
+    """fp64 oracle on whole sequences of the same workload until `seconds` pass
+    (q8: the oracle's 8-bit quantisation of the token factors, then attention
+    over the dequantized factors, both timed)."""
     import oracle
+    from oracle import quant
     toks, elapsed, done = 0, 0.0, 0
     for i in range(wl.batch):
         q, blocks, kt, vt, tl = oracle.logical_from_workload(wl, [i])
         t0 = time.perf_counter()
+        if q8:
+            blocks = quant.quantize_logical_blocks(blocks)
         oracle.attend_logical(q, blocks, kt, vt, tl, wl.scale)
         elapsed += time.perf_counter() - t0
         toks += sum(b.n_tok for b in wl.blocks[i]) + int(wl.tail_len[i])
@@ -341,7 +352,8 @@ def cpu_baseline(wl, seconds: float):
     return {"value": toks / elapsed, "unit": "context tokens/s", "cores": oracle.threads(),
             "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{done} of {wl.batch} sequences ({toks} context tokens, all {wl.cfg.n_q_heads} "
-                      f"query heads), fp64 reconstruct-then-attend, {elapsed:.1f} s"}
+                      f"query heads), {'fp32 8-bit quantisation, ' if q8 else ''}fp64 "
+                      f"reconstruct-then-attend, {elapsed:.1f} s"}
 
 
 def main(argv=None):
@@ -357,6 +369,8 @@ def main(argv=None):
                     help="encode step: factorise the dense K/V of one context (enc_* workloads)")
     ap.add_argument("--shared", action="store_true",
                     help="shared-context decode: the batch attends to sequence 0's context")
+    ap.add_argument("--q8", action="store_true",
+                    help="decode over 8-bit token factors (the bf16 pool quantised once before timing)")
     ap.add_argument("--copies", type=int, default=2,
                     help="pool copies read in rotation so no step finds the last one's bytes in cache")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -404,8 +418,12 @@ def main(argv=None):
         cfg = cfg.with_(n_q_heads=args.q_heads, desc=f"{cfg.desc}; {args.q_heads} query heads")
     is_chunk = cfg.path == "chunk"
     shared = args.shared
+    q8 = args.q8
     if shared and is_chunk:
         print("--shared needs a decode workload", file=sys.stderr)
+        return 2
+    if q8 and (is_chunk or shared or cfg.dtype != "bf16"):
+        print("--q8 needs a bf16 decode workload (and not --shared)", file=sys.stderr)
         return 2
     path_code = (_lib.MILO_PATH_CHUNK if is_chunk else
                  _lib.MILO_PATH_SHARED if shared else _lib.MILO_PATH_DECODE)
@@ -419,6 +437,9 @@ def main(argv=None):
         wl = synth.make_workload(cfg, variant=args.variant)
     pc = ra.pack(wl)
     dc = ra.DeviceCache(pc, device="cuda:0", scale=wl.scale)
+    if q8:
+        dc = dc.quantized()
+        torch.cuda.synchronize()
     copies = args.copies
     if shared:
         # the shared factors and the tails are small: rotate enough copies of
@@ -492,12 +513,18 @@ def main(argv=None):
     def pct(q):
         return kern_sorted[min(len(kern_sorted) - 1, int(q * (len(kern_sorted) - 1) + 0.5))] * 1e3
 
-    alg_bytes = wl.factor_bytes() + wl.tail_bytes()
+    factor_bytes = wl.factor_bytes()
+    if q8:
+        # per KV head and row: n_tok codes, d bf16 of W or W', one fp32 (scale, bias) pair
+        factor_bytes = sum(cfg.n_kv_heads * (b.rank_k + b.rank_v) * (b.n_tok + 2 * d + 8)
+                           for s_ in wl.blocks for b in s_)
+    alg_bytes = factor_bytes + wl.tail_bytes()
     es = 2 if cfg.dtype == "bf16" else 4
     # every byte a step moves: factors + tails + q, partials written and read, out and lse
-    all_bytes = (wl.factor_bytes() + wl.tail_bytes() + B * Q * Hq * d * es + 2 * int(need)
+    all_bytes = (factor_bytes + wl.tail_bytes() + B * Q * Hq * d * es + 2 * int(need)
                  + B * Q * Hq * (d + 1) * 4)
-    prof_key = (cfg.name + "_shared", "chunk") if shared else (cfg.name, cfg.path)
+    prof_key = ((cfg.name + "_shared", "chunk") if shared else (cfg.name + "_q8", "decode") if q8
+                else (cfg.name, cfg.path))
     if shared:
         flops = chunk_flops(wl, shared=True)
         alg_bytes = shared_factor_bytes + wl.tail_bytes()
@@ -529,7 +556,8 @@ def main(argv=None):
     else:
         achieved = alg_bytes / (kmean * 1e-3) / 1e9
         peak, unit, bound = HBM_PEAK_GBS, "GB/s", "hbm"
-        value, vunit, metric = wl.context_tokens() / (ms_per_step * 1e-3), "context tokens/s", METRIC
+        value, vunit, metric = (wl.context_tokens() / (ms_per_step * 1e-3), "context tokens/s",
+                                Q8_METRIC if q8 else METRIC)
         kname = "milo_decode_kernel"
         print(f"[bench] attention kernel: mean {kmean * 1e3:.1f} us, median "
               f"{kern_sorted[len(kern_sorted) // 2] * 1e3:.1f} us, min {kern_sorted[0] * 1e3:.1f} us; "
@@ -547,13 +575,14 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype,
+        "dtype": "bf16+u8" if q8 else cfg.dtype,
         "data": "synthetic",
         "config": {"workload": cfg.name, "desc": cfg.desc, "batch": cfg.batch, "q_len": cfg.q_len,
                    "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
                    "blocks_per_seq": cfg.n_blocks, "block_tokens": cfg.block_tokens,
                    "tail_len": cfg.tail_len, "context_tokens_per_step": wl.context_tokens(),
-                   "variant": args.variant, "pool_copies": len(pools), "shared_context": shared},
+                   "variant": args.variant, "pool_copies": len(pools), "shared_context": shared,
+                   "factor_storage": "u8 token factors, bf16 W/W'" if q8 else cfg.dtype},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic_from_profiles(*prof_key),
                      "kernel": kname, "kernel_us_mean": kmean * 1e3,
@@ -572,7 +601,7 @@ def main(argv=None):
               file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = (cpu_baseline_chunk(wl, args.cpu_seconds) if is_chunk
-                               else cpu_baseline(wl, args.cpu_seconds))
+                               else cpu_baseline(wl, args.cpu_seconds, q8=q8))
     print(json.dumps(res), flush=True)
     return 0
 

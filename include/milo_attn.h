@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MILO_ABI_VERSION 2
+#define MILO_ABI_VERSION 3
 
 typedef enum milo_status {
   MILO_OK = 0,
@@ -64,7 +64,8 @@ typedef enum milo_status {
 
 typedef enum milo_dtype {
   MILO_F32 = 0,              /* IEEE fp32 storage                                        */
-  MILO_BF16 = 1              /* bfloat16 storage                                         */
+  MILO_BF16 = 1,             /* bfloat16 storage                                         */
+  MILO_BF16_Q8 = 2           /* bfloat16 q, tail, W, W'; 8-bit token factors (decode)    */
 } milo_dtype;
 
 typedef enum milo_path {
@@ -84,17 +85,39 @@ typedef enum milo_path {
  * Elements n_tok..ld_tok-1 of each U^T / U'^T row are padding and are never
  * used (they may hold anything, NaN included).
  */
+/*
+ * MILO_BF16_Q8 pool (decode path only; built by milo_quantize_factors in
+ * milo_encode.h).  MILO's cache combines with asymmetric INT8 quantisation
+ * (summary page, "5.3 Performance Analysis"); here the token factors carry
+ * it.  Every row k of U^T and of U'^T (one rank component over the block's
+ * tokens) holds uint8 codes c with an fp32 pair (a_k, b_k):
+ *     element = a_k * c + b_k.
+ * Offsets and strides count BYTES: off and ld_tok are multiples of 16, and
+ * KV head g starts at byte off + g * H with
+ *     H = (rank_k + rank_v) * (ld_tok + 2 * head_dim) + pad16(8 * (rank_k + rank_v)),
+ * pad16(x) = x rounded up to a multiple of 16.  Per head, back to back:
+ *     U^T  codes  [rank_k][ld_tok]      uint8
+ *     W           [rank_k][head_dim]    bf16
+ *     U'^T codes  [rank_v][ld_tok]      uint8
+ *     W'          [rank_v][head_dim]    bf16
+ *     (a_k, b_k)  [rank_k + rank_v][2]  fp32, the keys' rows first, then
+ *                 padding to the next multiple of 16 bytes.
+ * Codes n_tok..ld_tok-1 of each row are padding (any value).
+ */
 typedef struct milo_block {
-  int64_t off;      /* element offset of KV head 0's U^T; multiple of 8           */
+  int64_t off;      /* element offset of KV head 0's U^T; multiple of 8 (Q8: bytes,
+                       multiple of 16)                                             */
   int32_t n_tok;    /* T_b >= 0                                                    */
-  int32_t ld_tok;   /* row stride of U^T and U'^T in elements; >= n_tok, mult. of 8 */
+  int32_t ld_tok;   /* row stride of U^T and U'^T in elements; >= n_tok, mult. of 8
+                       (Q8: multiple of 16)                                        */
   int32_t rank_k;   /* r_b  in [0, head_dim]                                       */
   int32_t rank_v;   /* r'_b in [0, head_dim]                                       */
 } milo_block;
 
 typedef struct milo_attn_args {
   int32_t struct_size;         /* sizeof(milo_attn_args)                                   */
-  int32_t dtype;               /* milo_dtype of q, pool, k_tail, v_tail                    */
+  int32_t dtype;               /* milo_dtype of q, pool, k_tail, v_tail (MILO_BF16_Q8:
+                                  decode only, pool layout above)                          */
   int32_t batch;               /* sequences, >= 0                                           */
   int32_t q_len;               /* query tokens per sequence: 1 (decode) or Q >= 1 (chunk)   */
   int32_t n_q_heads;           /* >= 1, multiple of n_kv_heads                              */
@@ -189,7 +212,8 @@ milo_status milo_attn_plan_decode(const milo_block* blocks, const int32_t* seq_b
  * With path MILO_PATH_SHARED only sequence 0's list is checked (the other
  * lists are not read by that path).  pool_elems is the pool size in
  * elements.  Host-checkable faults return a status as for the other entry
- * points (status must be 8-byte aligned).
+ * points (status must be 8-byte aligned).  With MILO_BF16_Q8, pool_elems
+ * counts bytes, and rules 4 and 5 ask for multiples of 16 instead of 8.
  */
 typedef enum milo_table_rule {
   MILO_TABLE_SEQ_RANGE = 1,        /* seq_blocks[i] < 0, decreasing, or past n_descriptors        */

@@ -129,6 +129,45 @@ size_t milo_rank_workspace_bytes(const milo_rank_args* args);
 /* Ranks of every block for keys and values (two kernels on the stream). */
 milo_status milo_rank_allocate(const milo_rank_args* args, void* hip_stream);
 
+/*
+ * 8-bit token factors ("5.3 Performance Analysis" of the summary page:
+ * the low-rank cache combines with asymmetric INT8 quantisation).  The
+ * pages fix neither the grouping nor the rounding; the reading: every row
+ * of U^T and U'^T (one rank component over the block's tokens, so each
+ * group holds one scale of the decaying spectrum) is quantised
+ * asymmetrically over its n_tok elements x_t, in fp32:
+ *     lo = min x,  a = (hi - lo) / 255 (hi = max x),  b = lo,
+ *     c_t = min(max(round_half_even((x_t - lo) / a), 0), 255)   (0 when a = 0),
+ * every operation correctly rounded; a row with n_tok = 0 gets a = b = 0.
+ * W and W' are copied unchanged.  The result is the MILO_BF16_Q8 pool of
+ * milo_attn.h, which milo_attn_decode reads.
+ */
+typedef struct milo_quant_args {
+  int32_t struct_size;         /* sizeof(milo_quant_args)                                   */
+  int32_t n_blocks;            /* >= 0                                                      */
+  int32_t n_kv_heads;          /* >= 1                                                      */
+  int32_t head_dim;            /* 64 or 128                                                 */
+  const void* src_pool;        /* MILO_BF16 pool (milo_attn.h layout), 16-B aligned         */
+  const milo_block* src_blocks;/* [n_blocks] its descriptors                                */
+  void* dst_pool;              /* MILO_BF16_Q8 pool, 16-B aligned, milo_quant_layout bytes  */
+  const milo_block* dst_blocks;/* [n_blocks] from milo_quant_layout on the same source
+                                  descriptors (same n_tok and ranks)                        */
+} milo_quant_args;
+
+/* Host-side layout of the MILO_BF16_Q8 pool for the blocks src_blocks
+ * (HOST array): the same n_tok and ranks, ld_tok = n_tok rounded up to 16,
+ * blocks back to back from byte 0 in the given order.  blocks_out (host)
+ * receives n_blocks descriptors and *pool_bytes the pool size.
+ * MILO_ERR_INVALID on null pointers, negative sizes or ranks outside
+ * [0, head_dim]. */
+milo_status milo_quant_layout(const milo_block* src_blocks, int32_t n_blocks, int32_t n_kv_heads,
+                              int32_t head_dim, milo_block* blocks_out, int64_t* pool_bytes);
+
+/* Quantise every block of the source pool into the destination pool (one
+ * kernel on the stream; codes past n_tok up to ld_tok are written as 0).
+ * The source tables are the caller's contract as in milo_attn.h. */
+milo_status milo_quantize_factors(const milo_quant_args* args, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

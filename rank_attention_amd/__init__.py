@@ -13,7 +13,7 @@ from typing import Optional, Tuple
 import numpy as np
 
 from . import _lib
-from ._lib import (MILO_BF16, MILO_F32, MILO_PATH_CHUNK, MILO_PATH_DECODE, MILO_PATH_SHARED, MiloAttnArgs,
+from ._lib import (MILO_BF16, MILO_BF16_Q8, MILO_F32, MILO_PATH_CHUNK, MILO_PATH_DECODE, MILO_PATH_SHARED, MiloAttnArgs,
                    MILO_OK, MILO_ERR_DEVICE)
 from .pack import BLOCK_DTYPE, PackedCache, pack  # noqa: F401
 
@@ -46,6 +46,11 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported storage dtype {t.dtype}")
 
 
+def _uint8():
+    import torch
+    return torch.uint8
+
+
 def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
@@ -60,6 +65,8 @@ def make_args(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_kv_hea
     a = MiloAttnArgs()
     a.struct_size = ctypes.sizeof(MiloAttnArgs)
     a.dtype = _dtype_code(q)
+    if pool is not None and a.dtype == MILO_BF16 and pool.dtype == _uint8():
+        a.dtype = MILO_BF16_Q8   # 8-bit token factors (milo_quantize_factors)
     a.batch, a.q_len, a.n_q_heads, a.n_kv_heads, a.head_dim = B, Q, Hq, int(n_kv_heads), d
     a.scale = float(scale)
     a.q, a.pool, a.blocks, a.seq_blocks = _ptr(q), _ptr(pool), _ptr(blocks), _ptr(seq_blocks)
@@ -204,3 +211,17 @@ class DeviceCache:
     def decode_shared(self, **kw):
         kw.setdefault("scale", self.scale)
         return decode_shared(*self.tensors(), n_kv_heads=self.n_kv_heads, max_blocks=self.max_blocks, **kw)
+
+    def quantized(self, stream=None) -> "DeviceCache":
+        """The same cache with 8-bit token factors (milo_quantize_factors on
+        this cache's bf16 pool): decode reads it as MILO_BF16_Q8 storage.
+        q, the tails and the decode schedule are shared with this cache."""
+        import copy
+        import torch
+        from .encode import quantize
+        if self.packed.dtype != "bf16" or self.pool.dtype == torch.uint8:
+            raise ValueError("8-bit factors are made from bf16 storage")
+        qc = copy.copy(self)
+        qc.pool, qc.blocks, qc.blocks_host = quantize(self.pool, self.blocks, self.packed.blocks,
+                                                      self.n_kv_heads, self.packed.head_dim, stream=stream)
+        return qc

@@ -9,12 +9,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmilo_attn.so")
 
 MILO_OK, MILO_ERR_INVALID, MILO_ERR_UNSUPPORTED, MILO_ERR_WORKSPACE, MILO_ERR_DEVICE = range(5)
-MILO_F32, MILO_BF16 = 0, 1
+MILO_F32, MILO_BF16, MILO_BF16_Q8 = 0, 1, 2
 MILO_PATH_DECODE, MILO_PATH_CHUNK, MILO_PATH_SHARED = 0, 1, 2
 EXPORTS = ("milo_attn_workspace_bytes", "milo_attn_decode", "milo_attn_chunk", "milo_attn_decode_shared",
            "milo_attn_plan_decode", "milo_status_str", "milo_abi_version",
            "milo_encode_workspace_bytes", "milo_encode_spectrum", "milo_encode_factors", "milo_encode_layout",
-           "milo_rank_workspace_bytes", "milo_rank_allocate", "milo_attn_validate", "milo_read_probe")
+           "milo_rank_workspace_bytes", "milo_rank_allocate", "milo_attn_validate", "milo_read_probe",
+           "milo_quant_layout", "milo_quantize_factors")
 TABLE_RULES = {1: "seq_range", 2: "too_many_blocks", 3: "rank", 4: "tokens", 5: "offset", 6: "pool_bounds",
                7: "tail_len"}
 
@@ -90,6 +91,19 @@ class MiloRankArgs(ctypes.Structure):
     ]
 
 
+class MiloQuantArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_int32),
+        ("n_blocks", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("src_pool", ctypes.c_void_p),
+        ("src_blocks", ctypes.c_void_p),
+        ("dst_pool", ctypes.c_void_p),
+        ("dst_blocks", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -132,6 +146,11 @@ def load() -> ctypes.CDLL:
         lib.milo_rank_workspace_bytes.restype = ctypes.c_size_t
         lib.milo_rank_allocate.argtypes = [ctypes.POINTER(MiloRankArgs), ctypes.c_void_p]
         lib.milo_rank_allocate.restype = ctypes.c_int
+        lib.milo_quant_layout.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]
+        lib.milo_quant_layout.restype = ctypes.c_int
+        lib.milo_quantize_factors.argtypes = [ctypes.POINTER(MiloQuantArgs), ctypes.c_void_p]
+        lib.milo_quantize_factors.restype = ctypes.c_int
         lib.milo_abi_version.argtypes = []
         lib.milo_abi_version.restype = ctypes.c_int32
         _lib = lib

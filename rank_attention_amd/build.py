@@ -30,12 +30,15 @@ UNITS = [
     ("decode.hip", ["-DMILO_INST_DT=0", "-DMILO_INST_D=128"], "decode_f32_128.o"),
     ("decode.hip", ["-DMILO_INST_DT=1", "-DMILO_INST_D=64"], "decode_bf16_64.o"),
     ("decode.hip", ["-DMILO_INST_DT=1", "-DMILO_INST_D=128"], "decode_bf16_128.o"),
+    ("decode.hip", ["-DMILO_INST_DT=2", "-DMILO_INST_D=64"], "decode_q8_64.o"),
+    ("decode.hip", ["-DMILO_INST_DT=2", "-DMILO_INST_D=128"], "decode_q8_128.o"),
     ("merge.hip", [], "merge.o"),
     ("chunk.hip", [], "chunk.o"),
     ("encode.hip", [], "encode.o"),
     ("rank.hip", [], "rank.o"),
     ("validate.hip", [], "validate.o"),
     ("probe.hip", [], "probe.o"),
+    ("quant.hip", [], "quant.o"),
     ("milo_attn.cpp", [], "milo_attn.o"),
     ("milo_encode.cpp", [], "milo_encode.o"),
 ]

@@ -341,6 +341,251 @@ __device__ __forceinline__ void block_unit_bf16(const DecodeParams& p, int i, in
 }
 
 // ---------------------------------------------------------------------------
+// 8-bit token factors (MILO_BF16_Q8): row k of U^T / U'^T holds codes c with
+// x = a_k c + b_k.  Folded into the absorbed order:
+//   s_t = sum_k p_k x_kt  = sum_k (p_k a_k) c_kt + C,   C = sum_k p_k b_k
+//   z_k = sum_t e_t x'_kt = a'_k sum_t e_t c'_kt + b'_k E,   E = sum_t e_t
+// The scores keep the fp32 path of bf16 storage (a code converts to fp32 in
+// one instruction).  For the values e is rounded to fp16 pairs, and a byte
+// permute with the constant 0x64 turns four codes into two fp16 pairs of
+// 1024 + c (exact: fp16 spacing is 1 on [1024, 2048)), so one dot2 per
+// token pair and head accumulates sum_t e_t (1024 + c); the 1024 E it adds
+// is taken off with E summed from the same fp16 e, which also feeds l.
+// A lane owns 16 consecutive tokens (one 16-byte load per row) of a
+// 1024-token tile.  Codes can not be NaN, so padding needs no mask: tokens
+// past the block end have e = 0.
+// ---------------------------------------------------------------------------
+
+constexpr int kQ8RowsPerStep = 8;   // U^T rows per prefetch step of the score loop
+constexpr uint32_t kF16Ones = 0x3C003C00u;   // fp16 pair (1, 1)
+constexpr uint32_t kF16Magic = 0x64646464u;  // high byte of fp16 1024 + c, c < 256
+
+// fp16 pairs (1024 + c0, 1024 + c1) and (1024 + c2, 1024 + c3) of four codes
+__device__ __forceinline__ uint32_t q8_pair_lo(uint32_t c) { return __builtin_amdgcn_perm(kF16Magic, c, 0x04010400u); }
+__device__ __forceinline__ uint32_t q8_pair_hi(uint32_t c) { return __builtin_amdgcn_perm(kF16Magic, c, 0x04030402u); }
+
+__device__ __forceinline__ void q8_load_rows(const uint8_t* Uc, int ld, int k0, int r, int tq,
+                                             u32x4_t (&A)[kQ8RowsPerStep]) {
+#pragma unroll
+  for (int j = 0; j < kQ8RowsPerStep; ++j) A[j] = ld16_stream(Uc + (size_t)min(k0 + j, r - 1) * ld + tq);
+}
+
+template <int G>
+__device__ __forceinline__ void q8_score_rows(const u32x4_t (&A)[kQ8RowsPerStep], int k0, int r,
+                                              const float* pf, float (&s)[16][G]) {
+#pragma unroll
+  for (int j = 0; j < kQ8RowsPerStep; ++j) {
+    if (k0 + j < r) {
+      const f32x4_t pq0 = *reinterpret_cast<const f32x4_t*>(pf + (k0 + j) * 8);
+      const f32x4_t pq1 = *reinterpret_cast<const f32x4_t*>(pf + (k0 + j) * 8 + 4);
+      const float pp[8] = {pq0[0], pq0[1], pq0[2], pq0[3], pq1[0], pq1[1], pq1[2], pq1[3]};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x = A[j][w];
+        const float c[4] = {(float)(x & 0xffu), (float)((x >> 8) & 0xffu), (float)((x >> 16) & 0xffu),
+                            (float)(x >> 24)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int h = 0; h < G; ++h) s[4 * w + e][h] = fmaf(c[e], pp[h], s[4 * w + e][h]);
+      }
+    }
+  }
+}
+
+template <int D, int G>
+__device__ __forceinline__ void q8_tiles(const uint8_t* Uc, const uint8_t* Upc, const uint16_t* Wp,
+                                         const float* sbv, int ld, int T, int r, int rv, const float* pf,
+                                         const float (&C)[G], float (&m_run)[G], float (&l_run)[G],
+                                         float (&o)[G][D / 64], float* zs, int lane) {
+  using S = Shape<D, G>;
+  constexpr int R = S::R, JPL = S::JPL;
+  const int hl = lane % G;   // head of the lane's z slot
+  for (int t0 = 0; t0 < T; t0 += 1024) {
+    const int tc = t0 + lane * 16;
+    // a lane whose chunk lies past the block end reads the tile's first
+    // chunk instead (always in bounds); its tokens are masked below
+    const int tq = tc < T ? tc : t0;
+
+    float s[16][G];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[e][h] = C[h];
+    if (r > 0) {
+      u32x4_t A0[kQ8RowsPerStep], A1[kQ8RowsPerStep];
+      q8_load_rows(Uc, ld, 0, r, tq, A0);
+      for (int k0 = 0; k0 < r; k0 += 2 * kQ8RowsPerStep) {
+        if (k0 + kQ8RowsPerStep < r) q8_load_rows(Uc, ld, k0 + kQ8RowsPerStep, r, tq, A1);
+        q8_score_rows<G>(A0, k0, r, pf, s);
+        if (k0 + 2 * kQ8RowsPerStep < r) q8_load_rows(Uc, ld, k0 + 2 * kQ8RowsPerStep, r, tq, A0);
+        if (k0 + kQ8RowsPerStep < r) q8_score_rows<G>(A1, k0 + kQ8RowsPerStep, r, pf, s);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      if (tc + e >= T) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) s[e][h] = kNegInf;
+      }
+    }
+
+    // online softmax; e as fp16 pairs, E (the sum of those fp16 values) per head
+    uint32_t e2[8][G];
+    float alpha[G], E[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mx = s[0][h];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e][h]);
+      mx = wave_max(mx);
+      const float mn = fmaxf(m_run[h], mx);
+      alpha[h] = fast_exp2(m_run[h] - mn);
+      float sum = 0.f;
+#pragma unroll
+      for (int pr = 0; pr < 8; ++pr) {
+        e2[pr][h] = pack_f16(fast_exp2(s[2 * pr][h] - mn), fast_exp2(s[2 * pr + 1][h] - mn));
+        sum = dot2h(e2[pr][h], kF16Ones, sum);
+      }
+      E[h] = wave_sum(sum);
+      l_run[h] = l_run[h] * alpha[h] + E[h];
+      m_run[h] = mn;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int jj = 0; jj < JPL; ++jj) o[h][jj] *= alpha[h];
+    float El = E[0];
+#pragma unroll
+    for (int h = 1; h < G; ++h) El = (hl == h) ? E[h] : El;
+
+    // ---- z per group of R rows of U'^T, then o~ += z W' for the group
+#pragma unroll 1
+    for (int gi = 0; gi * R < rv; ++gi) {
+      u32x4_t U[R];
+      uint32_t wr[R];
+#pragma unroll
+      for (int rho = 0; rho < R; ++rho)
+        U[rho] = ld16_stream(Upc + (size_t)min(gi * R + rho, rv - 1) * ld + tq);
+#pragma unroll
+      for (int rho = 0; rho < R; ++rho) {
+        const uint16_t* wrow = Wp + (size_t)min(gi * R + rho, rv - 1) * D;
+        wr[rho] = (JPL == 2) ? *reinterpret_cast<const uint32_t*>(wrow + 2 * lane)
+                             : (uint32_t)wrow[lane] << 16;
+      }
+      // (a', b') of the row of the lane's z slot (lanes >= R*G: unused)
+      const f32x2_t ab = *reinterpret_cast<const f32x2_t*>(sbv + 2 * min(gi * R + min(lane / G, R - 1), rv - 1));
+      float acc[64];
+#pragma unroll
+      for (int x = 0; x < 64; ++x) acc[x] = 0.f;
+#pragma unroll
+      for (int rho = 0; rho < R; ++rho) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t lo = q8_pair_lo(U[rho][w]), hi = q8_pair_hi(U[rho][w]);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            acc[rho * G + h] = dot2h(lo, e2[2 * w][h], acc[rho * G + h]);
+            acc[rho * G + h] = dot2h(hi, e2[2 * w + 1][h], acc[rho * G + h]);
+          }
+        }
+      }
+      // lane l ends with sum_t e_t (1024 + c) of slot l = (row rho, head h)
+      const float zg = reduce_transpose64(acc, lane);
+      if (lane < R * G) zs[(lane / G) * 8 + hl] = fmaf(ab[0], zg - 1024.f * El, ab[1] * El);
+      wave_lds_fence();
+#pragma unroll
+      for (int rho = 0; rho < R; ++rho) {
+        if (gi * R + rho < rv) {
+          const f32x4_t z0 = *reinterpret_cast<const f32x4_t*>(zs + rho * 8);
+          const f32x4_t z1 = *reinterpret_cast<const f32x4_t*>(zs + rho * 8 + 4);
+          const float zz[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
+          const float wv[2] = {bf_lo(wr[rho]), bf_hi(wr[rho])};
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int jj = 0; jj < JPL; ++jj) o[h][jj] = fmaf(zz[h], wv[JPL == 2 ? jj : 1], o[h][jj]);
+        }
+      }
+      wave_lds_fence();
+    }
+  }
+}
+
+template <int D, int G>
+__device__ __forceinline__ void block_unit_q8(const DecodeParams& p, int i, int g, int unit,
+                                              const milo_block& blk, uint32_t* lds) {
+  constexpr int JPL = D / 64;
+  const int lane = threadIdx.x;
+  const int T = max(blk.n_tok, 0);
+  const int ld = blk.ld_tok;
+  const int r = min(max(blk.rank_k, 0), D), rv = min(max(blk.rank_v, 0), D);
+  const int64_t head = (int64_t)(r + rv) * (ld + 2 * D) + ((8 * (r + rv) + 15) & ~15);
+  const uint8_t* Uc = reinterpret_cast<const uint8_t*>(p.pool) + blk.off + g * head;
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(Uc + (size_t)r * ld);
+  const uint8_t* Upc = Uc + (size_t)r * ld + (size_t)r * 2 * D;
+  const uint16_t* Wp = reinterpret_cast<const uint16_t*>(Upc + (size_t)rv * ld);
+  const float* sbk = reinterpret_cast<const float*>(Uc + (int64_t)(r + rv) * (ld + 2 * D));
+  const float* sbv = sbk + 2 * r;
+  const uint16_t* qh = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)i * p.n_q_heads + g * G) * D;
+
+  float* pf = reinterpret_cast<float*>(lds);
+  float C[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) C[h] = 0.f;
+  if (r > 0) {
+    // (a_k, b_k) of the lane's rows, in flight with the projection's loads
+    const f32x2_t ab0 = *reinterpret_cast<const f32x2_t*>(sbk + 2 * min(lane, r - 1));
+    f32x2_t ab1 = {0.f, 0.f};
+    if (D > 64) ab1 = *reinterpret_cast<const f32x2_t*>(sbk + 2 * min(lane + 64, r - 1));
+    bf16_project_q<D, G>(W, qh, r, p.scale_log2, pf, reinterpret_cast<uint16_t*>(lds + 2048), lane);
+    wave_lds_fence();
+    // p_k a_k replaces p_k; C = sum_k p_k b_k
+    const bool has0 = lane < r, has1 = D > 64 && lane + 64 < r;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float c = 0.f;
+      if (has0) {
+        const float x = pf[lane * 8 + h];
+        c = x * ab0[1];
+        pf[lane * 8 + h] = x * ab0[0];
+      }
+      if (has1) {
+        const float x = pf[(lane + 64) * 8 + h];
+        c = fmaf(x, ab1[1], c);
+        pf[(lane + 64) * 8 + h] = x * ab1[0];
+      }
+      C[h] = wave_sum(c);
+    }
+  }
+  float* zs = reinterpret_cast<float*>(lds + 1024);
+
+  float m_run[G], l_run[G], o[G][JPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m_run[h] = kNegInf;
+    l_run[h] = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < JPL; ++jj) o[h][jj] = 0.f;
+  }
+  wave_lds_fence();
+
+  q8_tiles<D, G>(Uc, Upc, Wp, sbv, ld, T, r, rv, pf, C, m_run, l_run, o, zs, lane);
+
+  float* po = p.part.o + (size_t)unit * G * D;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int jj = 0; jj < JPL; ++jj) po[h * D + lane * JPL + jj] = o[h][jj];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    if (lane == h) {
+      p.part.ml[((size_t)unit * G + h) * 2 + 0] = m_run[h];
+      p.part.ml[((size_t)unit * G + h) * 2 + 1] = l_run[h];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 storage (small workloads; same structure, plain FMA)
 // ---------------------------------------------------------------------------
 template <int D, int G, bool RAGGED>
@@ -552,7 +797,7 @@ __device__ __forceinline__ void tail_unit(const DecodeParams& p, int i, int g, i
   float* el = reinterpret_cast<float*>(lds);   // [64 tokens][8 heads]
   // bf16: q of the group staged in LDS (read back as broadcasts)
   uint16_t* ql = reinterpret_cast<uint16_t*>(lds + 2048);
-  if (DT == MILO_BF16 && L > 0) {
+  if (DT != MILO_F32 && L > 0) {
     constexpr int NQ = G * D / 8;
     const uint16_t* qh = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)i * p.n_q_heads + g * G) * D;
     if (lane < NQ) *reinterpret_cast<u32x4_t*>(ql + lane * 8) = ld16(qh + lane * 8);
@@ -566,7 +811,7 @@ __device__ __forceinline__ void tail_unit(const DecodeParams& p, int i, int g, i
 #pragma unroll
     for (int h = 0; h < G; ++h) s[h] = 0.f;
     const int tk = min(t, L - 1);   // lanes past the end re-read the last token (masked)
-    if (DT == MILO_BF16) {
+    if (DT != MILO_F32) {
       // the whole key row of the lane's token in flight at once
       const uint16_t* K = reinterpret_cast<const uint16_t*>(p.k_tail) + kv_off + (size_t)tk * D;
       u32x4_t kv[D / 8];
@@ -617,7 +862,7 @@ __device__ __forceinline__ void tail_unit(const DecodeParams& p, int i, int g, i
 #pragma unroll
       for (int j = 0; j < kVRows; ++j) {
         const size_t row = kv_off + (size_t)(t0 + min(tt0 + j, nt - 1)) * D;
-        if (DT == MILO_BF16) {
+        if (DT != MILO_F32) {
           const uint16_t* V = reinterpret_cast<const uint16_t*>(p.v_tail) + row;
           if (JPL == 2) {
             const uint32_t w = *reinterpret_cast<const uint32_t*>(V + 2 * lane);
@@ -678,6 +923,8 @@ __global__ __launch_bounds__(64) void milo_decode_kernel(DecodeParams p) {
   const milo_block blk = p.blocks[b0 + slot];
   if (DT == MILO_BF16)
     block_unit_bf16<D, G>(p, i, g, unit, blk, lds);
+  else if (DT == MILO_BF16_Q8)
+    block_unit_q8<D, G>(p, i, g, unit, blk, lds);
   else
     block_unit_f32<D, G>(p, i, g, unit, blk, lds);
 }
@@ -700,7 +947,7 @@ hipError_t launch_decode_dg(const DecodeParams& p, int group, hipStream_t s) {
 }  // namespace
 
 // One translation unit per (dtype, head_dim): compiled with
-// -DMILO_INST_DT=<0|1> -DMILO_INST_D=<64|128>.
+// -DMILO_INST_DT=<0|1|2> -DMILO_INST_D=<64|128>.
 #define MILO_CAT2(a, b, c) launch_decode_##a##_##b##_##c
 #define MILO_CAT(a, b, c) MILO_CAT2(a, b, c)
 hipError_t MILO_CAT(dt, MILO_INST_DT, MILO_INST_D)(const DecodeParams& p, int group, hipStream_t s) {

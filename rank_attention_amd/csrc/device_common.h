@@ -7,6 +7,7 @@
 namespace milo {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -45,6 +46,17 @@ __device__ __forceinline__ u32x4_t bld16(rsrc_t r, uint32_t voff, uint32_t soff)
 __device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// d = a.lo*b.lo + a.hi*b.hi + c, fp16 pairs, fp32 accumulate (exact products).
+__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+}
+
+// Two fp32 values to a packed fp16 pair (round to nearest even), a in the low half.
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
 }
 
 __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
@@ -102,6 +114,19 @@ __device__ __forceinline__ float wave_max(float v) {
   a = v; b = v;
   swap32(a, b);
   return fmaxf(a, b);
+}
+
+__device__ __forceinline__ float wave_min(float v) {
+  v = fminf(v, dpp<kQuadXor1>(v));
+  v = fminf(v, dpp<kQuadXor2>(v));
+  v = fminf(v, dpp<kHalfMirror>(v));
+  v = fminf(v, dpp<kRowRor8>(v));
+  float a = v, b = v;
+  swap16(a, b);
+  v = fminf(a, b);
+  a = v; b = v;
+  swap32(a, b);
+  return fminf(a, b);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

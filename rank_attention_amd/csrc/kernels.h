@@ -105,9 +105,21 @@ struct ValidateParams {
   const int32_t* seq_blocks;
   const int32_t* tail_len;
   unsigned long long* status;
-  int64_t pool_elems;
+  int64_t pool_elems;        // bytes for 8-bit factor storage
   int32_t n_descriptors, n_seqs_checked, batch, max_blocks, n_kv_heads, head_dim, tail_cap, tail_min;
+  int32_t q8;                // 8-bit factor storage: byte offsets, multiples of 16
 };
+
+// 8-bit factors: one workgroup per (block, KV head) quantises its U^T and
+// U'^T rows and copies W and W'.
+struct QuantParams {
+  const uint16_t* src_pool;
+  const milo_block* src_blocks;
+  uint8_t* dst_pool;
+  const milo_block* dst_blocks;
+  int32_t n_blocks, n_kv_heads;
+};
+hipError_t launch_quantize(const QuantParams& p, int head_dim, hipStream_t s);
 hipError_t launch_validate(const ValidateParams& p, hipStream_t s);
 
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int n_wg, hipStream_t s);
@@ -123,6 +135,8 @@ hipError_t launch_decode_dt_0_64(const DecodeParams& p, int group, hipStream_t s
 hipError_t launch_decode_dt_0_128(const DecodeParams& p, int group, hipStream_t s);
 hipError_t launch_decode_dt_1_64(const DecodeParams& p, int group, hipStream_t s);
 hipError_t launch_decode_dt_1_128(const DecodeParams& p, int group, hipStream_t s);
+hipError_t launch_decode_dt_2_64(const DecodeParams& p, int group, hipStream_t s);
+hipError_t launch_decode_dt_2_128(const DecodeParams& p, int group, hipStream_t s);
 
 inline hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int group,
                                 hipStream_t s) {
@@ -130,6 +144,8 @@ inline hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, 
   if (dtype == MILO_F32 && head_dim == 128) return launch_decode_dt_0_128(p, group, s);
   if (dtype == MILO_BF16 && head_dim == 64) return launch_decode_dt_1_64(p, group, s);
   if (dtype == MILO_BF16 && head_dim == 128) return launch_decode_dt_1_128(p, group, s);
+  if (dtype == MILO_BF16_Q8 && head_dim == 64) return launch_decode_dt_2_64(p, group, s);
+  if (dtype == MILO_BF16_Q8 && head_dim == 128) return launch_decode_dt_2_128(p, group, s);
   return hipErrorInvalidValue;
 }
 hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t s);

@@ -29,7 +29,7 @@ milo_status check_shape(const milo_attn_args* a, int32_t path) {
   if (!a) return MILO_ERR_INVALID;
   if (a->struct_size != (int32_t)sizeof(milo_attn_args)) return MILO_ERR_INVALID;
   if (path != MILO_PATH_DECODE && path != MILO_PATH_CHUNK && path != MILO_PATH_SHARED) return MILO_ERR_INVALID;
-  if (a->dtype != MILO_F32 && a->dtype != MILO_BF16) return MILO_ERR_UNSUPPORTED;
+  if (a->dtype != MILO_F32 && a->dtype != MILO_BF16 && a->dtype != MILO_BF16_Q8) return MILO_ERR_UNSUPPORTED;
   if (a->batch < 0 || a->q_len < 1 || a->n_q_heads < 1 || a->n_kv_heads < 1) return MILO_ERR_INVALID;
   if (a->n_q_heads % a->n_kv_heads != 0) return MILO_ERR_INVALID;
   if (a->max_blocks_per_seq < 0 || a->tail_cap < 0) return MILO_ERR_INVALID;
@@ -326,6 +326,7 @@ milo_status milo_attn_validate(const milo_attn_args* a, int32_t path, int32_t n_
   p.head_dim = a->head_dim;
   p.tail_cap = a->tail_cap;
   p.tail_min = path == MILO_PATH_CHUNK ? a->q_len : 0;
+  p.q8 = a->dtype == MILO_BF16_Q8;
   if (milo::launch_validate(p, reinterpret_cast<hipStream_t>(hip_stream)) != hipSuccess) return MILO_ERR_DEVICE;
   return MILO_OK;
 }

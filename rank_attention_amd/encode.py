@@ -10,7 +10,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 from . import _lib
-from ._lib import MILO_BF16, MILO_F32, MILO_OK, MILO_ERR_DEVICE, MiloEncodeArgs, MiloRankArgs
+from ._lib import MILO_BF16, MILO_F32, MILO_OK, MILO_ERR_DEVICE, MiloEncodeArgs, MiloQuantArgs, MiloRankArgs
 from .pack import BLOCK_DTYPE
 
 
@@ -32,6 +32,46 @@ def layout(n_tok: Sequence[int], rank_k: Sequence[int], rank_v: Sequence[int], n
     if rc != MILO_OK:
         raise MiloError(rc, status_str(rc))
     return blocks, int(elems.value)
+
+
+def quant_layout(src_blocks: np.ndarray, n_kv_heads: int, head_dim: int) -> Tuple[np.ndarray, int]:
+    """Descriptors (BLOCK_DTYPE) and size in bytes of the 8-bit pool for the
+    blocks of a bf16 pool (milo_quant_layout)."""
+    from . import MiloError, status_str
+    src = np.ascontiguousarray(src_blocks, BLOCK_DTYPE)
+    out = np.zeros(len(src), BLOCK_DTYPE)
+    nbytes = ctypes.c_int64(0)
+    rc = _lib.load().milo_quant_layout(src.ctypes.data if len(src) else None, len(src), int(n_kv_heads),
+                                       int(head_dim), out.ctypes.data if len(src) else None, ctypes.byref(nbytes))
+    if rc != MILO_OK:
+        raise MiloError(rc, status_str(rc))
+    return out, int(nbytes.value)
+
+
+def quantize(pool, blocks_dev, blocks_host: np.ndarray, n_kv_heads: int, head_dim: int, stream=None):
+    """8-bit token factors of a bf16 pool (milo_quantize_factors).  Returns
+    (pool uint8 tensor, descriptors on the device, descriptors on the host);
+    milo_attn_decode reads the result as MILO_BF16_Q8 storage."""
+    import torch
+    from . import MiloError, status_str
+    lib = _lib.load()
+    blocks, nbytes = quant_layout(blocks_host, n_kv_heads, head_dim)
+    dev = pool.device
+    qpool = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    qdev = torch.from_numpy(blocks.view(np.uint8).copy()).to(dev)
+    a = MiloQuantArgs()
+    a.struct_size = ctypes.sizeof(MiloQuantArgs)
+    a.n_blocks, a.n_kv_heads, a.head_dim = len(blocks), int(n_kv_heads), int(head_dim)
+    a.src_pool, a.src_blocks = pool.data_ptr(), blocks_dev.data_ptr()
+    a.dst_pool, a.dst_blocks = qpool.data_ptr(), qdev.data_ptr()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.milo_quantize_factors(ctypes.byref(a), ctypes.c_void_p(int(stream)))
+    if rc != MILO_OK:
+        if rc == MILO_ERR_DEVICE:
+            raise RuntimeError(f"milo_quantize_factors: {status_str(rc)}")
+        raise MiloError(rc, status_str(rc))
+    return qpool, qdev, blocks
 
 
 def allocate_ranks(sigma, budget_k: int, budget_v: int, r_min: int, unit: int = 1, stream=None):

@@ -5,6 +5,7 @@ import math
 import os
 import re
 
+import numpy as np
 import pytest
 
 import rank_attention_amd as ra
@@ -34,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_struct_size():
-    assert ra.abi_version() == 2
+    assert ra.abi_version() == 3
     # 7 int32 + float, 4 pointers, 2 int32, 6 pointers, size_t, 3 pointers; the
     # C side agrees, or the batch-0 call below would fail its struct_size check
     assert ctypes.sizeof(_lib.MiloAttnArgs) == 8 * 4 + 4 * 8 + 2 * 4 + 6 * 8 + 8 + 3 * 8
@@ -315,3 +316,66 @@ def test_validate_rejects_bad_host_arguments():
     c = good_args(head_dim=96)
     assert lib.milo_attn_validate(ctypes.byref(c), _lib.MILO_PATH_DECODE, 4, 1000, FAKE, None) == _lib.MILO_ERR_UNSUPPORTED
     assert lib.milo_attn_validate(None, _lib.MILO_PATH_DECODE, 4, 1000, FAKE, None) == _lib.MILO_ERR_INVALID
+
+
+def test_quant_layout():
+    from rank_attention_amd import encode as enc
+    src = np.zeros(3, ra.BLOCK_DTYPE)
+    src["n_tok"], src["rank_k"], src["rank_v"] = [37, 1024, 0], [5, 128, 0], [3, 1, 7]
+    src["off"], src["ld_tok"] = [8, 1000, 5000], [40, 1024, 0]       # the source's placement is irrelevant
+    blocks, nbytes = enc.quant_layout(src, n_kv_heads=2, head_dim=128)
+    assert list(blocks["ld_tok"]) == [48, 1024, 0]
+    assert list(blocks["n_tok"]) == [37, 1024, 0] and list(blocks["rank_k"]) == [5, 128, 0]
+    # per head: rows * (ld + 2d) bytes of codes and bf16 W, then 8 bytes of (a, b) per row padded to 16
+    h0 = 8 * (48 + 256) + 64
+    h1 = 129 * (1024 + 256) + (8 * 129 + 15) // 16 * 16
+    h2 = 7 * 256 + 64
+    assert list(blocks["off"]) == [0, 2 * h0, 2 * h0 + 2 * h1]
+    assert nbytes == 2 * (h0 + h1 + h2)
+    assert all(o % 16 == 0 for o in blocks["off"])
+    bad = src.copy()
+    bad["rank_k"][0] = 129
+    with pytest.raises(ra.MiloError):
+        enc.quant_layout(bad, n_kv_heads=2, head_dim=128)
+    lib = _lib.load()
+    out = ctypes.c_int64(0)
+    assert lib.milo_quant_layout(None, 1, 1, 128, None, ctypes.byref(out)) == _lib.MILO_ERR_INVALID
+    assert lib.milo_quant_layout(None, 0, 1, 128, None, ctypes.byref(out)) == _lib.MILO_OK and out.value == 0
+
+
+def quant_args(**over):
+    a = _lib.MiloQuantArgs()
+    a.struct_size = ctypes.sizeof(_lib.MiloQuantArgs)
+    a.n_blocks, a.n_kv_heads, a.head_dim = 3, 2, 128
+    a.src_pool = a.src_blocks = a.dst_pool = a.dst_blocks = FAKE
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"struct_size": 8}, _lib.MILO_ERR_INVALID),
+    ({"head_dim": 96}, _lib.MILO_ERR_UNSUPPORTED),
+    ({"n_blocks": -1}, _lib.MILO_ERR_INVALID),
+    ({"n_kv_heads": 0}, _lib.MILO_ERR_INVALID),
+    ({"src_pool": None}, _lib.MILO_ERR_INVALID),
+    ({"dst_blocks": None}, _lib.MILO_ERR_INVALID),
+    ({"dst_pool": FAKE + 8}, _lib.MILO_ERR_INVALID),
+    ({"n_blocks": 0, "src_pool": None}, _lib.MILO_OK),
+])
+def test_quantize_rejects_before_any_hip_call(over, code):
+    assert ctypes.sizeof(_lib.MiloQuantArgs) == 4 * 4 + 4 * 8
+    assert _lib.load().milo_quantize_factors(ctypes.byref(quant_args(**over)), None) == code
+    assert _lib.load().milo_quantize_factors(None, None) == _lib.MILO_ERR_INVALID
+
+
+def test_q8_storage_is_decode_only():
+    lib = _lib.load()
+    a = good_args(dtype=_lib.MILO_BF16_Q8)
+    assert lib.milo_attn_workspace_bytes(ctypes.byref(a), _lib.MILO_PATH_DECODE) > 0
+    c = good_args(dtype=_lib.MILO_BF16_Q8, head_dim=128, q_len=4, n_q_heads=4)
+    for path in (_lib.MILO_PATH_CHUNK, _lib.MILO_PATH_SHARED):
+        assert lib.milo_attn_workspace_bytes(ctypes.byref(c), path) == 0
+    assert lib.milo_attn_chunk(ctypes.byref(c), None) == _lib.MILO_ERR_UNSUPPORTED
+    d = good_args(dtype=_lib.MILO_BF16_Q8, head_dim=128, n_q_heads=4)
+    assert lib.milo_attn_decode_shared(ctypes.byref(d), None) == _lib.MILO_ERR_UNSUPPORTED
