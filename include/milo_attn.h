@@ -92,17 +92,21 @@ typedef enum milo_path {
  * it.  Every row k of U^T and of U'^T (one rank component over the block's
  * tokens) holds uint8 codes c with an fp32 pair (a_k, b_k):
  *     element = a_k * c + b_k.
- * Offsets and strides count BYTES: off and ld_tok are multiples of 16, and
- * KV head g starts at byte off + g * H with
- *     H = (rank_k + rank_v) * (ld_tok + 2 * head_dim) + pad16(8 * (rank_k + rank_v)),
+ * The keys' codes are stored token-major (U, one row of rank_k codes per
+ * token, padded to rk16 = rank_k rounded up to 16), the values' rank-major
+ * (U'^T), the orders in which the decode kernel's matrix-core operands
+ * take them.  Offsets and strides count BYTES: off and ld_tok are multiples
+ * of 16, and KV head g starts at byte off + g * H with
+ *     H = n_tok * rk16 + rank_v * ld_tok + 2 * (rank_k + rank_v) * head_dim
+ *         + pad16(8 * (rank_k + rank_v)),
  * pad16(x) = x rounded up to a multiple of 16.  Per head, back to back:
- *     U^T  codes  [rank_k][ld_tok]      uint8
+ *     U codes     [n_tok][rk16]         uint8 (codes rank_k.. of a row: padding)
  *     W           [rank_k][head_dim]    bf16
- *     U'^T codes  [rank_v][ld_tok]      uint8
+ *     U'^T codes  [rank_v][ld_tok]      uint8 (codes n_tok.. of a row: padding)
  *     W'          [rank_v][head_dim]    bf16
  *     (a_k, b_k)  [rank_k + rank_v][2]  fp32, the keys' rows first, then
  *                 padding to the next multiple of 16 bytes.
- * Codes n_tok..ld_tok-1 of each row are padding (any value).
+ * Padding codes may hold any value.
  */
 typedef struct milo_block {
   int64_t off;      /* element offset of KV head 0's U^T; multiple of 8 (Q8: bytes,

@@ -155,8 +155,9 @@ typedef struct milo_quant_args {
 } milo_quant_args;
 
 /* Host-side layout of the MILO_BF16_Q8 pool for the blocks src_blocks
- * (HOST array): the same n_tok and ranks, ld_tok = n_tok rounded up to 16,
- * blocks back to back from byte 0 in the given order.  blocks_out (host)
+ * (HOST array): the same n_tok and ranks, ld_tok = n_tok rounded up to 16
+ * (the value codes' row stride), blocks back to back from byte 0 in the
+ * given order.  blocks_out (host)
  * receives n_blocks descriptors and *pool_bytes the pool size.
  * MILO_ERR_INVALID on null pointers, negative sizes or ranks outside
  * [0, head_dim]. */
@@ -164,7 +165,7 @@ milo_status milo_quant_layout(const milo_block* src_blocks, int32_t n_blocks, in
                               int32_t head_dim, milo_block* blocks_out, int64_t* pool_bytes);
 
 /* Quantise every block of the source pool into the destination pool (one
- * kernel on the stream; codes past n_tok up to ld_tok are written as 0).
+ * kernel on the stream; padding codes are written as 0).
  * The source tables are the caller's contract as in milo_attn.h. */
 milo_status milo_quantize_factors(const milo_quant_args* args, void* hip_stream);
 

@@ -341,175 +341,328 @@ __device__ __forceinline__ void block_unit_bf16(const DecodeParams& p, int i, in
 }
 
 // ---------------------------------------------------------------------------
-// 8-bit token factors (MILO_BF16_Q8): row k of U^T / U'^T holds codes c with
-// x = a_k c + b_k.  Folded into the absorbed order:
+// 8-bit token factors (MILO_BF16_Q8), on the matrix cores.  Row k of U^T /
+// U'^T holds codes c with x = a_k c + b_k; the keys' codes are stored token-
+// major ([n_tok][rank_k rounded up to 16]), the values' rank-major.  Folded
+// into the absorbed order:
 //   s_t = sum_k p_k x_kt  = sum_k (p_k a_k) c_kt + C,   C = sum_k p_k b_k
 //   z_k = sum_t e_t x'_kt = a'_k sum_t e_t c'_kt + b'_k E,   E = sum_t e_t
-// The scores keep the fp32 path of bf16 storage (a code converts to fp32 in
-// one instruction).  For the values e is rounded to fp16 pairs, and a byte
-// permute with the constant 0x64 turns four codes into two fp16 pairs of
-// 1024 + c (exact: fp16 spacing is 1 on [1024, 2048)), so one dot2 per
-// token pair and head accumulates sum_t e_t (1024 + c); the 1024 E it adds
-// is taken off with E summed from the same fp16 e, which also feeds l.
-// A lane owns 16 consecutive tokens (one 16-byte load per row) of a
-// 1024-token tile.  Codes can not be NaN, so padding needs no mask: tokens
-// past the block end have e = 0.
+// A byte permute with the constant 0x64 turns four codes into two fp16 pairs
+// 1024 + c (exact: the fp16 spacing is 1 on [1024, 2048)), so both sums run
+// on v_mfma_f32_16x16x32_f16:
+//   scores  S^T (16 tokens x 16 heads) = codes (tokens x ranks) . p'
+//           (ranks x heads) with the key codes centred (one packed fp16 add
+//           of -1152 gives c - 128, exact) and p' = p a split into fp16
+//           hi + lo after scaling by a power of two sc (about 22 mantissa
+//           bits); the accumulator starts at sc (C + 128 sum_k p'_k);
+//   values  Z^T (16 ranks x 16 heads) = codes' (ranks x tokens) . e (tokens
+//           x heads), e rounded to fp16 and the codes left at 1024 + c
+//           (all terms positive); l sums those fp16 values, and
+//           z = a' (Z - 1024 l) + b' l at the end.
+// Heads are the N dimension (G <= 8 of 16 columns used).  A 16x16 result
+// holds, in lane l, column l%16 and rows 4(l/16) + v.  Score tile m of a
+// 64-token chunk gives row 4j + v token 16j + 4m + v, so after the four
+// tiles lane l holds 16 consecutive tokens 16(l/16) .. +15 of head l%16:
+// exactly the value MFMA's B operand (K slot 8(l/16) + i = token 16(l/16) +
+// i, and + 8 in the second MFMA), against one 16-byte load of a U'^T row.
+// A key row's 16-byte load (ranks 16(l/16) .. +15, + 64 for the second
+// pair) feeds two K = 32 steps; p' is laid out in that rank order.
+// Softmax: the running max m moves only when a chunk's scores exceed it by
+// more than 8 (log2 units), so weights stay <= 256, well inside fp16; Z and
+// l are rescaled only then.
 // ---------------------------------------------------------------------------
 
-constexpr int kQ8RowsPerStep = 8;   // U^T rows per prefetch step of the score loop
 constexpr uint32_t kF16Ones = 0x3C003C00u;   // fp16 pair (1, 1)
 constexpr uint32_t kF16Magic = 0x64646464u;  // high byte of fp16 1024 + c, c < 256
+constexpr int kQ8Chunk = 64;                 // tokens per chunk
+constexpr float kQ8Gap = 8.f;                // log2 units the running max may lag
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 // fp16 pairs (1024 + c0, 1024 + c1) and (1024 + c2, 1024 + c3) of four codes
 __device__ __forceinline__ uint32_t q8_pair_lo(uint32_t c) { return __builtin_amdgcn_perm(kF16Magic, c, 0x04010400u); }
 __device__ __forceinline__ uint32_t q8_pair_hi(uint32_t c) { return __builtin_amdgcn_perm(kF16Magic, c, 0x04030402u); }
 
-__device__ __forceinline__ void q8_load_rows(const uint8_t* Uc, int ld, int k0, int r, int tq,
-                                             u32x4_t (&A)[kQ8RowsPerStep]) {
-#pragma unroll
-  for (int j = 0; j < kQ8RowsPerStep; ++j) A[j] = ld16_stream(Uc + (size_t)min(k0 + j, r - 1) * ld + tq);
+// The K = 32 operand (8 fp16 of 1024 + c) of codes in words w, w + 1.
+__device__ __forceinline__ u32x4_t q8_operand(const u32x4_t& v, int w) {
+  u32x4_t a;
+  a[0] = q8_pair_lo(v[w]);
+  a[1] = q8_pair_hi(v[w]);
+  a[2] = q8_pair_lo(v[w + 1]);
+  a[3] = q8_pair_hi(v[w + 1]);
+  return a;
 }
 
-template <int G>
-__device__ __forceinline__ void q8_score_rows(const u32x4_t (&A)[kQ8RowsPerStep], int k0, int r,
-                                              const float* pf, float (&s)[16][G]) {
+// A code pair centred: (c0 - 128, c1 - 128) = (1024 + c) - 1152, exact in fp16.
+// (Each word is centred as it is made: an element-wise loop over the vector
+// with the same arithmetic is miscompiled by the toolchain in use.)
+__device__ __forceinline__ uint32_t q8_centre(uint32_t pair) {
+  const f16x2_t k = {(_Float16)-1152.f, (_Float16)-1152.f};
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, pair) + k);
+}
+
+// The K = 32 operand of codes in words w, w + 1, centred.
+__device__ __forceinline__ u32x4_t q8_operand_centred(const u32x4_t& v, int w) {
+  u32x4_t a;
+  a[0] = q8_centre(q8_pair_lo(v[w]));
+  a[1] = q8_centre(q8_pair_hi(v[w]));
+  a[2] = q8_centre(q8_pair_lo(v[w + 1]));
+  a[3] = q8_centre(q8_pair_hi(v[w + 1]));
+  return a;
+}
+
+__device__ __forceinline__ f32x4_t mfma_f16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                c, 0, 0, 0);
+}
+
+// Combine the four lanes l%16 + 16j (j = 0..3) that share a column.
+__device__ __forceinline__ float col_max(float v) {
+  float a = v, b = v;
+  swap16(a, b);
+  v = fmaxf(a, b);
+  a = v; b = v;
+  swap32(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float col_sum(float v) {
+  float a = v, b = v;
+  swap16(a, b);
+  v = a + b;
+  a = v; b = v;
+  swap32(a, b);
+  return a + b;
+}
+
+// Registers of the code loads in flight: 16 loads of 16 bytes per lane.  A
+// chunk of 64 tokens takes 4 NP key loads (four score tiles, NP pairs of 64
+// ranks) at R[KB + NP m + pr] and NTV value loads (tiles of 16 ranks) at
+// R[VB + kt].  Units with rank_k, rank_v <= 64 keep two chunks in R, larger
+// ones one.
+constexpr int kQ8Regs = 16;
+typedef u32x4_t Q8Regs[kQ8Regs];
+
+// Geometry of one unit's 8-bit factors (KV head g of one block).
+struct Q8Unit {
+  const uint8_t* Uk;   // key codes, token-major [T][rk16]
+  const uint8_t* Uv;   // value codes, rank-major [rv][ld]
+  int T, ld, r, rv, rk16, npairs, ntv, quad, col;
+};
+
+// Code loads of one chunk.  Every address is clamped into the unit's own
+// rows (rank offsets to rk16 - 16, tokens to T - 1, value rows to rv - 1),
+// so with rank_k, rank_v >= 1 every load is valid and ALL may be issued:
+// unguarded (ALL = true), the loop's load counts are static and each wait
+// covers only the loads it needs.  The loads are cached (not non-temporal):
+// a chunk reads 64 bytes of each value row and the next chunk the rest of
+// the 128-byte line, which must still be there.
+template <int NP, int KB, bool ALL>
+__device__ __forceinline__ void q8_load_keys(Q8Regs& R, const Q8Unit& u, int t0) {
+  // key row of score row `col` in tile m: token t0 + 16(col/4) + 4m + col%4
 #pragma unroll
-  for (int j = 0; j < kQ8RowsPerStep; ++j) {
-    if (k0 + j < r) {
-      const f32x4_t pq0 = *reinterpret_cast<const f32x4_t*>(pf + (k0 + j) * 8);
-      const f32x4_t pq1 = *reinterpret_cast<const f32x4_t*>(pf + (k0 + j) * 8 + 4);
-      const float pp[8] = {pq0[0], pq0[1], pq0[2], pq0[3], pq1[0], pq1[1], pq1[2], pq1[3]};
+  for (int m = 0; m < 4; ++m) {
+    const int tk = min(t0 + 16 * (u.col >> 2) + 4 * m + (u.col & 3), u.T - 1);
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr)
+      if (ALL || pr < u.npairs)
+        R[KB + NP * m + pr] = ld16(u.Uk + (size_t)tk * u.rk16 + min(64 * pr + 16 * u.quad, u.rk16 - 16));
+  }
+}
+
+template <int NTV, int VB, bool ALL>
+__device__ __forceinline__ void q8_load_values(Q8Regs& R, const Q8Unit& u, int t0) {
+  // tokens t0 + 16 quad .. + 15 of rank row 16 kt + col (a chunk past the
+  // padded row end reads the chunk start instead: its tokens have e = 0)
+  const int tv = t0 + 16 * u.quad < u.ld ? t0 + 16 * u.quad : t0;
+#pragma unroll
+  for (int kt = 0; kt < NTV; ++kt)
+    if (ALL || kt < u.ntv) R[VB + kt] = ld16(u.Uv + (size_t)min(16 * kt + u.col, u.rv - 1) * u.ld + tv);
+}
+
+// Scores of one chunk (consumes its key loads): S[m][v] for token t0 + 16 quad + 4m + v.
+template <int NP, int KB>
+__device__ __forceinline__ void q8_scores(const Q8Regs& R, const Q8Unit& u, const u32x4_t (&Bh)[NP][2],
+                                          const u32x4_t (&Bl)[NP][2], float s0, f32x4_t (&S)[4]) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    S[m] = f32x4_t{s0, s0, s0, s0};
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr)
+      if (pr < u.npairs) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const u32x4_t a = q8_operand_centred(R[KB + NP * m + pr], 2 * j);
+          S[m] = mfma_f16(a, Bh[pr][j], S[m]);
+          S[m] = mfma_f16(a, Bl[pr][j], S[m]);
+        }
+      }
+  }
+}
+
+// Online softmax of one chunk's scores and Z^T += codes' . e (consumes its value loads).
+template <int NTV, int VB>
+__device__ __forceinline__ void q8_values(const Q8Regs& R, const Q8Unit& u, const f32x4_t (&S)[4], int t0,
+                                          float inv_sc, float& m_run, float& l_run, f32x4_t (&Z)[NTV]) {
+  float x[4][4], cmax = kNegInf;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int tok = t0 + 16 * u.quad + 4 * m + v;
+      x[m][v] = tok < u.T ? S[m][v] * inv_sc : kNegInf;
+      cmax = fmaxf(cmax, x[m][v]);
+    }
+  cmax = col_max(cmax);
+  const bool up = cmax > m_run + kQ8Gap;
+  if (__builtin_amdgcn_ballot_w64(up) != 0) {
+    const float alpha = up ? fast_exp2(m_run - cmax) : 1.f;
+    m_run = up ? cmax : m_run;
+    l_run *= alpha;
+#pragma unroll
+    for (int kt = 0; kt < NTV; ++kt)
+      if (kt < u.ntv) Z[kt] *= alpha;
+  }
+  // e = exp2(s - m) as fp16 pairs in token order 16 quad + 0 .. 15
+  u32x4_t E0, E1;
+  float lp = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const uint32_t e2 = pack_f16(fast_exp2(x[m][2 * w] - m_run), fast_exp2(x[m][2 * w + 1] - m_run));
+      lp = dot2h(e2, kF16Ones, lp);
+      if (m < 2) E0[2 * m + w] = e2; else E1[2 * (m - 2) + w] = e2;
+    }
+  l_run += lp;
+#pragma unroll
+  for (int kt = 0; kt < NTV; ++kt)
+    if (kt < u.ntv) {
+      Z[kt] = mfma_f16(q8_operand(R[VB + kt], 0), E0, Z[kt]);
+      Z[kt] = mfma_f16(q8_operand(R[VB + kt], 2), E1, Z[kt]);
+    }
+}
+
+// Loads of chunk c into buffer d of the layout (NP, NTV, DEPTH).
+template <int NP, int NTV, int DEPTH, int d, bool ALL>
+__device__ __forceinline__ void q8_load_chunk(Q8Regs& R, const Q8Unit& u, int c) {
+  constexpr int per = kQ8Regs / DEPTH;
+  if (ALL || u.npairs > 0) q8_load_keys<NP, per * d, ALL>(R, u, c * kQ8Chunk);
+  if (ALL || u.ntv > 0) q8_load_values<NTV, per * d + 4 * NP, ALL>(R, u, c * kQ8Chunk);
+}
+
+// Chunk c from buffer d; PF: issue the loads of chunk c + DEPTH into the
+// buffer as it is consumed (keys after the scores, values after the values).
+template <int NP, int NTV, int DEPTH, int d, bool ALL>
+__device__ __forceinline__ void q8_chunk_step(Q8Regs& R, const Q8Unit& u, int c, bool pf,
+                                              const u32x4_t (&Bh)[NP][2], const u32x4_t (&Bl)[NP][2], float s0,
+                                              float inv_sc, float& m_run, float& l_run, f32x4_t (&Z)[NTV]) {
+  constexpr int per = kQ8Regs / DEPTH;
+  static_assert(4 * NP + NTV <= per, "a chunk's loads fit its buffer");
+  f32x4_t S[4];
+  q8_scores<NP, per * d>(R, u, Bh, Bl, s0, S);
+  if (pf && (ALL || u.npairs > 0)) q8_load_keys<NP, per * d, ALL>(R, u, (c + DEPTH) * kQ8Chunk);
+  q8_values<NTV, per * d + 4 * NP>(R, u, S, c * kQ8Chunk, inv_sc, m_run, l_run, Z);
+  if (pf && (ALL || u.ntv > 0)) q8_load_values<NTV, per * d + 4 * NP, ALL>(R, u, (c + DEPTH) * kQ8Chunk);
+}
+
+// The chunk loop: DEPTH chunks in flight, the loads of chunk c + DEPTH going
+// out as chunk c consumes its own.  With rank_k, rank_v >= 1 and at least
+// 2 DEPTH chunks the steady-state loop issues every load unguarded (static
+// counts); the last DEPTH chunks, and units with an empty factor, take the
+// guarded steps.
+template <int NP, int NTV, int DEPTH>
+__device__ __forceinline__ void q8_chunks(const Q8Unit& u, const u32x4_t (&Bh)[NP][2],
+                                          const u32x4_t (&Bl)[NP][2], float s0, float inv_sc, float& m_run,
+                                          float& l_run, f32x4_t (&Z)[NTV]) {
+  const int nch = (u.T + kQ8Chunk - 1) / kQ8Chunk;
+  Q8Regs R;
+  int c0 = 0;
+  if (u.npairs > 0 && u.ntv > 0 && nch >= 2 * DEPTH) {
+    q8_load_chunk<NP, NTV, DEPTH, 0, true>(R, u, 0);
+    if (DEPTH > 1) q8_load_chunk<NP, NTV, DEPTH, DEPTH - 1, true>(R, u, 1);
+    for (; c0 + 2 * DEPTH <= nch; c0 += DEPTH) {
+      q8_chunk_step<NP, NTV, DEPTH, 0, true>(R, u, c0, true, Bh, Bl, s0, inv_sc, m_run, l_run, Z);
+      if (DEPTH > 1)
+        q8_chunk_step<NP, NTV, DEPTH, DEPTH - 1, true>(R, u, c0 + 1, true, Bh, Bl, s0, inv_sc, m_run, l_run, Z);
+    }
+  } else {
+    if (nch > 0) q8_load_chunk<NP, NTV, DEPTH, 0, false>(R, u, 0);
+    if (DEPTH > 1 && nch > 1) q8_load_chunk<NP, NTV, DEPTH, DEPTH - 1, false>(R, u, 1);
+  }
+  // the remaining chunks c0 .. nch-1 (fewer than 2 DEPTH); chunks c0 ..
+  // c0 + DEPTH - 1 are loaded
+  for (; c0 < nch; c0 += DEPTH) {
+    q8_chunk_step<NP, NTV, DEPTH, 0, false>(R, u, c0, c0 + DEPTH < nch, Bh, Bl, s0, inv_sc, m_run, l_run, Z);
+    if (DEPTH > 1 && c0 + 1 < nch)
+      q8_chunk_step<NP, NTV, DEPTH, DEPTH - 1, false>(R, u, c0 + 1, c0 + 1 + DEPTH < nch, Bh, Bl, s0, inv_sc,
+                                                      m_run, l_run, Z);
+  }
+}
+
+// p' = p a (fp32) into the fp16 hi/lo B operands of the rank pairs < NP,
+// in the rank order of the key loads; returns this lane's sum of them.
+template <int NP, int G>
+__device__ __forceinline__ float q8_b_operands(const float* pf, int r, float sc, int quad, int col,
+                                               u32x4_t (&Bh)[NP][2], u32x4_t (&Bl)[NP][2]) {
+  float psum = 0.f;
+#pragma unroll
+  for (int pr = 0; pr < NP; ++pr)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t x = A[j][w];
-        const float c[4] = {(float)(x & 0xffu), (float)((x >> 8) & 0xffu), (float)((x >> 16) & 0xffu),
-                            (float)(x >> 24)};
+        float hv[2], lv[2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int h = 0; h < G; ++h) s[4 * w + e][h] = fmaf(c[e], pp[h], s[4 * w + e][h]);
+        for (int e = 0; e < 2; ++e) {
+          const int k = 64 * pr + 16 * quad + 8 * j + 2 * w + e;
+          const float v = (col < G && k < r) ? pf[k * 8 + col] * sc : 0.f;
+          const _Float16 hi = (_Float16)v;
+          const _Float16 lo = (_Float16)(v - (float)hi);
+          hv[e] = (float)hi;
+          lv[e] = (float)lo;
+          psum += hv[e] + lv[e];
+        }
+        Bh[pr][j][w] = pack_f16(hv[0], hv[1]);
+        Bl[pr][j][w] = pack_f16(lv[0], lv[1]);
       }
-    }
-  }
+  return psum;
 }
 
-template <int D, int G>
-__device__ __forceinline__ void q8_tiles(const uint8_t* Uc, const uint8_t* Upc, const uint16_t* Wp,
-                                         const float* sbv, int ld, int T, int r, int rv, const float* pf,
-                                         const float (&C)[G], float (&m_run)[G], float (&l_run)[G],
-                                         float (&o)[G][D / 64], float* zs, int lane) {
-  using S = Shape<D, G>;
-  constexpr int R = S::R, JPL = S::JPL;
-  const int hl = lane % G;   // head of the lane's z slot
-  for (int t0 = 0; t0 < T; t0 += 1024) {
-    const int tc = t0 + lane * 16;
-    // a lane whose chunk lies past the block end reads the tile's first
-    // chunk instead (always in bounds); its tokens are masked below
-    const int tq = tc < T ? tc : t0;
-
-    float s[16][G];
+// Z (per lane: ranks 16 kt + 4 quad + v, head col) to z = a' (Z - 1024 l) + b' l
+// staged as zs[k][h]; (a', b') of every value row are in LDS at abv.
+template <int NTV, int G>
+__device__ __forceinline__ void q8_stage_z(const f32x4_t (&Z)[NTV], const Q8Unit& u, const float* abv, float l_tot,
+                                           float* zs) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
+  for (int kt = 0; kt < NTV; ++kt)
+    if (kt < u.ntv) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) s[e][h] = C[h];
-    if (r > 0) {
-      u32x4_t A0[kQ8RowsPerStep], A1[kQ8RowsPerStep];
-      q8_load_rows(Uc, ld, 0, r, tq, A0);
-      for (int k0 = 0; k0 < r; k0 += 2 * kQ8RowsPerStep) {
-        if (k0 + kQ8RowsPerStep < r) q8_load_rows(Uc, ld, k0 + kQ8RowsPerStep, r, tq, A1);
-        q8_score_rows<G>(A0, k0, r, pf, s);
-        if (k0 + 2 * kQ8RowsPerStep < r) q8_load_rows(Uc, ld, k0 + 2 * kQ8RowsPerStep, r, tq, A0);
-        if (k0 + kQ8RowsPerStep < r) q8_score_rows<G>(A1, k0 + kQ8RowsPerStep, r, pf, s);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      if (tc + e >= T) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) s[e][h] = kNegInf;
-      }
-    }
-
-    // online softmax; e as fp16 pairs, E (the sum of those fp16 values) per head
-    uint32_t e2[8][G];
-    float alpha[G], E[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mx = s[0][h];
-#pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e][h]);
-      mx = wave_max(mx);
-      const float mn = fmaxf(m_run[h], mx);
-      alpha[h] = fast_exp2(m_run[h] - mn);
-      float sum = 0.f;
-#pragma unroll
-      for (int pr = 0; pr < 8; ++pr) {
-        e2[pr][h] = pack_f16(fast_exp2(s[2 * pr][h] - mn), fast_exp2(s[2 * pr + 1][h] - mn));
-        sum = dot2h(e2[pr][h], kF16Ones, sum);
-      }
-      E[h] = wave_sum(sum);
-      l_run[h] = l_run[h] * alpha[h] + E[h];
-      m_run[h] = mn;
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int jj = 0; jj < JPL; ++jj) o[h][jj] *= alpha[h];
-    float El = E[0];
-#pragma unroll
-    for (int h = 1; h < G; ++h) El = (hl == h) ? E[h] : El;
-
-    // ---- z per group of R rows of U'^T, then o~ += z W' for the group
-#pragma unroll 1
-    for (int gi = 0; gi * R < rv; ++gi) {
-      u32x4_t U[R];
-      uint32_t wr[R];
-#pragma unroll
-      for (int rho = 0; rho < R; ++rho)
-        U[rho] = ld16_stream(Upc + (size_t)min(gi * R + rho, rv - 1) * ld + tq);
-#pragma unroll
-      for (int rho = 0; rho < R; ++rho) {
-        const uint16_t* wrow = Wp + (size_t)min(gi * R + rho, rv - 1) * D;
-        wr[rho] = (JPL == 2) ? *reinterpret_cast<const uint32_t*>(wrow + 2 * lane)
-                             : (uint32_t)wrow[lane] << 16;
-      }
-      // (a', b') of the row of the lane's z slot (lanes >= R*G: unused)
-      const f32x2_t ab = *reinterpret_cast<const f32x2_t*>(sbv + 2 * min(gi * R + min(lane / G, R - 1), rv - 1));
-      float acc[64];
-#pragma unroll
-      for (int x = 0; x < 64; ++x) acc[x] = 0.f;
-#pragma unroll
-      for (int rho = 0; rho < R; ++rho) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t lo = q8_pair_lo(U[rho][w]), hi = q8_pair_hi(U[rho][w]);
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            acc[rho * G + h] = dot2h(lo, e2[2 * w][h], acc[rho * G + h]);
-            acc[rho * G + h] = dot2h(hi, e2[2 * w + 1][h], acc[rho * G + h]);
-          }
+      for (int v = 0; v < 4; ++v) {
+        const int k = 16 * kt + 4 * u.quad + v;
+        if (k < u.rv && u.col < G) {
+          const f32x2_t ab = *reinterpret_cast<const f32x2_t*>(abv + 2 * k);
+          zs[k * 8 + u.col] = fmaf(ab[0], Z[kt][v] - 1024.f * l_tot, ab[1] * l_tot);
         }
       }
-      // lane l ends with sum_t e_t (1024 + c) of slot l = (row rho, head h)
-      const float zg = reduce_transpose64(acc, lane);
-      if (lane < R * G) zs[(lane / G) * 8 + hl] = fmaf(ab[0], zg - 1024.f * El, ab[1] * El);
-      wave_lds_fence();
-#pragma unroll
-      for (int rho = 0; rho < R; ++rho) {
-        if (gi * R + rho < rv) {
-          const f32x4_t z0 = *reinterpret_cast<const f32x4_t*>(zs + rho * 8);
-          const f32x4_t z1 = *reinterpret_cast<const f32x4_t*>(zs + rho * 8 + 4);
-          const float zz[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
-          const float wv[2] = {bf_lo(wr[rho]), bf_hi(wr[rho])};
-#pragma unroll
-          for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int jj = 0; jj < JPL; ++jj) o[h][jj] = fmaf(zz[h], wv[JPL == 2 ? jj : 1], o[h][jj]);
-        }
-      }
-      wave_lds_fence();
     }
-  }
+}
+
+// Everything between the projection and o~ = z W' for one rank class: the
+// B operands, the chunk loop, and z staged in LDS.  Returns m and l (summed
+// over the four lanes of each head).
+template <int NP, int NTV, int DEPTH, int G>
+__device__ __forceinline__ void q8_body(const Q8Unit& u, const float* pf, const float* abv, float* zs, float Cl,
+                                        float sc, float inv_sc, float& m_run, float& l_run) {
+  u32x4_t Bh[NP][2], Bl[NP][2];
+  const float psum = q8_b_operands<NP, G>(pf, u.r, sc, u.quad, u.col, Bh, Bl);
+  // the centred codes add -128 sum p' sc to sc * (s - C): start the sum at sc C + that
+  const float s0 = fmaf(Cl, sc, 128.f * col_sum(psum));
+  f32x4_t Z[NTV];
+#pragma unroll
+  for (int kt = 0; kt < NTV; ++kt) Z[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  q8_chunks<NP, NTV, DEPTH>(u, Bh, Bl, s0, inv_sc, m_run, l_run, Z);
+  l_run = col_sum(l_run);
+  q8_stage_z<NTV, G>(Z, u, abv, l_run, zs);
 }
 
 template <int D, int G>
@@ -517,30 +670,46 @@ __device__ __forceinline__ void block_unit_q8(const DecodeParams& p, int i, int 
                                               const milo_block& blk, uint32_t* lds) {
   constexpr int JPL = D / 64;
   const int lane = threadIdx.x;
-  const int T = max(blk.n_tok, 0);
-  const int ld = blk.ld_tok;
-  const int r = min(max(blk.rank_k, 0), D), rv = min(max(blk.rank_v, 0), D);
-  const int64_t head = (int64_t)(r + rv) * (ld + 2 * D) + ((8 * (r + rv) + 15) & ~15);
-  const uint8_t* Uc = reinterpret_cast<const uint8_t*>(p.pool) + blk.off + g * head;
-  const uint16_t* W = reinterpret_cast<const uint16_t*>(Uc + (size_t)r * ld);
-  const uint8_t* Upc = Uc + (size_t)r * ld + (size_t)r * 2 * D;
-  const uint16_t* Wp = reinterpret_cast<const uint16_t*>(Upc + (size_t)rv * ld);
-  const float* sbk = reinterpret_cast<const float*>(Uc + (int64_t)(r + rv) * (ld + 2 * D));
+  Q8Unit u;
+  u.quad = lane >> 4;
+  u.col = lane & 15;
+  u.T = max(blk.n_tok, 0);
+  u.ld = blk.ld_tok;
+  u.r = min(max(blk.rank_k, 0), D);
+  u.rv = min(max(blk.rank_v, 0), D);
+  u.rk16 = (u.r + 15) & ~15;
+  u.npairs = (u.r + 63) >> 6;
+  u.ntv = (u.rv + 15) >> 4;
+  const int r = u.r, rv = u.rv, T = u.T;
+  const int64_t head =
+      (int64_t)T * u.rk16 + (int64_t)rv * u.ld + 2 * (int64_t)(r + rv) * D + ((8 * (r + rv) + 15) & ~15);
+  u.Uk = reinterpret_cast<const uint8_t*>(p.pool) + blk.off + g * head;
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(u.Uk + (int64_t)T * u.rk16);
+  u.Uv = reinterpret_cast<const uint8_t*>(W + (size_t)r * D);
+  const uint16_t* Wp = reinterpret_cast<const uint16_t*>(u.Uv + (size_t)rv * u.ld);
+  const float* sbk = reinterpret_cast<const float*>(Wp + (size_t)rv * D);
   const float* sbv = sbk + 2 * r;
   const uint16_t* qh = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)i * p.n_q_heads + g * G) * D;
+  float* pf = reinterpret_cast<float*>(lds);          // p' [rank][8 heads]
+  float* zs = reinterpret_cast<float*>(lds + 1024);   // z  [rank][8 heads]
+  float* abv = reinterpret_cast<float*>(lds + 2048);  // (a', b') of the value rows, after the projection
+  const bool small = u.npairs <= 1 && u.ntv <= 4;
 
-  float* pf = reinterpret_cast<float*>(lds);
+  // the value rows' (a', b') go out before the projection
+  f32x4_t abv_v = {0.f, 0.f, 0.f, 0.f};   // rows 2 lane, 2 lane + 1
+  if (2 * lane < rv) abv_v = *reinterpret_cast<const f32x4_t*>(sbv + 4 * min(lane, (rv - 1) >> 1));
+
+  // ---- p' = p a and C = sum p b (fp32)
   float C[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) C[h] = 0.f;
+  float mx = 0.f;
   if (r > 0) {
-    // (a_k, b_k) of the lane's rows, in flight with the projection's loads
     const f32x2_t ab0 = *reinterpret_cast<const f32x2_t*>(sbk + 2 * min(lane, r - 1));
     f32x2_t ab1 = {0.f, 0.f};
     if (D > 64) ab1 = *reinterpret_cast<const f32x2_t*>(sbk + 2 * min(lane + 64, r - 1));
     bf16_project_q<D, G>(W, qh, r, p.scale_log2, pf, reinterpret_cast<uint16_t*>(lds + 2048), lane);
     wave_lds_fence();
-    // p_k a_k replaces p_k; C = sum_k p_k b_k
     const bool has0 = lane < r, has1 = D > 64 && lane + 64 < r;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -549,40 +718,84 @@ __device__ __forceinline__ void block_unit_q8(const DecodeParams& p, int i, int 
         const float x = pf[lane * 8 + h];
         c = x * ab0[1];
         pf[lane * 8 + h] = x * ab0[0];
+        mx = fmaxf(mx, fabsf(x * ab0[0]));
       }
       if (has1) {
         const float x = pf[(lane + 64) * 8 + h];
         c = fmaf(x, ab1[1], c);
         pf[(lane + 64) * 8 + h] = x * ab1[0];
+        mx = fmaxf(mx, fabsf(x * ab1[0]));
       }
       C[h] = wave_sum(c);
     }
+    mx = wave_max(mx);
   }
-  float* zs = reinterpret_cast<float*>(lds + 1024);
+  // (a', b') of the value rows to LDS (the projection's q staging area is free now)
+  if (2 * lane < rv) *reinterpret_cast<f32x4_t*>(abv + 4 * lane) = abv_v;
+  wave_lds_fence();
+  // sc = 2^(13 - e) with mx < 2^e: the largest |p' sc| stays below 2^13
+  const int ex = mx > 0.f ? min(max(ilogbf(mx) + 1, -100), 100) : 0;
+  const float sc = ldexpf(1.f, 13 - ex), inv_sc = ldexpf(1.f, ex - 13);
+  float Cl = C[0];
+#pragma unroll
+  for (int h = 1; h < G; ++h) Cl = (u.col == h) ? C[h] : Cl;
+  if (u.col >= G) Cl = 0.f;
 
-  float m_run[G], l_run[G], o[G][JPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m_run[h] = kNegInf;
-    l_run[h] = 0.f;
-#pragma unroll
-    for (int jj = 0; jj < JPL; ++jj) o[h][jj] = 0.f;
-  }
+  float m_run = kNegInf, l_run = 0.f;
+  if (small)
+    q8_body<1, 4, 2, G>(u, pf, abv, zs, Cl, sc, inv_sc, m_run, l_run);
+  else
+    q8_body<2, 8, 1, G>(u, pf, abv, zs, Cl, sc, inv_sc, m_run, l_run);
   wave_lds_fence();
 
-  q8_tiles<D, G>(Uc, Upc, Wp, sbv, ld, T, r, rv, pf, C, m_run, l_run, o, zs, lane);
+  // ---- o~ = z W', W' rows in groups of 32, the next group loading while
+  // the current one is applied
+  float o[G][JPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int jj = 0; jj < JPL; ++jj) o[h][jj] = 0.f;
+  constexpr int kWRows = 32;
+  auto load_w = [&](int k0, uint32_t (&wr)[kWRows]) {
+#pragma unroll
+    for (int j = 0; j < kWRows; ++j) {
+      const uint16_t* wrow = Wp + (size_t)min(k0 + j, rv - 1) * D;
+      wr[j] = (JPL == 2) ? *reinterpret_cast<const uint32_t*>(wrow + 2 * lane) : (uint32_t)wrow[lane] << 16;
+    }
+  };
+  uint32_t wa[kWRows], wb[kWRows];
+  auto apply_w = [&](int k0, const uint32_t (&wr)[kWRows]) {
+#pragma unroll
+    for (int j = 0; j < kWRows; ++j) {
+      if (k0 + j < rv) {
+        const f32x4_t z0 = *reinterpret_cast<const f32x4_t*>(zs + (k0 + j) * 8);
+        const f32x4_t z1 = *reinterpret_cast<const f32x4_t*>(zs + (k0 + j) * 8 + 4);
+        const float zz[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
+        const float wv[2] = {bf_lo(wr[j]), bf_hi(wr[j])};
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int jj = 0; jj < JPL; ++jj) o[h][jj] = fmaf(zz[h], wv[JPL == 2 ? jj : 1], o[h][jj]);
+      }
+    }
+  };
+  if (rv > 0) load_w(0, wa);
+  for (int k0 = 0; k0 < rv; k0 += 2 * kWRows) {
+    if (k0 + kWRows < rv) load_w(k0 + kWRows, wb);
+    apply_w(k0, wa);
+    if (k0 + 2 * kWRows < rv) load_w(k0 + 2 * kWRows, wa);
+    if (k0 + kWRows < rv) apply_w(k0 + kWRows, wb);
+  }
 
   float* po = p.part.o + (size_t)unit * G * D;
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int jj = 0; jj < JPL; ++jj) po[h * D + lane * JPL + jj] = o[h][jj];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-    if (lane == h) {
-      p.part.ml[((size_t)unit * G + h) * 2 + 0] = m_run[h];
-      p.part.ml[((size_t)unit * G + h) * 2 + 1] = l_run[h];
-    }
+  if (lane < G) {
+    p.part.ml[((size_t)unit * G + lane) * 2 + 0] = m_run;
+    p.part.ml[((size_t)unit * G + lane) * 2 + 1] = l_run;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -905,8 +1118,7 @@ __device__ __forceinline__ void tail_unit(const DecodeParams& p, int i, int g, i
 }
 
 template <int D, int G, int DT>
-__global__ __launch_bounds__(64) void milo_decode_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
+__device__ __forceinline__ void decode_wave(const DecodeParams& p, uint32_t* lds) {
   const int S = p.max_blocks + 1;
   const int unit = p.unit_order ? p.unit_order[blockIdx.x] : (int)blockIdx.x;
   if ((unsigned)unit >= (unsigned)(p.batch * p.n_kv_heads * S)) return;   // not a unit index
@@ -929,14 +1141,36 @@ __global__ __launch_bounds__(64) void milo_decode_kernel(DecodeParams p) {
     block_unit_f32<D, G>(p, i, g, unit, blk, lds);
 }
 
+template <int D, int G, int DT>
+__global__ __launch_bounds__(64) void milo_decode_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
+  decode_wave<D, G, DT>(p, lds);
+}
+
+// The 8-bit kernel holds two chunks of code loads in flight; its register
+// budget is set to two waves per SIMD (the allocator fits it without spills).
+template <int D, int G>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void milo_decode_q8_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
+  decode_wave<D, G, MILO_BF16_Q8>(p, lds);
+}
+
+template <int D, int G, int DT>
+void launch_decode_g(const DecodeParams& p, dim3 grid, hipStream_t s) {
+  if constexpr (DT == MILO_BF16_Q8)
+    hipLaunchKernelGGL((milo_decode_q8_kernel<D, G>), grid, dim3(64), 0, s, p);
+  else
+    hipLaunchKernelGGL((milo_decode_kernel<D, G, DT>), grid, dim3(64), 0, s, p);
+}
+
 template <int D, int DT>
 hipError_t launch_decode_dg(const DecodeParams& p, int group, hipStream_t s) {
   const int64_t units = decode_units(p.batch, p.n_kv_heads, p.max_blocks);
   if (units == 0) return hipSuccess;
-  const dim3 grid((unsigned)units), block(64);
+  const dim3 grid((unsigned)units);
   switch (group) {
 #define MILO_G(GG) \
-  case GG: hipLaunchKernelGGL((milo_decode_kernel<D, GG, DT>), grid, block, 0, s, p); break;
+  case GG: launch_decode_g<D, GG, DT>(p, grid, s); break;
     MILO_G(1) MILO_G(2) MILO_G(3) MILO_G(4) MILO_G(5) MILO_G(6) MILO_G(7) MILO_G(8)
 #undef MILO_G
     default: return hipErrorInvalidValue;

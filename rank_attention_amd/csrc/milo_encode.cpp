@@ -186,7 +186,9 @@ milo_status milo_quant_layout(const milo_block* src_blocks, int32_t n_blocks, in
     blocks_out[b].ld_tok = ld;
     blocks_out[b].rank_k = s.rank_k;
     blocks_out[b].rank_v = s.rank_v;
-    off += (int64_t)n_kv_heads * (rows * ((int64_t)ld + 2 * head_dim) + (8 * rows + 15) / 16 * 16);
+    const int64_t rk16 = ((int64_t)s.rank_k + 15) / 16 * 16;
+    off += (int64_t)n_kv_heads * ((int64_t)s.n_tok * rk16 + (int64_t)s.rank_v * ld + rows * 2 * head_dim +
+                                  (8 * rows + 15) / 16 * 16);
   }
   *pool_bytes = off;
   return MILO_OK;

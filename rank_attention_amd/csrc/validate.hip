@@ -29,7 +29,9 @@ __global__ __launch_bounds__(kValThreads) void milo_validate_kernel(ValidatePara
     const int64_t rk = min(max(blk.rank_k, 0), d), rv = min(max(blk.rank_v, 0), d);
     const int64_t ld = max(blk.ld_tok, 0);
     // elements of the pool's dtype, or bytes of the 8-bit layout
-    const int64_t size = p.q8 ? (int64_t)p.n_kv_heads * ((rk + rv) * (ld + 2 * d) + ((8 * (rk + rv) + 15) & ~15ll))
+    const int64_t nt = max(blk.n_tok, 0), rk16 = (rk + 15) & ~15ll;
+    const int64_t size = p.q8 ? (int64_t)p.n_kv_heads * (nt * rk16 + rv * ld + (rk + rv) * 2 * d +
+                                                         ((8 * (rk + rv) + 15) & ~15ll))
                               : (int64_t)p.n_kv_heads * (rk + rv) * (ld + d);
     if (blk.off >= 0 && blk.off + size > p.pool_elems) report(p.status, 6, idx);
   }

@@ -41,16 +41,20 @@ def run_q8(wl, repeat=1, plan=True, **packkw):
 
 
 def parse_q8(pool: np.ndarray, desc, n_kv_heads: int, d: int):
-    """Per block and KV head: (codes_k, W bits, codes_v, W' bits, (a, b) rows)
+    """Per block and KV head: (n_tok, key codes [rank_k][n_tok] (stored
+    token-major), W bits, value codes [rank_v][ld_tok], W' bits, (a, b) rows)
     read from the 8-bit pool by the layout the header states."""
     out = []
     for blk in desc:
         off, T, ld, r, rv = (int(blk[k]) for k in ("off", "n_tok", "ld_tok", "rank_k", "rank_v"))
-        head = (r + rv) * (ld + 2 * d) + (8 * (r + rv) + 15) // 16 * 16
+        rk16 = (r + 15) // 16 * 16
+        head = T * rk16 + rv * ld + 2 * (r + rv) * d + (8 * (r + rv) + 15) // 16 * 16
         heads = []
         for g in range(n_kv_heads):
             o = off + g * head
-            ck = pool[o:o + r * ld].reshape(r, ld); o += r * ld
+            ku = pool[o:o + T * rk16].reshape(T, rk16); o += T * rk16
+            assert np.all(ku[:, r:] == 0), "key code padding not 0"
+            ck = np.ascontiguousarray(ku[:, :r].T)
             w = pool[o:o + 2 * r * d].view(np.uint16).reshape(r, d); o += 2 * r * d
             cv = pool[o:o + rv * ld].reshape(rv, ld); o += rv * ld
             wp = pool[o:o + 2 * rv * d].view(np.uint16).reshape(rv, d); o += 2 * rv * d
