@@ -558,7 +558,7 @@ def main(argv=None):
         peak, unit, bound = HBM_PEAK_GBS, "GB/s", "hbm"
         value, vunit, metric = (wl.context_tokens() / (ms_per_step * 1e-3), "context tokens/s",
                                 Q8_METRIC if q8 else METRIC)
-        kname = "milo_decode_kernel"
+        kname = "milo_decode_q8_kernel" if q8 else "milo_decode_kernel"
         print(f"[bench] attention kernel: mean {kmean * 1e3:.1f} us, median "
               f"{kern_sorted[len(kern_sorted) // 2] * 1e3:.1f} us, min {kern_sorted[0] * 1e3:.1f} us; "
               f"step {ms_per_step * 1e3:.1f} us; {achieved:.0f} GB/s on {alg_bytes / 1e6:.1f} MB",
