@@ -566,28 +566,41 @@ __device__ __forceinline__ void q8_chunk_step(Q8Regs& R, const Q8Unit& u, int c,
 }
 
 // The chunk loop: DEPTH chunks in flight, the loads of chunk c + DEPTH going
-// out as chunk c consumes its own.  With rank_k, rank_v >= 1 and at least
-// 2 DEPTH chunks the steady-state loop issues every load unguarded (static
-// counts); the last DEPTH chunks, and units with an empty factor, take the
-// guarded steps.
+// out as chunk c consumes its own (the first DEPTH come from q8_preload).
+// With rank_k, rank_v >= 1 and at least 2 DEPTH chunks the steady-state
+// loop issues every load unguarded (static counts); the last DEPTH chunks,
+// and units with an empty factor, take the guarded steps.
+// The steady-state loop runs when every load is valid and at least 2 DEPTH chunks exist.
+template <int DEPTH>
+__device__ __forceinline__ bool q8_steady(const Q8Unit& u) {
+  return u.npairs > 0 && u.ntv > 0 && (u.T + kQ8Chunk - 1) / kQ8Chunk >= 2 * DEPTH;
+}
+
+// Loads of the first DEPTH chunks (unguarded in the steady case).
 template <int NP, int NTV, int DEPTH>
-__device__ __forceinline__ void q8_chunks(const Q8Unit& u, const u32x4_t (&Bh)[NP][2],
+__device__ __forceinline__ void q8_preload(Q8Regs& R, const Q8Unit& u) {
+  const int nch = (u.T + kQ8Chunk - 1) / kQ8Chunk;
+  if (q8_steady<DEPTH>(u)) {
+    q8_load_chunk<NP, NTV, DEPTH, 0, true>(R, u, 0);
+    if (DEPTH > 1) q8_load_chunk<NP, NTV, DEPTH, DEPTH - 1, true>(R, u, 1);
+  } else {
+    if (nch > 0) q8_load_chunk<NP, NTV, DEPTH, 0, false>(R, u, 0);
+    if (DEPTH > 1 && nch > 1) q8_load_chunk<NP, NTV, DEPTH, DEPTH - 1, false>(R, u, 1);
+  }
+}
+
+template <int NP, int NTV, int DEPTH>
+__device__ __forceinline__ void q8_chunks(Q8Regs& R, const Q8Unit& u, const u32x4_t (&Bh)[NP][2],
                                           const u32x4_t (&Bl)[NP][2], float s0, float inv_sc, float& m_run,
                                           float& l_run, f32x4_t (&Z)[NTV]) {
   const int nch = (u.T + kQ8Chunk - 1) / kQ8Chunk;
-  Q8Regs R;
   int c0 = 0;
-  if (u.npairs > 0 && u.ntv > 0 && nch >= 2 * DEPTH) {
-    q8_load_chunk<NP, NTV, DEPTH, 0, true>(R, u, 0);
-    if (DEPTH > 1) q8_load_chunk<NP, NTV, DEPTH, DEPTH - 1, true>(R, u, 1);
+  if (q8_steady<DEPTH>(u)) {
     for (; c0 + 2 * DEPTH <= nch; c0 += DEPTH) {
       q8_chunk_step<NP, NTV, DEPTH, 0, true>(R, u, c0, true, Bh, Bl, s0, inv_sc, m_run, l_run, Z);
       if (DEPTH > 1)
         q8_chunk_step<NP, NTV, DEPTH, DEPTH - 1, true>(R, u, c0 + 1, true, Bh, Bl, s0, inv_sc, m_run, l_run, Z);
     }
-  } else {
-    if (nch > 0) q8_load_chunk<NP, NTV, DEPTH, 0, false>(R, u, 0);
-    if (DEPTH > 1 && nch > 1) q8_load_chunk<NP, NTV, DEPTH, DEPTH - 1, false>(R, u, 1);
   }
   // the remaining chunks c0 .. nch-1 (fewer than 2 DEPTH); chunks c0 ..
   // c0 + DEPTH - 1 are loaded
@@ -653,6 +666,8 @@ __device__ __forceinline__ void q8_stage_z(const f32x4_t (&Z)[NTV], const Q8Unit
 template <int NP, int NTV, int DEPTH, int G>
 __device__ __forceinline__ void q8_body(const Q8Unit& u, const float* pf, const float* abv, float* zs, float Cl,
                                         float sc, float inv_sc, float& m_run, float& l_run) {
+  Q8Regs R;
+  q8_preload<NP, NTV, DEPTH>(R, u);
   u32x4_t Bh[NP][2], Bl[NP][2];
   const float psum = q8_b_operands<NP, G>(pf, u.r, sc, u.quad, u.col, Bh, Bl);
   // the centred codes add -128 sum p' sc to sc * (s - C): start the sum at sc C + that
@@ -660,7 +675,7 @@ __device__ __forceinline__ void q8_body(const Q8Unit& u, const float* pf, const 
   f32x4_t Z[NTV];
 #pragma unroll
   for (int kt = 0; kt < NTV; ++kt) Z[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  q8_chunks<NP, NTV, DEPTH>(u, Bh, Bl, s0, inv_sc, m_run, l_run, Z);
+  q8_chunks<NP, NTV, DEPTH>(R, u, Bh, Bl, s0, inv_sc, m_run, l_run, Z);
   l_run = col_sum(l_run);
   q8_stage_z<NTV, G>(Z, u, abv, l_run, zs);
 }
