@@ -94,15 +94,17 @@ typedef enum milo_path {
  *     element = a_k * c + b_k.
  * The keys' codes are stored token-major (U, one row of rank_k codes per
  * token, padded to rk16 = rank_k rounded up to 16), the values' rank-major
- * (U'^T), the orders in which the decode kernel's matrix-core operands
- * take them.  Offsets and strides count BYTES: off and ld_tok are multiples
- * of 16, and KV head g starts at byte off + g * H with
+ * (U'^T) in tiles of 64 tokens, the orders in which the decode kernel's
+ * matrix-core operands take them.  Offsets and strides count BYTES: off is
+ * a multiple of 16, ld_tok = n_tok rounded up to 64, and KV head g starts
+ * at byte off + g * H with
  *     H = n_tok * rk16 + rank_v * ld_tok + 2 * (rank_k + rank_v) * head_dim
  *         + pad16(8 * (rank_k + rank_v)),
  * pad16(x) = x rounded up to a multiple of 16.  Per head, back to back:
  *     U codes     [n_tok][rk16]         uint8 (codes rank_k.. of a row: padding)
  *     W           [rank_k][head_dim]    bf16
- *     U'^T codes  [rank_v][ld_tok]      uint8 (codes n_tok.. of a row: padding)
+ *     U'^T codes  [ld_tok/64][rank_v][64] uint8: token t of row k at byte
+ *                 64 * (rank_v * (t / 64) + k) + t % 64 (tokens n_tok..: padding)
  *     W'          [rank_v][head_dim]    bf16
  *     (a_k, b_k)  [rank_k + rank_v][2]  fp32, the keys' rows first, then
  *                 padding to the next multiple of 16 bytes.
@@ -113,7 +115,7 @@ typedef struct milo_block {
                        multiple of 16)                                             */
   int32_t n_tok;    /* T_b >= 0                                                    */
   int32_t ld_tok;   /* row stride of U^T and U'^T in elements; >= n_tok, mult. of 8
-                       (Q8: multiple of 16)                                        */
+                       (Q8: multiple of 64, see the layout above)                  */
   int32_t rank_k;   /* r_b  in [0, head_dim]                                       */
   int32_t rank_v;   /* r'_b in [0, head_dim]                                       */
 } milo_block;
@@ -217,7 +219,8 @@ milo_status milo_attn_plan_decode(const milo_block* blocks, const int32_t* seq_b
  * lists are not read by that path).  pool_elems is the pool size in
  * elements.  Host-checkable faults return a status as for the other entry
  * points (status must be 8-byte aligned).  With MILO_BF16_Q8, pool_elems
- * counts bytes, and rules 4 and 5 ask for multiples of 16 instead of 8.
+ * counts bytes, rule 4 asks for ld_tok a multiple of 64 and rule 5 for off a
+ * multiple of 16.
  */
 typedef enum milo_table_rule {
   MILO_TABLE_SEQ_RANGE = 1,        /* seq_blocks[i] < 0, decreasing, or past n_descriptors        */

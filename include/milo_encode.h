@@ -155,9 +155,8 @@ typedef struct milo_quant_args {
 } milo_quant_args;
 
 /* Host-side layout of the MILO_BF16_Q8 pool for the blocks src_blocks
- * (HOST array): the same n_tok and ranks, ld_tok = n_tok rounded up to 16
- * (the value codes' row stride), blocks back to back from byte 0 in the
- * given order.  blocks_out (host)
+ * (HOST array): the same n_tok and ranks, ld_tok = n_tok rounded up to 64,
+ * blocks back to back from byte 0 in the given order.  blocks_out (host)
  * receives n_blocks descriptors and *pool_bytes the pool size.
  * MILO_ERR_INVALID on null pointers, negative sizes or ranks outside
  * [0, head_dim]. */

@@ -27,6 +27,12 @@
 // flight at once (one memory round trip).  A unit is one wave, so LDS
 // hand-offs between its lanes need no barrier (a barrier would also wait
 // for every load in flight).
+//
+// That is the path of bf16 and fp32 storage.  With 8-bit token factors
+// (MILO_BF16_Q8) the same work units run the scores and the value side on
+// the matrix cores instead (block_unit_q8 and milo_decode_q8_kernel below):
+// the codes are exact fp16 operands, so the vector ALUs are left with the
+// softmax and o~ += z W'.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -343,7 +349,8 @@ __device__ __forceinline__ void block_unit_bf16(const DecodeParams& p, int i, in
 // ---------------------------------------------------------------------------
 // 8-bit token factors (MILO_BF16_Q8), on the matrix cores.  Row k of U^T /
 // U'^T holds codes c with x = a_k c + b_k; the keys' codes are stored token-
-// major ([n_tok][rank_k rounded up to 16]), the values' rank-major.  Folded
+// major ([n_tok][rank_k rounded up to 16]), the values' rank-major in tiles
+// of 64 tokens ([n_tok / 64][rank_v][64]).  Folded
 // into the absorbed order:
 //   s_t = sum_k p_k x_kt  = sum_k (p_k a_k) c_kt + C,   C = sum_k p_k b_k
 //   z_k = sum_t e_t x'_kt = a'_k sum_t e_t c'_kt + b'_k E,   E = sum_t e_t
@@ -445,7 +452,7 @@ typedef u32x4_t Q8Regs[kQ8Regs];
 // Geometry of one unit's 8-bit factors (KV head g of one block).
 struct Q8Unit {
   const uint8_t* Uk;   // key codes, token-major [T][rk16]
-  const uint8_t* Uv;   // value codes, rank-major [rv][ld]
+  const uint8_t* Uv;   // value codes, rank-major in 64-token tiles [ld / 64][rv][64]
   int T, ld, r, rv, rk16, npairs, ntv, quad, col;
 };
 
@@ -454,8 +461,7 @@ struct Q8Unit {
 // so with rank_k, rank_v >= 1 every load is valid and ALL may be issued:
 // unguarded (ALL = true), the loop's load counts are static and each wait
 // covers only the loads it needs.  The loads are cached (not non-temporal):
-// a chunk reads 64 bytes of each value row and the next chunk the rest of
-// the 128-byte line, which must still be there.
+// a chunk's key rows are read by its four score tiles in turn.
 template <int NP, int KB, bool ALL>
 __device__ __forceinline__ void q8_load_keys(Q8Regs& R, const Q8Unit& u, int t0) {
   // key row of score row `col` in tile m: token t0 + 16(col/4) + 4m + col%4
@@ -471,12 +477,13 @@ __device__ __forceinline__ void q8_load_keys(Q8Regs& R, const Q8Unit& u, int t0)
 
 template <int NTV, int VB, bool ALL>
 __device__ __forceinline__ void q8_load_values(Q8Regs& R, const Q8Unit& u, int t0) {
-  // tokens t0 + 16 quad .. + 15 of rank row 16 kt + col (a chunk past the
-  // padded row end reads the chunk start instead: its tokens have e = 0)
-  const int tv = t0 + 16 * u.quad < u.ld ? t0 + 16 * u.quad : t0;
+  // tokens t0 + 16 quad .. + 15 of rank row 16 kt + col: the value codes are
+  // stored in 64-token tiles [ld / 64][rv][64], so one load instruction
+  // reads 16 rows x 64 contiguous bytes
+  const uint8_t* tile = u.Uv + (size_t)t0 * u.rv + 16 * u.quad;
 #pragma unroll
   for (int kt = 0; kt < NTV; ++kt)
-    if (ALL || kt < u.ntv) R[VB + kt] = ld16(u.Uv + (size_t)min(16 * kt + u.col, u.rv - 1) * u.ld + tv);
+    if (ALL || kt < u.ntv) R[VB + kt] = ld16(tile + (size_t)min(16 * kt + u.col, u.rv - 1) * 64);
 }
 
 // Scores of one chunk (consumes its key loads): S[m][v] for token t0 + 16 quad + 4m + v.

@@ -177,9 +177,9 @@ milo_status milo_quant_layout(const milo_block* src_blocks, int32_t n_blocks, in
   int64_t off = 0;
   for (int32_t b = 0; b < n_blocks; ++b) {
     const milo_block& s = src_blocks[b];
-    if (s.n_tok < 0 || s.n_tok > INT32_MAX - 15) return MILO_ERR_INVALID;
+    if (s.n_tok < 0 || s.n_tok > INT32_MAX - 63) return MILO_ERR_INVALID;
     if (s.rank_k < 0 || s.rank_k > head_dim || s.rank_v < 0 || s.rank_v > head_dim) return MILO_ERR_INVALID;
-    const int32_t ld = (s.n_tok + 15) / 16 * 16;
+    const int32_t ld = (s.n_tok + 63) / 64 * 64;
     const int64_t rows = (int64_t)s.rank_k + s.rank_v;
     blocks_out[b].off = off;
     blocks_out[b].n_tok = s.n_tok;

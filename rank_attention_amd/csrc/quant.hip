@@ -11,9 +11,9 @@
 //
 // One 256-thread workgroup per (block, KV head): wave w takes rows w, w+4,
 // ... of the head's rank_k + rank_v token-factor rows (min and max are wave
-// reductions) and writes the value rows' codes rank-major, four per lane and
-// step; then the workgroup writes the key codes token-major, one dword of
-// four ranks per thread.
+// reductions) and writes the value rows' codes (rank-major in 64-token
+// tiles), four per lane and step; then the workgroup writes the key codes
+// token-major, one dword of four ranks per thread.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -71,13 +71,14 @@ __global__ __launch_bounds__(kQuantThreads) void milo_quantize_kernel(QuantParam
     if (row < r) {
       if (lane == 0) { lo_s[row] = lo; a_s[row] = a; }
     } else {
-      uint8_t* dst = dUp + (size_t)(row - r) * ldd;
+      // tiles of 64 tokens: token t of value row k at 64 (rv (t / 64) + k) + t % 64
+      uint8_t* dst = dUp + (size_t)(row - r) * 64;
       for (int t0 = lane * 4; t0 < ldd; t0 += 256) {
         uint32_t word = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (t0 + e < T) word |= quant_code(__uint_as_float((uint32_t)src[t0 + e] << 16), lo, a) << (8 * e);
-        *reinterpret_cast<uint32_t*>(dst + t0) = word;
+        *reinterpret_cast<uint32_t*>(dst + (size_t)(t0 >> 6) * rv * 64 + (t0 & 63)) = word;
       }
     }
     if (lane == 0) {

@@ -23,9 +23,9 @@ __global__ __launch_bounds__(kValThreads) void milo_validate_kernel(ValidatePara
     const milo_block blk = p.blocks[idx];
     const int d = p.head_dim;
     if (blk.rank_k < 0 || blk.rank_k > d || blk.rank_v < 0 || blk.rank_v > d) report(p.status, 3, idx);
-    const int align = p.q8 ? 15 : 7;
-    if (blk.n_tok < 0 || blk.ld_tok < blk.n_tok || (blk.ld_tok & align) != 0) report(p.status, 4, idx);
-    if (blk.off < 0 || (blk.off & align) != 0) report(p.status, 5, idx);
+    const int ld_align = p.q8 ? 63 : 7, off_align = p.q8 ? 15 : 7;
+    if (blk.n_tok < 0 || blk.ld_tok < blk.n_tok || (blk.ld_tok & ld_align) != 0) report(p.status, 4, idx);
+    if (blk.off < 0 || (blk.off & off_align) != 0) report(p.status, 5, idx);
     const int64_t rk = min(max(blk.rank_k, 0), d), rv = min(max(blk.rank_v, 0), d);
     const int64_t ld = max(blk.ld_tok, 0);
     // elements of the pool's dtype, or bytes of the 8-bit layout

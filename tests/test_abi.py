@@ -324,11 +324,11 @@ def test_quant_layout():
     src["n_tok"], src["rank_k"], src["rank_v"] = [37, 1024, 0], [5, 128, 0], [3, 1, 7]
     src["off"], src["ld_tok"] = [8, 1000, 5000], [40, 1024, 0]       # the source's placement is irrelevant
     blocks, nbytes = enc.quant_layout(src, n_kv_heads=2, head_dim=128)
-    assert list(blocks["ld_tok"]) == [48, 1024, 0]
+    assert list(blocks["ld_tok"]) == [64, 1024, 0]
     assert list(blocks["n_tok"]) == [37, 1024, 0] and list(blocks["rank_k"]) == [5, 128, 0]
     # per head: n_tok * rk16 key codes, rank_v * ld value codes, bf16 W and W', then 8 bytes of
     # (a, b) per row padded to 16
-    h0 = 37 * 16 + 3 * 48 + 8 * 256 + 64
+    h0 = 37 * 16 + 3 * 64 + 8 * 256 + 64
     h1 = 1024 * 128 + 1 * 1024 + 129 * 256 + (8 * 129 + 15) // 16 * 16
     h2 = 0 * 0 + 7 * 0 + 7 * 256 + 64
     assert list(blocks["off"]) == [0, 2 * h0, 2 * h0 + 2 * h1]

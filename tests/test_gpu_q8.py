@@ -42,8 +42,9 @@ def run_q8(wl, repeat=1, plan=True, **packkw):
 
 def parse_q8(pool: np.ndarray, desc, n_kv_heads: int, d: int):
     """Per block and KV head: (n_tok, key codes [rank_k][n_tok] (stored
-    token-major), W bits, value codes [rank_v][ld_tok], W' bits, (a, b) rows)
-    read from the 8-bit pool by the layout the header states."""
+    token-major), W bits, value codes [rank_v][ld_tok] (stored in 64-token
+    tiles), W' bits, (a, b) rows) read from the 8-bit pool by the layout the
+    header states."""
     out = []
     for blk in desc:
         off, T, ld, r, rv = (int(blk[k]) for k in ("off", "n_tok", "ld_tok", "rank_k", "rank_v"))
@@ -56,7 +57,8 @@ def parse_q8(pool: np.ndarray, desc, n_kv_heads: int, d: int):
             assert np.all(ku[:, r:] == 0), "key code padding not 0"
             ck = np.ascontiguousarray(ku[:, :r].T)
             w = pool[o:o + 2 * r * d].view(np.uint16).reshape(r, d); o += 2 * r * d
-            cv = pool[o:o + rv * ld].reshape(rv, ld); o += rv * ld
+            # value codes in 64-token tiles [ld / 64][rv][64]
+            cv = pool[o:o + rv * ld].reshape(ld // 64, rv, 64).transpose(1, 0, 2).reshape(rv, ld); o += rv * ld
             wp = pool[o:o + 2 * rv * d].view(np.uint16).reshape(rv, d); o += 2 * rv * d
             sb = pool[o:o + 8 * (r + rv)].view(np.float32).reshape(r + rv, 2)
             heads.append((T, ck, w, cv, wp, sb))
