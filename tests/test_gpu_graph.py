@@ -81,3 +81,10 @@ def test_shared_graph_replays():
     wl.blocks = [wl.blocks[0] for _ in range(wl.batch)]
     _capture_and_replay(ra.DeviceCache(ra.pack(wl), scale=wl.scale), ra.MILO_PATH_SHARED,
                         "milo_attn_decode_shared")
+
+
+def test_q8_decode_graph_replays():
+    cfg = synth.get_config("qwen7b_64k").with_(batch=3, n_blocks=6)
+    wl = synth.make_workload(cfg, variant="sharp", n_blocks=[6, 2, 5], tail_len=[256, 3, 0])
+    qc = ra.DeviceCache(ra.pack(wl), scale=wl.scale).quantized()
+    _capture_and_replay(qc, ra.MILO_PATH_DECODE, "milo_attn_decode")
