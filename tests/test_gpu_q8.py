@@ -128,6 +128,17 @@ def test_decode_q8_qwen7b_64k_sampled(variant):
     compare(out[seqs], lse[seqs], ref_o, ref_l, sharp_gates=(variant == "sharp"), name=f"q8 qwen7b_64k/{variant}")
 
 
+def test_decode_q8_qwen7b_128k_sampled():
+    """The largest workload (bimodal ranks: both rank classes of the kernel);
+    the oracle on two whole sequences."""
+    cfg = synth.get_config("qwen7b_128k")
+    wl = synth.make_workload(cfg, variant="sharp")
+    out, lse = run_q8(wl)
+    seqs = [0, 17]
+    ref_o, ref_l = quant.attend_q8(wl, seq_index=seqs)
+    compare(out[seqs], lse[seqs], ref_o, ref_l, sharp_gates=True, name="q8 qwen7b_128k/sharp")
+
+
 RAGGED = [(128, 7, 1), (128, 8, 1), (128, 10, 2), (64, 12, 4), (64, 3, 3), (128, 12, 2), (128, 6, 2),
           (64, 14, 2), (128, 4, 2), (64, 16, 2), (64, 8, 2)]
 
