@@ -23,8 +23,9 @@
 //     reduced; the group's W' rows load with its U'^T rows, so no memory
 //     round trip is left after the last group.
 // The U^T and U'^T streams are read once and wave-coalesced, so they are
-// loaded non-temporally.  W is read lane-per-row, all of the unit's rows in
-// flight at once (one memory round trip).  A unit is one wave, so LDS
+// loaded non-temporally.  The projection p = W q (bf16 storage) runs on the
+// matrix cores with all of the unit's W loads in flight at once (one memory
+// round trip).  A unit is one wave, so LDS
 // hand-offs between its lanes need no barrier (a barrier would also wait
 // for every load in flight).
 //
@@ -62,57 +63,48 @@ struct Shape {
 // is needed.
 __device__ __forceinline__ void wave_lds_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
 
-// p = scale*log2(e) * W q for the G heads, fp32; lane k owns rows k and k+64
-// (the second only when r > 64).  q is staged in LDS (ql) and read back as
-// broadcasts; every W load of the lane is issued before the first product,
-// so the projection costs one memory round trip.  q and W are bf16, so the
-// dot2 products are exact.  Rows are clamped to r-1; rows >= r are never
-// read from pf.  Requires r >= 1.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4_t mfma_bf16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+
+// p = scale*log2(e) * W q for the G heads (fp32) on the matrix cores: P^T
+// (16 ranks x 16 heads) per tile of 16 rows of W, K = head_dim in steps of
+// 32 (exact bf16 products, fp32 sums).  Lane l loads 8 dims 32s + 8(l/16) .. +7 of W row 16t + l%16
+// (clamped to r-1) and of q head l%16 (zero for l%16 >= G); the result
+// holds ranks 16t + 4(l/16) + v of head l%16, written to pf[rank*8 + head]
+// for heads < G.  Every W load of the unit is issued first (one round
+// trip).  Rows >= r of pf are not meaningful.  Requires r >= 1.
 template <int D, int G>
-__device__ __forceinline__ void bf16_project_q(const uint16_t* W, const uint16_t* qh, int r,
-                                               float scale_log2, float* pf, uint16_t* ql, int lane) {
-  constexpr int NC = D / 8, NQ = G * NC;   // 16-byte chunks per row; q chunks of the group
-  u32x4_t q0 = {0u, 0u, 0u, 0u}, q1 = {0u, 0u, 0u, 0u};
-  if (lane < NQ) q0 = ld16(qh + lane * 8);
-  if (lane + 64 < NQ) q1 = ld16(qh + (lane + 64) * 8);
-  const bool two = D > 64 && r > 64;
-  u32x4_t wa[NC], wb[NC];
-  const uint16_t* wa_row = W + (size_t)min(lane, r - 1) * D;
-  const uint16_t* wb_row = W + (size_t)min(lane + 64, r - 1) * D;
+__device__ __forceinline__ void mfma_project_q(const uint16_t* W, const uint16_t* qh, int r, float scale_log2,
+                                               float* pf, int lane) {
+  constexpr int KS = D / 32, MT = D / 16;   // K steps; rank tiles for r <= D
+  const int quad = lane >> 4, col = lane & 15;
+  const int nt = (r + 15) >> 4;
+  u32x4_t qb[KS], wt[MT][KS];
 #pragma unroll
-  for (int jc = 0; jc < NC; ++jc) wa[jc] = ld16(wa_row + jc * 8);
-  if (two) {
+  for (int t = 0; t < MT; ++t)
+    if (t < nt) {
+      const uint16_t* row = W + (size_t)min(16 * t + col, r - 1) * D + 8 * quad;
 #pragma unroll
-    for (int jc = 0; jc < NC; ++jc) wb[jc] = ld16(wb_row + jc * 8);
-  }
-  if (lane < NQ) *reinterpret_cast<u32x4_t*>(ql + lane * 8) = q0;
-  if (lane + 64 < NQ) *reinterpret_cast<u32x4_t*>(ql + (lane + 64) * 8) = q1;
-  wave_lds_fence();
-  float pa[G], pb[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) { pa[h] = 0.f; pb[h] = 0.f; }
-#pragma unroll
-  for (int jc = 0; jc < NC; ++jc)
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const u32x4_t qv = *reinterpret_cast<const u32x4_t*>(ql + h * D + jc * 8);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) pa[h] = dot2bf(wa[jc][w], qv[w], pa[h]);
+      for (int k = 0; k < KS; ++k) wt[t][k] = ld16(row + 32 * k);
     }
 #pragma unroll
-  for (int h = 0; h < G; ++h) pf[lane * 8 + h] = pa[h] * scale_log2;
-  if (two) {
+  for (int k = 0; k < KS; ++k)
+    qb[k] = col < G ? ld16(qh + (size_t)col * D + 32 * k + 8 * quad) : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int jc = 0; jc < NC; ++jc)
+  for (int t = 0; t < MT; ++t)
+    if (t < nt) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const u32x4_t qv = *reinterpret_cast<const u32x4_t*>(ql + h * D + jc * 8);
+      for (int k = 0; k < KS; ++k) acc = mfma_bf16(wt[t][k], qb[k], acc);
+      if (col < G) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) pb[h] = dot2bf(wb[jc][w], qv[w], pb[h]);
+        for (int v = 0; v < 4; ++v) pf[(16 * t + 4 * quad + v) * 8 + col] = acc[v] * scale_log2;
       }
-#pragma unroll
-    for (int h = 0; h < G; ++h) pf[(lane + 64) * 8 + h] = pb[h] * scale_log2;
-  }
+    }
 }
 
 constexpr int kRowsPerStep = 4;   // U^T rows per prefetch step of the score loop
@@ -314,7 +306,7 @@ __device__ __forceinline__ void block_unit_bf16(const DecodeParams& p, int i, in
   const uint16_t* qh = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)i * p.n_q_heads + g * G) * D;
 
   float* pf = reinterpret_cast<float*>(lds);
-  if (r > 0) bf16_project_q<D, G>(W, qh, r, p.scale_log2, pf, reinterpret_cast<uint16_t*>(lds + 2048), lane);
+  if (r > 0) mfma_project_q<D, G>(W, qh, r, p.scale_log2, pf, lane);
   // z of one row group, staged for broadcast reads: zs[rho*8 + h]
   float* zs = reinterpret_cast<float*>(lds + 1024);
 
@@ -730,7 +722,7 @@ __device__ __forceinline__ void block_unit_q8(const DecodeParams& p, int i, int 
     const f32x2_t ab0 = *reinterpret_cast<const f32x2_t*>(sbk + 2 * min(lane, r - 1));
     f32x2_t ab1 = {0.f, 0.f};
     if (D > 64) ab1 = *reinterpret_cast<const f32x2_t*>(sbk + 2 * min(lane + 64, r - 1));
-    bf16_project_q<D, G>(W, qh, r, p.scale_log2, pf, reinterpret_cast<uint16_t*>(lds + 2048), lane);
+    mfma_project_q<D, G>(W, qh, r, p.scale_log2, pf, lane);
     wave_lds_fence();
     const bool has0 = lane < r, has1 = D > 64 && lane + 64 < r;
 #pragma unroll
