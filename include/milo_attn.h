@@ -198,7 +198,11 @@ milo_status milo_attn_decode_shared(const milo_attn_args* args, void* hip_stream
  * tails (longest first), then block units (largest first), then empty slots
  * and empty tails; ties in natural order.  The cache is static across
  * decode steps, so the plan is computed once and copied to the device.
- * Returns MILO_ERR_INVALID on null pointers or negative sizes.
+ * For sequence i it reads blocks[seq_blocks[i] .. seq_blocks[i] +
+ * min(seq_blocks[i+1] - seq_blocks[i], max_blocks_per_seq)).
+ * Returns MILO_ERR_INVALID on null pointers, negative sizes or a sequence
+ * with seq_blocks[i] < 0 or seq_blocks[i+1] < seq_blocks[i];
+ * MILO_ERR_UNSUPPORTED when the unit count exceeds INT32_MAX.
  */
 milo_status milo_attn_plan_decode(const milo_block* blocks, const int32_t* seq_blocks,
                                   const int32_t* tail_len, int32_t batch, int32_t n_kv_heads,

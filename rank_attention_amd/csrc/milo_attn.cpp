@@ -349,6 +349,10 @@ milo_status milo_attn_plan_decode(const milo_block* blocks, const int32_t* seq_b
   if (batch > 0 && max_blocks > 0 && !blocks) return MILO_ERR_INVALID;
   const int64_t slots = (int64_t)max_blocks + 1;
   const int64_t units = (int64_t)batch * n_kv_heads * slots;
+  if (units > INT32_MAX) return MILO_ERR_UNSUPPORTED;   // unit indices are 32-bit
+  // the host tables are read here, so their ranges are checked first
+  for (int32_t i = 0; i < batch; ++i)
+    if (seq_blocks[i] < 0 || seq_blocks[i + 1] < seq_blocks[i]) return MILO_ERR_INVALID;
   // rank 0: dense-tail units (few, and per byte the slowest, so they go
   // first and never finish last); rank 1: block units, largest first;
   // rank 2: empty slots and empty tails
@@ -356,7 +360,7 @@ milo_status milo_attn_plan_decode(const milo_block* blocks, const int32_t* seq_b
   std::vector<int8_t> rank((size_t)units, 2);
   for (int32_t i = 0; i < batch; ++i) {
     const int32_t b0 = seq_blocks[i];
-    const int32_t nb = std::min(std::max(seq_blocks[i + 1] - b0, 0), max_blocks);
+    const int32_t nb = std::min(seq_blocks[i + 1] - b0, max_blocks);
     for (int32_t g = 0; g < n_kv_heads; ++g) {
       const int64_t base = ((int64_t)i * n_kv_heads + g) * slots;
       for (int32_t s = 0; s < nb; ++s) {

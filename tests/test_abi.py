@@ -182,6 +182,14 @@ def test_plan_rejects_bad_arguments():
     assert lib.milo_attn_plan_decode(None, sb, None, 1, 0, 0, 64, out) == _lib.MILO_ERR_INVALID
     assert lib.milo_attn_plan_decode(None, sb, None, 1, 1, 0, 64, out) == _lib.MILO_OK
     assert out[0] == 0
+    # a negative or decreasing block range is refused before any descriptor is read
+    blk = (_lib.MiloBlock * 2)()
+    for bad in ((-1, 1), (1, 0)):
+        sb2 = (ctypes.c_int32 * 2)(*bad)
+        assert lib.milo_attn_plan_decode(blk, sb2, None, 1, 1, 2, 64, out) == _lib.MILO_ERR_INVALID
+    # unit indices are 32-bit
+    big = (ctypes.c_int32 * 2)(0, 0)
+    assert lib.milo_attn_plan_decode(blk, big, None, 1, 1 << 16, 1 << 16, 64, out) == _lib.MILO_ERR_UNSUPPORTED
 
 
 # --------------------------------------------------------------------------
