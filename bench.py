@@ -332,13 +332,15 @@ def cpu_baseline_chunk(wl, seconds: float):
 
 
 def cpu_baseline(wl, seconds: float, q8: bool = False):
-    """fp64 oracle on whole sequences of the same workload until `seconds` pass
-    (q8: the oracle's 8-bit quantisation of the token factors, then attention
-    over the dequantized factors, both timed)."""
+    """fp64 oracle on whole sequences of the same workload, in order and again
+    from the first when the batch is done, until `seconds` pass (q8: the
+    oracle's 8-bit quantisation of the token factors, then attention over the
+    dequantized factors, both timed)."""
     import oracle
     from oracle import quant
     toks, elapsed, done = 0, 0.0, 0
-    for i in range(wl.batch):
+    while wl.batch > 0 and elapsed < seconds:
+        i = done % wl.batch
         q, blocks, kt, vt, tl = oracle.logical_from_workload(wl, [i])
         t0 = time.perf_counter()
         if q8:
@@ -347,13 +349,11 @@ def cpu_baseline(wl, seconds: float, q8: bool = False):
         elapsed += time.perf_counter() - t0
         toks += sum(b.n_tok for b in wl.blocks[i]) + int(wl.tail_len[i])
         done += 1
-        if elapsed >= seconds:
-            break
     return {"value": toks / elapsed, "unit": "context tokens/s", "cores": oracle.threads(),
             "kind": "oracle", "cpu": cpu_model(),
-            "sample": f"{done} of {wl.batch} sequences ({toks} context tokens, all {wl.cfg.n_q_heads} "
-                      f"query heads), {'fp32 8-bit quantisation, ' if q8 else ''}fp64 "
-                      f"reconstruct-then-attend, {elapsed:.1f} s"}
+            "sample": f"{done} sequence evaluations over the {wl.batch} of the workload ({toks} context "
+                      f"tokens, all {wl.cfg.n_q_heads} query heads), {'fp32 8-bit quantisation, ' if q8 else ''}"
+                      f"fp64 reconstruct-then-attend, {elapsed:.1f} s"}
 
 
 def main(argv=None):
