@@ -6,7 +6,7 @@
 // The softmax over the union of the units' tokens is then
 //   M = max_u m_u,  l = sum_u l_u 2^(m_u - M),  out = sum_u o~_u 2^(m_u - M) / l,
 //   lse = (M + log2 l) ln 2.
-// Each query row is folded by four waves with that running rescale.
+// Each query row is folded by one to eight waves with that running rescale.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -16,18 +16,20 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
-constexpr int kMergeWaves = 4;   // waves per query row
-constexpr int kMergeBatch = 8;   // slots whose loads one wave issues together
+constexpr int kMergeBatch = 9;   // slots whose loads one wave issues together
 
-// One workgroup of four waves per query row.  Wave w folds the slots
-// s = w, w+4, ... into a running (M, l, o) in batches of eight slots, all of
-// whose loads are issued before any is used; the four waves' results are
-// then combined through LDS.
-template <int D>
-__global__ __launch_bounds__(64 * kMergeWaves) void milo_merge_kernel(MergeParams p) {
+// One workgroup of W waves per query row.  Wave w folds the slots s = w,
+// w+W, ... into a running (M, l, o) in batches of nine slots, all of whose
+// loads are issued before any is used; the waves' results are then combined
+// through LDS.  The launcher picks the fewest waves that cover the slots in
+// one batch each (at most eight), so every load of a row is in flight at once
+// for up to 72 slots and no wave of a short row idles.
+template <int D, int W>
+__global__ __launch_bounds__(64 * W) void milo_merge_kernel(MergeParams p) {
+  constexpr int kMergeWaves = W;
   constexpr int JPL = D / 64;
   __shared__ float sh_m[kMergeWaves], sh_l[kMergeWaves];
-  __shared__ __attribute__((aligned(16))) float sh_o[kMergeWaves][D];
+  __shared__ __attribute__((aligned(16))) float sh_o[kMergeWaves][D];   // unused when W = 1
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.x;  // (i * q_len + j) * n_q_heads + h
   const int h = row % p.n_q_heads;
@@ -73,24 +75,30 @@ __global__ __launch_bounds__(64 * kMergeWaves) void milo_merge_kernel(MergeParam
     }
     M = bm;
   }
-  if (lane == 0) { sh_m[wave] = M; sh_l[wave] = l; }
+  // every lane holds the same M and l; one wave needs no combination
+  float Mt = M, lt = l, ot[JPL];
 #pragma unroll
-  for (int jj = 0; jj < JPL; ++jj) sh_o[wave][lane * JPL + jj] = o[jj];
-  __syncthreads();
-  if (wave != 0) return;
-  float Mt = kNegInf;
+  for (int jj = 0; jj < JPL; ++jj) ot[jj] = o[jj];
+  if constexpr (kMergeWaves > 1) {
+    if (lane == 0) { sh_m[wave] = M; sh_l[wave] = l; }
 #pragma unroll
-  for (int w = 0; w < kMergeWaves; ++w) Mt = fmaxf(Mt, sh_m[w]);
-  float lt = 0.f, ot[JPL];
+    for (int jj = 0; jj < JPL; ++jj) sh_o[wave][lane * JPL + jj] = o[jj];
+    __syncthreads();
+    if (wave != 0) return;
+    Mt = kNegInf;
 #pragma unroll
-  for (int jj = 0; jj < JPL; ++jj) ot[jj] = 0.f;
-  if (Mt != kNegInf) {
+    for (int w = 0; w < kMergeWaves; ++w) Mt = fmaxf(Mt, sh_m[w]);
+    lt = 0.f;
 #pragma unroll
-    for (int w = 0; w < kMergeWaves; ++w) {
-      const float sc = fast_exp2(sh_m[w] - Mt);
-      lt += sh_l[w] * sc;
+    for (int jj = 0; jj < JPL; ++jj) ot[jj] = 0.f;
+    if (Mt != kNegInf) {
 #pragma unroll
-      for (int jj = 0; jj < JPL; ++jj) ot[jj] = fmaf(sc, sh_o[w][lane * JPL + jj], ot[jj]);
+      for (int w = 0; w < kMergeWaves; ++w) {
+        const float sc = fast_exp2(sh_m[w] - Mt);
+        lt += sh_l[w] * sc;
+#pragma unroll
+        for (int jj = 0; jj < JPL; ++jj) ot[jj] = fmaf(sc, sh_o[w][lane * JPL + jj], ot[jj]);
+      }
     }
   }
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
@@ -100,16 +108,29 @@ __global__ __launch_bounds__(64 * kMergeWaves) void milo_merge_kernel(MergeParam
   if (p.lse && lane == 0) p.lse[row] = lt > 0.f ? (Mt + __log2f(lt)) * kLn2 : kNegInf;
 }
 
+template <int D>
+void launch_merge_d(const MergeParams& p, int64_t rows, hipStream_t s) {
+  const int need = (p.slots + kMergeBatch - 1) / kMergeBatch;
+  const dim3 grid((unsigned)rows);
+  if (need <= 1)
+    hipLaunchKernelGGL((milo_merge_kernel<D, 1>), grid, dim3(64), 0, s, p);
+  else if (need <= 2)
+    hipLaunchKernelGGL((milo_merge_kernel<D, 2>), grid, dim3(128), 0, s, p);
+  else if (need <= 4)
+    hipLaunchKernelGGL((milo_merge_kernel<D, 4>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((milo_merge_kernel<D, 8>), grid, dim3(512), 0, s, p);
+}
+
 }  // namespace
 
 hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t s) {
   const int64_t rows = (int64_t)p.batch * p.q_len * p.n_q_heads;
   if (rows == 0) return hipSuccess;
-  const dim3 grid((unsigned)rows), block(64 * kMergeWaves);
   if (head_dim == 128)
-    hipLaunchKernelGGL(milo_merge_kernel<128>, grid, block, 0, s, p);
+    launch_merge_d<128>(p, rows, s);
   else if (head_dim == 64)
-    hipLaunchKernelGGL(milo_merge_kernel<64>, grid, block, 0, s, p);
+    launch_merge_d<64>(p, rows, s);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
