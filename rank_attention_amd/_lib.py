@@ -115,6 +115,13 @@ def load() -> ctypes.CDLL:
             raise RuntimeError(
                 f"{LIB_PATH} is missing: build the HIP library first "
                 "(python -c 'import __graft_entry__ as g; g.build()')")
+        # Stream handles and device pointers from torch cross the boundary, so
+        # the library must run on torch's HIP runtime.  torch bundles its own
+        # libamdhip64 with the same soname as the system one the library
+        # names; loading torch first makes that dependency resolve to torch's
+        # copy instead of a second runtime (which would not know torch's
+        # streams and, on some hosts, finds no device).
+        import torch  # noqa: F401
         lib = ctypes.CDLL(LIB_PATH)
         lib.milo_attn_workspace_bytes.argtypes = [ctypes.POINTER(MiloAttnArgs), ctypes.c_int32]
         lib.milo_attn_workspace_bytes.restype = ctypes.c_size_t

@@ -10,6 +10,12 @@ namespace milo {
 
 constexpr float kLog2eHost = 1.4426950408889634f;
 
+// The launchers check their launches with hipGetLastError, which reports
+// the last error of any HIP call on the thread, also a hipErrorNotReady left
+// behind by another library's event or stream query.  The entry points call
+// this first, so that the check sees only their own launches.
+inline void clear_stale_error() { (void)hipGetLastError(); }
+
 // Partial results of one work unit for its rows: unnormalised output o~
 // ([rows][head_dim]) and the pair (m, l) per row, m in log2 units.
 struct Partials {

@@ -147,6 +147,7 @@ milo_status milo_attn_decode(const milo_attn_args* a, void* hip_stream) {
   p.scale_log2 = a->scale * milo::kLog2eHost;
   p.unit_order = a->unit_order;
 
+  milo::clear_stale_error();
   const bool timing = a->prof_events[0] && a->prof_events[1];
   if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[0]), stream) != hipSuccess)
     return MILO_ERR_DEVICE;
@@ -209,6 +210,7 @@ milo_status milo_attn_chunk(const milo_attn_args* a, void* hip_stream) {
   p.no_tail = 0;
   p.scale_log2 = a->scale * milo::kLog2eHost;
 
+  milo::clear_stale_error();
   const bool timing = a->prof_events[0] && a->prof_events[1];
   if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[0]), stream) != hipSuccess)
     return MILO_ERR_DEVICE;
@@ -278,6 +280,7 @@ milo_status milo_attn_decode_shared(const milo_attn_args* a, void* hip_stream) {
   p.tail_units = a->batch * a->n_kv_heads;
   p.scale_log2 = a->scale * milo::kLog2eHost;
 
+  milo::clear_stale_error();
   const bool timing = a->prof_events[0] && a->prof_events[1];
   if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[0]), stream) != hipSuccess)
     return MILO_ERR_DEVICE;
@@ -327,6 +330,7 @@ milo_status milo_attn_validate(const milo_attn_args* a, int32_t path, int32_t n_
   p.tail_cap = a->tail_cap;
   p.tail_min = path == MILO_PATH_CHUNK ? a->q_len : 0;
   p.q8 = a->dtype == MILO_BF16_Q8;
+  milo::clear_stale_error();
   if (milo::launch_validate(p, reinterpret_cast<hipStream_t>(hip_stream)) != hipSuccess) return MILO_ERR_DEVICE;
   return MILO_OK;
 }
@@ -335,6 +339,7 @@ milo_status milo_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32
                             void* hip_stream) {
   if (!buf || !sink || bytes % 16 != 0 || !aligned(buf, 16) || n_workgroups < 1) return MILO_ERR_INVALID;
   if (bytes == 0) return MILO_OK;
+  milo::clear_stale_error();
   if (milo::launch_read_probe(buf, bytes, sink, n_workgroups, reinterpret_cast<hipStream_t>(hip_stream)) !=
       hipSuccess)
     return MILO_ERR_DEVICE;

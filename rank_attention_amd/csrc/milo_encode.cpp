@@ -112,6 +112,7 @@ milo_status milo_rank_allocate(const milo_rank_args* a, void* hip_stream) {
   p.unit = a->unit;
   p.k_units_k = ((int64_t)a->budget_k - (int64_t)a->n_blocks * a->r_min) / a->unit;
   p.k_units_v = ((int64_t)a->budget_v - (int64_t)a->n_blocks * a->r_min) / a->unit;
+  milo::clear_stale_error();
   if (milo::launch_rank(p, a->head_dim, reinterpret_cast<hipStream_t>(hip_stream)) != hipSuccess)
     return MILO_ERR_DEVICE;
   return MILO_OK;
@@ -129,6 +130,7 @@ milo_status milo_encode_spectrum(const milo_encode_args* a, void* hip_stream) {
   if ((a->sigma && !enc_aligned(a->sigma, 4)) || (a->sweeps && !enc_aligned(a->sweeps, 4)))
     return MILO_ERR_INVALID;
   const milo::EncodeParams p = params_of(a);
+  milo::clear_stale_error();
   if (milo::launch_encode_spectrum(p, a->dtype, a->head_dim, reinterpret_cast<hipStream_t>(hip_stream)) !=
       hipSuccess)
     return MILO_ERR_DEVICE;
@@ -141,6 +143,7 @@ milo_status milo_encode_factors(const milo_encode_args* a, void* hip_stream) {
   if (a->n_blocks == 0) return MILO_OK;
   if (!a->pool || !enc_aligned(a->pool, 16)) return MILO_ERR_INVALID;
   const milo::EncodeParams p = params_of(a);
+  milo::clear_stale_error();
   if (milo::launch_encode_factors(p, a->dtype, a->head_dim, reinterpret_cast<hipStream_t>(hip_stream)) !=
       hipSuccess)
     return MILO_ERR_DEVICE;
@@ -212,6 +215,7 @@ milo_status milo_quantize_factors(const milo_quant_args* a, void* hip_stream) {
   p.dst_blocks = a->dst_blocks;
   p.n_blocks = a->n_blocks;
   p.n_kv_heads = a->n_kv_heads;
+  milo::clear_stale_error();
   if (milo::launch_quantize(p, a->head_dim, reinterpret_cast<hipStream_t>(hip_stream)) != hipSuccess)
     return MILO_ERR_DEVICE;
   return MILO_OK;
