@@ -1,0 +1,101 @@
+"""Seeded sweep of shapes for GPU parity: each case draws group size, KV
+heads, head_dim, per-block token counts (empty, ragged, over 1024), ranks
+(0 .. d, independent for keys and values) and tail lengths from a fixed
+seed, checks the tables with the library's own validator, then compares the
+decode (bf16 and 8-bit storage) and chunk paths with the fp64 oracle.
+
+Every row gets the elementwise and lse gates.  The per-row relative L2 gate
+applies to rows whose reference norm is at least a tenth of the case's
+median: random ranks and causal masks can leave a row whose output nearly
+cancels, and the relative error of such a row measures the cancellation,
+not the kernel (its absolute error is still held by the elementwise gate)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import quant
+from tests.gpu_util import compare, note
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def draw_case(seed: int, d=None, q_len: int = 1):
+    """A workload of random shape within the documented limits."""
+    rng = np.random.default_rng(1000 + seed)
+    d = d or int(rng.choice([64, 128]))
+    hkv = int(rng.integers(1, 5))
+    g = int(rng.integers(1, 9))
+    batch = int(rng.integers(1, 5))
+    toks = []
+    for _ in range(batch):
+        nb = int(rng.integers(0, 6))
+        toks.append([int(rng.choice([0, 1, 63, 64, 65, 1024, 1025])) if rng.random() < 0.3
+                     else int(rng.integers(1, 1400)) for _ in range(nb)])
+    # decode allows an empty tail; the chunk path needs at least q_len tail tokens
+    tails = [int(rng.integers(q_len, q_len + 300)) if rng.random() < 0.8 else (0 if q_len == 1 else q_len)
+             for _ in range(batch)]
+    cfg = synth.get_config("qwen05b_16k").with_(
+        name=f"sweep_{seed}_d{d}_g{g}_h{hkv}_q{q_len}", batch=batch, n_q_heads=g * hkv, n_kv_heads=hkv,
+        head_dim=d, q_len=q_len, tail_len=max(tails), dtype="bf16",
+        ranks=synth.configs.RankDist("uniform", lo=1, hi=d), v_rank_equals_k=False, seed=2000 + seed)
+    wl = synth.make_workload(cfg, variant="sharp", n_blocks=[len(t) for t in toks], tokens=toks,
+                             tail_len=tails)
+    return wl
+
+
+def device_cache(wl):
+    import rank_attention_amd as ra
+    pc = ra.pack(wl, shuffle_pool=7)
+    dc = ra.DeviceCache(pc, scale=wl.scale)
+    note(f"sweep cfg={wl.cfg.name} B={wl.batch} blocks={[len(s) for s in wl.blocks]} "
+         f"tails={list(map(int, wl.tail_len))} max_blocks={pc.max_blocks}")
+    return dc
+
+
+def gate(out, lse, ref_o, ref_l, name):
+    compare(out, lse, ref_o, ref_l, sharp_gates=False, name=name)
+    n = np.linalg.norm(ref_o, axis=-1)
+    rows = np.argwhere(n >= 0.1 * np.median(n[n > 0]))
+    compare(out, lse, ref_o, ref_l, rows=rows, sharp_gates=True, name=name + " (well-conditioned rows)")
+
+
+def fetch(res):
+    import torch
+    torch.cuda.synchronize()
+    out, lse = res
+    return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sweep_decode_bf16_and_8bit(seed):
+    wl = draw_case(seed)
+    dc = device_cache(wl)
+    assert dc.validate() is None
+    out, lse = fetch(dc.decode())
+    ref_o, ref_l = oracle.attend(wl)
+    gate(out, lse, ref_o, ref_l, wl.cfg.name)
+    qc = dc.quantized()
+    assert qc.validate() is None
+    out, lse = fetch(qc.decode())
+    ref_o, ref_l = quant.attend_q8(wl)
+    gate(out, lse, ref_o, ref_l, wl.cfg.name + "/q8")
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_sweep_chunk(seed):
+    q_len = int(np.random.default_rng(3000 + seed).integers(1, 90))
+    wl = draw_case(seed, d=128, q_len=q_len)
+    dc = device_cache(wl)
+    import rank_attention_amd as ra
+    assert dc.validate(ra.MILO_PATH_CHUNK) is None
+    out, lse = fetch(dc.chunk())
+    ref_o, ref_l = oracle.attend(wl)
+    gate(out, lse, ref_o, ref_l, wl.cfg.name + "/chunk")
