@@ -388,3 +388,23 @@ def test_q8_storage_is_decode_only():
     assert lib.milo_attn_chunk(ctypes.byref(c), None) == _lib.MILO_ERR_UNSUPPORTED
     d = good_args(dtype=_lib.MILO_BF16_Q8, head_dim=128, n_q_heads=4)
     assert lib.milo_attn_decode_shared(ctypes.byref(d), None) == _lib.MILO_ERR_UNSUPPORTED
+
+
+def test_library_binds_to_torchs_hip_runtime():
+    """A process that opens the library before touching torch must still have
+    one HIP runtime: torch's bundled copy, which shares the soname of the ROCm
+    one the library links.  Two runtimes would give the library a runtime that
+    knows none of torch's streams."""
+    import subprocess
+    import sys
+    code = ("from rank_attention_amd import _lib; _lib.load(); import torch; "
+            "maps = open('/proc/self/maps').read().split(chr(10)); "
+            "print(sorted({l.split()[-1] for l in maps if 'libamdhip64' in l}))")
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=600,
+                         cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert res.returncode == 0, res.stderr[-2000:]
+    import ast
+    libs = ast.literal_eval(res.stdout.strip().splitlines()[-1])
+    assert len(libs) == 1, libs
+    import torch
+    assert os.path.realpath(libs[0]).startswith(os.path.realpath(os.path.dirname(torch.__file__))), libs
