@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MILO_ABI_VERSION 3
+#define MILO_ABI_VERSION 4
 
 typedef enum milo_status {
   MILO_OK = 0,
@@ -192,8 +192,8 @@ milo_status milo_attn_decode_shared(const milo_attn_args* args, void* hip_stream
  * are few and stream more slowly per byte, and started late they would be
  * the last to finish.
  *
- * blocks, seq_blocks, tail_len are HOST copies of the device tables
- * (tail_len may be NULL when tail_cap is 0);  order_out (host) receives
+ * blocks (n_descriptors entries), seq_blocks, tail_len are HOST copies of
+ * the device tables (tail_len may be NULL when tail_cap is 0);  order_out (host) receives
  * batch * n_kv_heads * (max_blocks_per_seq + 1) unit indices: non-empty
  * tails (longest first), then block units (largest first), then empty slots
  * and empty tails; ties in natural order.  The cache is static across
@@ -201,30 +201,36 @@ milo_status milo_attn_decode_shared(const milo_attn_args* args, void* hip_stream
  * For sequence i it reads blocks[seq_blocks[i] .. seq_blocks[i] +
  * min(seq_blocks[i+1] - seq_blocks[i], max_blocks_per_seq)).
  * Returns MILO_ERR_INVALID on null pointers, negative sizes or a sequence
- * with seq_blocks[i] < 0 or seq_blocks[i+1] < seq_blocks[i];
+ * with seq_blocks[i] < 0, seq_blocks[i+1] < seq_blocks[i] or
+ * seq_blocks[i+1] > n_descriptors (checked before any descriptor is read);
  * MILO_ERR_UNSUPPORTED when the unit count exceeds INT32_MAX.
  */
-milo_status milo_attn_plan_decode(const milo_block* blocks, const int32_t* seq_blocks,
-                                  const int32_t* tail_len, int32_t batch, int32_t n_kv_heads,
-                                  int32_t max_blocks_per_seq, int32_t head_dim,
+milo_status milo_attn_plan_decode(const milo_block* blocks, int32_t n_descriptors,
+                                  const int32_t* seq_blocks, const int32_t* tail_len, int32_t batch,
+                                  int32_t n_kv_heads, int32_t max_blocks_per_seq, int32_t head_dim,
                                   int32_t* order_out);
 
 /*
  * Device-side check of the tables a call reads, for debugging callers: the
- * kernels clamp counts and lengths but trust offsets and ranks.  Reads only
- * blocks[0 .. n_descriptors), seq_blocks and tail_len (never the pool), in
- * two kernels on the stream, and writes *status (device, 8 bytes):
+ * kernels clamp counts and lengths but trust offsets, ranks and the decode
+ * schedule.  Reads only blocks[0 .. n_descriptors), seq_blocks, tail_len and
+ * unit_order (never the pool), in up to three kernels on the stream, and
+ * writes *status (device, 8 bytes):
  *     UINT64_MAX                          every rule holds;
  *     ((uint64_t)rule << 32) | index     otherwise, the smallest violated
  *                                         milo_table_rule and, for it, the
  *                                         smallest offending index (sequence
- *                                         for rules 1, 2, 7; descriptor else).
+ *                                         for rules 1, 2, 7; schedule position
+ *                                         for rule 8; descriptor else).
  * With path MILO_PATH_SHARED only sequence 0's list is checked (the other
  * lists are not read by that path).  pool_elems is the pool size in
  * elements.  Host-checkable faults return a status as for the other entry
  * points (status must be 8-byte aligned).  With MILO_BF16_Q8, pool_elems
  * counts bytes, rule 4 asks for ld_tok a multiple of 64 and rule 5 for off a
- * multiple of 16.
+ * multiple of 16.  When args->unit_order is set, rule 8 checks that it is a
+ * permutation of the decode units; the check counts units in args->workspace
+ * (256-B aligned, at least 4 bytes per unit, which a decode workspace always
+ * has; its contents are overwritten) and returns MILO_ERR_WORKSPACE without it.
  */
 typedef enum milo_table_rule {
   MILO_TABLE_SEQ_RANGE = 1,        /* seq_blocks[i] < 0, decreasing, or past n_descriptors        */
@@ -233,8 +239,11 @@ typedef enum milo_table_rule {
   MILO_TABLE_TOKENS = 4,           /* n_tok < 0, ld_tok < n_tok, or ld_tok not a multiple of 8    */
   MILO_TABLE_OFFSET = 5,           /* off < 0 or not a multiple of 8                              */
   MILO_TABLE_POOL_BOUNDS = 6,      /* the block's factors end past pool_elems                     */
-  MILO_TABLE_TAIL_LEN = 7          /* tail_len[i] outside [0, tail_cap] (decode, shared) or
+  MILO_TABLE_TAIL_LEN = 7,         /* tail_len[i] outside [0, tail_cap] (decode, shared) or
                                       [q_len, tail_cap] (chunk)                                   */
+  MILO_TABLE_UNIT_ORDER = 8        /* unit_order[u] outside [0, units) or naming a unit that
+                                      another entry also names (units = batch * n_kv_heads *
+                                      (max_blocks_per_seq + 1))                                  */
 } milo_table_rule;
 
 milo_status milo_attn_validate(const milo_attn_args* args, int32_t path, int32_t n_descriptors,

@@ -143,14 +143,19 @@ def decode_shared(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_kv
 
 
 def validate_tables(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_kv_heads: int,
-                    max_blocks: int, path: int = MILO_PATH_DECODE, scale: float = 1.0):
+                    max_blocks: int, path: int = MILO_PATH_DECODE, scale: float = 1.0, unit_order=None):
     """Check the device tables against the contract (milo_attn_validate) and
-    wait for the result: None if every rule holds, else (rule name, index)."""
+    wait for the result: None if every rule holds, else (rule name, index).
+    With a decode schedule (unit_order) it is checked too, using a scratch
+    workspace of 4 bytes per unit."""
     import torch
     lib = _lib.load()
     status = torch.empty(1, dtype=torch.int64, device=q.device)
+    workspace = None
+    if unit_order is not None:
+        workspace = torch.empty(max(4 * int(unit_order.numel()), 256), dtype=torch.uint8, device=q.device)
     a = make_args(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, n_kv_heads=n_kv_heads, scale=scale,
-                  max_blocks=max_blocks)
+                  max_blocks=max_blocks, workspace=workspace, unit_order=unit_order)
     n_desc = int(blocks.numel() * blocks.element_size()) // BLOCK_DTYPE.itemsize
     pool_elems = int(pool.numel()) if pool is not None else 0
     stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -206,7 +211,9 @@ class DeviceCache:
         return chunk(*self.tensors(), n_kv_heads=self.n_kv_heads, max_blocks=self.max_blocks, **kw)
 
     def validate(self, path: int = MILO_PATH_DECODE):
-        return validate_tables(*self.tensors(), n_kv_heads=self.n_kv_heads, max_blocks=self.max_blocks, path=path)
+        order = self.unit_order if path == MILO_PATH_DECODE else None
+        return validate_tables(*self.tensors(), n_kv_heads=self.n_kv_heads, max_blocks=self.max_blocks, path=path,
+                               unit_order=order)
 
     def decode_shared(self, **kw):
         kw.setdefault("scale", self.scale)

@@ -17,7 +17,7 @@ EXPORTS = ("milo_attn_workspace_bytes", "milo_attn_decode", "milo_attn_chunk", "
            "milo_rank_workspace_bytes", "milo_rank_allocate", "milo_attn_validate", "milo_read_probe",
            "milo_quant_layout", "milo_quantize_factors")
 TABLE_RULES = {1: "seq_range", 2: "too_many_blocks", 3: "rank", 4: "tokens", 5: "offset", 6: "pool_bounds",
-               7: "tail_len"}
+               7: "tail_len", 8: "unit_order"}
 
 
 class MiloBlock(ctypes.Structure):
@@ -134,9 +134,9 @@ def load() -> ctypes.CDLL:
         lib.milo_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32,
                                         ctypes.c_void_p]
         lib.milo_read_probe.restype = ctypes.c_int
-        lib.milo_attn_plan_decode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                              ctypes.c_int32, ctypes.c_void_p]
+        lib.milo_attn_plan_decode.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
         lib.milo_attn_plan_decode.restype = ctypes.c_int
         lib.milo_status_str.argtypes = [ctypes.c_int]
         lib.milo_status_str.restype = ctypes.c_char_p

@@ -275,7 +275,10 @@ __device__ __forceinline__ void issue_tile(const BlockInfo& io, char* buf, int t
     const int row = rb * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ (is_v ? swz_v(row) : swz_u(row));
     const uint32_t off = (is_v ? io.v_off : 0u) + (uint32_t)(row * io.ld + t0 + chunk * 8) * 2;
-    const bool ok = row < (is_v ? io.rv : io.r) && t0 + chunk * 8 < io.ld;
+    // chunks that start past the block's last token load zeros: row padding
+    // beyond it may hold anything (NaN included) and would meet e = 0 in the
+    // value MFMA (0 * NaN = NaN); the partial chunk at n_tok is masked later
+    const bool ok = row < (is_v ? io.rv : io.r) && t0 + chunk * 8 < io.T;
     dma16(rs, buf + (is_v ? kHalfTile : 0) + rb * 1024, off, ok);
   }
 }
@@ -454,6 +457,15 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
       advance_pre();
       return true;
     };
+    // W of block b + 1 goes into ldsW during block b's last tile.  It is
+    // taken from that block's own descriptor: the prefetch cursor pb is two
+    // tiles ahead and already past b + 1 when b + 1 has a single tile.
+    int cur_b = blk_lo;
+    auto issue_next_w = [&](int ln) {
+      BlockInfo nb;
+      block_info(nb, p, b0 + cur_b + 1, g);
+      issue_w(nb, ldsW, false, ln, wave);
+    };
     issue_w(cb, ldsW, false, lane, wave);
     issue_w(cb, ldsWp, true, lane, wave);
     issue_next(lane);
@@ -462,6 +474,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
     int k = 0;                            // global index of the tile computed now
 
     for (int b = blk_lo; b < blk_hi; ++b) {
+      cur_b = b;
       if (b > blk_lo) block_info(cb, p, b0 + b, g);
       const int T = cb.T, r = cb.r, nv = cb.nv, ntiles = cb.ntiles;
       const bool has_next = b + 1 < blk_hi;
@@ -504,10 +517,10 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
             }
             if (ntiles == 1 && has_next) {   // W is read: the next block's may land
               wait_barrier<63>();
-              issue_w(pb, ldsW, false, ln, wave);
+              issue_next_w(ln);
             }
           } else if (t == ntiles - 1 && has_next) {
-            issue_w(pb, ldsW, false, ln, wave);   // W of the next block
+            issue_next_w(ln);   // W of the next block
           }
           newest = issue_next(ln);
           if (t0 + kTT > T && (T & 7)) {

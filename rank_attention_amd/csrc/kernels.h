@@ -114,6 +114,11 @@ struct ValidateParams {
   int64_t pool_elems;        // bytes for 8-bit factor storage
   int32_t n_descriptors, n_seqs_checked, batch, max_blocks, n_kv_heads, head_dim, tail_cap, tail_min;
   int32_t q8;                // 8-bit factor storage: byte offsets, multiples of 16
+  // decode schedule check (unit_order non-null): n_units entries, and one
+  // count per unit in caller scratch
+  const int32_t* unit_order;
+  unsigned* unit_count;
+  int64_t n_units;
 };
 
 // 8-bit factors: one workgroup per (block, KV head) quantises its U^T and

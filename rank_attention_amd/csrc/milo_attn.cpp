@@ -330,6 +330,14 @@ milo_status milo_attn_validate(const milo_attn_args* a, int32_t path, int32_t n_
   p.tail_cap = a->tail_cap;
   p.tail_min = path == MILO_PATH_CHUNK ? a->q_len : 0;
   p.q8 = a->dtype == MILO_BF16_Q8;
+  if (a->unit_order) {
+    // the schedule's permutation check counts units in the call's workspace
+    p.n_units = milo::decode_units(a->batch, a->n_kv_heads, a->max_blocks_per_seq);
+    if (!a->workspace || !aligned(a->workspace, kWsAlign) || a->workspace_bytes < (size_t)p.n_units * 4)
+      return MILO_ERR_WORKSPACE;
+    p.unit_order = a->unit_order;
+    p.unit_count = static_cast<unsigned*>(a->workspace);
+  }
   milo::clear_stale_error();
   if (milo::launch_validate(p, reinterpret_cast<hipStream_t>(hip_stream)) != hipSuccess) return MILO_ERR_DEVICE;
   return MILO_OK;
@@ -346,18 +354,21 @@ milo_status milo_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32
   return MILO_OK;
 }
 
-milo_status milo_attn_plan_decode(const milo_block* blocks, const int32_t* seq_blocks,
-                                  const int32_t* tail_len, int32_t batch, int32_t n_kv_heads,
-                                  int32_t max_blocks, int32_t head_dim, int32_t* order_out) {
-  if (batch < 0 || n_kv_heads < 1 || max_blocks < 0 || head_dim < 1) return MILO_ERR_INVALID;
+milo_status milo_attn_plan_decode(const milo_block* blocks, int32_t n_descriptors,
+                                  const int32_t* seq_blocks, const int32_t* tail_len, int32_t batch,
+                                  int32_t n_kv_heads, int32_t max_blocks, int32_t head_dim,
+                                  int32_t* order_out) {
+  if (batch < 0 || n_kv_heads < 1 || max_blocks < 0 || head_dim < 1 || n_descriptors < 0) return MILO_ERR_INVALID;
   if (batch > 0 && (!seq_blocks || !order_out)) return MILO_ERR_INVALID;
-  if (batch > 0 && max_blocks > 0 && !blocks) return MILO_ERR_INVALID;
+  if (n_descriptors > 0 && !blocks) return MILO_ERR_INVALID;
   const int64_t slots = (int64_t)max_blocks + 1;
   const int64_t units = (int64_t)batch * n_kv_heads * slots;
   if (units > INT32_MAX) return MILO_ERR_UNSUPPORTED;   // unit indices are 32-bit
-  // the host tables are read here, so their ranges are checked first
+  // the host tables are read here, so their ranges are checked first: every
+  // list lies inside the n_descriptors entries of blocks
   for (int32_t i = 0; i < batch; ++i)
-    if (seq_blocks[i] < 0 || seq_blocks[i + 1] < seq_blocks[i]) return MILO_ERR_INVALID;
+    if (seq_blocks[i] < 0 || seq_blocks[i + 1] < seq_blocks[i] || seq_blocks[i + 1] > n_descriptors)
+      return MILO_ERR_INVALID;
   // rank 0: dense-tail units (few, and per byte the slowest, so they go
   // first and never finish last); rank 1: block units, largest first;
   // rank 2: empty slots and empty tails

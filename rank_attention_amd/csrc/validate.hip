@@ -1,7 +1,7 @@
 // validate.hip -- device-side check of the caller-owned tables (descriptors,
-// CSR, tail lengths) against the contract in include/milo_attn.h.  Reads
-// only the tables, never the pool; records the smallest (rule, index) of
-// any violation with a 64-bit atomic minimum.
+// CSR, tail lengths, the decode schedule) against the contract in
+// include/milo_attn.h.  Reads only the tables, never the pool; records the
+// smallest (rule, index) of any violation with a 64-bit atomic minimum.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -11,7 +11,12 @@ namespace {
 
 constexpr int kValThreads = 256;
 
-__global__ void milo_validate_init_kernel(unsigned long long* status) { *status = ~0ull; }
+// status word to "no violation"; the schedule's per-unit counts to zero
+__global__ __launch_bounds__(kValThreads) void milo_validate_init_kernel(ValidateParams p) {
+  const int64_t idx = (int64_t)blockIdx.x * kValThreads + threadIdx.x;
+  if (idx == 0) *p.status = ~0ull;
+  if (p.unit_order && idx < p.n_units) p.unit_count[idx] = 0;
+}
 
 __device__ __forceinline__ void report(unsigned long long* status, int rule, int64_t index) {
   atomicMin(status, ((unsigned long long)rule << 32) | (unsigned long long)(uint32_t)index);
@@ -44,16 +49,37 @@ __global__ __launch_bounds__(kValThreads) void milo_validate_kernel(ValidatePara
     const int L = p.tail_len[idx];
     if (L < p.tail_min || L > p.tail_cap) report(p.status, 7, idx);
   }
+  if (p.unit_order && idx < p.n_units) {
+    const int u = p.unit_order[idx];
+    if (u >= 0 && (int64_t)u < p.n_units) atomicAdd(&p.unit_count[u], 1u);
+  }
+}
+
+// The schedule is a permutation iff every entry is in range and its unit is
+// listed once; positions breaking that are reported (the smallest wins, so
+// of two entries naming the same unit the first is reported).
+__global__ __launch_bounds__(kValThreads) void milo_validate_order_kernel(ValidateParams p) {
+  const int64_t idx = (int64_t)blockIdx.x * kValThreads + threadIdx.x;
+  if (idx >= p.n_units) return;
+  const int u = p.unit_order[idx];
+  if (u < 0 || (int64_t)u >= p.n_units || p.unit_count[u] != 1u) report(p.status, 8, idx);
 }
 
 }  // namespace
 
 hipError_t launch_validate(const ValidateParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(milo_validate_init_kernel, dim3(1), dim3(1), 0, s, p.status);
+  const int64_t nu = p.unit_order ? p.n_units : 0;
+  const unsigned init_grid = (unsigned)((std::max<int64_t>(nu, 1) + kValThreads - 1) / kValThreads);
+  hipLaunchKernelGGL(milo_validate_init_kernel, dim3(init_grid), dim3(kValThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t n = std::max<int64_t>(std::max<int64_t>(p.n_descriptors, p.n_seqs_checked), std::max(p.batch, 1));
+  const int64_t n = std::max<int64_t>(std::max<int64_t>(std::max<int64_t>(p.n_descriptors, p.n_seqs_checked),
+                                                        std::max(p.batch, 1)), nu);
   hipLaunchKernelGGL(milo_validate_kernel, dim3((unsigned)((n + kValThreads - 1) / kValThreads)),
+                     dim3(kValThreads), 0, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess || nu == 0) return e;
+  hipLaunchKernelGGL(milo_validate_order_kernel, dim3((unsigned)((nu + kValThreads - 1) / kValThreads)),
                      dim3(kValThreads), 0, s, p);
   return hipGetLastError();
 }

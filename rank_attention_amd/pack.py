@@ -3,8 +3,9 @@
 Pool layout (elements of the storage dtype):  for every block, its KV heads
 back to back;  per head
     U^T [rank_k][ld_tok] | W [rank_k][d] | U'^T [rank_v][ld_tok] | W' [rank_v][d]
-with ld_tok = n_tok rounded up to a multiple of 8.  Row padding and the gaps
-between blocks hold NaN, so a kernel that reads them produces NaN.
+with ld_tok = n_tok rounded up to a multiple of 8 (plus ``ld_extra``).  Row
+padding and the gaps between blocks hold NaN, so a kernel that reads them
+produces NaN.
 """
 from __future__ import annotations
 
@@ -42,7 +43,7 @@ def _nan(dtype: str):
 
 def pack(wl, gap: int = 8, shuffle_pool: Optional[int] = None,
          max_blocks: Optional[int] = None, poison_tail: bool = True,
-         plan: bool = True) -> PackedCache:
+         plan: bool = True, ld_extra: int = 0) -> PackedCache:
     """Pack a ``synth`` workload.
 
     gap           NaN elements left between consecutive blocks (multiple of 8)
@@ -50,14 +51,16 @@ def pack(wl, gap: int = 8, shuffle_pool: Optional[int] = None,
                   order is unchanged), to exercise arbitrary offsets
     max_blocks    host bound for the grid (default: the largest count)
     plan          compute the largest-first decode schedule (unit_order)
+    ld_extra      extra NaN padding per U^T / U'^T row beyond n_tok rounded up
+                  to 8 (multiple of 8): whole padding chunks past the block end
     """
-    assert gap % 8 == 0
+    assert gap % 8 == 0 and ld_extra % 8 == 0 and ld_extra >= 0
     d, hkv = wl.cfg.head_dim, wl.cfg.n_kv_heads
     st = np.uint16 if wl.dtype == "bf16" else np.float32
     flat = [b for s in wl.blocks for b in s]
     sizes = []
     for b in flat:
-        ld = (b.n_tok + 7) // 8 * 8
+        ld = (b.n_tok + 7) // 8 * 8 + ld_extra
         sizes.append(hkv * (b.rank_k + b.rank_v) * (ld + d))
     order = np.arange(len(flat))
     if shuffle_pool is not None:
@@ -70,7 +73,7 @@ def pack(wl, gap: int = 8, shuffle_pool: Optional[int] = None,
     pool = np.full(max(pos, 8), _nan(wl.dtype), dtype=st)
     desc = np.zeros(len(flat), BLOCK_DTYPE)
     for k, b in enumerate(flat):
-        ld = (b.n_tok + 7) // 8 * 8
+        ld = (b.n_tok + 7) // 8 * 8 + ld_extra
         desc[k] = (offs[k], b.n_tok, ld, b.rank_k, b.rank_v)
         head = (b.rank_k + b.rank_v) * (ld + d)
         for g in range(hkv):
@@ -116,7 +119,7 @@ def plan_decode(blocks: np.ndarray, seq_blocks: np.ndarray, tail_len, n_kv_heads
     blocks = np.ascontiguousarray(blocks)
     sb = np.ascontiguousarray(seq_blocks, np.int32)
     tl = None if tail_len is None else np.ascontiguousarray(tail_len, np.int32)
-    rc = lib.milo_attn_plan_decode(blocks.ctypes.data if len(blocks) else None, sb.ctypes.data,
+    rc = lib.milo_attn_plan_decode(blocks.ctypes.data if len(blocks) else None, len(blocks), sb.ctypes.data,
                                    None if tl is None else tl.ctypes.data, B, n_kv_heads,
                                    max_blocks, head_dim, out.ctypes.data)
     if rc != 0:

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_struct_size():
-    assert ra.abi_version() == 3
+    assert ra.abi_version() == 4
     # 7 int32 + float, 4 pointers, 2 int32, 6 pointers, size_t, 3 pointers; the
     # C side agrees, or the batch-0 call below would fail its struct_size check
     assert ctypes.sizeof(_lib.MiloAttnArgs) == 8 * 4 + 4 * 8 + 2 * 4 + 6 * 8 + 8 + 3 * 8
@@ -176,20 +176,24 @@ def test_plan_rejects_bad_arguments():
     lib = _lib.load()
     out = (ctypes.c_int32 * 8)()
     sb = (ctypes.c_int32 * 2)(0, 0)
-    assert lib.milo_attn_plan_decode(None, sb, None, -1, 1, 0, 64, out) == _lib.MILO_ERR_INVALID
-    assert lib.milo_attn_plan_decode(None, None, None, 1, 1, 0, 64, out) == _lib.MILO_ERR_INVALID
-    assert lib.milo_attn_plan_decode(None, sb, None, 1, 1, 2, 64, out) == _lib.MILO_ERR_INVALID
-    assert lib.milo_attn_plan_decode(None, sb, None, 1, 0, 0, 64, out) == _lib.MILO_ERR_INVALID
-    assert lib.milo_attn_plan_decode(None, sb, None, 1, 1, 0, 64, out) == _lib.MILO_OK
+    assert lib.milo_attn_plan_decode(None, 0, sb, None, -1, 1, 0, 64, out) == _lib.MILO_ERR_INVALID
+    assert lib.milo_attn_plan_decode(None, 0, None, None, 1, 1, 0, 64, out) == _lib.MILO_ERR_INVALID
+    assert lib.milo_attn_plan_decode(None, 2, sb, None, 1, 1, 2, 64, out) == _lib.MILO_ERR_INVALID
+    assert lib.milo_attn_plan_decode(None, 0, sb, None, 1, 0, 0, 64, out) == _lib.MILO_ERR_INVALID
+    assert lib.milo_attn_plan_decode(None, -1, sb, None, 1, 1, 0, 64, out) == _lib.MILO_ERR_INVALID
+    assert lib.milo_attn_plan_decode(None, 0, sb, None, 1, 1, 0, 64, out) == _lib.MILO_OK
     assert out[0] == 0
-    # a negative or decreasing block range is refused before any descriptor is read
+    # a negative or decreasing block range, or one past the descriptor table,
+    # is refused before any descriptor is read
     blk = (_lib.MiloBlock * 2)()
-    for bad in ((-1, 1), (1, 0)):
+    for bad in ((-1, 1), (1, 0), (0, 3), (2, 3)):
         sb2 = (ctypes.c_int32 * 2)(*bad)
-        assert lib.milo_attn_plan_decode(blk, sb2, None, 1, 1, 2, 64, out) == _lib.MILO_ERR_INVALID
+        assert lib.milo_attn_plan_decode(blk, 2, sb2, None, 1, 1, 2, 64, out) == _lib.MILO_ERR_INVALID
+    sb2 = (ctypes.c_int32 * 2)(0, 2)
+    assert lib.milo_attn_plan_decode(blk, 2, sb2, None, 1, 1, 2, 64, out) == _lib.MILO_OK
     # unit indices are 32-bit
     big = (ctypes.c_int32 * 2)(0, 0)
-    assert lib.milo_attn_plan_decode(blk, big, None, 1, 1 << 16, 1 << 16, 64, out) == _lib.MILO_ERR_UNSUPPORTED
+    assert lib.milo_attn_plan_decode(blk, 2, big, None, 1, 1 << 16, 1 << 16, 64, out) == _lib.MILO_ERR_UNSUPPORTED
 
 
 # --------------------------------------------------------------------------

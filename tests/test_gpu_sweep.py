@@ -6,16 +6,21 @@ decode (bf16 and 8-bit storage) and chunk paths with the fp64 oracle.
 
 Every row gets the elementwise and lse gates.  The per-row relative L2 gate
 applies to rows whose reference norm is at least a tenth of the case's
-median: random ranks and causal masks can leave a row whose output nearly
-cancels, and the relative error of such a row measures the cancellation,
-not the kernel (its absolute error is still held by the elementwise gate)."""
+median.  Random ranks and causal masks can leave a row whose output nearly
+cancels (norms down to 2e-3 of the median here): the kernels round each
+softmax weight to bf16 (relative 2^-9) before the value product, which
+moves such a row by up to 2^-9 ||sum_t a_t |v_t| || (up to a few percent of
+its own norm).  Those rows are held to twice that bound instead (abs L2
+error <= 2^-8 ||sum_t a_t |v_t| ||, which also covers the other fp32 and
+split roundings) and are logged with their norm, error, bound and the
+blocks that carry their softmax mass."""
 import numpy as np
 import pytest
 
 import oracle
 import synth
 from oracle import quant
-from tests.gpu_util import compare, note
+from tests.gpu_util import compare, note, weight_abs_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +50,7 @@ def draw_case(seed: int, d=None, q_len: int = 1):
     cfg = synth.get_config("qwen05b_16k").with_(
         name=f"sweep_{seed}_d{d}_g{g}_h{hkv}_q{q_len}", batch=batch, n_q_heads=g * hkv, n_kv_heads=hkv,
         head_dim=d, q_len=q_len, tail_len=max(tails), dtype="bf16",
-        ranks=synth.configs.RankDist("uniform", lo=1, hi=d), v_rank_equals_k=False, seed=2000 + seed)
+        ranks=synth.configs.RankDist("uniform", lo=0, hi=d), v_rank_equals_k=False, seed=2000 + seed)
     wl = synth.make_workload(cfg, variant="sharp", n_blocks=[len(t) for t in toks], tokens=toks,
                              tail_len=tails)
     return wl
@@ -60,11 +65,24 @@ def device_cache(wl):
     return dc
 
 
-def gate(out, lse, ref_o, ref_l, name):
+def gate(out, lse, ref_o, ref_l, name, wl=None):
     compare(out, lse, ref_o, ref_l, sharp_gates=False, name=name)
     n = np.linalg.norm(ref_o, axis=-1)
-    rows = np.argwhere(n >= 0.1 * np.median(n[n > 0]))
+    med = np.median(n[n > 0])
+    rows = np.argwhere(n >= 0.1 * med)
     compare(out, lse, ref_o, ref_l, rows=rows, sharp_gates=True, name=name + " (well-conditioned rows)")
+    low = np.argwhere((n < 0.1 * med) & (n > 0))
+    if wl is None or len(low) == 0:
+        return
+    bound, mass = weight_abs_bound(wl, [tuple(int(x) for x in r) for r in low])
+    err = np.linalg.norm(out[tuple(low.T)] - ref_o[tuple(low.T)], axis=-1)
+    for r, e, bd, ms in zip(low, err, bound, mass):
+        top = np.argsort(ms)[::-1][:3]
+        note(f"{name} low-norm row {tuple(int(x) for x in r)}: norm {n[tuple(r)]:.3g} (median {med:.3g}), "
+             f"abs L2 err {e:.3g}, rel {e / n[tuple(r)]:.3g}, ||sum a|v| || {bd:.3g}, "
+             f"mass " + ", ".join(f"{'tail' if k == len(ms) - 1 else 'block %d' % k}: {ms[k]:.2f}" for k in top))
+    ok = err <= 2.0 ** -8 * bound
+    assert ok.all(), f"{name}: {int((~ok).sum())} low-norm rows above 2^-8 ||sum a|v| ||"
 
 
 def fetch(res):
@@ -81,12 +99,12 @@ def test_sweep_decode_bf16_and_8bit(seed):
     assert dc.validate() is None
     out, lse = fetch(dc.decode())
     ref_o, ref_l = oracle.attend(wl)
-    gate(out, lse, ref_o, ref_l, wl.cfg.name)
+    gate(out, lse, ref_o, ref_l, wl.cfg.name, wl)
     qc = dc.quantized()
     assert qc.validate() is None
     out, lse = fetch(qc.decode())
     ref_o, ref_l = quant.attend_q8(wl)
-    gate(out, lse, ref_o, ref_l, wl.cfg.name + "/q8")
+    gate(out, lse, ref_o, ref_l, wl.cfg.name + "/q8", wl)
 
 
 @pytest.mark.parametrize("seed", range(5))
@@ -98,4 +116,4 @@ def test_sweep_chunk(seed):
     assert dc.validate(ra.MILO_PATH_CHUNK) is None
     out, lse = fetch(dc.chunk())
     ref_o, ref_l = oracle.attend(wl)
-    gate(out, lse, ref_o, ref_l, wl.cfg.name + "/chunk")
+    gate(out, lse, ref_o, ref_l, wl.cfg.name + "/chunk", wl)

@@ -26,7 +26,8 @@ def packed():
     return ra.pack(wl)
 
 
-def check(pc, path=ra.MILO_PATH_DECODE, blocks=None, seq_blocks=None, tail_len=None, max_blocks=None):
+def check(pc, path=ra.MILO_PATH_DECODE, blocks=None, seq_blocks=None, tail_len=None, max_blocks=None,
+          unit_order=None):
     import torch
     dc = ra.DeviceCache(pc)
     if blocks is not None:
@@ -37,6 +38,8 @@ def check(pc, path=ra.MILO_PATH_DECODE, blocks=None, seq_blocks=None, tail_len=N
         dc.tail_len = torch.from_numpy(np.ascontiguousarray(tail_len, np.int32)).to("cuda")
     if max_blocks is not None:
         dc.max_blocks = max_blocks
+    if unit_order is not None:
+        dc.unit_order = torch.from_numpy(np.ascontiguousarray(unit_order, np.int32)).to("cuda")
     note(f"validate path={path}")
     return dc.validate(path)
 
@@ -80,3 +83,25 @@ def test_smallest_rule_wins_and_shared_checks_sequence_zero_only(packed):
     sb[3] = sb[2] - 1                                  # breaks sequence 2's list only
     assert check(packed, seq_blocks=sb) == ("seq_range", 2)
     assert check(packed, path=ra.MILO_PATH_SHARED, seq_blocks=sb) is None
+
+
+def test_schedule_rule(packed):
+    """The decode schedule (unit_order) must be a permutation of the units:
+    an entry out of range, or a unit named twice, is reported at the
+    smallest offending position."""
+    order = packed.unit_order.copy()
+    assert check(packed, unit_order=order) is None
+    n = len(order)
+    bad = order.copy()
+    bad[17] = n                                         # out of range
+    assert check(packed, unit_order=bad) == ("unit_order", 17)
+    bad = order.copy()
+    bad[40] = -3
+    assert check(packed, unit_order=bad) == ("unit_order", 40)
+    bad = order.copy()
+    bad[30] = bad[9]                                    # unit named at 9 and 30; unit bad[30] unlisted
+    assert check(packed, unit_order=bad) == ("unit_order", 9)
+    # a descriptor rule (smaller rule number) still wins over the schedule rule
+    blocks = packed.blocks.copy()
+    blocks[2]["rank_v"] = 1000
+    assert check(packed, blocks=blocks, unit_order=bad) == ("rank", 2)
