@@ -181,6 +181,23 @@ milo_status milo_attn_chunk(const milo_attn_args* args, void* hip_stream);
 milo_status milo_attn_decode_shared(const milo_attn_args* args, void* hip_stream);
 
 /*
+ * Decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * milo_attn_decode with the same arguments and result, except that
+ * args->workspace and args->workspace_bytes are ignored.  The split-K
+ * partials go to a static device buffer of MILO_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends; the
+ * call allocates nothing.  Calls needing more than that
+ * (milo_attn_workspace_bytes(args, MILO_PATH_DECODE) >
+ * MILO_NOALLOC_SCRATCH_BYTES) return MILO_ERR_WORKSPACE before any HIP call.
+ * Every call on one GPU shares that GPU's buffer: calls that overlap on one
+ * GPU (concurrent streams or threads) race and must be serialised by the
+ * caller.  Stream-ordered calls on one stream are safe.
+ */
+#define MILO_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+milo_status milo_attn_decode_noalloc(const milo_attn_args* args, void* hip_stream);
+
+/*
  * Host-side scheduler for the decode kernel.  Decode work unit
  *     u = (i * n_kv_heads + g) * (max_blocks_per_seq + 1) + slot
  * covers block slot `slot` of sequence i, KV head g (slot = max_blocks_per_seq

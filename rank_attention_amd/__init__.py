@@ -17,7 +17,7 @@ from ._lib import (MILO_BF16, MILO_BF16_Q8, MILO_F32, MILO_PATH_CHUNK, MILO_PATH
                    MILO_OK, MILO_ERR_DEVICE)
 from .pack import BLOCK_DTYPE, PackedCache, pack  # noqa: F401
 
-__all__ = ["decode", "chunk", "decode_shared", "validate_tables", "workspace_bytes", "abi_version", "status_str", "DeviceCache",
+__all__ = ["decode", "decode_noalloc", "chunk", "decode_shared", "validate_tables", "workspace_bytes", "abi_version", "status_str", "DeviceCache",
            "pack", "PackedCache", "MiloError", "library_path"]
 
 library_path = _lib.LIB_PATH
@@ -126,6 +126,30 @@ def decode(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_kv_heads:
                 n_kv_heads=n_kv_heads, scale=scale, max_blocks=max_blocks, **kw)
 
 
+def decode_noalloc(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_kv_heads: int, scale: float,
+                   max_blocks: int, out=None, lse=None, stream=None, unit_order=None):
+    """Decode (q_len = 1) through milo_attn_decode_noalloc: the library keeps
+    the partials in its own static device buffer, so no workspace is passed.
+    out and lse may be preallocated (then nothing is allocated here either)."""
+    import torch
+    lib = _lib.load()
+    B, Q, Hq, d = (int(x) for x in q.shape)
+    if out is None:
+        out = torch.empty((B, Q, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Q, Hq), dtype=torch.float32, device=q.device)
+    a = make_args(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, n_kv_heads=n_kv_heads,
+                  scale=scale, max_blocks=max_blocks, out=out, lse=lse, unit_order=unit_order)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib.milo_attn_decode_noalloc(ctypes.byref(a), ctypes.c_void_p(int(stream)))
+    if rc != MILO_OK:
+        if rc == MILO_ERR_DEVICE:
+            raise RuntimeError(f"milo_attn: {status_str(rc)}")
+        raise MiloError(rc, status_str(rc))
+    return out, lse
+
+
 def chunk(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_kv_heads: int, scale: float,
           max_blocks: int, **kw):
     """Chunked-query attention (q_len = Q, bottom-right causal over the tail)."""
@@ -205,6 +229,11 @@ class DeviceCache:
         kw.setdefault("scale", self.scale)
         kw.setdefault("unit_order", self.unit_order)
         return decode(*self.tensors(), n_kv_heads=self.n_kv_heads, max_blocks=self.max_blocks, **kw)
+
+    def decode_noalloc(self, **kw):
+        kw.setdefault("scale", self.scale)
+        kw.setdefault("unit_order", self.unit_order)
+        return decode_noalloc(*self.tensors(), n_kv_heads=self.n_kv_heads, max_blocks=self.max_blocks, **kw)
 
     def chunk(self, **kw):
         kw.setdefault("scale", self.scale)

@@ -11,11 +11,12 @@ LIB_PATH = os.path.join(HERE, "libmilo_attn.so")
 MILO_OK, MILO_ERR_INVALID, MILO_ERR_UNSUPPORTED, MILO_ERR_WORKSPACE, MILO_ERR_DEVICE = range(5)
 MILO_F32, MILO_BF16, MILO_BF16_Q8 = 0, 1, 2
 MILO_PATH_DECODE, MILO_PATH_CHUNK, MILO_PATH_SHARED = 0, 1, 2
+MILO_NOALLOC_SCRATCH_BYTES = 32 << 20   # static scratch of milo_attn_decode_noalloc
 EXPORTS = ("milo_attn_workspace_bytes", "milo_attn_decode", "milo_attn_chunk", "milo_attn_decode_shared",
            "milo_attn_plan_decode", "milo_status_str", "milo_abi_version",
            "milo_encode_workspace_bytes", "milo_encode_spectrum", "milo_encode_factors", "milo_encode_layout",
            "milo_rank_workspace_bytes", "milo_rank_allocate", "milo_attn_validate", "milo_read_probe",
-           "milo_quant_layout", "milo_quantize_factors")
+           "milo_quant_layout", "milo_quantize_factors", "milo_attn_decode_noalloc")
 TABLE_RULES = {1: "seq_range", 2: "too_many_blocks", 3: "rank", 4: "tokens", 5: "offset", 6: "pool_bounds",
                7: "tail_len", 8: "unit_order"}
 
@@ -125,7 +126,8 @@ def load() -> ctypes.CDLL:
         lib = ctypes.CDLL(LIB_PATH)
         lib.milo_attn_workspace_bytes.argtypes = [ctypes.POINTER(MiloAttnArgs), ctypes.c_int32]
         lib.milo_attn_workspace_bytes.restype = ctypes.c_size_t
-        for fn in (lib.milo_attn_decode, lib.milo_attn_chunk, lib.milo_attn_decode_shared):
+        for fn in (lib.milo_attn_decode, lib.milo_attn_chunk, lib.milo_attn_decode_shared,
+                   lib.milo_attn_decode_noalloc):
             fn.argtypes = [ctypes.POINTER(MiloAttnArgs), ctypes.c_void_p]
             fn.restype = ctypes.c_int
         lib.milo_attn_validate.argtypes = [ctypes.POINTER(MiloAttnArgs), ctypes.c_int32, ctypes.c_int32,

@@ -39,6 +39,7 @@ UNITS = [
     ("validate.hip", [], "validate.o"),
     ("probe.hip", [], "probe.o"),
     ("quant.hip", [], "quant.o"),
+    ("noalloc.hip", [], "noalloc.o"),
     ("milo_attn.cpp", [], "milo_attn.o"),
     ("milo_encode.cpp", [], "milo_encode.o"),
 ]

@@ -162,4 +162,11 @@ inline hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, 
 hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t s);
 hipError_t launch_chunk(const ChunkParams& p, int group, hipStream_t s);
 
+// The decode entry point in two halves (milo_attn.cpp), shared by
+// milo_attn_decode and its variant with library-owned scratch: every
+// argument check but the workspace's, giving the workspace size the call
+// needs (no HIP call); then the launches with the partials at `workspace`.
+milo_status decode_check(const milo_attn_args* a, size_t* workspace_bytes);
+milo_status decode_launch(const milo_attn_args* a, void* workspace, void* hip_stream);
+
 }  // namespace milo

@@ -110,24 +110,27 @@ milo_status check_pointers(const milo_attn_args* a, const Layout& L) {
 
 }  // namespace
 
-extern "C" {
+namespace milo {
 
-size_t milo_attn_workspace_bytes(const milo_attn_args* a, int32_t path) {
-  if (check_shape(a, path) != MILO_OK) return 0;
-  return layout_of(a, path).total;
-}
-
-milo_status milo_attn_decode(const milo_attn_args* a, void* hip_stream) {
+milo_status decode_check(const milo_attn_args* a, size_t* workspace_bytes) {
   milo_status st = check_shape(a, MILO_PATH_DECODE);
   if (st != MILO_OK) return st;
   const Layout L = layout_of(a, MILO_PATH_DECODE);
-  st = check_pointers(a, L);
-  if (st != MILO_OK) return st;
+  *workspace_bytes = L.total;
   if (a->batch == 0) return MILO_OK;
+  // every pointer rule but the workspace's
+  milo_attn_args b = *a;
+  b.workspace = reinterpret_cast<void*>(kWsAlign);
+  b.workspace_bytes = L.total;
+  return check_pointers(&b, L);
+}
 
+milo_status decode_launch(const milo_attn_args* a, void* workspace, void* hip_stream) {
+  if (a->batch == 0) return MILO_OK;
+  const Layout L = layout_of(a, MILO_PATH_DECODE);
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
   const int group = a->n_q_heads / a->n_kv_heads;
-  char* ws = static_cast<char*>(a->workspace);
+  char* ws = static_cast<char*>(workspace);
   Partials part{reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + L.o_bytes)};
 
   DecodeParams p{};
@@ -172,6 +175,26 @@ milo_status milo_attn_decode(const milo_attn_args* a, void* hip_stream) {
   m.seq_stride = 1;
   if (milo::launch_merge(m, a->head_dim, stream) != hipSuccess) return MILO_ERR_DEVICE;
   return MILO_OK;
+}
+
+}  // namespace milo
+
+extern "C" {
+
+size_t milo_attn_workspace_bytes(const milo_attn_args* a, int32_t path) {
+  if (check_shape(a, path) != MILO_OK) return 0;
+  return layout_of(a, path).total;
+}
+
+milo_status milo_attn_decode(const milo_attn_args* a, void* hip_stream) {
+  size_t need = 0;
+  milo_status st = milo::decode_check(a, &need);
+  if (st != MILO_OK) return st;
+  if (a->batch > 0) {
+    if (!a->workspace || a->workspace_bytes < need) return MILO_ERR_WORKSPACE;
+    if (!aligned(a->workspace, kWsAlign)) return MILO_ERR_WORKSPACE;
+  }
+  return milo::decode_launch(a, a->workspace, hip_stream);
 }
 
 milo_status milo_attn_chunk(const milo_attn_args* a, void* hip_stream) {

@@ -172,6 +172,25 @@ def test_python_binding_raises_without_a_built_library(monkeypatch, tmp_path):
         _lib.load()
 
 
+def test_noalloc_decode_checks_before_any_hip_call():
+    """milo_attn_decode_noalloc ignores the workspace fields, applies every
+    other check of milo_attn_decode, and refuses a call whose partials exceed
+    its static buffer, all before any HIP call."""
+    lib = _lib.load()
+    a = good_args()
+    a.workspace, a.workspace_bytes = None, 0
+    bad = good_args(q=None)
+    assert lib.milo_attn_decode_noalloc(ctypes.byref(bad), None) == _lib.MILO_ERR_INVALID
+    bad = good_args(q_len=2)
+    assert lib.milo_attn_decode_noalloc(ctypes.byref(bad), None) == _lib.MILO_ERR_INVALID
+    a.batch, a.n_q_heads, a.n_kv_heads, a.head_dim, a.max_blocks_per_seq = 64, 28, 4, 128, 64
+    need = lib.milo_attn_workspace_bytes(ctypes.byref(a), _lib.MILO_PATH_DECODE)
+    assert need > _lib.MILO_NOALLOC_SCRATCH_BYTES      # 64 x 4 x 65 units x 7 rows: 60 MB
+    assert lib.milo_attn_decode_noalloc(ctypes.byref(a), None) == _lib.MILO_ERR_WORKSPACE
+    a.batch = 0
+    assert lib.milo_attn_decode_noalloc(ctypes.byref(a), None) == _lib.MILO_OK
+
+
 def test_plan_rejects_bad_arguments():
     lib = _lib.load()
     out = (ctypes.c_int32 * 8)()
