@@ -127,7 +127,10 @@ typedef struct milo_attn_args {
   int32_t batch;               /* sequences, >= 0                                           */
   int32_t q_len;               /* query tokens per sequence: 1 (decode) or Q >= 1 (chunk)   */
   int32_t n_q_heads;           /* >= 1, multiple of n_kv_heads                              */
-  int32_t n_kv_heads;          /* >= 1; group size n_q_heads / n_kv_heads in [1, 8]         */
+  int32_t n_kv_heads;          /* >= 1; group size n_q_heads / n_kv_heads in [1, 16]; above
+                                  8 only with MILO_BF16 storage and head_dim 128 (decode
+                                  then runs on the matrix-core kernel of the chunked path,
+                                  and its workspace follows that path's layout)              */
   int32_t head_dim;            /* 64 or 128                                                 */
   float scale;                 /* softmax scale (e.g. 1/sqrt(head_dim)); finite             */
   const void* q;               /* [batch][q_len][n_q_heads][head_dim], 16-B aligned         */

@@ -659,7 +659,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
 hipError_t launch_chunk(const ChunkParams& p, int group, hipStream_t s) {
   const int64_t groups = (int64_t)p.batch * p.n_kv_heads * (p.n_ranges + 1);
   if (groups == 0) return hipSuccess;
-  if (group < 1 || group > 8) return hipErrorInvalidValue;
+  if (group < 1 || group > 16) return hipErrorInvalidValue;
   const int64_t wgs = (p.tail_units + 7) / 8 * 8 + (groups + 7) / 8 * 8 * p.n_qtiles;
   ChunkParams q = p;
   q.group = group;

@@ -38,7 +38,9 @@ milo_status check_shape(const milo_attn_args* a, int32_t path) {
   if (path == MILO_PATH_CHUNK && a->tail_cap < a->q_len) return MILO_ERR_INVALID;
   if (a->head_dim != 64 && a->head_dim != 128) return MILO_ERR_UNSUPPORTED;
   const int group = a->n_q_heads / a->n_kv_heads;
-  if (group > 8) return MILO_ERR_UNSUPPORTED;
+  // group sizes above 8 run on the MFMA kernel (bf16 storage, head_dim 128)
+  if (group > 16) return MILO_ERR_UNSUPPORTED;
+  if (group > 8 && (a->dtype != MILO_BF16 || a->head_dim != 128)) return MILO_ERR_UNSUPPORTED;
   // partial records (query rows x unit slots) are indexed in 32 bits on the device
   if ((int64_t)a->batch * a->q_len * a->n_q_heads * ((int64_t)a->max_blocks_per_seq + 1) > INT32_MAX)
     return MILO_ERR_UNSUPPORTED;
@@ -76,10 +78,16 @@ struct Layout {
   int32_t slots;
 };
 
+// Decode with more than 8 query heads per KV head runs on the MFMA kernel of
+// the chunked path (q_len = 1: the whole tail is visible, as in decode); the
+// vector-ALU decode kernel keeps G scores per token in registers.
+bool decode_on_mfma(const milo_attn_args* a) { return a->n_q_heads / a->n_kv_heads > 8; }
+
 Layout layout_of(const milo_attn_args* a, int32_t path) {
   Layout L{};
   const int group = a->n_q_heads / a->n_kv_heads;
-  L.slots = path == MILO_PATH_CHUNK    ? chunk_split(a).n_ranges + 1
+  const bool ranges = path == MILO_PATH_CHUNK || (path == MILO_PATH_DECODE && decode_on_mfma(a));
+  L.slots = ranges                     ? chunk_split(a).n_ranges + 1
             : path == MILO_PATH_SHARED ? chunk_split(a, true).n_ranges + 1
                                        : a->max_blocks_per_seq + 1;
   L.rows_per_unit = a->q_len * group;
@@ -108,6 +116,63 @@ milo_status check_pointers(const milo_attn_args* a, const Layout& L) {
   return MILO_OK;
 }
 
+// The chunked path's launches (MFMA kernel, then the merge) with the
+// partials at ws; q_len may be 1 (decode with G > 8).
+milo_status chunk_launch(const milo_attn_args* a, char* ws, hipStream_t stream) {
+  const Layout L = layout_of(a, MILO_PATH_CHUNK);
+  const int group = a->n_q_heads / a->n_kv_heads;
+  const ChunkSplit cs = chunk_split(a);
+  Partials part{reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + L.o_bytes)};
+
+  milo::ChunkParams p{};
+  p.q = a->q;
+  p.pool = a->pool;
+  p.blocks = a->blocks;
+  p.seq_blocks = a->seq_blocks;
+  p.k_tail = a->k_tail;
+  p.v_tail = a->v_tail;
+  p.tail_len = a->tail_len;
+  p.part = part;
+  p.batch = a->batch;
+  p.q_len = a->q_len;
+  p.n_q_heads = a->n_q_heads;
+  p.n_kv_heads = a->n_kv_heads;
+  p.max_blocks = a->max_blocks_per_seq;
+  p.tail_cap = a->tail_cap;
+  p.n_qtiles = cs.n_qtiles;
+  p.n_ranges = cs.n_ranges;
+  p.blocks_per_range = cs.blocks_per_range;
+  p.part_rows = a->q_len * group;
+  p.no_tail = 0;
+  p.scale_log2 = a->scale * milo::kLog2eHost;
+
+  milo::clear_stale_error();
+  const bool timing = a->prof_events[0] && a->prof_events[1];
+  if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[0]), stream) != hipSuccess)
+    return MILO_ERR_DEVICE;
+  if (milo::launch_chunk(p, group, stream) != hipSuccess) return MILO_ERR_DEVICE;
+  if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[1]), stream) != hipSuccess)
+    return MILO_ERR_DEVICE;
+
+  MergeParams m{};
+  m.part = part;
+  m.seq_blocks = a->seq_blocks;
+  m.out = a->out;
+  m.lse = a->lse;
+  m.batch = a->batch;
+  m.q_len = a->q_len;
+  m.n_q_heads = a->n_q_heads;
+  m.n_kv_heads = a->n_kv_heads;
+  m.max_blocks = a->max_blocks_per_seq;
+  m.slots = L.slots;
+  m.rows_per_unit = L.rows_per_unit;
+  m.tail_slot = cs.n_ranges;
+  m.blocks_per_slot = cs.blocks_per_range;
+  m.seq_stride = 1;
+  if (milo::launch_merge(m, a->head_dim, stream) != hipSuccess) return MILO_ERR_DEVICE;
+  return MILO_OK;
+}
+
 }  // namespace
 
 namespace milo {
@@ -127,8 +192,9 @@ milo_status decode_check(const milo_attn_args* a, size_t* workspace_bytes) {
 
 milo_status decode_launch(const milo_attn_args* a, void* workspace, void* hip_stream) {
   if (a->batch == 0) return MILO_OK;
-  const Layout L = layout_of(a, MILO_PATH_DECODE);
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  if (decode_on_mfma(a)) return chunk_launch(a, static_cast<char*>(workspace), stream);
+  const Layout L = layout_of(a, MILO_PATH_DECODE);
   const int group = a->n_q_heads / a->n_kv_heads;
   char* ws = static_cast<char*>(workspace);
   Partials part{reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + L.o_bytes)};
@@ -204,60 +270,7 @@ milo_status milo_attn_chunk(const milo_attn_args* a, void* hip_stream) {
   st = check_pointers(a, L);
   if (st != MILO_OK) return st;
   if (a->batch == 0) return MILO_OK;
-
-  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
-  const int group = a->n_q_heads / a->n_kv_heads;
-  const ChunkSplit cs = chunk_split(a);
-  char* ws = static_cast<char*>(a->workspace);
-  Partials part{reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + L.o_bytes)};
-
-  milo::ChunkParams p{};
-  p.q = a->q;
-  p.pool = a->pool;
-  p.blocks = a->blocks;
-  p.seq_blocks = a->seq_blocks;
-  p.k_tail = a->k_tail;
-  p.v_tail = a->v_tail;
-  p.tail_len = a->tail_len;
-  p.part = part;
-  p.batch = a->batch;
-  p.q_len = a->q_len;
-  p.n_q_heads = a->n_q_heads;
-  p.n_kv_heads = a->n_kv_heads;
-  p.max_blocks = a->max_blocks_per_seq;
-  p.tail_cap = a->tail_cap;
-  p.n_qtiles = cs.n_qtiles;
-  p.n_ranges = cs.n_ranges;
-  p.blocks_per_range = cs.blocks_per_range;
-  p.part_rows = a->q_len * group;
-  p.no_tail = 0;
-  p.scale_log2 = a->scale * milo::kLog2eHost;
-
-  milo::clear_stale_error();
-  const bool timing = a->prof_events[0] && a->prof_events[1];
-  if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[0]), stream) != hipSuccess)
-    return MILO_ERR_DEVICE;
-  if (milo::launch_chunk(p, group, stream) != hipSuccess) return MILO_ERR_DEVICE;
-  if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[1]), stream) != hipSuccess)
-    return MILO_ERR_DEVICE;
-
-  MergeParams m{};
-  m.part = part;
-  m.seq_blocks = a->seq_blocks;
-  m.out = a->out;
-  m.lse = a->lse;
-  m.batch = a->batch;
-  m.q_len = a->q_len;
-  m.n_q_heads = a->n_q_heads;
-  m.n_kv_heads = a->n_kv_heads;
-  m.max_blocks = a->max_blocks_per_seq;
-  m.slots = L.slots;
-  m.rows_per_unit = L.rows_per_unit;
-  m.tail_slot = cs.n_ranges;
-  m.blocks_per_slot = cs.blocks_per_range;
-  m.seq_stride = 1;
-  if (milo::launch_merge(m, a->head_dim, stream) != hipSuccess) return MILO_ERR_DEVICE;
-  return MILO_OK;
+  return chunk_launch(a, static_cast<char*>(a->workspace), reinterpret_cast<hipStream_t>(hip_stream));
 }
 
 milo_status milo_attn_decode_shared(const milo_attn_args* a, void* hip_stream) {

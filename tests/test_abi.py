@@ -123,7 +123,7 @@ def test_decode_rejects_before_any_hip_call(over, code):
     ({"dtype": _lib.MILO_F32}, _lib.MILO_ERR_UNSUPPORTED),   # the MFMA path is bf16 only
     ({"head_dim": 64}, _lib.MILO_ERR_UNSUPPORTED),           # and head_dim 128 only
     ({"q_len": 2}, _lib.MILO_ERR_INVALID),                  # one query token per sequence
-    ({"n_q_heads": 32, "n_kv_heads": 2}, _lib.MILO_ERR_UNSUPPORTED),
+    ({"n_q_heads": 34, "n_kv_heads": 2}, _lib.MILO_ERR_UNSUPPORTED),   # group size 17
     ({"workspace": None}, _lib.MILO_ERR_WORKSPACE),
 ])
 def test_shared_rejects_before_any_hip_call(over, code):
@@ -147,6 +147,31 @@ def test_shared_workspace_query():
     exp_ml = -(-units * rows * 2 * 4 // 256) * 256
     assert need == exp_o + exp_ml
     assert lib.milo_attn_workspace_bytes(ctypes.byref(good_args(head_dim=64)), _lib.MILO_PATH_SHARED) == 0
+
+
+def test_group_sizes_above_eight():
+    """Group sizes 9-16 are served by the MFMA kernel (bf16 storage, head_dim
+    128); decode then takes the chunked path's workspace layout (block ranges
+    + a tail slot per (sequence, KV head), G rows each).  Other storage,
+    head_dim 64 and groups above 16 are unsupported."""
+    lib = _lib.load()
+    for path in (_lib.MILO_PATH_DECODE, _lib.MILO_PATH_CHUNK, _lib.MILO_PATH_SHARED):
+        q_len = 5 if path == _lib.MILO_PATH_CHUNK else 1
+        a = good_args(head_dim=128, n_q_heads=32, n_kv_heads=2, q_len=q_len)
+        assert lib.milo_attn_workspace_bytes(ctypes.byref(a), path) > 0
+        for over in ({"dtype": _lib.MILO_F32}, {"head_dim": 64}, {"n_q_heads": 34}):
+            b = good_args(**{"head_dim": 128, "n_q_heads": 32, "n_kv_heads": 2, "q_len": q_len, **over})
+            assert lib.milo_attn_workspace_bytes(ctypes.byref(b), path) == 0
+            assert call(b, path) if path != _lib.MILO_PATH_SHARED else True
+    # decode, G = 16, batch 2, 4 blocks: 16 rows -> 1 query tile; base 2 * 2 * 1 = 4;
+    # ranges = min(4, 256) = 4 of one block, + 1 tail slot
+    a = good_args(head_dim=128, n_q_heads=32, n_kv_heads=2, batch=2, max_blocks_per_seq=4)
+    units, rows = 2 * 2 * (4 + 1), 16
+    exp = -(-units * rows * 128 * 4 // 256) * 256 + -(-units * rows * 2 * 4 // 256) * 256
+    assert lib.milo_attn_workspace_bytes(ctypes.byref(a), _lib.MILO_PATH_DECODE) == exp
+    b = good_args(head_dim=128, n_q_heads=32, n_kv_heads=2, dtype=_lib.MILO_F32)
+    b.workspace_bytes = 1 << 30
+    assert call(b) == _lib.MILO_ERR_UNSUPPORTED
 
 
 def test_small_workspace_is_rejected():

@@ -264,3 +264,14 @@ def test_chunk_one_hot_ranges_of_three():
     ref_o, _ = oracle.attend(wl, sel=sel)
     idx = tuple(np.array(sel).T)
     np.testing.assert_allclose(ref_o[idx], exp[idx], rtol=0, atol=1e-9)
+
+
+@pytest.mark.parametrize("hq,hkv,q_len", [(16, 1, 24), (32, 2, 9)])
+def test_chunk_large_group(hq, hkv, q_len):
+    """Group sizes 9-16 on the chunked path: more query rows per KV head."""
+    cfg = small_chunk_cfg(name=f"chunk_large_group_{hq}_{hkv}", batch=2, n_q_heads=hq, n_kv_heads=hkv,
+                          q_len=q_len, tail_len=q_len + 40, seed=62)
+    wl = synth.make_workload(cfg, variant="sharp", tail_len=[q_len + 40, q_len])
+    out, lse = run_hip(wl, path="chunk", ld_extra=8)
+    ref_o, ref_l = oracle.attend(wl)
+    compare(out, lse, ref_o, ref_l, sharp_gates=True, name=cfg.name)

@@ -202,3 +202,19 @@ def test_one_hot_indexing_is_bit_exact(dtype, d, hq, hkv):
     assert np.array_equal(out, exp), f"max diff {np.abs(out - exp).max()}"
     ref_o, _ = oracle.attend(wl)
     np.testing.assert_allclose(ref_o, exp, rtol=0, atol=1e-9)
+
+
+# --------------------------------------------------------------------------
+# group sizes 9-16: decode on the matrix-core kernel of the chunked path
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("hq,hkv", [(12, 1), (32, 2), (48, 4)])
+def test_large_group_decode(hq, hkv):
+    cfg = synth.get_config("qwen7b_64k").with_(name=f"large_group_{hq}_{hkv}", batch=3, n_q_heads=hq,
+                                               n_kv_heads=hkv, n_blocks=6, seed=61,
+                                               ranks=synth.configs.RankDist("uniform", lo=0, hi=128))
+    toks = [[1024, 37, 0, 64, 700, 2], [65], []]
+    wl = synth.make_workload(cfg, variant="sharp", n_blocks=[len(t) for t in toks], tokens=toks,
+                             tail_len=[256, 0, 9])
+    out, lse = run_hip(wl, shuffle_pool=4, ld_extra=8)
+    ref_o, ref_l = oracle.attend(wl)
+    compare(out, lse, ref_o, ref_l, sharp_gates=True, name=cfg.name)

@@ -45,10 +45,11 @@ def test_shared_matches_decode():
     compare(os_, ls, od, ld, sharp_gates=True, name="shared_vs_decode")
 
 
-@pytest.mark.parametrize("batch,hq,hkv", [(3, 15, 3), (40, 28, 4), (1, 8, 1), (19, 40, 8)])
+@pytest.mark.parametrize("batch,hq,hkv", [(3, 15, 3), (40, 28, 4), (1, 8, 1), (19, 40, 8), (5, 32, 2), (9, 12, 1)])
 def test_shared_ragged(batch, hq, hkv):
     """Odd row counts (batch * group not a multiple of 16, several 128-row
-    tiles), ragged tokens, ranks 0..128, empty and short tails."""
+    tiles), group sizes up to 16, ragged tokens, ranks 0..128, empty and
+    short tails, and 16 extra NaN padding elements per token-factor row."""
     cfg = synth.get_config("qwen7b_64k").with_(name=f"shared_ragged_{batch}_{hq}_{hkv}", batch=batch,
                                                n_q_heads=hq, n_kv_heads=hkv,
                                                ranks=synth.configs.RankDist("uniform", lo=0, hi=128),
@@ -58,7 +59,7 @@ def test_shared_ragged(batch, hq, hkv):
     wl = synth.make_workload(cfg, variant="sharp", n_blocks=[len(t) for t in toks], tokens=toks,
                              tail_len=tails)
     wl = shared(wl)
-    out, lse = run_hip(wl, path="shared")
+    out, lse = run_hip(wl, path="shared", ld_extra=16)
     ref_o, ref_l = oracle.attend(wl)
     compare(out, lse, ref_o, ref_l, sharp_gates=True, name=cfg.name)
 
