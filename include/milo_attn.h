@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MILO_ABI_VERSION 4
+#define MILO_ABI_VERSION 5
 
 typedef enum milo_status {
   MILO_OK = 0,
@@ -65,7 +65,10 @@ typedef enum milo_status {
 typedef enum milo_dtype {
   MILO_F32 = 0,              /* IEEE fp32 storage                                        */
   MILO_BF16 = 1,             /* bfloat16 storage                                         */
-  MILO_BF16_Q8 = 2           /* bfloat16 q, tail, W, W'; 8-bit token factors (decode)    */
+  MILO_BF16_Q8 = 2,          /* bfloat16 q, tail, W, W'; 8-bit token factors (decode)    */
+  MILO_BF16_KV4 = 3,         /* bfloat16 q, tail, W, W'; KIVI-style 4-bit token factors
+                                (decode)                                                 */
+  MILO_BF16_KV2 = 4          /* the same with 2-bit codes                                */
 } milo_dtype;
 
 typedef enum milo_path {
@@ -110,20 +113,64 @@ typedef enum milo_path {
  *                 padding to the next multiple of 16 bytes.
  * Padding codes may hold any value.
  */
+/*
+ * MILO_BF16_KV4 / MILO_BF16_KV2 pool (decode path only; built by
+ * milo_quantize_kivi in milo_encode.h).  MILO's cache also combines with
+ * KIVI quantisation (summary page, "5.3 Performance Analysis"): keys per
+ * channel, values per token, asymmetric low-bit codes with an fp16 scale
+ * and bias per group.  Here the token factors carry it (W and W' stay
+ * bf16), with BITS = 4 or 2 and L = 2^BITS - 1:
+ *   keys   U  (n_tok x rank_k): a group is one rank component k over the
+ *          64 tokens of a chunk c (tokens 64c .. 64c+63 of the block);
+ *   values U' (n_tok x rank_v): a group is one token t over 32 rank
+ *          components (ranks 32v .. 32v+31);
+ * element = a * code + b with the group's fp16 scale a and bias b.
+ * Offsets and strides count BYTES: off is a multiple of 16, ld_tok = n_tok
+ * rounded up to 64 (nch = ld_tok / 64 chunks), and with
+ *     ng8 = ceil(rank_k / 8),  ngv = ceil(rank_v / 32),  ntv = ceil(rank_v / 16)
+ * KV head g starts at byte off + g * H,
+ *     H = 16 + nch * (32 ng8 + 64 BITS ng8 + 256 ngv + 128 BITS ntv)
+ *         + 2 * head_dim * (rank_k + rank_v).
+ * Per head, back to back:
+ *     header  amax_k, amax_v (fp32: the largest key and value scale of the
+ *             head), 8 zero bytes
+ *     KA      [nch][8 ng8] fp16   key scales a (ranks rank_k..: 0)
+ *     KB      [nch][8 ng8] fp16   key biases b
+ *     KC      [nch][ng8][16][4]   key code words (see below)
+ *     VA      [nch][ngv][64] fp16 value scales a' (token 64c + x; tokens
+ *                                 n_tok..: 0)
+ *     VB      [nch][ngv][64] fp16 value biases b'
+ *     VC      [nch][ntv][64][2 BITS bytes]  value code words
+ *     W       [rank_k][head_dim] bf16
+ *     W'      [rank_v][head_dim] bf16
+ * Code words hold 8 codes (a 4-bit word is 32 bits, a 2-bit word 16 bits)
+ * in the order of the decode kernel's matrix-core operands.  Key word
+ * (g8, col, m) of chunk c holds ranks 8 g8 + i (i = 0..7) of chunk token
+ * 16 (col / 4) + 4 m + col % 4.  Value words of tile kt, lane l of chunk c
+ * hold rank 16 kt + l % 16 at chunk tokens 16 (l / 16) + 8 s + i for two
+ * 8-code words s = 0, 1.  Inside a 4-bit word, code i sits at bits
+ * 4 (i / 2 + 4 (i % 2)) .. +3.  2-bit words come in pairs sharing one
+ * 32-bit word: the key words (g8, col, 2d) and (g8, col, 2d + 1) form
+ * dword d, the value words s = 0, 1 form the lane's dword; code i of word
+ * u in {0, 1} sits at bits 2 (4 u + i / 2 + 8 (i % 2)) .. +1.
+ * Padding codes (ranks past rank_k, tokens past n_tok) may hold any value;
+ * padding scales and biases are 0.
+ */
 typedef struct milo_block {
-  int64_t off;      /* element offset of KV head 0's U^T; multiple of 8 (Q8: bytes,
-                       multiple of 16)                                             */
+  int64_t off;      /* element offset of KV head 0's U^T; multiple of 8 (Q8, KV4,
+                       KV2: bytes, multiple of 16)                                 */
   int32_t n_tok;    /* T_b >= 0                                                    */
   int32_t ld_tok;   /* row stride of U^T and U'^T in elements; >= n_tok, mult. of 8
-                       (Q8: multiple of 64, see the layout above)                  */
+                       (Q8, KV4, KV2: multiple of 64, see the layouts above)       */
   int32_t rank_k;   /* r_b  in [0, head_dim]                                       */
   int32_t rank_v;   /* r'_b in [0, head_dim]                                       */
 } milo_block;
 
 typedef struct milo_attn_args {
   int32_t struct_size;         /* sizeof(milo_attn_args)                                   */
-  int32_t dtype;               /* milo_dtype of q, pool, k_tail, v_tail (MILO_BF16_Q8:
-                                  decode only, pool layout above)                          */
+  int32_t dtype;               /* milo_dtype of q, pool, k_tail, v_tail (MILO_BF16_Q8,
+                                  MILO_BF16_KV4, MILO_BF16_KV2: decode only, group size
+                                  <= 8, pool layouts above)                                */
   int32_t batch;               /* sequences, >= 0                                           */
   int32_t q_len;               /* query tokens per sequence: 1 (decode) or Q >= 1 (chunk)   */
   int32_t n_q_heads;           /* >= 1, multiple of n_kv_heads                              */
@@ -245,8 +292,8 @@ milo_status milo_attn_plan_decode(const milo_block* blocks, int32_t n_descriptor
  * With path MILO_PATH_SHARED only sequence 0's list is checked (the other
  * lists are not read by that path).  pool_elems is the pool size in
  * elements.  Host-checkable faults return a status as for the other entry
- * points (status must be 8-byte aligned).  With MILO_BF16_Q8, pool_elems
- * counts bytes, rule 4 asks for ld_tok a multiple of 64 and rule 5 for off a
+ * points (status must be 8-byte aligned).  With MILO_BF16_Q8, MILO_BF16_KV4
+ * and MILO_BF16_KV2, pool_elems counts bytes, rule 4 asks for ld_tok a multiple of 64 and rule 5 for off a
  * multiple of 16.  When args->unit_order is set, rule 8 checks that it is a
  * permutation of the decode units; the check counts units in args->workspace
  * (256-B aligned, at least 4 bytes per unit, which a decode workspace always

@@ -168,6 +168,38 @@ milo_status milo_quant_layout(const milo_block* src_blocks, int32_t n_blocks, in
  * The source tables are the caller's contract as in milo_attn.h. */
 milo_status milo_quantize_factors(const milo_quant_args* args, void* hip_stream);
 
+/*
+ * KIVI-style token factors ("5.3 Performance Analysis" of the summary page:
+ * the low-rank cache combines with KIVI quantisation, keys per channel and
+ * values per token).  The pages fix neither group sizes nor rounding; the
+ * reading, with L = 2^bits - 1 and bits = 4 or 2: the keys' token factor U
+ * is grouped per rank component over each 64-token chunk of the block, the
+ * values' U' per token over each run of 32 rank components; every group of
+ * elements x (bf16 values, in fp32) gets
+ *     a = fp16((max x - min x) / L),  b = fp16(min x),
+ *     code = min(max(round_half_even((x - b) / a), 0), L)   (0 when a = 0)
+ * with each fp32 step correctly rounded and a, b taken at their fp16
+ * values.  W and W' are copied unchanged.  The result is the MILO_BF16_KV4
+ * or MILO_BF16_KV2 pool of milo_attn.h, which milo_attn_decode reads.
+ * Scales overflow to infinity when a group's range exceeds L times the
+ * largest fp16 value (65504); such factors are outside the format.
+ */
+
+/* Host-side layout of the KIVI-style pool (bits 4 or 2) for the blocks
+ * src_blocks (HOST array): the same n_tok and ranks, ld_tok = n_tok rounded
+ * up to 64, blocks back to back from byte 0 in the given order.  blocks_out
+ * (host) receives n_blocks descriptors and *pool_bytes the pool size.
+ * MILO_ERR_INVALID on null pointers, negative sizes, ranks outside
+ * [0, head_dim] or bits other than 4 and 2. */
+milo_status milo_kivi_layout(const milo_block* src_blocks, int32_t n_blocks, int32_t n_kv_heads,
+                             int32_t head_dim, int32_t bits, milo_block* blocks_out, int64_t* pool_bytes);
+
+/* Quantise every block of the source pool (args->src_*) into the KIVI-style
+ * pool args->dst_pool laid out by milo_kivi_layout with the same bits (one
+ * kernel on the stream; padding codes, scales and biases are written as 0).
+ * MILO_ERR_INVALID for bits other than 4 and 2. */
+milo_status milo_quantize_kivi(const milo_quant_args* args, int32_t bits, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,10 +57,10 @@ def quantize_groups(x: np.ndarray, bits: int) -> Tuple[np.ndarray, np.ndarray, n
     b16 = lo.astype(np.float16)
     a = a16.astype(np.float32)
     b = b16.astype(np.float32)
-    for k in range(g):
-        if a[k] > 0:
-            q = np.rint((x[k] - b[k]) / a[k])          # float32 ops, round half to even
-            codes[k] = np.clip(q, 0, L).astype(np.uint8)
+    ok = a > 0
+    # float32 ops, round half to even; groups with a = 0 keep code 0
+    q = np.rint((x - b[:, None]) / np.where(ok, a, np.float32(1))[:, None])
+    codes = np.where(ok[:, None], np.clip(q, 0, L), 0).astype(np.uint8)
     return codes, a16, b16
 
 

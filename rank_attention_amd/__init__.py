@@ -13,7 +13,7 @@ from typing import Optional, Tuple
 import numpy as np
 
 from . import _lib
-from ._lib import (MILO_BF16, MILO_BF16_Q8, MILO_F32, MILO_PATH_CHUNK, MILO_PATH_DECODE, MILO_PATH_SHARED, MiloAttnArgs,
+from ._lib import (MILO_BF16, MILO_BF16_KV2, MILO_BF16_KV4, MILO_BF16_Q8, MILO_F32, MILO_PATH_CHUNK, MILO_PATH_DECODE, MILO_PATH_SHARED, MiloAttnArgs,
                    MILO_OK, MILO_ERR_DEVICE)
 from .pack import BLOCK_DTYPE, PackedCache, pack  # noqa: F401
 
@@ -58,8 +58,10 @@ def _ptr(t) -> Optional[int]:
 def make_args(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_kv_heads: int,
               scale: float, max_blocks: int, out=None, lse=None, workspace=None,
               workspace_bytes: Optional[int] = None, prof_events=(None, None),
-              unit_order=None) -> MiloAttnArgs:
-    """Fill the C argument struct from device tensors (no checks: the library checks)."""
+              unit_order=None, storage: Optional[int] = None) -> MiloAttnArgs:
+    """Fill the C argument struct from device tensors (no checks: the library
+    checks).  ``storage`` sets the dtype code of the pool (a byte pool is
+    8-bit storage unless it says otherwise)."""
     B, Q, Hq, d = (int(x) for x in q.shape)
     cap = 0 if k_tail is None else int(k_tail.shape[2])
     a = MiloAttnArgs()
@@ -67,6 +69,8 @@ def make_args(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_kv_hea
     a.dtype = _dtype_code(q)
     if pool is not None and a.dtype == MILO_BF16 and pool.dtype == _uint8():
         a.dtype = MILO_BF16_Q8   # 8-bit token factors (milo_quantize_factors)
+    if storage is not None:
+        a.dtype = int(storage)
     a.batch, a.q_len, a.n_q_heads, a.n_kv_heads, a.head_dim = B, Q, Hq, int(n_kv_heads), d
     a.scale = float(scale)
     a.q, a.pool, a.blocks, a.seq_blocks = _ptr(q), _ptr(pool), _ptr(blocks), _ptr(seq_blocks)
@@ -88,7 +92,7 @@ def workspace_bytes(args: MiloAttnArgs, path: int) -> int:
 
 def _run(path: int, q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_kv_heads, scale,
          max_blocks, out=None, lse=None, workspace=None, stream=None, prof_events=(None, None),
-         unit_order=None, want_lse=True) -> Tuple[object, object]:
+         unit_order=None, want_lse=True, storage=None) -> Tuple[object, object]:
     import torch
     lib = _lib.load()
     B, Q, Hq, d = (int(x) for x in q.shape)
@@ -99,7 +103,7 @@ def _run(path: int, q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_
         lse = torch.empty((B, Q, Hq), dtype=torch.float32, device=dev)
     a = make_args(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, n_kv_heads=n_kv_heads,
                   scale=scale, max_blocks=max_blocks, out=out, lse=lse, workspace=workspace,
-                  prof_events=prof_events, unit_order=unit_order)
+                  prof_events=prof_events, unit_order=unit_order, storage=storage)
     fn = {MILO_PATH_DECODE: lib.milo_attn_decode, MILO_PATH_CHUNK: lib.milo_attn_chunk,
           MILO_PATH_SHARED: lib.milo_attn_decode_shared}[path]
     if workspace is None:
@@ -127,7 +131,7 @@ def decode(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_kv_heads:
 
 
 def decode_noalloc(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_kv_heads: int, scale: float,
-                   max_blocks: int, out=None, lse=None, stream=None, unit_order=None):
+                   max_blocks: int, out=None, lse=None, stream=None, unit_order=None, storage=None):
     """Decode (q_len = 1) through milo_attn_decode_noalloc: the library keeps
     the partials in its own static device buffer, so no workspace is passed.
     out and lse may be preallocated (then nothing is allocated here either)."""
@@ -139,7 +143,7 @@ def decode_noalloc(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_k
     if lse is None:
         lse = torch.empty((B, Q, Hq), dtype=torch.float32, device=q.device)
     a = make_args(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, n_kv_heads=n_kv_heads,
-                  scale=scale, max_blocks=max_blocks, out=out, lse=lse, unit_order=unit_order)
+                  scale=scale, max_blocks=max_blocks, out=out, lse=lse, unit_order=unit_order, storage=storage)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     rc = lib.milo_attn_decode_noalloc(ctypes.byref(a), ctypes.c_void_p(int(stream)))
@@ -167,7 +171,8 @@ def decode_shared(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_kv
 
 
 def validate_tables(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_kv_heads: int,
-                    max_blocks: int, path: int = MILO_PATH_DECODE, scale: float = 1.0, unit_order=None):
+                    max_blocks: int, path: int = MILO_PATH_DECODE, scale: float = 1.0, unit_order=None,
+                    storage=None):
     """Check the device tables against the contract (milo_attn_validate) and
     wait for the result: None if every rule holds, else (rule name, index).
     With a decode schedule (unit_order) it is checked too, using a scratch
@@ -179,7 +184,7 @@ def validate_tables(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, *, n_
     if unit_order is not None:
         workspace = torch.empty(max(4 * int(unit_order.numel()), 256), dtype=torch.uint8, device=q.device)
     a = make_args(q, pool, blocks, seq_blocks, k_tail, v_tail, tail_len, n_kv_heads=n_kv_heads, scale=scale,
-                  max_blocks=max_blocks, workspace=workspace, unit_order=unit_order)
+                  max_blocks=max_blocks, workspace=workspace, unit_order=unit_order, storage=storage)
     n_desc = int(blocks.numel() * blocks.element_size()) // BLOCK_DTYPE.itemsize
     pool_elems = int(pool.numel()) if pool is not None else 0
     stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -220,6 +225,7 @@ class DeviceCache:
         self.v_tail = dev(packed.v_tail, bf) if cap > 0 else None
         self.tail_len = dev(packed.tail_len) if cap > 0 else None
         self.unit_order = dev(packed.unit_order) if packed.unit_order is not None else None
+        self.storage = None     # pool dtype code when not inferred from the tensors
 
     def tensors(self):
         return (self.q, self.pool, self.blocks, self.seq_blocks, self.k_tail, self.v_tail,
@@ -228,11 +234,13 @@ class DeviceCache:
     def decode(self, **kw):
         kw.setdefault("scale", self.scale)
         kw.setdefault("unit_order", self.unit_order)
+        kw.setdefault("storage", self.storage)
         return decode(*self.tensors(), n_kv_heads=self.n_kv_heads, max_blocks=self.max_blocks, **kw)
 
     def decode_noalloc(self, **kw):
         kw.setdefault("scale", self.scale)
         kw.setdefault("unit_order", self.unit_order)
+        kw.setdefault("storage", self.storage)
         return decode_noalloc(*self.tensors(), n_kv_heads=self.n_kv_heads, max_blocks=self.max_blocks, **kw)
 
     def chunk(self, **kw):
@@ -242,7 +250,7 @@ class DeviceCache:
     def validate(self, path: int = MILO_PATH_DECODE):
         order = self.unit_order if path == MILO_PATH_DECODE else None
         return validate_tables(*self.tensors(), n_kv_heads=self.n_kv_heads, max_blocks=self.max_blocks, path=path,
-                               unit_order=order)
+                               unit_order=order, storage=self.storage)
 
     def decode_shared(self, **kw):
         kw.setdefault("scale", self.scale)
@@ -260,4 +268,21 @@ class DeviceCache:
         qc = copy.copy(self)
         qc.pool, qc.blocks, qc.blocks_host = quantize(self.pool, self.blocks, self.packed.blocks,
                                                       self.n_kv_heads, self.packed.head_dim, stream=stream)
+        return qc
+
+    def kivi(self, bits: int = 4, stream=None) -> "DeviceCache":
+        """The same cache with KIVI-style token factors of the given width
+        (milo_quantize_kivi on this cache's bf16 pool): decode reads it as
+        MILO_BF16_KV4 or MILO_BF16_KV2 storage.  q, the tails and the decode
+        schedule are shared with this cache."""
+        import copy
+        import torch
+        from .encode import quantize_kivi
+        if self.packed.dtype != "bf16" or self.pool.dtype == torch.uint8:
+            raise ValueError("KIVI-style factors are made from bf16 storage")
+        qc = copy.copy(self)
+        qc.pool, qc.blocks, qc.blocks_host = quantize_kivi(self.pool, self.blocks, self.packed.blocks,
+                                                           self.n_kv_heads, self.packed.head_dim, bits,
+                                                           stream=stream)
+        qc.storage = MILO_BF16_KV4 if bits == 4 else MILO_BF16_KV2
         return qc

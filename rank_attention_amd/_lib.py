@@ -9,14 +9,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmilo_attn.so")
 
 MILO_OK, MILO_ERR_INVALID, MILO_ERR_UNSUPPORTED, MILO_ERR_WORKSPACE, MILO_ERR_DEVICE = range(5)
-MILO_F32, MILO_BF16, MILO_BF16_Q8 = 0, 1, 2
+MILO_F32, MILO_BF16, MILO_BF16_Q8, MILO_BF16_KV4, MILO_BF16_KV2 = 0, 1, 2, 3, 4
 MILO_PATH_DECODE, MILO_PATH_CHUNK, MILO_PATH_SHARED = 0, 1, 2
 MILO_NOALLOC_SCRATCH_BYTES = 32 << 20   # static scratch of milo_attn_decode_noalloc
 EXPORTS = ("milo_attn_workspace_bytes", "milo_attn_decode", "milo_attn_chunk", "milo_attn_decode_shared",
            "milo_attn_plan_decode", "milo_status_str", "milo_abi_version",
            "milo_encode_workspace_bytes", "milo_encode_spectrum", "milo_encode_factors", "milo_encode_layout",
            "milo_rank_workspace_bytes", "milo_rank_allocate", "milo_attn_validate", "milo_read_probe",
-           "milo_quant_layout", "milo_quantize_factors", "milo_attn_decode_noalloc")
+           "milo_quant_layout", "milo_quantize_factors", "milo_attn_decode_noalloc", "milo_kivi_layout",
+           "milo_quantize_kivi")
 TABLE_RULES = {1: "seq_range", 2: "too_many_blocks", 3: "rank", 4: "tokens", 5: "offset", 6: "pool_bounds",
                7: "tail_len", 8: "unit_order"}
 
@@ -160,6 +161,11 @@ def load() -> ctypes.CDLL:
         lib.milo_quant_layout.restype = ctypes.c_int
         lib.milo_quantize_factors.argtypes = [ctypes.POINTER(MiloQuantArgs), ctypes.c_void_p]
         lib.milo_quantize_factors.restype = ctypes.c_int
+        lib.milo_kivi_layout.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]
+        lib.milo_kivi_layout.restype = ctypes.c_int
+        lib.milo_quantize_kivi.argtypes = [ctypes.POINTER(MiloQuantArgs), ctypes.c_int32, ctypes.c_void_p]
+        lib.milo_quantize_kivi.restype = ctypes.c_int
         lib.milo_abi_version.argtypes = []
         lib.milo_abi_version.restype = ctypes.c_int32
         _lib = lib

@@ -32,6 +32,10 @@ UNITS = [
     ("decode.hip", ["-DMILO_INST_DT=1", "-DMILO_INST_D=128"], "decode_bf16_128.o"),
     ("decode.hip", ["-DMILO_INST_DT=2", "-DMILO_INST_D=64"], "decode_q8_64.o"),
     ("decode.hip", ["-DMILO_INST_DT=2", "-DMILO_INST_D=128"], "decode_q8_128.o"),
+    ("decode.hip", ["-DMILO_INST_DT=3", "-DMILO_INST_D=64"], "decode_kv4_64.o"),
+    ("decode.hip", ["-DMILO_INST_DT=3", "-DMILO_INST_D=128"], "decode_kv4_128.o"),
+    ("decode.hip", ["-DMILO_INST_DT=4", "-DMILO_INST_D=64"], "decode_kv2_64.o"),
+    ("decode.hip", ["-DMILO_INST_DT=4", "-DMILO_INST_D=128"], "decode_kv2_128.o"),
     ("merge.hip", [], "merge.o"),
     ("chunk.hip", [], "chunk.o"),
     ("encode.hip", [], "encode.o"),
@@ -39,6 +43,7 @@ UNITS = [
     ("validate.hip", [], "validate.o"),
     ("probe.hip", [], "probe.o"),
     ("quant.hip", [], "quant.o"),
+    ("kivi.hip", [], "kivi.o"),
     ("noalloc.hip", [], "noalloc.o"),
     ("milo_attn.cpp", [], "milo_attn.o"),
     ("milo_encode.cpp", [], "milo_encode.o"),

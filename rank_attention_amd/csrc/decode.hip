@@ -679,10 +679,64 @@ __device__ __forceinline__ void q8_body(const Q8Unit& u, const float* pf, const 
   q8_stage_z<NTV, G>(Z, u, abv, l_run, zs);
 }
 
+// o~ = z W' for the G heads of a unit whose z (ranks x 8 heads) is staged in
+// LDS at zs, W' rows in groups of 32 (the next group loading while the
+// current one is applied); writes the unit's partials (o~, m, l).
+template <int D, int G>
+__device__ __forceinline__ void store_zwp(const DecodeParams& p, int unit, const uint16_t* Wp, int rv,
+                                          const float* zs, float m_run, float l_run, int lane) {
+  constexpr int JPL = D / 64;
+  float o[G][JPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int jj = 0; jj < JPL; ++jj) o[h][jj] = 0.f;
+  constexpr int kWRows = 32;
+  auto load_w = [&](int k0, uint32_t (&wr)[kWRows]) {
+#pragma unroll
+    for (int j = 0; j < kWRows; ++j) {
+      const uint16_t* wrow = Wp + (size_t)min(k0 + j, rv - 1) * D;
+      wr[j] = (JPL == 2) ? *reinterpret_cast<const uint32_t*>(wrow + 2 * lane) : (uint32_t)wrow[lane] << 16;
+    }
+  };
+  uint32_t wa[kWRows], wb[kWRows];
+  auto apply_w = [&](int k0, const uint32_t (&wr)[kWRows]) {
+#pragma unroll
+    for (int j = 0; j < kWRows; ++j) {
+      if (k0 + j < rv) {
+        const f32x4_t z0 = *reinterpret_cast<const f32x4_t*>(zs + (k0 + j) * 8);
+        const f32x4_t z1 = *reinterpret_cast<const f32x4_t*>(zs + (k0 + j) * 8 + 4);
+        const float zz[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
+        const float wv[2] = {bf_lo(wr[j]), bf_hi(wr[j])};
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int jj = 0; jj < JPL; ++jj) o[h][jj] = fmaf(zz[h], wv[JPL == 2 ? jj : 1], o[h][jj]);
+      }
+    }
+  };
+  if (rv > 0) load_w(0, wa);
+  for (int k0 = 0; k0 < rv; k0 += 2 * kWRows) {
+    if (k0 + kWRows < rv) load_w(k0 + kWRows, wb);
+    apply_w(k0, wa);
+    if (k0 + 2 * kWRows < rv) load_w(k0 + 2 * kWRows, wa);
+    if (k0 + kWRows < rv) apply_w(k0 + kWRows, wb);
+  }
+
+  float* po = p.part.o + (size_t)unit * G * D;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int jj = 0; jj < JPL; ++jj) po[h * D + lane * JPL + jj] = o[h][jj];
+  if (lane < G) {
+    p.part.ml[((size_t)unit * G + lane) * 2 + 0] = m_run;
+    p.part.ml[((size_t)unit * G + lane) * 2 + 1] = l_run;
+  }
+}
+
 template <int D, int G>
 __device__ __forceinline__ void block_unit_q8(const DecodeParams& p, int i, int g, int unit,
                                               const milo_block& blk, uint32_t* lds) {
-  constexpr int JPL = D / 64;
   const int lane = threadIdx.x;
   Q8Unit u;
   u.quad = lane >> 4;
@@ -761,56 +815,10 @@ __device__ __forceinline__ void block_unit_q8(const DecodeParams& p, int i, int 
   else
     q8_body<2, 8, 1, G>(u, pf, abv, zs, Cl, sc, inv_sc, m_run, l_run);
   wave_lds_fence();
-
-  // ---- o~ = z W', W' rows in groups of 32, the next group loading while
-  // the current one is applied
-  float o[G][JPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int jj = 0; jj < JPL; ++jj) o[h][jj] = 0.f;
-  constexpr int kWRows = 32;
-  auto load_w = [&](int k0, uint32_t (&wr)[kWRows]) {
-#pragma unroll
-    for (int j = 0; j < kWRows; ++j) {
-      const uint16_t* wrow = Wp + (size_t)min(k0 + j, rv - 1) * D;
-      wr[j] = (JPL == 2) ? *reinterpret_cast<const uint32_t*>(wrow + 2 * lane) : (uint32_t)wrow[lane] << 16;
-    }
-  };
-  uint32_t wa[kWRows], wb[kWRows];
-  auto apply_w = [&](int k0, const uint32_t (&wr)[kWRows]) {
-#pragma unroll
-    for (int j = 0; j < kWRows; ++j) {
-      if (k0 + j < rv) {
-        const f32x4_t z0 = *reinterpret_cast<const f32x4_t*>(zs + (k0 + j) * 8);
-        const f32x4_t z1 = *reinterpret_cast<const f32x4_t*>(zs + (k0 + j) * 8 + 4);
-        const float zz[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
-        const float wv[2] = {bf_lo(wr[j]), bf_hi(wr[j])};
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int jj = 0; jj < JPL; ++jj) o[h][jj] = fmaf(zz[h], wv[JPL == 2 ? jj : 1], o[h][jj]);
-      }
-    }
-  };
-  if (rv > 0) load_w(0, wa);
-  for (int k0 = 0; k0 < rv; k0 += 2 * kWRows) {
-    if (k0 + kWRows < rv) load_w(k0 + kWRows, wb);
-    apply_w(k0, wa);
-    if (k0 + 2 * kWRows < rv) load_w(k0 + 2 * kWRows, wa);
-    if (k0 + kWRows < rv) apply_w(k0 + kWRows, wb);
-  }
-
-  float* po = p.part.o + (size_t)unit * G * D;
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int jj = 0; jj < JPL; ++jj) po[h * D + lane * JPL + jj] = o[h][jj];
-  if (lane < G) {
-    p.part.ml[((size_t)unit * G + lane) * 2 + 0] = m_run;
-    p.part.ml[((size_t)unit * G + lane) * 2 + 1] = l_run;
-  }
+  store_zwp<D, G>(p, unit, Wp, rv, zs, m_run, l_run, lane);
 }
+
+#include "decode_kivi.inc"
 
 // ---------------------------------------------------------------------------
 // fp32 storage (small workloads; same structure, plain FMA)
@@ -1147,10 +1155,14 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, uint32_t* lds
   const int nb = min(max(p.seq_blocks[i + 1] - b0, 0), p.max_blocks);
   if (slot >= nb) return;
   const milo_block blk = p.blocks[b0 + slot];
-  if (DT == MILO_BF16)
+  if constexpr (DT == MILO_BF16)
     block_unit_bf16<D, G>(p, i, g, unit, blk, lds);
-  else if (DT == MILO_BF16_Q8)
+  else if constexpr (DT == MILO_BF16_Q8)
     block_unit_q8<D, G>(p, i, g, unit, blk, lds);
+  else if constexpr (DT == MILO_BF16_KV4)
+    block_unit_kivi<D, G, 4>(p, i, g, unit, blk, lds);
+  else if constexpr (DT == MILO_BF16_KV2)
+    block_unit_kivi<D, G, 2>(p, i, g, unit, blk, lds);
   else
     block_unit_f32<D, G>(p, i, g, unit, blk, lds);
 }
@@ -1169,10 +1181,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void mi
   decode_wave<D, G, MILO_BF16_Q8>(p, lds);
 }
 
+// The KIVI-style kernel holds one or two chunks of loads in flight, with the
+// same register budget.
+template <int D, int G, int DT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void milo_decode_kv_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
+  decode_wave<D, G, DT>(p, lds);
+}
+
 template <int D, int G, int DT>
 void launch_decode_g(const DecodeParams& p, dim3 grid, hipStream_t s) {
   if constexpr (DT == MILO_BF16_Q8)
     hipLaunchKernelGGL((milo_decode_q8_kernel<D, G>), grid, dim3(64), 0, s, p);
+  else if constexpr (DT == MILO_BF16_KV4 || DT == MILO_BF16_KV2)
+    hipLaunchKernelGGL((milo_decode_kv_kernel<D, G, DT>), grid, dim3(64), 0, s, p);
   else
     hipLaunchKernelGGL((milo_decode_kernel<D, G, DT>), grid, dim3(64), 0, s, p);
 }

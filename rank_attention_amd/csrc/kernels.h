@@ -113,7 +113,8 @@ struct ValidateParams {
   unsigned long long* status;
   int64_t pool_elems;        // bytes for 8-bit factor storage
   int32_t n_descriptors, n_seqs_checked, batch, max_blocks, n_kv_heads, head_dim, tail_cap, tail_min;
-  int32_t q8;                // 8-bit factor storage: byte offsets, multiples of 16
+  int32_t dtype;             // storage type; the 8-bit and KIVI-style pools count bytes,
+                             // with offsets multiples of 16 and ld_tok multiples of 64
   // decode schedule check (unit_order non-null): n_units entries, and one
   // count per unit in caller scratch
   const int32_t* unit_order;
@@ -131,6 +132,18 @@ struct QuantParams {
   int32_t n_blocks, n_kv_heads;
 };
 hipError_t launch_quantize(const QuantParams& p, int head_dim, hipStream_t s);
+
+// KIVI-style factors: one workgroup per (block, KV head) quantises its
+// chunks (keys per rank component and 64-token chunk, values per token and
+// 32 rank components) and copies W and W'.
+hipError_t launch_quantize_kivi(const QuantParams& p, int head_dim, int bits, hipStream_t s);
+
+// Bytes of one KV head of a KIVI-style block with nch 64-token chunks
+// (bits 4 or 2; the layout of milo_attn.h).
+__host__ __device__ inline int64_t kivi_head_bytes(int64_t nch, int64_t r, int64_t rv, int64_t d, int bits) {
+  const int64_t ng8 = (r + 7) / 8, ngv = (rv + 31) / 32, ntv = (rv + 15) / 16;
+  return 16 + nch * (32 * ng8 + 64 * bits * ng8 + 256 * ngv + 128 * bits * ntv) + 2 * d * (r + rv);
+}
 hipError_t launch_validate(const ValidateParams& p, hipStream_t s);
 
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int n_wg, hipStream_t s);
@@ -148,6 +161,10 @@ hipError_t launch_decode_dt_1_64(const DecodeParams& p, int group, hipStream_t s
 hipError_t launch_decode_dt_1_128(const DecodeParams& p, int group, hipStream_t s);
 hipError_t launch_decode_dt_2_64(const DecodeParams& p, int group, hipStream_t s);
 hipError_t launch_decode_dt_2_128(const DecodeParams& p, int group, hipStream_t s);
+hipError_t launch_decode_dt_3_64(const DecodeParams& p, int group, hipStream_t s);
+hipError_t launch_decode_dt_3_128(const DecodeParams& p, int group, hipStream_t s);
+hipError_t launch_decode_dt_4_64(const DecodeParams& p, int group, hipStream_t s);
+hipError_t launch_decode_dt_4_128(const DecodeParams& p, int group, hipStream_t s);
 
 inline hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int group,
                                 hipStream_t s) {
@@ -157,6 +174,10 @@ inline hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, 
   if (dtype == MILO_BF16 && head_dim == 128) return launch_decode_dt_1_128(p, group, s);
   if (dtype == MILO_BF16_Q8 && head_dim == 64) return launch_decode_dt_2_64(p, group, s);
   if (dtype == MILO_BF16_Q8 && head_dim == 128) return launch_decode_dt_2_128(p, group, s);
+  if (dtype == MILO_BF16_KV4 && head_dim == 64) return launch_decode_dt_3_64(p, group, s);
+  if (dtype == MILO_BF16_KV4 && head_dim == 128) return launch_decode_dt_3_128(p, group, s);
+  if (dtype == MILO_BF16_KV2 && head_dim == 64) return launch_decode_dt_4_64(p, group, s);
+  if (dtype == MILO_BF16_KV2 && head_dim == 128) return launch_decode_dt_4_128(p, group, s);
   return hipErrorInvalidValue;
 }
 hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t s);

@@ -197,6 +197,53 @@ milo_status milo_quant_layout(const milo_block* src_blocks, int32_t n_blocks, in
   return MILO_OK;
 }
 
+milo_status milo_kivi_layout(const milo_block* src_blocks, int32_t n_blocks, int32_t n_kv_heads, int32_t head_dim,
+                             int32_t bits, milo_block* blocks_out, int64_t* pool_bytes) {
+  if (n_blocks < 0 || n_kv_heads < 1 || head_dim < 1 || head_dim % 8 != 0 || !pool_bytes) return MILO_ERR_INVALID;
+  if (bits != 4 && bits != 2) return MILO_ERR_INVALID;
+  if (n_blocks > 0 && (!src_blocks || !blocks_out)) return MILO_ERR_INVALID;
+  int64_t off = 0;
+  for (int32_t b = 0; b < n_blocks; ++b) {
+    const milo_block& s = src_blocks[b];
+    if (s.n_tok < 0 || s.n_tok > INT32_MAX - 63) return MILO_ERR_INVALID;
+    if (s.rank_k < 0 || s.rank_k > head_dim || s.rank_v < 0 || s.rank_v > head_dim) return MILO_ERR_INVALID;
+    const int32_t ld = (s.n_tok + 63) / 64 * 64;
+    blocks_out[b].off = off;
+    blocks_out[b].n_tok = s.n_tok;
+    blocks_out[b].ld_tok = ld;
+    blocks_out[b].rank_k = s.rank_k;
+    blocks_out[b].rank_v = s.rank_v;
+    off += (int64_t)n_kv_heads * milo::kivi_head_bytes(ld / 64, s.rank_k, s.rank_v, head_dim, bits);
+  }
+  *pool_bytes = off;
+  return MILO_OK;
+}
+
+milo_status milo_quantize_kivi(const milo_quant_args* a, int32_t bits, void* hip_stream) {
+  if (!a) return MILO_ERR_INVALID;
+  if (a->struct_size != (int32_t)sizeof(milo_quant_args)) return MILO_ERR_INVALID;
+  if (bits != 4 && bits != 2) return MILO_ERR_INVALID;
+  if (a->n_blocks < 0 || a->n_kv_heads < 1) return MILO_ERR_INVALID;
+  if (a->head_dim != 64 && a->head_dim != 128) return MILO_ERR_UNSUPPORTED;
+  if ((int64_t)a->n_blocks * a->n_kv_heads > INT32_MAX) return MILO_ERR_UNSUPPORTED;
+  if (a->n_blocks == 0) return MILO_OK;
+  if (!a->src_pool || !a->src_blocks || !a->dst_pool || !a->dst_blocks) return MILO_ERR_INVALID;
+  if (!enc_aligned(a->src_pool, 16) || !enc_aligned(a->dst_pool, 16) || !enc_aligned(a->src_blocks, 8) ||
+      !enc_aligned(a->dst_blocks, 8))
+    return MILO_ERR_INVALID;
+  milo::QuantParams p{};
+  p.src_pool = static_cast<const uint16_t*>(a->src_pool);
+  p.src_blocks = a->src_blocks;
+  p.dst_pool = static_cast<uint8_t*>(a->dst_pool);
+  p.dst_blocks = a->dst_blocks;
+  p.n_blocks = a->n_blocks;
+  p.n_kv_heads = a->n_kv_heads;
+  milo::clear_stale_error();
+  if (milo::launch_quantize_kivi(p, a->head_dim, bits, reinterpret_cast<hipStream_t>(hip_stream)) != hipSuccess)
+    return MILO_ERR_DEVICE;
+  return MILO_OK;
+}
+
 milo_status milo_quantize_factors(const milo_quant_args* a, void* hip_stream) {
   if (!a) return MILO_ERR_INVALID;
   if (a->struct_size != (int32_t)sizeof(milo_quant_args)) return MILO_ERR_INVALID;

@@ -28,16 +28,19 @@ __global__ __launch_bounds__(kValThreads) void milo_validate_kernel(ValidatePara
     const milo_block blk = p.blocks[idx];
     const int d = p.head_dim;
     if (blk.rank_k < 0 || blk.rank_k > d || blk.rank_v < 0 || blk.rank_v > d) report(p.status, 3, idx);
-    const int ld_align = p.q8 ? 63 : 7, off_align = p.q8 ? 15 : 7;
+    const bool bytes = p.dtype == MILO_BF16_Q8 || p.dtype == MILO_BF16_KV4 || p.dtype == MILO_BF16_KV2;
+    const int ld_align = bytes ? 63 : 7, off_align = bytes ? 15 : 7;
     if (blk.n_tok < 0 || blk.ld_tok < blk.n_tok || (blk.ld_tok & ld_align) != 0) report(p.status, 4, idx);
     if (blk.off < 0 || (blk.off & off_align) != 0) report(p.status, 5, idx);
     const int64_t rk = min(max(blk.rank_k, 0), d), rv = min(max(blk.rank_v, 0), d);
     const int64_t ld = max(blk.ld_tok, 0);
-    // elements of the pool's dtype, or bytes of the 8-bit layout
+    // elements of the pool's dtype, or bytes of the 8-bit and KIVI-style layouts
     const int64_t nt = max(blk.n_tok, 0), rk16 = (rk + 15) & ~15ll;
-    const int64_t size = p.q8 ? (int64_t)p.n_kv_heads * (nt * rk16 + rv * ld + (rk + rv) * 2 * d +
-                                                         ((8 * (rk + rv) + 15) & ~15ll))
-                              : (int64_t)p.n_kv_heads * (rk + rv) * (ld + d);
+    int64_t size = (int64_t)p.n_kv_heads * (rk + rv) * (ld + d);
+    if (p.dtype == MILO_BF16_Q8)
+      size = (int64_t)p.n_kv_heads * (nt * rk16 + rv * ld + (rk + rv) * 2 * d + ((8 * (rk + rv) + 15) & ~15ll));
+    else if (p.dtype == MILO_BF16_KV4 || p.dtype == MILO_BF16_KV2)
+      size = (int64_t)p.n_kv_heads * kivi_head_bytes(ld / 64, rk, rv, d, p.dtype == MILO_BF16_KV4 ? 4 : 2);
     if (blk.off >= 0 && blk.off + size > p.pool_elems) report(p.status, 6, idx);
   }
   if (idx < p.n_seqs_checked) {

@@ -74,6 +74,48 @@ def quantize(pool, blocks_dev, blocks_host: np.ndarray, n_kv_heads: int, head_di
     return qpool, qdev, blocks
 
 
+def kivi_layout(src_blocks: np.ndarray, n_kv_heads: int, head_dim: int, bits: int) -> Tuple[np.ndarray, int]:
+    """Descriptors (BLOCK_DTYPE) and size in bytes of the KIVI-style pool
+    (bits 4 or 2) for the blocks of a bf16 pool (milo_kivi_layout)."""
+    from . import MiloError, status_str
+    src = np.ascontiguousarray(src_blocks, BLOCK_DTYPE)
+    out = np.zeros(len(src), BLOCK_DTYPE)
+    nbytes = ctypes.c_int64(0)
+    rc = _lib.load().milo_kivi_layout(src.ctypes.data if len(src) else None, len(src), int(n_kv_heads),
+                                      int(head_dim), int(bits), out.ctypes.data if len(src) else None,
+                                      ctypes.byref(nbytes))
+    if rc != MILO_OK:
+        raise MiloError(rc, status_str(rc))
+    return out, int(nbytes.value)
+
+
+def quantize_kivi(pool, blocks_dev, blocks_host: np.ndarray, n_kv_heads: int, head_dim: int, bits: int,
+                  stream=None):
+    """KIVI-style token factors of a bf16 pool (milo_quantize_kivi).  Returns
+    (pool uint8 tensor, descriptors on the device, descriptors on the host);
+    milo_attn_decode reads the result as MILO_BF16_KV4 / MILO_BF16_KV2 storage."""
+    import torch
+    from . import MiloError, status_str
+    lib = _lib.load()
+    blocks, nbytes = kivi_layout(blocks_host, n_kv_heads, head_dim, bits)
+    dev = pool.device
+    qpool = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    qdev = torch.from_numpy(blocks.view(np.uint8).copy()).to(dev)
+    a = MiloQuantArgs()
+    a.struct_size = ctypes.sizeof(MiloQuantArgs)
+    a.n_blocks, a.n_kv_heads, a.head_dim = len(blocks), int(n_kv_heads), int(head_dim)
+    a.src_pool, a.src_blocks = pool.data_ptr(), blocks_dev.data_ptr()
+    a.dst_pool, a.dst_blocks = qpool.data_ptr(), qdev.data_ptr()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.milo_quantize_kivi(ctypes.byref(a), int(bits), ctypes.c_void_p(int(stream)))
+    if rc != MILO_OK:
+        if rc == MILO_ERR_DEVICE:
+            raise RuntimeError(f"milo_quantize_kivi: {status_str(rc)}")
+        raise MiloError(rc, status_str(rc))
+    return qpool, qdev, blocks
+
+
 def allocate_ranks(sigma, budget_k: int, budget_v: int, r_min: int, unit: int = 1, stream=None):
     """Entropy-driven ranks (milo_rank_allocate) from device spectra sigma
     [n_blocks][Hkv][2][d] (fp32, descending per head).  Returns (ranks int32

@@ -64,8 +64,13 @@ MILO_STUB_DECODE(launch_decode_dt_1_64)
 MILO_STUB_DECODE(launch_decode_dt_1_128)
 MILO_STUB_DECODE(launch_decode_dt_2_64)
 MILO_STUB_DECODE(launch_decode_dt_2_128)
+MILO_STUB_DECODE(launch_decode_dt_3_64)
+MILO_STUB_DECODE(launch_decode_dt_3_128)
+MILO_STUB_DECODE(launch_decode_dt_4_64)
+MILO_STUB_DECODE(launch_decode_dt_4_128)
 hipError_t launch_rank(const RankParams&, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_quantize(const QuantParams&, int, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_quantize_kivi(const QuantParams&, int, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_encode_factors(const EncodeParams&, int, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_encode_spectrum(const EncodeParams&, int, int, hipStream_t) { ++g_launches; return hipSuccess; }
 }  // namespace milo
@@ -223,6 +228,13 @@ void layouts(std::mt19937& rng) {
     int64_t bytes = -1;
     EXPECT(milo_quant_layout(nb ? out.data() : nullptr, nb, hkv, d, nb ? q8.data() : nullptr, &bytes) == MILO_OK);
     for (int b = 0; b < nb; ++b) EXPECT(q8[b].off % 16 == 0 && q8[b].ld_tok % 64 == 0 && q8[b].off < bytes + 1);
+    for (int bits = 2; bits <= 4; bits += 2) {
+      std::vector<milo_block> kv(nb);
+      int64_t kbytes = -1;
+      EXPECT(milo_kivi_layout(nb ? out.data() : nullptr, nb, hkv, d, bits, nb ? kv.data() : nullptr, &kbytes) ==
+             MILO_OK);
+      for (int b = 0; b < nb; ++b) EXPECT(kv[b].off % 16 == 0 && kv[b].ld_tok % 64 == 0 && kv[b].off < kbytes + 1);
+    }
   }
   int32_t one = 5;
   milo_block ob{};

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_struct_size():
-    assert ra.abi_version() == 4
+    assert ra.abi_version() == 5
     # 7 int32 + float, 4 pointers, 2 int32, 6 pointers, size_t, 3 pointers; the
     # C side agrees, or the batch-0 call below would fail its struct_size check
     assert ctypes.sizeof(_lib.MiloAttnArgs) == 8 * 4 + 4 * 8 + 2 * 4 + 6 * 8 + 8 + 3 * 8
@@ -436,6 +436,75 @@ def test_q8_storage_is_decode_only():
     assert lib.milo_attn_chunk(ctypes.byref(c), None) == _lib.MILO_ERR_UNSUPPORTED
     d = good_args(dtype=_lib.MILO_BF16_Q8, head_dim=128, n_q_heads=4)
     assert lib.milo_attn_decode_shared(ctypes.byref(d), None) == _lib.MILO_ERR_UNSUPPORTED
+
+
+def test_kivi_layout():
+    """Sizes from the layout milo_attn.h states: per head a 16-byte header,
+    per 64-token chunk 32 ng8 bytes of key scales and biases, 8 BITS ng8 x 8
+    bytes of key codes, 256 ngv bytes of value scales and biases and
+    16 BITS ntv x 8 bytes of value codes, then bf16 W and W'."""
+    from rank_attention_amd import encode as enc
+    src = np.zeros(3, ra.BLOCK_DTYPE)
+    src["n_tok"], src["rank_k"], src["rank_v"] = [37, 1024, 0], [5, 128, 0], [33, 1, 7]
+    src["off"], src["ld_tok"] = [8, 1000, 5000], [40, 1024, 0]
+    for bits in (4, 2):
+        blocks, nbytes = enc.kivi_layout(src, n_kv_heads=2, head_dim=128, bits=bits)
+        assert list(blocks["ld_tok"]) == [64, 1024, 0]
+        assert list(blocks["rank_k"]) == [5, 128, 0] and list(blocks["rank_v"]) == [33, 1, 7]
+        def head(nch, r, rv):
+            ng8, ngv, ntv = -(-r // 8), -(-rv // 32), -(-rv // 16)
+            return 16 + nch * (32 * ng8 + 64 * bits * ng8 + 256 * ngv + 128 * bits * ntv) + 256 * (r + rv)
+        h0, h1, h2 = head(1, 5, 33), head(16, 128, 1), head(0, 0, 7)
+        assert h0 == 16 + (32 + 64 * bits + 512 + 128 * bits * 3) + 256 * 38
+        assert list(blocks["off"]) == [0, 2 * h0, 2 * h0 + 2 * h1]
+        assert nbytes == 2 * (h0 + h1 + h2)
+        assert all(o % 16 == 0 for o in blocks["off"])
+    bad = src.copy()
+    bad["rank_v"][0] = 129
+    with pytest.raises(ra.MiloError):
+        enc.kivi_layout(bad, n_kv_heads=2, head_dim=128, bits=4)
+    with pytest.raises(ra.MiloError):
+        enc.kivi_layout(src, n_kv_heads=2, head_dim=128, bits=3)
+    lib = _lib.load()
+    out = ctypes.c_int64(0)
+    assert lib.milo_kivi_layout(None, 1, 1, 128, 4, None, ctypes.byref(out)) == _lib.MILO_ERR_INVALID
+    assert lib.milo_kivi_layout(None, 0, 1, 128, 2, None, ctypes.byref(out)) == _lib.MILO_OK and out.value == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"struct_size": 8}, _lib.MILO_ERR_INVALID),
+    ({"head_dim": 96}, _lib.MILO_ERR_UNSUPPORTED),
+    ({"n_blocks": -1}, _lib.MILO_ERR_INVALID),
+    ({"src_pool": None}, _lib.MILO_ERR_INVALID),
+    ({"dst_pool": FAKE + 8}, _lib.MILO_ERR_INVALID),
+    ({"n_blocks": 0, "src_pool": None}, _lib.MILO_OK),
+])
+def test_quantize_kivi_rejects_before_any_hip_call(over, code):
+    lib = _lib.load()
+    for bits in (4, 2):
+        assert lib.milo_quantize_kivi(ctypes.byref(quant_args(**over)), bits, None) == code
+    for bits in (0, 1, 3, 8):
+        assert lib.milo_quantize_kivi(ctypes.byref(quant_args()), bits, None) == _lib.MILO_ERR_INVALID
+    assert lib.milo_quantize_kivi(None, 4, None) == _lib.MILO_ERR_INVALID
+
+
+@pytest.mark.parametrize("dtype", [_lib.MILO_BF16_KV4, _lib.MILO_BF16_KV2])
+def test_kivi_storage_is_decode_only_with_groups_up_to_eight(dtype):
+    lib = _lib.load()
+    for d in (64, 128):
+        a = good_args(dtype=dtype, head_dim=d)
+        assert lib.milo_attn_workspace_bytes(ctypes.byref(a), _lib.MILO_PATH_DECODE) > 0
+    c = good_args(dtype=dtype, head_dim=128, q_len=4, n_q_heads=4)
+    for path in (_lib.MILO_PATH_CHUNK, _lib.MILO_PATH_SHARED):
+        assert lib.milo_attn_workspace_bytes(ctypes.byref(c), path) == 0
+    assert lib.milo_attn_chunk(ctypes.byref(c), None) == _lib.MILO_ERR_UNSUPPORTED
+    d = good_args(dtype=dtype, head_dim=128, n_q_heads=4)
+    assert lib.milo_attn_decode_shared(ctypes.byref(d), None) == _lib.MILO_ERR_UNSUPPORTED
+    g9 = good_args(dtype=dtype, head_dim=128, n_q_heads=9, n_kv_heads=1)
+    assert lib.milo_attn_workspace_bytes(ctypes.byref(g9), _lib.MILO_PATH_DECODE) == 0
+    assert lib.milo_attn_decode(ctypes.byref(g9), None) == _lib.MILO_ERR_UNSUPPORTED
+    bad = good_args(dtype=5)
+    assert lib.milo_attn_decode(ctypes.byref(bad), None) == _lib.MILO_ERR_UNSUPPORTED
 
 
 def test_library_binds_to_torchs_hip_runtime():

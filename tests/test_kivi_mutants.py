@@ -8,14 +8,15 @@ from oracle import kivi as real
 from tests import test_kivi_pins as pins
 
 MUTANTS = {
-    "floor_not_round": ("q = np.rint((x[k] - b[k]) / a[k])", "q = np.floor((x[k] - b[k]) / a[k])"),
-    "round_half_up": ("q = np.rint((x[k] - b[k]) / a[k])",
-                      "q = np.floor((x[k] - b[k]) / a[k] + np.float32(0.5))"),
+    "floor_not_round": ("q = np.rint((x - b[:, None])", "q = np.floor((x - b[:, None])"),
+    "round_half_up": ("q = np.rint((x - b[:, None]) / np.where(ok, a, np.float32(1))[:, None])",
+                      "q = np.floor((x - b[:, None]) / np.where(ok, a, np.float32(1))[:, None] + np.float32(0.5))"),
     "2_to_the_bits_levels": ("return (1 << bits) - 1", "return 1 << bits"),
     "symmetric_no_bias": ("b16 = lo.astype(np.float16)", "b16 = np.zeros_like(lo, dtype=np.float16)"),
     "fp32_scale_decides": ("a = a16.astype(np.float32)", "a = (hi - lo) / L"),
     "fp32_bias_decides": ("b = b16.astype(np.float32)", "b = lo"),
-    "no_clamp": ("codes[k] = np.clip(q, 0, L).astype(np.uint8)", "codes[k] = q.astype(np.int64).astype(np.uint8)"),
+    "no_clamp": ("codes = np.where(ok[:, None], np.clip(q, 0, L), 0).astype(np.uint8)",
+                 "codes = np.where(ok[:, None], q, 0).astype(np.int64).astype(np.uint8)"),
     "keys_grouped_per_token": ("Uq[g] = dequantize_keys(*quantize_keys(U[g], bits))",
                                "Uq[g] = dequantize_values(*quantize_values(U[g], bits))"),
     "values_grouped_per_channel": ("Upq[g] = dequantize_values(*quantize_values(Up[g], bits))",
