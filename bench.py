@@ -23,13 +23,19 @@ once (milo_quantize_factors, outside the timed region) and the decode path
 reads the 8-bit pool; algorithmic bytes are the codes, the bf16 W/W' and the
 per-row (scale, bias) pairs plus the tails.
 
+KIVI-style token factors (--kivi 4 or --kivi 2, on a decode workload): the
+bf16 pool is quantised once (milo_quantize_kivi) and the decode path reads
+the 4- or 2-bit pool; algorithmic bytes are the codes at their width, one
+fp16 (scale, bias) pair per key group (rank component x 64-token chunk) and
+per value group (token x 32 rank components), the bf16 W/W' and the tails.
+
 Encode (--encode, workload enc_qwen7b_64k): one step runs the encode
 workflow over the dense keys and values of one 64k-token context (spectra,
 entropy-driven ranks at a 50% budget, host layout, factors); context
 tokens/s, and the spectrum kernel's algorithmic fp32 rate against the 157.3
 TFLOP/s vector peak.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen7b_64k] [--shared | --q8]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen7b_64k] [--shared | --q8 | --kivi 4|2]
     python bench.py --encode [--workload enc_qwen7b_64k]
 """
 from __future__ import annotations
@@ -49,6 +55,8 @@ ENCODE_METRIC = "low-rank-KV encode: context tokens/s factorised (dense K/V -> p
 FP32_VECTOR_PEAK_TFLOPS = 157.3
 METRIC = "low-rank-KV decode attn: context tokens/s and % of HBM peak (7B, 64k)"
 Q8_METRIC = "low-rank-KV decode attn, 8-bit token factors: context tokens/s and % of HBM peak (7B, 64k)"
+KIVI_METRIC = ("low-rank-KV decode attn, KIVI-style {bits}-bit token factors: context tokens/s and % of HBM peak "
+               "(7B, 64k)")
 SHARED_METRIC = "low-rank-KV shared-context decode attn: context tokens/s (7B, 64k context shared by the batch)"
 CHUNK_METRIC = "low-rank-KV chunked-query attn: query tokens/s and % of bf16 MFMA peak (32B, Q=256)"
 HBM_PEAK_GBS = 8000.0
@@ -56,7 +64,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 LAST_LEVEL_CACHE_BYTES = 256 << 20   # MI355X Infinity Cache
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
-    "decode": ["rank_attention_amd/csrc/decode.hip", "rank_attention_amd/csrc/device_common.h"],
+    "decode": ["rank_attention_amd/csrc/decode.hip", "rank_attention_amd/csrc/decode_kivi.inc",
+               "rank_attention_amd/csrc/device_common.h"],
     "chunk": ["rank_attention_amd/csrc/chunk.hip", "rank_attention_amd/csrc/device_common.h"],
     "encode": ["rank_attention_amd/csrc/encode.hip", "rank_attention_amd/csrc/device_common.h"],
 }
@@ -331,13 +340,29 @@ def cpu_baseline_chunk(wl, seconds: float):
                       f"fp64 reconstruct-then-attend, {elapsed:.1f} s"}
 
 
-def cpu_baseline(wl, seconds: float, q8: bool = False):
+def kivi_factor_bytes(wl, bits: int) -> int:
+    """Algorithmic bytes of the KIVI-style factors: per block and KV head the
+    codes at `bits` per element, an fp16 (scale, bias) pair per key group
+    (rank component x 64-token chunk) and per value group (token x 32 rank
+    components), and the bf16 W and W'."""
+    d, h = wl.cfg.head_dim, wl.cfg.n_kv_heads
+    total = 0
+    for s_ in wl.blocks:
+        for b in s_:
+            T, r, rv = b.n_tok, b.rank_k, b.rank_v
+            codes = (T * (r + rv) * bits + 7) // 8
+            groups = -(-T // 64) * r + T * -(-rv // 32)
+            total += h * (codes + 4 * groups + 2 * d * (r + rv))
+    return total
+
+
+def cpu_baseline(wl, seconds: float, q8: bool = False, kivi_bits: int = 0):
     """fp64 oracle on whole sequences of the same workload, in order and again
-    from the first when the batch is done, until `seconds` pass (q8: the
-    oracle's 8-bit quantisation of the token factors, then attention over the
-    dequantized factors, both timed)."""
+    from the first when the batch is done, until `seconds` pass (q8 or
+    kivi_bits: the oracle's quantisation of the token factors, then attention
+    over the dequantized factors, both timed)."""
     import oracle
-    from oracle import quant
+    from oracle import kivi, quant
     toks, elapsed, done = 0, 0.0, 0
     while wl.batch > 0 and elapsed < seconds:
         i = done % wl.batch
@@ -345,6 +370,8 @@ def cpu_baseline(wl, seconds: float, q8: bool = False):
         t0 = time.perf_counter()
         if q8:
             blocks = quant.quantize_logical_blocks(blocks)
+        if kivi_bits:
+            blocks = kivi.quantize_logical_blocks(blocks, kivi_bits)
         oracle.attend_logical(q, blocks, kt, vt, tl, wl.scale)
         elapsed += time.perf_counter() - t0
         toks += sum(b.n_tok for b in wl.blocks[i]) + int(wl.tail_len[i])
@@ -353,6 +380,7 @@ def cpu_baseline(wl, seconds: float, q8: bool = False):
             "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{done} sequence evaluations over the {wl.batch} of the workload ({toks} context "
                       f"tokens, all {wl.cfg.n_q_heads} query heads), {'fp32 8-bit quantisation, ' if q8 else ''}"
+                      f"{f'fp32 KIVI-style {kivi_bits}-bit quantisation, ' if kivi_bits else ''}"
                       f"fp64 reconstruct-then-attend, {elapsed:.1f} s"}
 
 
@@ -373,6 +401,8 @@ def main(argv=None):
                     help="shared-context decode: the batch attends to sequence 0's context")
     ap.add_argument("--q8", action="store_true",
                     help="decode over 8-bit token factors (the bf16 pool quantised once before timing)")
+    ap.add_argument("--kivi", type=int, default=0, choices=(0, 2, 4),
+                    help="decode over KIVI-style 4- or 2-bit token factors (quantised once before timing)")
     ap.add_argument("--copies", type=int, default=2,
                     help="pool copies read in rotation so no step finds the last one's bytes in cache")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -421,6 +451,10 @@ def main(argv=None):
     is_chunk = cfg.path == "chunk"
     shared = args.shared
     q8 = args.q8
+    kv = args.kivi
+    if kv and (q8 or is_chunk or shared or cfg.dtype != "bf16"):
+        print("--kivi needs a bf16 decode workload (and neither --shared nor --q8)", file=sys.stderr)
+        return 2
     if shared and is_chunk:
         print("--shared needs a decode workload", file=sys.stderr)
         return 2
@@ -442,6 +476,9 @@ def main(argv=None):
     if q8:
         dc = dc.quantized()
         torch.cuda.synchronize()
+    if kv:
+        dc = dc.kivi(kv)
+        torch.cuda.synchronize()
     copies = args.copies
     if shared:
         # the shared factors and the tails are small: rotate enough copies of
@@ -459,7 +496,7 @@ def main(argv=None):
     out = torch.empty((B, Q, Hq, d), dtype=torch.float32, device="cuda:0")
     lse = torch.empty((B, Q, Hq), dtype=torch.float32, device="cuda:0")
     a0 = ra.make_args(*dc.tensors(), n_kv_heads=dc.n_kv_heads, scale=dc.scale, max_blocks=dc.max_blocks,
-                      out=out, lse=lse)
+                      out=out, lse=lse, storage=dc.storage)
     need = lib.milo_attn_workspace_bytes(ctypes.byref(a0), path_code)
     ws = torch.empty(int(need), dtype=torch.uint8, device="cuda:0")
     argsets = []
@@ -467,7 +504,8 @@ def main(argv=None):
         a = ra.make_args(dc.q, pool, dc.blocks, dc.seq_blocks, kt, vt, dc.tail_len,
                          n_kv_heads=dc.n_kv_heads, scale=dc.scale, max_blocks=dc.max_blocks, out=out,
                          lse=lse, workspace=ws,
-                         unit_order=None if (args.no_plan or is_chunk or shared) else dc.unit_order)
+                         unit_order=None if (args.no_plan or is_chunk or shared) else dc.unit_order,
+                         storage=dc.storage)
         argsets.append(a)
     stream = torch.cuda.current_stream().cuda_stream
     setup_s = time.time() - t0
@@ -520,13 +558,15 @@ def main(argv=None):
         # per KV head and row: n_tok codes, d bf16 of W or W', one fp32 (scale, bias) pair
         factor_bytes = sum(cfg.n_kv_heads * (b.rank_k + b.rank_v) * (b.n_tok + 2 * d + 8)
                            for s_ in wl.blocks for b in s_)
+    if kv:
+        factor_bytes = kivi_factor_bytes(wl, kv)
     alg_bytes = factor_bytes + wl.tail_bytes()
     es = 2 if cfg.dtype == "bf16" else 4
     # every byte a step moves: factors + tails + q, partials written and read, out and lse
     all_bytes = (factor_bytes + wl.tail_bytes() + B * Q * Hq * d * es + 2 * int(need)
                  + B * Q * Hq * (d + 1) * 4)
     prof_key = ((cfg.name + "_shared", "chunk") if shared else (cfg.name + "_q8", "decode") if q8
-                else (cfg.name, cfg.path))
+                else (cfg.name + f"_kv{kv}", "decode") if kv else (cfg.name, cfg.path))
     if shared:
         flops = chunk_flops(wl, shared=True)
         alg_bytes = shared_factor_bytes + wl.tail_bytes()
@@ -559,8 +599,8 @@ def main(argv=None):
         achieved = alg_bytes / (kmean * 1e-3) / 1e9
         peak, unit, bound = HBM_PEAK_GBS, "GB/s", "hbm"
         value, vunit, metric = (wl.context_tokens() / (ms_per_step * 1e-3), "context tokens/s",
-                                Q8_METRIC if q8 else METRIC)
-        kname = "milo_decode_q8_kernel" if q8 else "milo_decode_kernel"
+                                Q8_METRIC if q8 else KIVI_METRIC.format(bits=kv) if kv else METRIC)
+        kname = "milo_decode_q8_kernel" if q8 else "milo_decode_kv_kernel" if kv else "milo_decode_kernel"
         print(f"[bench] attention kernel: mean {kmean * 1e3:.1f} us, median "
               f"{kern_sorted[len(kern_sorted) // 2] * 1e3:.1f} us, min {kern_sorted[0] * 1e3:.1f} us; "
               f"step {ms_per_step * 1e3:.1f} us; {achieved:.0f} GB/s on {alg_bytes / 1e6:.1f} MB",
@@ -577,19 +617,23 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16+u8" if q8 else cfg.dtype,
+        "dtype": "bf16+u8" if q8 else f"bf16+u{kv}" if kv else cfg.dtype,
         "data": "synthetic",
         "config": {"workload": cfg.name, "desc": cfg.desc, "batch": cfg.batch, "q_len": cfg.q_len,
                    "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
                    "blocks_per_seq": cfg.n_blocks, "block_tokens": cfg.block_tokens,
                    "tail_len": cfg.tail_len, "context_tokens_per_step": wl.context_tokens(),
                    "variant": args.variant, "pool_copies": len(pools), "shared_context": shared,
-                   "factor_storage": "u8 token factors, bf16 W/W'" if q8 else cfg.dtype},
+                   "factor_storage": ("u8 token factors, bf16 W/W'" if q8 else
+                                      f"KIVI-style u{kv} token factors, fp16 group scales, bf16 W/W'" if kv
+                                      else cfg.dtype)},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic_from_profiles(*prof_key),
                      "kernel": kname, "kernel_us_mean": kmean * 1e3,
                      "kernel_us_p10": pct(0.1), "kernel_us_median": pct(0.5), "kernel_us_p90": pct(0.9),
                      "algorithmic_bytes_per_launch": alg_bytes, "all_bytes_per_step": all_bytes,
+                     "algorithmic_factor_bytes_per_launch": factor_bytes,
+                     "achieved_factor_only": factor_bytes / (kmean * 1e-3) / 1e9,
                      "kernel_source_sha": kernel_source_sha(prof_key[1])},
         "cpu_baseline": None,
     }
@@ -603,7 +647,7 @@ def main(argv=None):
               file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = (cpu_baseline_chunk(wl, args.cpu_seconds) if is_chunk
-                               else cpu_baseline(wl, args.cpu_seconds, q8=q8))
+                               else cpu_baseline(wl, args.cpu_seconds, q8=q8, kivi_bits=kv))
     print(json.dumps(res), flush=True)
     return 0
 
