@@ -148,11 +148,12 @@ typedef enum milo_path {
  * (g8, col, m) of chunk c holds ranks 8 g8 + i (i = 0..7) of chunk token
  * 16 (col / 4) + 4 m + col % 4.  Value words of tile kt, lane l of chunk c
  * hold rank 16 kt + l % 16 at chunk tokens 16 (l / 16) + 8 s + i for two
- * 8-code words s = 0, 1.  Inside a 4-bit word, code i sits at bits
- * 4 (i / 2 + 4 (i % 2)) .. +3.  2-bit words come in pairs sharing one
- * 32-bit word: the key words (g8, col, 2d) and (g8, col, 2d + 1) form
- * dword d, the value words s = 0, 1 form the lane's dword; code i of word
- * u in {0, 1} sits at bits 2 (4 u + i / 2 + 8 (i % 2)) .. +1.
+ * 8-code words s = 0, 1.  Inside a 4-bit word, code i sits in nibble 2i
+ * (i < 4) or 2 (i - 4) + 1 (i >= 4), bits 4 nibble .. +3.  2-bit words come
+ * in pairs sharing one 32-bit word: the key words (g8, col, 2d) and
+ * (g8, col, 2d + 1) form dword d, the value words s = 0, 1 form the lane's
+ * dword; with P = 4 u + i / 2, code i of word u in {0, 1} sits at bits
+ * 8 (2 (P % 2) + i % 2) + 2 (P / 2) .. +1.
  * Padding codes (ranks past rank_k, tokens past n_tok) may hold any value;
  * padding scales and biases are 0.
  */

@@ -38,11 +38,15 @@ __device__ __forceinline__ float bf16_at(const uint16_t* p, size_t i) { return _
 
 __device__ __forceinline__ uint16_t f16_bits(_Float16 h) { return __builtin_bit_cast(uint16_t, h); }
 
-// Bit position of code i (0..7) of an 8-code word: codes 2j and 2j + 1 land
-// in the two halves of one 32-bit lane of a packed fp16 pair.
+// Bit position of code i (0..7) of 8-code word `word` (the layout of
+// milo_attn.h): 4-bit, nibble 2i (i < 4) or 2(i - 4) + 1; 2-bit (two words
+// per dword), pair P = 4 word + i / 2 is in bytes 2 (P % 2) and 2 (P % 2) + 1
+// at field P / 2, so code i is at bit 8 (2 (P % 2) + i % 2) + 2 (P / 2).
 template <int BITS>
 __device__ __forceinline__ int code_shift(int word, int i) {
-  return BITS == 4 ? 4 * (i / 2 + 4 * (i % 2)) : 2 * (4 * word + i / 2 + 8 * (i % 2));
+  if (BITS == 4) return 4 * (i < 4 ? 2 * i : 2 * (i - 4) + 1);
+  const int P = 4 * word + i / 2;
+  return 8 * (2 * (P % 2) + i % 2) + 2 * (P / 2);
 }
 
 template <int D, int BITS>

@@ -48,7 +48,10 @@ def run_kivi(wl, bits, repeat=1, plan=True, **packkw):
 def _shift(bits, u, i):
     """Bit position of code i (0..7) of 8-code word u (2-bit words pair up in a dword)."""
     i = np.asarray(i)
-    return 4 * (i // 2 + 4 * (i % 2)) if bits == 4 else 2 * (4 * u + i // 2 + 8 * (i % 2))
+    if bits == 4:
+        return 4 * np.where(i < 4, 2 * i, 2 * (i - 4) + 1)
+    P = 4 * u + i // 2
+    return 8 * (2 * (P % 2) + i % 2) + 2 * (P // 2)
 
 
 def parse_kivi(pool: np.ndarray, desc, n_kv_heads: int, d: int, bits: int):
