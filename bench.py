@@ -215,7 +215,7 @@ def cpu_baseline_encode(ctx, seconds: float):
 
 
 def run_encode(args) -> int:
-    """The encode workflow per step: spectra (Gram + Jacobi), entropy-driven
+    """The encode workflow per step: spectra (Gram + tridiagonal QL), entropy-driven
     ranks at a 50% rank budget for keys and for values (r_min 8), the pool
     layout on the host, then the factors at those ranks."""
     import numpy as np
@@ -240,13 +240,13 @@ def run_encode(args) -> int:
     dense_bytes = 2 * dc.k.numel() * dc.k.element_size()
     copies = max(args.copies, -(-3 * LAST_LEVEL_CACHE_BYTES // max(1, dense_bytes)))
     kvs = [(dc.k, dc.v)] + [(dc.k.clone(), dc.v.clone()) for _ in range(copies - 1)]
-    sigma, sweeps = dc.spectrum()           # sizes the workspace
+    sigma, iters = dc.spectrum()            # sizes the workspace
     _, full_elems = layout(ctx.n_tok, [d] * nb, [d] * nb, h, d)
     pool = torch.empty(full_elems, dtype=torch.int16 if cfg.dtype == "bf16" else torch.float32, device="cuda:0")
     torch.cuda.synchronize()
-    sw = sweeps.cpu().numpy()
+    sw = iters.cpu().numpy()
     spec_blocks = dc._spectrum_blocks
-    print(f"[bench] {cfg.desc}: dense K/V {dense_bytes / 1e6:.1f} MB, {copies} copies, Jacobi sweeps "
+    print(f"[bench] {cfg.desc}: dense K/V {dense_bytes / 1e6:.1f} MB, {copies} copies, QL iterations "
           f"{sw.min()}..{sw.max()} (mean {sw.mean():.1f}), rank budget {budget} per K/V (50%), r_min {r_min}, "
           f"setup {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
@@ -254,7 +254,7 @@ def run_encode(args) -> int:
         dc.k, dc.v = kvs[k % len(kvs)]
         rec = (lambda i: evs[i].record()) if evs is not None else (lambda i: None)
         rec(0)
-        rc = lib.milo_encode_spectrum(ctypes.byref(dc._args(spec_blocks, sigma=sigma, sweeps=sweeps)),
+        rc = lib.milo_encode_spectrum(ctypes.byref(dc._args(spec_blocks, sigma=sigma, iters=iters)),
                                       ctypes.c_void_p(stream))
         if rc != 0:
             raise RuntimeError(f"milo_encode_spectrum failed: {ra.status_str(rc)}")
@@ -302,7 +302,7 @@ def run_encode(args) -> int:
         "data": "synthetic",
         "config": {"workload": cfg.name, "desc": cfg.desc, "n_blocks": nb, "block_tokens": cfg.block_tokens,
                    "n_kv_heads": h, "head_dim": d, "context_tokens_per_step": tokens, "copies": copies,
-                   "rank_budget": budget, "r_min": r_min, "jacobi_sweeps_mean": float(sw.mean())},
+                   "rank_budget": budget, "r_min": r_min, "ql_iterations_mean": float(sw.mean())},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
                      "traffic": traffic_from_profiles(cfg.name, "encode"),

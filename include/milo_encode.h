@@ -52,9 +52,10 @@ typedef struct milo_encode_args {
   float* sigma;                /* [n_blocks][n_kv_heads][2][head_dim] singular values,
                                   descending, K then V; written by the spectrum call; may
                                   be NULL                                                   */
-  int32_t* sweeps;             /* [n_blocks][n_kv_heads][2] Jacobi sweeps used by the
-                                  spectrum call (negative: stopped at the limit of 16
-                                  before converging); may be NULL                           */
+  int32_t* iters;              /* [n_blocks][n_kv_heads][2] implicit QL iterations of the
+                                  spectrum call (0: already diagonal; negative: an
+                                  eigenvalue did not converge within 30 iterations); may
+                                  be NULL                                                   */
   void* pool;                  /* factor pool written by the factors call, 16-B aligned     */
   void* workspace;             /* milo_encode_workspace_bytes() bytes, 256-B aligned: the
                                   spectrum call writes it, the factors call reads it        */
@@ -66,9 +67,10 @@ typedef struct milo_encode_args {
 size_t milo_encode_workspace_bytes(const milo_encode_args* args);
 
 /* Spectra: per (block, KV head, K/V) the Gram matrix X^T X (fp32 sums of
- * exact products) and its eigen-decomposition by cyclic Jacobi rotations
- * (fp32).  sigma_i = sqrt(max(lambda_i, 0)).  Writes sigma, sweeps and the
- * workspace. */
+ * exact products) and its eigen-decomposition in fp32: Householder
+ * reduction to tridiagonal form, then implicit QL iterations with the
+ * rotations accumulated into the Householder factor.  sigma_i =
+ * sqrt(max(lambda_i, 0)).  Writes sigma, iters and the workspace. */
 milo_status milo_encode_spectrum(const milo_encode_args* args, void* hip_stream);
 
 /* Factors: for every block, KV head and K/V, W = the first rank rows of the

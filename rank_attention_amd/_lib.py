@@ -68,7 +68,7 @@ class MiloEncodeArgs(ctypes.Structure):
         ("tok_start", ctypes.c_void_p),
         ("blocks", ctypes.c_void_p),
         ("sigma", ctypes.c_void_p),
-        ("sweeps", ctypes.c_void_p),
+        ("iters", ctypes.c_void_p),
         ("pool", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),

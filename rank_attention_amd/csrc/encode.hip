@@ -9,14 +9,12 @@
 // U = X W^T, so that U W is the best rank-r approximation of X.
 //
 // Two kernels, one workgroup per (block, KV head, K/V) matrix:
-//  spectrum  G = X^T X in fp32 (products of bf16/fp32 inputs are exact, sums
-//            fp32), then the cyclic Jacobi eigenvalue method on G in LDS:
-//            every round applies d/2 disjoint plane rotations chosen by the
-//            round-robin (circle) pairing, so a sweep of d-1 rounds meets
-//            every index pair once.  A rotation's 2x2 blocks of G are
-//            owned by single threads, so a round is two barriers; each
-//            thread reads all of its blocks before writing any.  Sweeps
-//            stop after one without rotations.  Output: sigma_i =
+//  spectrum  G = X^T X (fp32 sums of exact products), then its symmetric
+//            eigen-decomposition in fp32 by Householder reduction to
+//            tridiagonal form and implicit QL iterations whose rotations
+//            are accumulated into the Householder factor (the scheme of
+//            the textbook tred2/tql2 pair, organised for one workgroup;
+//            the steps are listed before the kernel).  Output: sigma_i =
 //            sqrt(max(lambda_i, 0)) descending and the eigenvectors as
 //            rows, sorted the same way (workspace).
 //  factors   W = the first r eigenvector rows, U^T = W X^T (fp32 sums),
@@ -24,33 +22,14 @@
 //            U^T rows zero-padded to ld_tok.
 #include "device_common.h"
 #include "kernels.h"
+#include "mfma_common.h"
 
 namespace milo {
 
 namespace {
 
 constexpr int kEncThreads = 512;
-constexpr int kEncMaxSweeps = 16;
-// A rotation is applied when |g_pq| exceeds both tolerances: relative to
-// sqrt(|g_pp g_qq|) and absolute relative to trace(G).  Without the absolute
-// floor, rounding noise between the tiny eigenvalues of a rank-deficient
-// block keeps rotations going in every sweep.
-constexpr float kEncTolRel = 1e-7f;
-constexpr float kEncTolAbs = 1e-8f;
 constexpr int kFacTokens = 64;     // tokens per staged chunk in the factors kernel
-
-template <int D>
-struct EncSmem {
-  static constexpr int S = D + 1;  // padded row stride
-  float g[D * S];
-  float v[D * S];                  // eigenvectors (columns); the Gram's staging buffer first
-  float pc[D / 2], ps[D / 2], pt[D / 2];
-  int pp[D / 2], pq[D / 2];
-  int rank[D];
-  float trace;
-  int nrot;              // rotations in the current sweep
-  int nrot_round[2];     // rotations in the current round (alternating by round parity)
-};
 
 // 8 consecutive elements of a dense array as fp32 (16-byte aligned).
 template <int DT>
@@ -114,204 +93,521 @@ __device__ __forceinline__ EncMat enc_mat(const EncodeParams& p, int m, int D) {
   return e;
 }
 
+// ---------------------------------------------------------------------------
+// Spectrum.  One 256-thread workgroup per matrix, about 72 KB of LDS, so two
+// matrices share a CU.  Phases:
+//  1. G = X^T X: bf16 inputs on v_mfma_f32_16x16x32_bf16 (exact products,
+//     fp32 sums) from token chunks staged transposed in LDS; fp32 inputs on
+//     the vector ALUs.  G is mirrored from its upper triangle (exactly
+//     symmetric) and scaled by a power of two (exact) to trace ~ 1.
+//  2. Householder reduction to tridiagonal form (d, e), in place: step k
+//     annihilates row k right of the superdiagonal with H = I - tau v v^T
+//     (v_0 = 1), whose v is kept in that row; the trailing block is updated
+//     as A -= v w^T + w v^T, w = p - (tau/2)(p.v) v, p = tau A v.  The row
+//     is scaled by a power of two before its norm is taken.
+//  3. Q^T = H_{d-3} ... H_1 H_0 accumulated in place (from the last
+//     reflector back: Q^T <- Q^T H_k on the trailing block).
+//  4. Implicit QL with a Wilkinson-type shift on (d, e), every plane rotation
+//     applied to the rows of Q^T (the columns of Q): one wave per 64 entries
+//     of a row runs the same scalar recurrence (each on its own copy of d
+//     and e) and rotates its entries of the two rows.
+//     e_m counts as zero when |e_m| <= 2^-24 (|d_m| + |d_m+1|) or <= 1e-8
+//     trace; at most 30 iterations per eigenvalue.
+//  5. sigma_i = sqrt(max(lambda_i, 0)) descending and the eigenvectors (the
+//     rows of Q^T) in the same order.
+// Rows of the matrix phases are read and written as aligned 16-byte chunks
+// (row stride D + 4 floats: eight rows' chunks fall in distinct banks).
+// ---------------------------------------------------------------------------
+constexpr int kEigThreads = 256;
+constexpr int kEigMaxIt = 30;
+constexpr float kEigTolRel = 0x1p-24f;
+constexpr float kEigTolAbs = 1e-8f;
+constexpr int kGramTok = 128;           // tokens per staged chunk (bf16 Gram)
+constexpr int kGramXs = kGramTok + 8;   // bf16 per staged row (272 B: 8 rows hit 8 distinct 16-B bank groups)
+
+template <int D>
+struct EigSmem {
+  static constexpr int S = D + 4;   // row stride of a, in floats
+  float a[D * S];                   // X staging, then G, the reflectors and Q^T, then the eigenvectors
+  float vb[D];                      // v of the current reflector by column (0 left of the block)
+  float part[2][D];                 // partial row products of the two column halves
+  float tau[D];
+  float dq[2][D], eq[2][D];         // d and e, one copy per QL wave
+  float lam[D];                     // eigenvalues
+  int rank[D];
+  float trace;
+};
+
+// Products that must not be contracted into fused multiply-adds, so that
+// A -= v w^T + w v^T stays exactly symmetric.
+__device__ __forceinline__ float sym2(float vi, float wj, float wi, float vj) {
+  return __fadd_rn(__fmul_rn(vi, wj), __fmul_rn(wi, vj));
+}
+
+__device__ __forceinline__ f32x4_t lds4(const float* p) { return *reinterpret_cast<const f32x4_t*>(p); }
+__device__ __forceinline__ void sts4(float* p, const f32x4_t& v) { *reinterpret_cast<f32x4_t*>(p) = v; }
+
+// The trailing block of step k covers columns k+1 .. D-1, walked in
+// aligned 4-column chunks from (k+1) & ~3; the first ceil(n/2) of its n
+// chunks form half 0, the rest half 1 (at most D/8 each).
+struct Halves {
+  int c0, n;   // first chunk column, chunk count
+};
+template <int D>
+__device__ __forceinline__ Halves half_of(int k, int hh) {
+  const int c0 = (k + 1) & ~3, nt = (D - c0) / 4, n0 = (nt + 1) / 2;
+  Halves h;
+  h.c0 = hh ? c0 + 4 * n0 : c0;
+  h.n = hh ? nt - n0 : n0;
+  return h;
+}
+
+// G = X^T X for bf16 X on the matrix cores.  Chunks of kGramTok tokens are
+// staged as xt[dim][token] (token pairs packed per dword).  Wave w owns the
+// 16-row tile rows I = (D/64) w .. +D/64 - 1 and every tile column J; lane l
+// of tile (I, J) ends with G[16I + 4(l/16) + v][16J + l%16].
+template <int D>
+__device__ __forceinline__ void gram_bf16(const uint16_t* x, int64_t row0, int T, EigSmem<D>& sm, int tid) {
+  constexpr int NT = D / 16, IPW = NT / 4;
+  constexpr int ITEMS = (kGramTok / 2) * (D / 8) / kEigThreads;   // (token pair, 8 dims) items per thread
+  static_assert(ITEMS * kEigThreads == (kGramTok / 2) * (D / 8), "staging split");
+  uint32_t* xt = reinterpret_cast<uint32_t*>(sm.a);   // [D][kGramXs / 2] dwords
+  const int lane = tid & 63, wave = tid >> 6;
+  f32x4_t acc[IPW][NT];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t r0[ITEMS], r1[ITEMS];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < ITEMS; ++u) {
+      const int it = tid + kEigThreads * u;
+      const int tp = it % (kGramTok / 2), cg = it / (kGramTok / 2);
+      const int ta = t0 + 2 * tp, tb = ta + 1;
+      r0[u] = ta < T ? ld16(x + row0 + (int64_t)ta * D + 8 * cg) : u32x4_t{0u, 0u, 0u, 0u};
+      r1[u] = tb < T ? ld16(x + row0 + (int64_t)tb * D + 8 * cg) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  if (T > 0) fetch(0);
+  for (int t0 = 0; t0 < T; t0 += kGramTok) {
+    __syncthreads();   // the previous chunk's operand reads are done
+#pragma unroll
+    for (int u = 0; u < ITEMS; ++u) {
+      const int it = tid + kEigThreads * u;
+      const int tp = it % (kGramTok / 2), cg = it / (kGramTok / 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xt[(8 * cg + 2 * i) * (kGramXs / 2) + tp] = perm_lo(r0[u][i], r1[u][i]);
+        xt[(8 * cg + 2 * i + 1) * (kGramXs / 2) + tp] = perm_hi(r0[u][i], r1[u][i]);
+      }
+    }
+    __syncthreads();
+    if (t0 + kGramTok < T) fetch(t0 + kGramTok);
+    const int nk = min(kGramTok, T - t0 + 31) / 32;   // K steps holding tokens (the rest of the chunk is zero)
+    for (int s = 0; s < nk; ++s) {
+      const int off = 16 * s + 4 * (lane >> 4);       // dword offset of the lane's 8 tokens
+      u32x4_t bo[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        bo[j] = *reinterpret_cast<const u32x4_t*>(xt + (16 * j + (lane & 15)) * (kGramXs / 2) + off);
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int I = IPW * wave + i;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = mfma32(bo[I], bo[j], acc[i][j]);
+      }
+    }
+  }
+  __syncthreads();   // staging reads are done before G overwrites it
+  constexpr int S = EigSmem<D>::S;
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int I = IPW * wave + i;
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sm.a[(16 * I + 4 * (lane >> 4) + v) * S + 16 * j + (lane & 15)] = acc[i][j][v];
+  }
+}
+
+// G = X^T X for fp32 X on the vector ALUs: chunks of D tokens staged as
+// rows; thread (ti, tj) of a 16 x 16 grid owns a (D/16) x (D/16) tile.
+template <int D>
+__device__ __forceinline__ void gram_f32(const float* x, int64_t row0, int T, EigSmem<D>& sm, int tid) {
+  constexpr int TI = D / 16;
+  const int i0 = (tid >> 4) * TI, j0 = (tid & 15) * TI;
+  float acc[TI][TI];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TI; ++j) acc[i][j] = 0.f;
+  float* xs = sm.a;   // D token rows x D
+  for (int t0 = 0; t0 < T; t0 += D) {
+    const int n = min(D, T - t0);
+    __syncthreads();
+    for (int q = tid; q < D * (D / 4); q += kEigThreads) {
+      const int t = q / (D / 4), c = (q % (D / 4)) * 4;
+      const f32x4_t v = t < n ? ld16f(x + row0 + (int64_t)(t0 + t) * D + c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      sts4(xs + t * D + c, v);
+    }
+    __syncthreads();
+    for (int t = 0; t < n; ++t) {
+      float u[TI], w[TI];
+#pragma unroll
+      for (int i = 0; i < TI; ++i) u[i] = xs[t * D + i0 + i];
+#pragma unroll
+      for (int j = 0; j < TI; ++j) w[j] = xs[t * D + j0 + j];
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TI; ++j) acc[i][j] = fmaf(u[i], w[j], acc[i][j]);
+    }
+  }
+  __syncthreads();
+  constexpr int S = EigSmem<D>::S;
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TI; ++j) sm.a[(i0 + i) * S + j0 + j] = acc[i][j];
+}
+
+// Householder reduction of the symmetric matrix in sm.a to tridiagonal
+// form.  Thread (hh, ii) = (tid / 128, tid % 128) owns row k+1+ii of the
+// trailing block over column half hh, as up to 16 aligned chunks held in
+// registers between the product and the update of a step.
+template <int D>
+__device__ __forceinline__ void tridiagonalize(EigSmem<D>& sm, int tid) {
+  constexpr int S = EigSmem<D>::S, NC = D / 8;   // chunks per half, at most
+  float* A = sm.a;
+  const int lane = tid & 63, wave = tid >> 6, hh = tid >> 7, ii = tid & 127;
+  auto pvec = [&](int c, float tk) { return tk * (sm.part[0][c] + sm.part[1][c]); };
+  for (int k = 0; k < D - 2; ++k) {
+    const int m = D - 1 - k;   // trailing size
+    if (wave == 0) {
+      // reflector from row k, columns k+1 .. D-1 (x_i = A[k][k+1+i])
+      const int i0 = lane, i1 = lane + 64;
+      float x0 = i0 < m ? A[k * S + k + 1 + i0] : 0.f;
+      float x1 = i1 < m ? A[k * S + k + 1 + i1] : 0.f;
+      const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+      float tk = 0.f, ek = A[k * S + k + 1], v0 = i0 == 0 ? 1.f : 0.f, v1 = 0.f;
+      if (amax > 0.f) {
+        int ex;
+        frexpf(amax, &ex);
+        x0 = ldexpf(x0, -ex);   // exact
+        x1 = ldexpf(x1, -ex);
+        const float alpha = __shfl(x0, 0);
+        const float xn2 = wave_sum((i0 == 0 ? 0.f : x0 * x0) + x1 * x1);
+        if (xn2 > 0.f) {
+          const float beta = -copysignf(sqrtf(alpha * alpha + xn2), alpha);
+          tk = (beta - alpha) / beta;
+          const float inv = 1.f / (alpha - beta);
+          v0 = i0 == 0 ? 1.f : x0 * inv;
+          v1 = x1 * inv;
+          ek = ldexpf(beta, ex);
+        }
+      }
+      // vb by column (v at k+1.., zero left of the block), one store per
+      // entry; v past v_0 is kept in row k
+#pragma unroll
+      for (int hc = 0; hc < 2; ++hc) {
+        const int c = lane + 64 * hc, idx = c - (k + 1);
+        const float s0 = __shfl(v0, idx & 63), s1 = __shfl(v1, idx & 63);
+        if (c < D) sm.vb[c] = idx < 0 ? 0.f : (idx < 64 ? s0 : s1);
+      }
+      if (i0 > 0 && i0 < m) A[k * S + k + 1 + i0] = v0;
+      if (i1 < m) A[k * S + k + 1 + i1] = v1;
+      if (lane == 0) {
+        sm.tau[k] = tk;
+        sm.dq[0][k] = sm.dq[1][k] = A[k * S + k];
+        sm.eq[0][k] = sm.eq[1][k] = ek;
+      }
+    }
+    __syncthreads();
+    const float tk = sm.tau[k];
+    if (tk == 0.f) continue;   // H = I (uniform)
+    const Halves h = half_of<D>(k, hh);
+    const bool act = ii < m;
+    float* ar = A + (k + 1 + ii) * S + h.c0;
+    f32x4_t row[NC];
+    float dot = 0.f;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) {
+      if (q < h.n && act) {
+        row[q] = lds4(ar + 4 * q);
+        const f32x4_t vq = lds4(sm.vb + h.c0 + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dot = fmaf(row[q][e], vq[e], dot);
+      }
+    }
+    if (act) sm.part[hh][k + 1 + ii] = dot;
+    __syncthreads();
+    // K = (tau/2) p.v with p_i = tau (part0_i + part1_i), formed alike by
+    // every wave; w_c = p_c - K v_c is formed where it is used
+    float kc;
+    {
+      const int ca = lane, cb = lane + 64;
+      const bool ina = ca >= k + 1, inb = cb >= k + 1 && cb < D;
+      const float pa = ina ? pvec(ca, tk) : 0.f, pb = inb ? pvec(cb, tk) : 0.f;
+      const float va = ina ? sm.vb[ca] : 0.f, vbb = inb ? sm.vb[cb] : 0.f;
+      kc = 0.5f * tk * wave_sum(fmaf(pa, va, pb * vbb));
+    }
+    if (act) {
+      const int r = k + 1 + ii;
+      const float vi = sm.vb[r], wi = __fsub_rn(pvec(r, tk), __fmul_rn(kc, vi));
+#pragma unroll
+      for (int q = 0; q < NC; ++q) {
+        if (q < h.n) {
+          const int c = h.c0 + 4 * q;
+          const f32x4_t vq = lds4(sm.vb + c), p0 = lds4(sm.part[0] + c), p1 = lds4(sm.part[1] + c);
+          // columns left of the block have v = 0 (and stale p): they are written back unchanged
+          f32x4_t o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float wc = c + e >= k + 1 ? __fsub_rn(tk * (p0[e] + p1[e]), __fmul_rn(kc, vq[e])) : 0.f;
+            o[e] = __fsub_rn(row[q][e], sym2(vi, wc, wi, vq[e]));
+          }
+          sts4(ar + 4 * q, o);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    sm.dq[0][D - 2] = sm.dq[1][D - 2] = A[(D - 2) * S + D - 2];
+    sm.dq[0][D - 1] = sm.dq[1][D - 1] = A[(D - 1) * S + D - 1];
+    sm.eq[0][D - 2] = sm.eq[1][D - 2] = A[(D - 2) * S + D - 1];
+    sm.eq[0][D - 1] = sm.eq[1][D - 1] = 0.f;
+  }
+  __syncthreads();
+}
+
+// Q^T = H_{D-3} ... H_0, accumulated from the last reflector back in place:
+// before step k the unit vector fills row and column k+1 of the block
+// [k+1.., k+1..]; then Q^T_b -= tau (Q^T_b v) v^T.  Thread (hh, ii) owns
+// row k+1+ii of the block over column half hh.  The reflector of step k is
+// row k (outside the block), those of later steps were used already.
+template <int D>
+__device__ __forceinline__ void accumulate_qt(EigSmem<D>& sm, int tid) {
+  constexpr int S = EigSmem<D>::S, NC = D / 8;
+  float* A = sm.a;
+  const int hh = tid >> 7, ii = tid & 127;
+  if (tid == 0) A[(D - 1) * S + D - 1] = 1.f;
+  for (int k = D - 3; k >= 0; --k) {
+    const int m = D - 1 - k;
+    for (int c = tid; c < D; c += kEigThreads) {
+      sm.vb[c] = c < k + 1 ? 0.f : (c == k + 1 ? 1.f : A[k * S + c]);
+      if (c >= k + 1) {
+        A[(k + 1) * S + c] = c == k + 1 ? 1.f : 0.f;   // row k+1
+        A[c * S + k + 1] = c == k + 1 ? 1.f : 0.f;     // column k+1
+      }
+    }
+    __syncthreads();
+    const float tk = sm.tau[k];
+    if (tk == 0.f) continue;
+    const Halves h = half_of<D>(k, hh);
+    const bool act = ii < m;
+    float* ar = A + (k + 1 + ii) * S + h.c0;
+    f32x4_t row[NC];
+    float dot = 0.f;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) {
+      if (q < h.n && act) {
+        row[q] = lds4(ar + 4 * q);
+        const f32x4_t vq = lds4(sm.vb + h.c0 + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dot = fmaf(row[q][e], vq[e], dot);
+      }
+    }
+    if (act) sm.part[hh][k + 1 + ii] = dot;
+    __syncthreads();
+    if (act) {
+      const float tw = tk * (sm.part[0][k + 1 + ii] + sm.part[1][k + 1 + ii]);
+#pragma unroll
+      for (int q = 0; q < NC; ++q) {
+        if (q < h.n) {
+          const f32x4_t vq = lds4(sm.vb + h.c0 + 4 * q);   // zero left of the block: those entries stay
+          f32x4_t o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = fmaf(-tw, vq[e], row[q][e]);
+          sts4(ar + 4 * q, o);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  for (int c = tid; c < D; c += kEigThreads) {
+    A[c] = c == 0 ? 1.f : 0.f;       // row 0
+    A[c * S] = c == 0 ? 1.f : 0.f;   // column 0
+  }
+  __syncthreads();
+}
+
+// Entry i (uniform) of a vector held across the lanes of two registers
+// (lane i % 64 of lo for i < 64, of hi otherwise).
+template <int D>
+__device__ __forceinline__ float lane_get(float lo, float hi, int i) {
+  const float v = (D > 64 && i >= 64) ? hi : lo;
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), i & 63));
+}
+
+// Implicit QL on (d, e) of this wave's copy; rotations applied to entries
+// 64 w + lane of the rows of Q^T (one wave per 64 entries).  Returns the
+// iteration count, negative when an eigenvalue took more than kEigMaxIt
+// iterations.  Every lane computes the same scalar recurrence.  At the start
+// of an iteration d and e are read from LDS into lane registers; a sweep
+// reads entries only before it changes them, so it reads that snapshot and
+// writes its new values to LDS.  A rotation of f = g = 0 is the identity
+// (c = 1, s = 0, r = 0), so a sweep never stops early.
+template <int D>
+__device__ __forceinline__ int ql_implicit(EigSmem<D>& sm, int wave, int lane, float tol_abs) {
+  constexpr int S = EigSmem<D>::S;
+  float* dq = sm.dq[wave];
+  float* eq = sm.eq[wave];
+  float* zc0 = sm.a + 64 * wave + lane;   // Q^T[i][64 w + lane] at zc0[i * S]
+  int iters = 0;
+  for (int l = 0; l < D; ++l) {
+    for (int it = 0;; ++it) {
+      const float dlo = dq[lane], elo = eq[lane];
+      const float dhi = D > 64 ? dq[min(lane + 64, D - 1)] : 0.f, ehi = D > 64 ? eq[min(lane + 64, D - 1)] : 0.f;
+      // m = the first index >= l whose e_m is negligible (e_{D-1} = 0)
+      int m = D - 1;
+      {
+        const float d64 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dhi), 0));
+        const float d1lo = lane == 63 ? d64 : __shfl_down(dlo, 1);
+        const bool nega = lane >= l && lane < D - 1 &&
+                          (fabsf(elo) <= kEigTolRel * (fabsf(dlo) + fabsf(d1lo)) || fabsf(elo) <= tol_abs);
+        const uint64_t ba = __builtin_amdgcn_ballot_w64(nega);
+        if (ba != 0) {
+          m = __builtin_ctzll(ba);
+        } else if (D > 64) {
+          const float d1hi = __shfl_down(dhi, 1);
+          const int jb = lane + 64;
+          const bool negb = jb >= l && jb < D - 1 &&
+                            (fabsf(ehi) <= kEigTolRel * (fabsf(dhi) + fabsf(d1hi)) || fabsf(ehi) <= tol_abs);
+          const uint64_t bb = __builtin_amdgcn_ballot_w64(negb);
+          if (bb != 0) m = 64 + __builtin_ctzll(bb);
+        }
+      }
+      if (m == l) break;
+      if (it == kEigMaxIt) return -(iters + 1);
+      ++iters;
+      const float dl = lane_get<D>(dlo, dhi, l), el = lane_get<D>(elo, ehi, l);
+      float g = (lane_get<D>(dlo, dhi, l + 1) - dl) / (2.f * el);
+      const float rr = sqrtf(fmaf(g, g, 1.f));
+      g = lane_get<D>(dlo, dhi, m) - dl + el / (g + copysignf(rr, g));
+      float s = 1.f, c = 1.f, p = 0.f;
+      float zc = zc0[m * S];
+      float dn = lane_get<D>(dlo, dhi, m);   // d_{i+1} before this sweep
+      float ei = lane_get<D>(elo, ehi, m - 1), di = lane_get<D>(dlo, dhi, m - 1);
+      for (int i = m - 1; i >= l; --i) {
+        const int ip = i > 0 ? i - 1 : 0;    // next step's entries (not yet changed in this sweep)
+        const float ein = eq[ip], din = dq[ip];
+        const float zi = zc0[i * S];
+        const float f = s * ei, b = c * ei;
+        const float r2 = fmaf(f, f, g * g);
+        const bool zero = r2 == 0.f;
+        const float ri = zero ? 0.f : __builtin_amdgcn_rsqf(r2);
+        eq[i + 1] = r2 * ri;
+        s = f * ri;
+        c = zero ? 1.f : g * ri;
+        const float gg = dn - p;
+        const float t = fmaf(di - gg, s, 2.f * c * b);
+        p = s * t;
+        dq[i + 1] = gg + p;
+        g = fmaf(c, t, -b);
+        zc0[(i + 1) * S] = fmaf(s, zi, c * zc);
+        zc = fmaf(c, zi, -s * zc);
+        dn = di;
+        ei = ein;
+        di = din;
+      }
+      dq[l] = dn - p;
+      eq[l] = g;
+      eq[m] = 0.f;
+      zc0[l * S] = zc;
+    }
+  }
+  if (wave == 0) {   // eigenvalues out (wave 1 works on its own copy)
+    sm.lam[lane] = dq[lane];
+    if (D > 64) sm.lam[lane + 64] = dq[lane + 64];
+  }
+  return iters;
+}
+
 template <int D, int DT>
-__global__ __launch_bounds__(kEncThreads) void milo_encode_spectrum_kernel(EncodeParams p) {
-  __shared__ __attribute__((aligned(16))) EncSmem<D> sm;
-  constexpr int S = EncSmem<D>::S;
-  constexpr int H = D / 2;
-  constexpr int KS = kEncThreads / H;   // rows of blocks (and of V) between a thread's items
-  constexpr int NB = H * H / kEncThreads;   // 2x2 blocks of G per thread per round
-  constexpr int NV = D * H / kEncThreads;   // (row, pair) items of V per thread per round
-  static_assert(kEncThreads % H == 0 && NB * kEncThreads == H * H && NV * kEncThreads == D * H, "work split");
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(kEigThreads) void milo_encode_spectrum_kernel(EncodeParams p) {
+  __shared__ __attribute__((aligned(16))) EigSmem<D> sm;
+  constexpr int S = EigSmem<D>::S;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = blockIdx.x;
   const EncMat e = enc_mat(p, m, D);
   const void* x = e.kv ? p.v : p.k;
 
-  // ---- G = X^T X: thread owns rows i0..i0+TI-1, columns j0..j0+TJ-1
-  constexpr int TI = D / 32, TJ = D / 16;
-  const int i0 = (tid >> 4) * TI, j0 = (tid & 15) * TJ;
-  float acc[TI][TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[i][j] = 0.f;
-  float* xs = sm.v;   // staging: D token rows x D, row stride D
-  for (int t0 = 0; t0 < e.T; t0 += D) {
-    const int n = min(D, e.T - t0);
-    __syncthreads();   // the previous chunk's reads are done
-    for (int q = tid; q < D * (D / 8); q += kEncThreads) {
-      const int t = q / (D / 8), c = (q % (D / 8)) * 8;
-      float v8[8];
-      if (t < n) {
-        load8<DT>(x, e.row0 + (int64_t)(t0 + t) * D + c, v8);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v8[i] = 0.f;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xs[t * D + c + i] = v8[i];
-    }
-    __syncthreads();
-    for (int t = 0; t < n; ++t) {
-      float a[TI], c[TJ];
-#pragma unroll
-      for (int i = 0; i < TI; ++i) a[i] = xs[t * D + i0 + i];
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) c[j] = xs[t * D + j0 + j];
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i][j] = fmaf(a[i], c[j], acc[i][j]);
-    }
-  }
+  if (DT == MILO_BF16)
+    gram_bf16<D>(reinterpret_cast<const uint16_t*>(x), e.row0, e.T, sm, tid);
+  else
+    gram_f32<D>(reinterpret_cast<const float*>(x), e.row0, e.T, sm, tid);
   __syncthreads();
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) sm.g[(i0 + i) * S + j0 + j] = acc[i][j];
-  for (int q = tid; q < D * D; q += kEncThreads) {
+  // exact symmetry from the upper triangle; the trace
+  for (int q = tid; q < D * D; q += kEigThreads) {
     const int i = q / D, j = q % D;
-    sm.v[i * S + j] = (i == j) ? 1.f : 0.f;
+    if (i > j) sm.a[i * S + j] = sm.a[j * S + i];
   }
-  if (tid == 0) {
-    sm.nrot = 0;
-    sm.nrot_round[0] = sm.nrot_round[1] = 0;
-  }
-  __syncthreads();
   if (tid < 64) {
-    float s = 0.f;
-    for (int i = tid; i < D; i += 64) s += sm.g[i * S + i];
-    s = wave_sum(s);
-    if (tid == 0) sm.trace = s;
+    float t = 0.f;
+    for (int i = tid; i < D; i += 64) t += sm.a[i * S + i];
+    t = wave_sum(t);
+    if (tid == 0) sm.trace = t;
   }
   __syncthreads();
-  const float tol_abs = kEncTolAbs * fabsf(sm.trace);
-
-  // ---- cyclic Jacobi sweeps
-  int sweeps = 0, rounds = 0;   // rounds: over all sweeps (parity of the round counter)
-  bool converged = false;
-  while (sweeps < kEncMaxSweeps) {
-    ++sweeps;
-    for (int rnd = 0; rnd < D - 1; ++rnd, ++rounds) {
-      __syncthreads();   // the previous round's updates are visible
-      // the previous round's counter was read before the barrier above; it
-      // is the one the next round uses, so clear it now
-      if (tid == 0) sm.nrot_round[(rounds + 1) & 1] = 0;
-      if (tid < H) {
-        // circle pairing: position 0 holds index 0, position k > 0 holds
-        // 1 + (k - 1 + rnd) mod (D - 1); pair = positions (tid, D - 1 - tid)
-        const int ka = tid, kb = D - 1 - tid;
-        const int ia = ka == 0 ? 0 : 1 + (ka - 1 + rnd) % (D - 1);
-        const int ib = 1 + (kb - 1 + rnd) % (D - 1);
-        const int pi = min(ia, ib), qi = max(ia, ib);
-        const float gpp = sm.g[pi * S + pi], gqq = sm.g[qi * S + qi], gpq = sm.g[pi * S + qi];
-        float c = 1.f, s = 0.f, t = 0.f;
-        if (fabsf(gpq) > fmaxf(kEncTolRel * sqrtf(fabsf(gpp * gqq)), tol_abs)) {
-          // the smaller-angle root of t^2 + 2 theta t - 1 = 0 zeroes g_pq
-          const float theta = (gqq - gpp) / (2.f * gpq);
-          t = (theta >= 0.f ? 1.f : -1.f) / (fabsf(theta) + sqrtf(fmaf(theta, theta, 1.f)));
-          c = 1.f / sqrtf(fmaf(t, t, 1.f));
-          s = t * c;
-          atomicAdd(&sm.nrot, 1);
-          atomicAdd(&sm.nrot_round[rounds & 1], 1);
-        }
-        sm.pp[tid] = pi;
-        sm.pq[tid] = qi;
-        sm.pc[tid] = c;
-        sm.ps[tid] = s;
-        sm.pt[tid] = t;
-      }
-      __syncthreads();
-      if (sm.nrot_round[rounds & 1] == 0) continue;   // no rotation in this round (uniform)
-      // G <- J^T G J, J = the round's rotations ([[c, s], [-s, c]] on (p, q)):
-      // 2x2 block (k, l) of G becomes R_k^T B R_l.  Thread tid owns the
-      // blocks l = tid % H, k = tid / H + KS * i: it reads all of them, then
-      // rotates, then writes (the blocks are disjoint, and an identity
-      // rotation reproduces its block exactly, so no block is skipped).
-      {
-        const int l = tid % H, kb = tid / H;
-        const int pl = sm.pp[l], ql = sm.pq[l];
-        const float cl = sm.pc[l], sl = sm.ps[l];
-        float b[NB][4];
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-          const int k = kb + KS * i;
-          const int pk = sm.pp[k], qk = sm.pq[k];
-          b[i][0] = sm.g[pk * S + pl];
-          b[i][1] = sm.g[pk * S + ql];
-          b[i][2] = sm.g[qk * S + pl];
-          b[i][3] = sm.g[qk * S + ql];
-        }
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-          const int k = kb + KS * i;
-          const int pk = sm.pp[k], qk = sm.pq[k];
-          if (k == l) {
-            // diagonal block: closed form, a rotated coupling becomes exactly 0
-            const float t = sm.pt[k];
-            const bool rot = sl != 0.f;
-            sm.g[pk * S + pk] = b[i][0] - t * b[i][1];
-            sm.g[qk * S + qk] = b[i][3] + t * b[i][1];
-            sm.g[pk * S + qk] = rot ? 0.f : b[i][1];
-            sm.g[qk * S + pk] = rot ? 0.f : b[i][2];
-          } else {
-            const float ck = sm.pc[k], sk = sm.ps[k];
-            const float m00 = ck * b[i][0] - sk * b[i][2], m01 = ck * b[i][1] - sk * b[i][3];
-            const float m10 = sk * b[i][0] + ck * b[i][2], m11 = sk * b[i][1] + ck * b[i][3];
-            sm.g[pk * S + pl] = cl * m00 - sl * m01;
-            sm.g[pk * S + ql] = sl * m00 + cl * m01;
-            sm.g[qk * S + pl] = cl * m10 - sl * m11;
-            sm.g[qk * S + ql] = sl * m10 + cl * m11;
-          }
-        }
-        // V <- V J: columns p_l, q_l of rows tid / H + KS * i
-        if (sl != 0.f) {
-          float va[NV], vb[NV];
-#pragma unroll
-          for (int i = 0; i < NV; ++i) {
-            const int row = kb + KS * i;
-            va[i] = sm.v[row * S + pl];
-            vb[i] = sm.v[row * S + ql];
-          }
-#pragma unroll
-          for (int i = 0; i < NV; ++i) {
-            const int row = kb + KS * i;
-            sm.v[row * S + pl] = cl * va[i] - sl * vb[i];
-            sm.v[row * S + ql] = sl * va[i] + cl * vb[i];
-          }
-        }
-      }
+  const float trace = sm.trace;
+  const bool finite = trace < __builtin_huge_valf();   // false for inf and NaN (inputs must be finite)
+  int iters = finite ? 0 : -1;
+  float unscale = 0.f;
+  if (trace > 0.f && finite) {
+    int ex;
+    frexpf(trace, &ex);
+    for (int q = tid; q < D * D; q += kEigThreads) {
+      const int i = q / D, j = q % D;
+      sm.a[i * S + j] = ldexpf(sm.a[i * S + j], -ex);   // exact
     }
+    unscale = ldexpf(1.f, ex);
     __syncthreads();
-    const int n = sm.nrot;
-    __syncthreads();   // every thread has read the count before it is reset
-    if (tid == 0) sm.nrot = 0;
-    if (n == 0) {
-      converged = true;
-      break;
+    tridiagonalize<D>(sm, tid);
+    accumulate_qt<D>(sm, tid);
+    if (wave < D / 64) {
+      const int it = ql_implicit<D>(sm, wave, lane, kEigTolAbs * ldexpf(trace, -ex));
+      if (tid == 0) iters = it;
     }
+  } else {
+    // no energy: eigenvalues 0, eigenvectors the unit vectors
+    for (int q = tid; q < D * D; q += kEigThreads) {
+      const int i = q / D, j = q % D;
+      sm.a[i * S + j] = i == j ? 1.f : 0.f;
+    }
+    for (int i = tid; i < D; i += kEigThreads) sm.lam[i] = 0.f;
   }
+  __syncthreads();
 
   // ---- sort by descending eigenvalue; sigma and eigenvector rows out
-  __syncthreads();
   if (tid < D) {
-    const float li = sm.g[tid * S + tid];
+    const float li = sm.lam[tid];
     int r = 0;
     for (int j = 0; j < D; ++j) {
-      const float lj = sm.g[j * S + j];
+      const float lj = sm.lam[j];
       r += (lj > li) || (lj == li && j < tid);
     }
     sm.rank[tid] = r;
-    if (p.sigma) p.sigma[(size_t)m * D + r] = sqrtf(fmaxf(li, 0.f));
+    if (p.sigma) p.sigma[(size_t)m * D + r] = finite ? sqrtf(fmaxf(li * unscale, 0.f)) : __builtin_nanf("");
   }
   __syncthreads();
   float* vec = p.vecs + (size_t)m * D * D;
-  for (int q = tid; q < D * D; q += kEncThreads) {
-    const int i = q / D, j = q % D;   // eigenvector i (column i of V), component j
-    vec[(size_t)sm.rank[i] * D + j] = sm.v[j * S + i];
+  for (int q = tid; q < D * D; q += kEigThreads) {
+    const int i = q / D, j = q % D;   // eigenvector i (row i of Q^T), component j
+    vec[(size_t)sm.rank[i] * D + j] = sm.a[i * S + j];
   }
-  if (tid == 0 && p.sweeps) p.sweeps[m] = converged ? sweeps : -sweeps;
+  if (tid == 0 && p.iters) p.iters[m] = iters;
 }
 
 template <int D, int DT>
@@ -391,7 +687,7 @@ hipError_t launch_enc(const EncodeParams& p, bool spectrum, hipStream_t s) {
   const int64_t mats = (int64_t)p.n_blocks * p.n_kv_heads * 2;
   if (mats == 0) return hipSuccess;
   if (spectrum)
-    hipLaunchKernelGGL((milo_encode_spectrum_kernel<D, DT>), dim3((unsigned)mats), dim3(kEncThreads), 0, s, p);
+    hipLaunchKernelGGL((milo_encode_spectrum_kernel<D, DT>), dim3((unsigned)mats), dim3(kEigThreads), 0, s, p);
   else
     hipLaunchKernelGGL((milo_encode_factors_kernel<D, DT>), dim3((unsigned)mats), dim3(kEncThreads), 0, s, p);
   return hipGetLastError();

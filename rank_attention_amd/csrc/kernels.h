@@ -85,7 +85,7 @@ struct EncodeParams {
   const int64_t* tok_start;    // [n_blocks]
   const milo_block* blocks;    // [n_blocks]
   float* sigma;                // [n_mats][head_dim] descending, or null
-  int32_t* sweeps;             // [n_mats] Jacobi sweeps (negative: not converged), or null
+  int32_t* iters;              // [n_mats] QL iterations (negative: not converged), or null
   float* vecs;                 // [n_mats][head_dim][head_dim] eigenvector rows, descending
   void* pool;
   int32_t n_blocks, n_kv_heads, n_tokens;

@@ -53,7 +53,7 @@ milo::EncodeParams params_of(const milo_encode_args* a) {
   p.tok_start = a->tok_start;
   p.blocks = a->blocks;
   p.sigma = a->sigma;
-  p.sweeps = a->sweeps;
+  p.iters = a->iters;
   p.vecs = static_cast<float*>(a->workspace);
   p.pool = a->pool;
   p.n_blocks = a->n_blocks;
@@ -127,7 +127,7 @@ milo_status milo_encode_spectrum(const milo_encode_args* a, void* hip_stream) {
   milo_status st = check_common(a);
   if (st != MILO_OK) return st;
   if (a->n_blocks == 0) return MILO_OK;
-  if ((a->sigma && !enc_aligned(a->sigma, 4)) || (a->sweeps && !enc_aligned(a->sweeps, 4)))
+  if ((a->sigma && !enc_aligned(a->sigma, 4)) || (a->iters && !enc_aligned(a->iters, 4)))
     return MILO_ERR_INVALID;
   const milo::EncodeParams p = params_of(a);
   milo::clear_stale_error();

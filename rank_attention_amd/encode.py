@@ -178,7 +178,7 @@ class DeviceContext:
         self.workspace = None
         self._spectrum_blocks = None
 
-    def _args(self, blocks_dev, pool=None, sigma=None, sweeps=None) -> MiloEncodeArgs:
+    def _args(self, blocks_dev, pool=None, sigma=None, iters=None) -> MiloEncodeArgs:
         a = MiloEncodeArgs()
         a.struct_size = ctypes.sizeof(MiloEncodeArgs)
         a.dtype = self.code
@@ -188,7 +188,7 @@ class DeviceContext:
         a.tok_start = self.tok_start.data_ptr()
         a.blocks = blocks_dev.data_ptr()
         a.sigma = None if sigma is None else sigma.data_ptr()
-        a.sweeps = None if sweeps is None else sweeps.data_ptr()
+        a.iters = None if iters is None else iters.data_ptr()
         a.pool = None if pool is None else pool.data_ptr()
         if self.workspace is not None:
             a.workspace, a.workspace_bytes = self.workspace.data_ptr(), self.workspace.numel()
@@ -207,7 +207,7 @@ class DeviceContext:
 
     def spectrum(self, stream=None):
         """Singular values [n_blocks][Hkv][2][d] (fp32, descending; K then V)
-        and Jacobi sweep counts [n_blocks][Hkv][2]; keeps the singular
+        and QL iteration counts [n_blocks][Hkv][2]; keeps the singular
         vectors in this context's workspace for factors()."""
         import torch
         lib = _lib.load()
@@ -216,14 +216,14 @@ class DeviceContext:
         self._spectrum_blocks = torch.from_numpy(blocks.view(np.uint8)).to(self.device)
         sigma = torch.empty((self.n_blocks, self.n_kv_heads, 2, self.head_dim), dtype=torch.float32,
                             device=self.device)
-        sweeps = torch.empty((self.n_blocks, self.n_kv_heads, 2), dtype=torch.int32, device=self.device)
-        a = self._args(self._spectrum_blocks, sigma=sigma, sweeps=sweeps)
+        iters = torch.empty((self.n_blocks, self.n_kv_heads, 2), dtype=torch.int32, device=self.device)
+        a = self._args(self._spectrum_blocks, sigma=sigma, iters=iters)
         need = lib.milo_encode_workspace_bytes(ctypes.byref(a))
         if need and (self.workspace is None or self.workspace.numel() < need):
             self.workspace = torch.empty(int(need), dtype=torch.uint8, device=self.device)
-        a = self._args(self._spectrum_blocks, sigma=sigma, sweeps=sweeps)
+        a = self._args(self._spectrum_blocks, sigma=sigma, iters=iters)
         self._call(lib.milo_encode_spectrum, a, stream)
-        return sigma, sweeps
+        return sigma, iters
 
     def factors(self, rank_k, rank_v, stream=None):
         """Factors at the given per-block ranks (after spectrum()): returns

@@ -249,7 +249,7 @@ def enc_args(**over):
     a.dtype = _lib.MILO_BF16
     a.n_blocks, a.n_kv_heads, a.head_dim, a.n_tokens = 3, 2, 128, 1000
     a.k = a.v = a.tok_start = a.blocks = a.pool = FAKE
-    a.sigma = a.sweeps = FAKE
+    a.sigma = a.iters = FAKE
     a.workspace, a.workspace_bytes = FAKE, 1 << 30
     for k, v in over.items():
         setattr(a, k, v)
