@@ -129,10 +129,11 @@ template <int D>
 struct EigSmem {
   static constexpr int S = D + 4;   // row stride of a, in floats
   float a[D * S];                   // X staging, then G, the reflectors and Q^T, then the eigenvectors
-  float vb[D];                      // v of the current reflector by column (0 left of the block)
+  float vb[1][D];                   // v of the current reflector by column (0 left of its block)
+  float wb[4][D];                   // w by column, one copy per wave
   float part[2][D];                 // partial row products of the two column halves
   float tau[D];
-  float dq[2][D], eq[2][D];         // d and e, one copy per QL wave
+  f32x2_t de[2][D];                 // (d_i, e_i), one copy per QL wave
   float lam[D];                     // eigenvalues
   int rank[D];
   float trace;
@@ -296,31 +297,29 @@ __device__ __forceinline__ void tridiagonalize(EigSmem<D>& sm, int tid) {
         frexpf(amax, &ex);
         x0 = ldexpf(x0, -ex);   // exact
         x1 = ldexpf(x1, -ex);
-        const float alpha = __shfl(x0, 0);
+        const float alpha = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x0)));
         const float xn2 = wave_sum((i0 == 0 ? 0.f : x0 * x0) + x1 * x1);
         if (xn2 > 0.f) {
           const float beta = -copysignf(sqrtf(alpha * alpha + xn2), alpha);
-          tk = (beta - alpha) / beta;
-          const float inv = 1.f / (alpha - beta);
+          tk = (beta - alpha) * __builtin_amdgcn_rcpf(beta);
+          const float inv = __builtin_amdgcn_rcpf(alpha - beta);
           v0 = i0 == 0 ? 1.f : x0 * inv;
           v1 = x1 * inv;
           ek = ldexpf(beta, ex);
         }
       }
-      // vb by column (v at k+1.., zero left of the block), one store per
-      // entry; v past v_0 is kept in row k
-#pragma unroll
-      for (int hc = 0; hc < 2; ++hc) {
-        const int c = lane + 64 * hc, idx = c - (k + 1);
-        const float s0 = __shfl(v0, idx & 63), s1 = __shfl(v1, idx & 63);
-        if (c < D) sm.vb[c] = idx < 0 ? 0.f : (idx < 64 ? s0 : s1);
-      }
+      // vb by column: v at k+1.., zero left of the block (disjoint stores);
+      // v past v_0 is kept in row k
+      float* vb = sm.vb[0];
+      if (lane < k + 1) vb[lane] = 0.f;
+      if (lane + 64 < k + 1) vb[lane + 64] = 0.f;
+      if (i0 < m) vb[k + 1 + i0] = v0;
+      if (i1 < m) vb[k + 1 + i1] = v1;
       if (i0 > 0 && i0 < m) A[k * S + k + 1 + i0] = v0;
       if (i1 < m) A[k * S + k + 1 + i1] = v1;
       if (lane == 0) {
         sm.tau[k] = tk;
-        sm.dq[0][k] = sm.dq[1][k] = A[k * S + k];
-        sm.eq[0][k] = sm.eq[1][k] = ek;
+        sm.de[0][k] = sm.de[1][k] = f32x2_t{A[k * S + k], ek};
       }
     }
     __syncthreads();
@@ -335,7 +334,7 @@ __device__ __forceinline__ void tridiagonalize(EigSmem<D>& sm, int tid) {
     for (int q = 0; q < NC; ++q) {
       if (q < h.n && act) {
         row[q] = lds4(ar + 4 * q);
-        const f32x4_t vq = lds4(sm.vb + h.c0 + 4 * q);
+        const f32x4_t vq = lds4(sm.vb[0] + h.c0 + 4 * q);
 #pragma unroll
         for (int e = 0; e < 4; ++e) dot = fmaf(row[q][e], vq[e], dot);
       }
@@ -343,30 +342,30 @@ __device__ __forceinline__ void tridiagonalize(EigSmem<D>& sm, int tid) {
     if (act) sm.part[hh][k + 1 + ii] = dot;
     __syncthreads();
     // K = (tau/2) p.v with p_i = tau (part0_i + part1_i), formed alike by
-    // every wave; w_c = p_c - K v_c is formed where it is used
-    float kc;
+    // every wave, then w_c = p_c - K v_c into the wave's own copy of w (zero
+    // left of the block); the wave reads back only what it wrote itself
+    float* wb = sm.wb[tid >> 6];
     {
       const int ca = lane, cb = lane + 64;
       const bool ina = ca >= k + 1, inb = cb >= k + 1 && cb < D;
       const float pa = ina ? pvec(ca, tk) : 0.f, pb = inb ? pvec(cb, tk) : 0.f;
-      const float va = ina ? sm.vb[ca] : 0.f, vbb = inb ? sm.vb[cb] : 0.f;
-      kc = 0.5f * tk * wave_sum(fmaf(pa, va, pb * vbb));
+      const float va = ina ? sm.vb[0][ca] : 0.f, vbb = inb ? sm.vb[0][cb] : 0.f;
+      const float kc = 0.5f * tk * wave_sum(fmaf(pa, va, pb * vbb));
+      wb[ca] = ina ? __fsub_rn(pa, __fmul_rn(kc, va)) : 0.f;
+      if (cb < D) wb[cb] = inb ? __fsub_rn(pb, __fmul_rn(kc, vbb)) : 0.f;
     }
     if (act) {
       const int r = k + 1 + ii;
-      const float vi = sm.vb[r], wi = __fsub_rn(pvec(r, tk), __fmul_rn(kc, vi));
+      const float vi = sm.vb[0][r], wi = wb[r];
 #pragma unroll
       for (int q = 0; q < NC; ++q) {
         if (q < h.n) {
           const int c = h.c0 + 4 * q;
-          const f32x4_t vq = lds4(sm.vb + c), p0 = lds4(sm.part[0] + c), p1 = lds4(sm.part[1] + c);
-          // columns left of the block have v = 0 (and stale p): they are written back unchanged
+          const f32x4_t vq = lds4(sm.vb[0] + c), wq = lds4(wb + c);
+          // columns left of the block have v = w = 0: they are written back unchanged
           f32x4_t o;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float wc = c + e >= k + 1 ? __fsub_rn(tk * (p0[e] + p1[e]), __fmul_rn(kc, vq[e])) : 0.f;
-            o[e] = __fsub_rn(row[q][e], sym2(vi, wc, wi, vq[e]));
-          }
+          for (int e = 0; e < 4; ++e) o[e] = __fsub_rn(row[q][e], sym2(vi, wq[e], wi, vq[e]));
           sts4(ar + 4 * q, o);
         }
       }
@@ -374,10 +373,8 @@ __device__ __forceinline__ void tridiagonalize(EigSmem<D>& sm, int tid) {
     __syncthreads();
   }
   if (tid == 0) {
-    sm.dq[0][D - 2] = sm.dq[1][D - 2] = A[(D - 2) * S + D - 2];
-    sm.dq[0][D - 1] = sm.dq[1][D - 1] = A[(D - 1) * S + D - 1];
-    sm.eq[0][D - 2] = sm.eq[1][D - 2] = A[(D - 2) * S + D - 1];
-    sm.eq[0][D - 1] = sm.eq[1][D - 1] = 0.f;
+    sm.de[0][D - 2] = sm.de[1][D - 2] = f32x2_t{A[(D - 2) * S + D - 2], A[(D - 2) * S + D - 1]};
+    sm.de[0][D - 1] = sm.de[1][D - 1] = f32x2_t{A[(D - 1) * S + D - 1], 0.f};
   }
   __syncthreads();
 }
@@ -396,7 +393,7 @@ __device__ __forceinline__ void accumulate_qt(EigSmem<D>& sm, int tid) {
   for (int k = D - 3; k >= 0; --k) {
     const int m = D - 1 - k;
     for (int c = tid; c < D; c += kEigThreads) {
-      sm.vb[c] = c < k + 1 ? 0.f : (c == k + 1 ? 1.f : A[k * S + c]);
+      sm.vb[0][c] = c < k + 1 ? 0.f : (c == k + 1 ? 1.f : A[k * S + c]);
       if (c >= k + 1) {
         A[(k + 1) * S + c] = c == k + 1 ? 1.f : 0.f;   // row k+1
         A[c * S + k + 1] = c == k + 1 ? 1.f : 0.f;     // column k+1
@@ -414,7 +411,7 @@ __device__ __forceinline__ void accumulate_qt(EigSmem<D>& sm, int tid) {
     for (int q = 0; q < NC; ++q) {
       if (q < h.n && act) {
         row[q] = lds4(ar + 4 * q);
-        const f32x4_t vq = lds4(sm.vb + h.c0 + 4 * q);
+        const f32x4_t vq = lds4(sm.vb[0] + h.c0 + 4 * q);
 #pragma unroll
         for (int e = 0; e < 4; ++e) dot = fmaf(row[q][e], vq[e], dot);
       }
@@ -426,7 +423,7 @@ __device__ __forceinline__ void accumulate_qt(EigSmem<D>& sm, int tid) {
 #pragma unroll
       for (int q = 0; q < NC; ++q) {
         if (q < h.n) {
-          const f32x4_t vq = lds4(sm.vb + h.c0 + 4 * q);   // zero left of the block: those entries stay
+          const f32x4_t vq = lds4(sm.vb[0] + h.c0 + 4 * q);   // zero left of the block: those entries stay
           f32x4_t o;
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = fmaf(-tw, vq[e], row[q][e]);
@@ -455,21 +452,21 @@ __device__ __forceinline__ float lane_get(float lo, float hi, int i) {
 // 64 w + lane of the rows of Q^T (one wave per 64 entries).  Returns the
 // iteration count, negative when an eigenvalue took more than kEigMaxIt
 // iterations.  Every lane computes the same scalar recurrence.  At the start
-// of an iteration d and e are read from LDS into lane registers; a sweep
-// reads entries only before it changes them, so it reads that snapshot and
-// writes its new values to LDS.  A rotation of f = g = 0 is the identity
-// (c = 1, s = 0, r = 0), so a sweep never stops early.
+// of an iteration (d, e) is read from LDS into lane registers for the
+// deflation test and the shift; the sweep reads each pair one step ahead
+// (before it is changed) and writes the new pair of the step behind it.  A
+// rotation of f = g = 0 is the identity (c = 1, s = 0, r = 0), so a sweep
+// never stops early.
 template <int D>
 __device__ __forceinline__ int ql_implicit(EigSmem<D>& sm, int wave, int lane, float tol_abs) {
   constexpr int S = EigSmem<D>::S;
-  float* dq = sm.dq[wave];
-  float* eq = sm.eq[wave];
+  f32x2_t* de = sm.de[wave];
   float* zc0 = sm.a + 64 * wave + lane;   // Q^T[i][64 w + lane] at zc0[i * S]
   int iters = 0;
   for (int l = 0; l < D; ++l) {
     for (int it = 0;; ++it) {
-      const float dlo = dq[lane], elo = eq[lane];
-      const float dhi = D > 64 ? dq[min(lane + 64, D - 1)] : 0.f, ehi = D > 64 ? eq[min(lane + 64, D - 1)] : 0.f;
+      const f32x2_t plo = de[lane], phi = D > 64 ? de[min(lane + 64, D - 1)] : f32x2_t{0.f, 0.f};
+      const float dlo = plo[0], elo = plo[1], dhi = phi[0], ehi = phi[1];
       // m = the first index >= l whose e_m is negligible (e_{D-1} = 0)
       int m = D - 1;
       {
@@ -499,38 +496,32 @@ __device__ __forceinline__ int ql_implicit(EigSmem<D>& sm, int wave, int lane, f
       float s = 1.f, c = 1.f, p = 0.f;
       float zc = zc0[m * S];
       float dn = lane_get<D>(dlo, dhi, m);   // d_{i+1} before this sweep
-      float ei = lane_get<D>(elo, ehi, m - 1), di = lane_get<D>(dlo, dhi, m - 1);
+      f32x2_t cur = de[m - 1];               // (d_i, e_i) of the step
       for (int i = m - 1; i >= l; --i) {
-        const int ip = i > 0 ? i - 1 : 0;    // next step's entries (not yet changed in this sweep)
-        const float ein = eq[ip], din = dq[ip];
+        const f32x2_t nxt = de[i > 0 ? i - 1 : 0];   // next step's pair (not yet changed)
         const float zi = zc0[i * S];
-        const float f = s * ei, b = c * ei;
+        const float di = cur[0], ei = cur[1];
+        const float f = s * ei, b = c * ei, b2 = 2.f * b;
         const float r2 = fmaf(f, f, g * g);
-        const bool zero = r2 == 0.f;
-        const float ri = zero ? 0.f : __builtin_amdgcn_rsqf(r2);
-        eq[i + 1] = r2 * ri;
+        // r2 = 0 (f = g = 0): ri is finite, s = 0 and c = 0 + 1
+        const float one = r2 == 0.f ? 1.f : 0.f;
+        const float ri = __builtin_amdgcn_rsqf(fmaxf(r2, 0x1p-126f));
         s = f * ri;
-        c = zero ? 1.f : g * ri;
+        c = fmaf(g, ri, one);
         const float gg = dn - p;
-        const float t = fmaf(di - gg, s, 2.f * c * b);
+        const float t = fmaf(di - gg, s, c * b2);
         p = s * t;
-        dq[i + 1] = gg + p;
+        de[i + 1] = f32x2_t{gg + p, r2 * ri};
         g = fmaf(c, t, -b);
         zc0[(i + 1) * S] = fmaf(s, zi, c * zc);
         zc = fmaf(c, zi, -s * zc);
         dn = di;
-        ei = ein;
-        di = din;
+        cur = nxt;
       }
-      dq[l] = dn - p;
-      eq[l] = g;
-      eq[m] = 0.f;
+      de[l] = f32x2_t{dn - p, g};
+      de[m][1] = 0.f;
       zc0[l * S] = zc;
     }
-  }
-  if (wave == 0) {   // eigenvalues out (wave 1 works on its own copy)
-    sm.lam[lane] = dq[lane];
-    if (D > 64) sm.lam[lane + 64] = dq[lane + 64];
   }
   return iters;
 }
@@ -579,6 +570,10 @@ __global__ __launch_bounds__(kEigThreads) void milo_encode_spectrum_kernel(Encod
     if (wave < D / 64) {
       const int it = ql_implicit<D>(sm, wave, lane, kEigTolAbs * ldexpf(trace, -ex));
       if (tid == 0) iters = it;
+      if (wave == 0) {   // eigenvalues out (wave 1 works on its own copy)
+        sm.lam[lane] = sm.de[0][lane][0];
+        if (D > 64) sm.lam[lane + 64] = sm.de[0][lane + 64][0];
+      }
     }
   } else {
     // no energy: eigenvalues 0, eigenvectors the unit vectors
