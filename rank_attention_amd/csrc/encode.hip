@@ -107,10 +107,13 @@ __device__ __forceinline__ EncMat enc_mat(const EncodeParams& p, int m, int D) {
 //     is scaled by a power of two before its norm is taken.
 //  3. Q^T = H_{d-3} ... H_1 H_0 accumulated in place (from the last
 //     reflector back: Q^T <- Q^T H_k on the trailing block).
-//  4. Implicit QL with a Wilkinson-type shift on (d, e), every plane rotation
-//     applied to the rows of Q^T (the columns of Q): one wave per 64 entries
-//     of a row runs the same scalar recurrence (each on its own copy of d
-//     and e) and rotates its entries of the two rows.
+//  4. Implicit QL with a Wilkinson-type shift on (d, e) taken in reverse
+//     order (the tridiagonal forms of these Gram matrices are graded, large
+//     at the top, and QL from the other end needs about a third fewer
+//     rotations in the worst case), every plane rotation applied to the rows
+//     of Q^T (the columns of Q): one wave per 64 entries of a row runs the
+//     same scalar recurrence (each on its own copy of d and e) and rotates
+//     its entries of the two rows.
 //     e_m counts as zero when |e_m| <= 2^-24 (|d_m| + |d_m+1|) or <= 1e-8
 //     trace; at most 30 iterations per eigenvalue.
 //  5. sigma_i = sqrt(max(lambda_i, 0)) descending and the eigenvectors (the
@@ -133,7 +136,8 @@ struct EigSmem {
   float wb[4][D];                   // w by column, one copy per wave
   float part[2][D];                 // partial row products of the two column halves
   float tau[D];
-  f32x2_t de[2][D];                 // (d_i, e_i), one copy per QL wave
+  f32x2_t de[2][D];                 // (d, e) of the tridiagonal form in reverse order, (d_{D-1-i}, e_{D-2-i});
+                                    // one copy per QL wave
   float lam[D];                     // eigenvalues
   int rank[D];
   float trace;
@@ -319,7 +323,8 @@ __device__ __forceinline__ void tridiagonalize(EigSmem<D>& sm, int tid) {
       if (i1 < m) A[k * S + k + 1 + i1] = v1;
       if (lane == 0) {
         sm.tau[k] = tk;
-        sm.de[0][k] = sm.de[1][k] = f32x2_t{A[k * S + k], ek};
+        sm.de[0][D - 1 - k][0] = sm.de[1][D - 1 - k][0] = A[k * S + k];
+        sm.de[0][D - 2 - k][1] = sm.de[1][D - 2 - k][1] = ek;
       }
     }
     __syncthreads();
@@ -373,8 +378,9 @@ __device__ __forceinline__ void tridiagonalize(EigSmem<D>& sm, int tid) {
     __syncthreads();
   }
   if (tid == 0) {
-    sm.de[0][D - 2] = sm.de[1][D - 2] = f32x2_t{A[(D - 2) * S + D - 2], A[(D - 2) * S + D - 1]};
-    sm.de[0][D - 1] = sm.de[1][D - 1] = f32x2_t{A[(D - 1) * S + D - 1], 0.f};
+    sm.de[0][1][0] = sm.de[1][1][0] = A[(D - 2) * S + D - 2];
+    sm.de[0][0] = sm.de[1][0] = f32x2_t{A[(D - 1) * S + D - 1], A[(D - 2) * S + D - 1]};
+    sm.de[0][D - 1][1] = sm.de[1][D - 1][1] = 0.f;
   }
   __syncthreads();
 }
@@ -461,7 +467,10 @@ template <int D>
 __device__ __forceinline__ int ql_implicit(EigSmem<D>& sm, int wave, int lane, float tol_abs) {
   constexpr int S = EigSmem<D>::S;
   f32x2_t* de = sm.de[wave];
-  float* zc0 = sm.a + 64 * wave + lane;   // Q^T[i][64 w + lane] at zc0[i * S]
+  // the QL runs on the reversed tridiagonal (it converges in fewer
+  // rotations from that end for these graded matrices): its index i is row
+  // D-1-i of Q^T, and Q^T[D-1-i][64 w + lane] is at zr[-i * S]
+  float* zr = sm.a + (D - 1) * S + 64 * wave + lane;
   int iters = 0;
   for (int l = 0; l < D; ++l) {
     for (int it = 0;; ++it) {
@@ -494,12 +503,12 @@ __device__ __forceinline__ int ql_implicit(EigSmem<D>& sm, int wave, int lane, f
       const float rr = sqrtf(fmaf(g, g, 1.f));
       g = lane_get<D>(dlo, dhi, m) - dl + el / (g + copysignf(rr, g));
       float s = 1.f, c = 1.f, p = 0.f;
-      float zc = zc0[m * S];
+      float zc = zr[-m * S];
       float dn = lane_get<D>(dlo, dhi, m);   // d_{i+1} before this sweep
       f32x2_t cur = de[m - 1];               // (d_i, e_i) of the step
       for (int i = m - 1; i >= l; --i) {
         const f32x2_t nxt = de[i > 0 ? i - 1 : 0];   // next step's pair (not yet changed)
-        const float zi = zc0[i * S];
+        const float zi = zr[-i * S];
         const float di = cur[0], ei = cur[1];
         const float f = s * ei, b = c * ei, b2 = 2.f * b;
         const float r2 = fmaf(f, f, g * g);
@@ -513,14 +522,14 @@ __device__ __forceinline__ int ql_implicit(EigSmem<D>& sm, int wave, int lane, f
         p = s * t;
         de[i + 1] = f32x2_t{gg + p, r2 * ri};
         g = fmaf(c, t, -b);
-        zc0[(i + 1) * S] = fmaf(s, zi, c * zc);
+        zr[-(i + 1) * S] = fmaf(s, zi, c * zc);
         zc = fmaf(c, zi, -s * zc);
         dn = di;
         cur = nxt;
       }
       de[l] = f32x2_t{dn - p, g};
       de[m][1] = 0.f;
-      zc0[l * S] = zc;
+      zr[-l * S] = zc;
     }
   }
   return iters;
@@ -571,8 +580,8 @@ __global__ __launch_bounds__(kEigThreads) void milo_encode_spectrum_kernel(Encod
       const int it = ql_implicit<D>(sm, wave, lane, kEigTolAbs * ldexpf(trace, -ex));
       if (tid == 0) iters = it;
       if (wave == 0) {   // eigenvalues out (wave 1 works on its own copy)
-        sm.lam[lane] = sm.de[0][lane][0];
-        if (D > 64) sm.lam[lane + 64] = sm.de[0][lane + 64][0];
+        sm.lam[D - 1 - lane] = sm.de[0][lane][0];   // by row of Q^T
+        if (D > 64) sm.lam[D - 65 - lane] = sm.de[0][lane + 64][0];
       }
     }
   } else {
