@@ -17,9 +17,10 @@
 //            the steps are listed before the kernel).  Output: sigma_i =
 //            sqrt(max(lambda_i, 0)) descending and the eigenvectors as
 //            rows, sorted the same way (workspace).
-//  factors   W = the first r eigenvector rows, U^T = W X^T (fp32 sums),
-//            written into the pool in the storage type (RNE for bf16),
-//            U^T rows zero-padded to ld_tok.
+//  factors   W = the first r eigenvector rows, U^T = W X^T, written into
+//            the pool in the storage type (RNE for bf16), U^T rows
+//            zero-padded to ld_tok: bf16 on the matrix cores (W split into
+//            bf16 hi + lo), fp32 on the vector ALUs (fp32 sums).
 #include "device_common.h"
 #include "kernels.h"
 #include "mfma_common.h"
@@ -686,14 +687,79 @@ __global__ __launch_bounds__(kEncThreads) void milo_encode_factors_kernel(Encode
   }
 }
 
+
+// Factors for bf16 storage on the matrix cores: U^T = W X^T as
+// v_mfma_f32_16x16x32_bf16 with W (fp32) split into bf16 hi + lo (about 17
+// significant bits; the X products are exact and the sums fp32), stored
+// rounded to nearest even.  Workgroup (matrix, c) of kFacGroups per matrix
+// takes the 256-token chunks c, c + kFacGroups, ...; its wave w the 16-rank
+// tiles w and w + 4.  Lane l of a tile's 16 x 16 result holds token l%16 of
+// the step and ranks 4(l/16) .. +3; tokens past n_tok load as zero, so U^T is
+// zero up to ld_tok.  The workgroup of chunk 0 also writes W.
+constexpr int kFacGroups = 4;
+constexpr int kFacChunk = 256;
+
+template <int D>
+__global__ __launch_bounds__(256) void milo_encode_factors_mfma_kernel(EncodeParams p) {
+  constexpr int KS = D / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = blockIdx.x / kFacGroups, grp = blockIdx.x % kFacGroups;
+  const EncMat e = enc_mat(p, m, D);
+  const milo_block blk = p.blocks[e.b];
+  const int rk = min(max(blk.rank_k, 0), D), rv = min(max(blk.rank_v, 0), D);
+  const int r = e.kv ? rv : rk;
+  const int ld = blk.ld_tok;
+  if (r == 0) return;
+  const int64_t head = blk.off + (int64_t)e.g * (rk + rv) * (ld + D);
+  const int64_t u_off = head + (e.kv ? (int64_t)rk * (ld + D) : 0);
+  const int64_t w_off = u_off + (int64_t)r * ld;
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(e.kv ? p.v : p.k);
+  const float* vec = p.vecs + (size_t)m * D * D;
+  if (grp == 0)
+    for (int q = tid; q < r * D; q += 256) store1<MILO_BF16>(p.pool, w_off + q, vec[q]);
+  const int col = lane & 15, quad = lane >> 4;
+  for (int kt = wave; 16 * kt < r; kt += 4) {
+    // W rows 16 kt + col (clamped; rows past r are not stored), dims 32 s + 8 quad .. +7
+    const float* wr = vec + (size_t)min(16 * kt + col, r - 1) * D + 8 * quad;
+    u32x4_t ah[KS], al[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) split_pair(ld16f(wr + 32 * s), ld16f(wr + 32 * s + 4), ah[s], al[s]);
+    for (int c0 = grp * kFacChunk; c0 < ld; c0 += kFacGroups * kFacChunk) {
+      const int c1 = min(c0 + kFacChunk, ld);
+      for (int t0 = c0; t0 < c1; t0 += 16) {
+        const int t = t0 + col;
+        const uint16_t* xr = x + e.row0 + (int64_t)t * D + 8 * quad;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const u32x4_t b = t < e.T ? ld16(xr + 32 * s) : u32x4_t{0u, 0u, 0u, 0u};
+          acc = mfma32(ah[s], b, acc);
+          acc = mfma32(al[s], b, acc);
+        }
+        if (t < c1) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int k = 16 * kt + 4 * quad + v;
+            if (k < r) store1<MILO_BF16>(p.pool, u_off + (int64_t)k * ld + t, acc[v]);
+          }
+        }
+      }
+    }
+  }
+}
+
 template <int D, int DT>
 hipError_t launch_enc(const EncodeParams& p, bool spectrum, hipStream_t s) {
   const int64_t mats = (int64_t)p.n_blocks * p.n_kv_heads * 2;
   if (mats == 0) return hipSuccess;
-  if (spectrum)
+  if (spectrum) {
     hipLaunchKernelGGL((milo_encode_spectrum_kernel<D, DT>), dim3((unsigned)mats), dim3(kEigThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL((milo_encode_factors_kernel<D, DT>), dim3((unsigned)mats), dim3(kEncThreads), 0, s, p);
+  } else {
+    if constexpr (DT == MILO_BF16)
+      hipLaunchKernelGGL((milo_encode_factors_mfma_kernel<D>), dim3((unsigned)(mats * kFacGroups)), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((milo_encode_factors_kernel<D, DT>), dim3((unsigned)mats), dim3(kEncThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 
