@@ -109,22 +109,21 @@ __device__ __forceinline__ void mfma_project_q(const uint16_t* W, const uint16_t
 
 constexpr int kRowsPerStep = 4;   // U^T rows per prefetch step of the score loop
 
-// Loads rows k0 .. k0+3 of U^T (clamped to r-1) at the lane's two chunks.
-__device__ __forceinline__ void load_rows4(const uint16_t* Ut, int ld, int k0, int r, int tq0,
-                                           int tq1, u32x4_t (&A)[kRowsPerStep],
-                                           u32x4_t (&B)[kRowsPerStep]) {
+// Loads rows k0 .. k0+3 of U^T (clamped to r-1) at the lane's CH chunks.
+template <int CH>
+__device__ __forceinline__ void load_rows4(const uint16_t* Ut, int ld, int k0, int r, const int (&tq)[CH],
+                                           u32x4_t (&A)[CH][kRowsPerStep]) {
 #pragma unroll
   for (int j = 0; j < kRowsPerStep; ++j) {
     const uint16_t* row = Ut + (size_t)min(k0 + j, r - 1) * ld;
-    A[j] = ld16_stream(row + tq0);
-    B[j] = ld16_stream(row + tq1);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) A[c][j] = ld16_stream(row + tq[c]);
   }
 }
 
-template <int G>
-__device__ __forceinline__ void score_rows4(const u32x4_t (&A)[kRowsPerStep],
-                                            const u32x4_t (&B)[kRowsPerStep], int k0, int r,
-                                            const float* pf, float (&s)[16][G]) {
+template <int G, int CH>
+__device__ __forceinline__ void score_rows4(const u32x4_t (&A)[CH][kRowsPerStep], int k0, int r,
+                                            const float* pf, float (&s)[8 * CH][G]) {
 #pragma unroll
   for (int j = 0; j < kRowsPerStep; ++j) {
     if (k0 + j < r) {
@@ -133,58 +132,65 @@ __device__ __forceinline__ void score_rows4(const u32x4_t (&A)[kRowsPerStep],
       const float pp[8] = {pq0[0], pq0[1], pq0[2], pq0[3], pq1[0], pq1[1], pq1[2], pq1[3]};
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float a0 = bf_lo(A[j][w]), a1 = bf_hi(A[j][w]);
-        const float b0 = bf_lo(B[j][w]), b1 = bf_hi(B[j][w]);
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          s[2 * w][h] = fmaf(a0, pp[h], s[2 * w][h]);
-          s[2 * w + 1][h] = fmaf(a1, pp[h], s[2 * w + 1][h]);
-          s[8 + 2 * w][h] = fmaf(b0, pp[h], s[8 + 2 * w][h]);
-          s[8 + 2 * w + 1][h] = fmaf(b1, pp[h], s[8 + 2 * w + 1][h]);
+        for (int c = 0; c < CH; ++c) {
+          const float a0 = bf_lo(A[c][j][w]), a1 = bf_hi(A[c][j][w]);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            s[8 * c + 2 * w][h] = fmaf(a0, pp[h], s[8 * c + 2 * w][h]);
+            s[8 * c + 2 * w + 1][h] = fmaf(a1, pp[h], s[8 * c + 2 * w + 1][h]);
+          }
         }
       }
     }
   }
 }
 
-// One 1024-token tile at a time: scores, online softmax, then per group of
-// R rows of U'^T the group's z = e^T U' and at once o~ += z W' for those
-// rows (W' rows load with the group), so no pass over W' is left at the end.
-// o~ is rescaled with the softmax like l.
-template <int D, int G, bool RAGGED>
+// One tile of 512 CH tokens at a time (lane l holds tokens t0 + 512 c + 8 l
+// .. +7 of chunk c): scores, online softmax, then per group of R rows of
+// U'^T the group's z = e^T U' and at once o~ += z W' for those rows (W'
+// rows load with the group), so no pass over W' is left at the end.  o~ is
+// rescaled with the softmax like l.  Blocks of at most 512 tokens take CH =
+// 1, so no lane carries a chunk that lies wholly past the block.
+template <int D, int G, bool RAGGED, int CH>
 __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* Upt,
                                            const uint16_t* Wp, int ld, int T, int r, int rv,
                                            const float* pf, float (&m_run)[G], float (&l_run)[G],
                                            float (&o)[G][D / 64], float* zs, int lane) {
   using S = Shape<D, G>;
-  constexpr int R = S::R, JPL = S::JPL;
-  for (int t0 = 0; t0 < T; t0 += 1024) {
-    const int tc0 = t0 + lane * 8, tc1 = t0 + 512 + lane * 8;
-    const bool ok0 = tc0 < T, ok1 = tc1 < T;
-    // A lane whose chunk lies past the block end reads the tile's first
-    // chunk instead (always in bounds) and its tokens are masked below.
-    const int tq0 = ok0 ? tc0 : t0, tq1 = ok1 ? tc1 : t0;
+  constexpr int R = S::R, JPL = S::JPL, NE = 8 * CH;
+  for (int t0 = 0; t0 < T; t0 += 512 * CH) {
+    int tc[CH], tq[CH];
+    bool ok[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      tc[c] = t0 + 512 * c + lane * 8;
+      ok[c] = tc[c] < T;
+      // A lane whose chunk lies past the block end reads the tile's first
+      // chunk instead (always in bounds) and its tokens are masked below.
+      tq[c] = ok[c] ? tc[c] : t0;
+    }
 
     // ---- scores s[c*8+e][h] for token tc_c + e: U rows unpacked to fp32
     // and met with fp32 p (bf16 rounding of p would cost ~1% on sharp softmax)
-    float s[16][G];
+    float s[NE][G];
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
+    for (int e = 0; e < NE; ++e)
 #pragma unroll
       for (int h = 0; h < G; ++h) s[e][h] = 0.f;
     if (r > 0) {
-      u32x4_t A0[kRowsPerStep], B0[kRowsPerStep], A1[kRowsPerStep], B1[kRowsPerStep];
-      load_rows4(Ut, ld, 0, r, tq0, tq1, A0, B0);
+      u32x4_t A0[CH][kRowsPerStep], A1[CH][kRowsPerStep];
+      load_rows4<CH>(Ut, ld, 0, r, tq, A0);
       for (int k0 = 0; k0 < r; k0 += 2 * kRowsPerStep) {
-        if (k0 + kRowsPerStep < r) load_rows4(Ut, ld, k0 + kRowsPerStep, r, tq0, tq1, A1, B1);
-        score_rows4<G>(A0, B0, k0, r, pf, s);
-        if (k0 + 2 * kRowsPerStep < r) load_rows4(Ut, ld, k0 + 2 * kRowsPerStep, r, tq0, tq1, A0, B0);
-        if (k0 + kRowsPerStep < r) score_rows4<G>(A1, B1, k0 + kRowsPerStep, r, pf, s);
+        if (k0 + kRowsPerStep < r) load_rows4<CH>(Ut, ld, k0 + kRowsPerStep, r, tq, A1);
+        score_rows4<G, CH>(A0, k0, r, pf, s);
+        if (k0 + 2 * kRowsPerStep < r) load_rows4<CH>(Ut, ld, k0 + 2 * kRowsPerStep, r, tq, A0);
+        if (k0 + kRowsPerStep < r) score_rows4<G, CH>(A1, k0 + kRowsPerStep, r, pf, s);
       }
     }
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int tok = (e < 8 ? tc0 : tc1) + (e & 7);
+    for (int e = 0; e < NE; ++e) {
+      const int tok = tc[e >> 3] + (e & 7);
       if (tok >= T) {
 #pragma unroll
         for (int h = 0; h < G; ++h) s[e][h] = kNegInf;
@@ -192,19 +198,19 @@ __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* U
     }
 
     // ---- online softmax statistics; e packed to bf16 token pairs
-    uint32_t e2[2][4][G];
+    uint32_t e2[CH][4][G];
     float alpha[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float mx = s[0][h];
 #pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e][h]);
+      for (int e = 1; e < NE; ++e) mx = fmaxf(mx, s[e][h]);
       mx = wave_max(mx);
       const float mn = fmaxf(m_run[h], mx);
       alpha[h] = fast_exp2(m_run[h] - mn);
       float sum = 0.f;
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < CH; ++c)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const float x0 = fast_exp2(s[c * 8 + 2 * w][h] - mn);
@@ -225,25 +231,27 @@ __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* U
     // land in slots that are never read.
     // Masks zero the U' elements of tokens past the block end (padding may
     // hold NaN); a lane with no valid token has e = 0 and a finite chunk.
-    u32x4_t mask0 = {~0u, ~0u, ~0u, ~0u}, mask1 = {~0u, ~0u, ~0u, ~0u};
-    if (RAGGED) {
-      const int n0 = ok0 ? T - tc0 : 0, n1 = ok1 ? T - tc1 : 0;
+    u32x4_t mask[CH];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        mask0[w] = (2 * w < n0 ? 0xffffu : 0u) | (2 * w + 1 < n0 ? 0xffff0000u : 0u);
-        mask1[w] = (2 * w < n1 ? 0xffffu : 0u) | (2 * w + 1 < n1 ? 0xffff0000u : 0u);
+    for (int c = 0; c < CH; ++c) {
+      mask[c] = u32x4_t{~0u, ~0u, ~0u, ~0u};
+      if (RAGGED) {
+        const int n = ok[c] ? T - tc[c] : 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          mask[c][w] = (2 * w < n ? 0xffffu : 0u) | (2 * w + 1 < n ? 0xffff0000u : 0u);
       }
     }
 #pragma unroll 1
     for (int gi = 0; gi * R < rv; ++gi) {
-      u32x4_t U0[R], U1[R];
+      u32x4_t U[CH][R];
       uint32_t wr[R];   // the lane's JPL columns of the group's W' rows
 #pragma unroll
       for (int rho = 0; rho < R; ++rho) {
         const int k = min(gi * R + rho, rv - 1);
         const uint16_t* row = Upt + (size_t)k * ld;
-        U0[rho] = ld16_stream(row + tq0);
-        U1[rho] = ld16_stream(row + tq1);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) U[c][rho] = ld16_stream(row + tq[c]);
       }
 #pragma unroll
       for (int rho = 0; rho < R; ++rho) {
@@ -256,15 +264,18 @@ __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* U
       for (int x = 0; x < 64; ++x) acc[x] = 0.f;
 #pragma unroll
       for (int rho = 0; rho < R; ++rho) {
-        u32x4_t u0 = U0[rho], u1 = U1[rho];
-        if (RAGGED) { u0 &= mask0; u1 &= mask1; }
+        u32x4_t u[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          u[c] = U[c][rho];
+          if (RAGGED) u[c] &= mask[c];
+        }
 #pragma unroll
         for (int w = 0; w < 4; ++w)
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            acc[rho * G + h] = dot2bf(u0[w], e2[0][w][h], acc[rho * G + h]);
-            acc[rho * G + h] = dot2bf(u1[w], e2[1][w][h], acc[rho * G + h]);
-          }
+          for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int c = 0; c < CH; ++c) acc[rho * G + h] = dot2bf(u[c][w], e2[c][w][h], acc[rho * G + h]);
       }
       // lane l ends with z of slot l = (row rho, head h); staged in LDS as
       // zs[rho*8 + h] and read back as broadcasts
@@ -320,10 +331,17 @@ __device__ __forceinline__ void block_unit_bf16(const DecodeParams& p, int i, in
   }
   wave_lds_fence();
 
-  if (T & 7)
-    bf16_tiles<D, G, true>(Ut, Upt, Wp, ld, T, r, rv, pf, m_run, l_run, o, zs, lane);
-  else
-    bf16_tiles<D, G, false>(Ut, Upt, Wp, ld, T, r, rv, pf, m_run, l_run, o, zs, lane);
+  if (T <= 512) {
+    if (T & 7)
+      bf16_tiles<D, G, true, 1>(Ut, Upt, Wp, ld, T, r, rv, pf, m_run, l_run, o, zs, lane);
+    else
+      bf16_tiles<D, G, false, 1>(Ut, Upt, Wp, ld, T, r, rv, pf, m_run, l_run, o, zs, lane);
+  } else {
+    if (T & 7)
+      bf16_tiles<D, G, true, 2>(Ut, Upt, Wp, ld, T, r, rv, pf, m_run, l_run, o, zs, lane);
+    else
+      bf16_tiles<D, G, false, 2>(Ut, Upt, Wp, ld, T, r, rv, pf, m_run, l_run, o, zs, lane);
+  }
 
   float* po = p.part.o + (size_t)unit * G * D;
 #pragma unroll
