@@ -239,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
   // (k / n_qtiles) * 8 + x.  A shared-context launch then has tail_units
   // more, each the dense tail of one (sequence i, KV head g) for its one
   // query token; placed last, they take the CUs that finish first.
-  const int S = p.n_ranges + 1;
+  const int S = p.n_ranges + p.tail_pieces;
   const int n_groups = p.batch * p.n_kv_heads * S;
   const int n_block_wgs = (n_groups + 7) / 8 * 8 * p.n_qtiles;
   const bool extra = (int)blockIdx.x >= n_block_wgs;
@@ -247,9 +247,9 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
   if (extra) {
     const int u = (int)blockIdx.x - n_block_wgs;
     if (u >= p.tail_units) return;
-    i = u / p.n_kv_heads;
-    g = u % p.n_kv_heads;
-    slot = p.n_ranges;
+    i = u / (p.n_kv_heads * p.tail_pieces);
+    g = (u / p.tail_pieces) % p.n_kv_heads;
+    slot = p.n_ranges + u % p.tail_pieces;
     qt = 0;
     qlen = 1;
   } else {
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
   const bool wave_live = qt * kRowsPerTile + wave * kRowsPerWave < MQ;
   const int j_l = m_l / G, hl = m_l - j_l * G;
 
-  const bool tail = slot == p.n_ranges;
+  const bool tail = slot >= p.n_ranges;
   if (tail && p.no_tail && !extra) return;
   int b0 = 0, blk_lo = 0, blk_hi = 0;
   if (!tail) {
@@ -577,7 +577,10 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
     const u32x4_t rk = rsrc_words(kt, (uint32_t)(cap * kD) * 2);
     const u32x4_t rvv = rsrc_words(vtp, (uint32_t)(cap * kD) * 2);
     const int vis = L - qlen + j_l;   // last visible tail token of this row
-    const int nt = (L + kTT - 1) / kTT;
+    // this unit's piece of the tail: tiles toff .. toff + nt - 1
+    const int tpp = ((cap + kTT - 1) / kTT + p.tail_pieces - 1) / p.tail_pieces;
+    const int toff = (slot - p.n_ranges) * tpp;
+    const int nt = max(0, min((L + kTT - 1) / kTT, toff + tpp) - toff);
     auto stage = [&](int t) { return lds + (t % kTailStages) * kTailStageBytes; };
     auto issue_tail = [&](int t) {
       const int ln = opaque(lane);
@@ -586,10 +589,10 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
       for (int k = 0; k < 2; ++k) {
         const int rb = 8 * k + wave;
         const int row = rb * 4 + (ln >> 4);
-        const bool ok = t * kTT + row < L;
-        dma16(rk, sk + rb * 1024, (uint32_t)((t * kTT + row) * kD + ((ln & 15) ^ swz_w(row)) * 8) * 2, ok);
-        dma16(rvv, sk + kTailHalf + rb * 1024,
-              (uint32_t)((t * kTT + row) * kD + ((ln & 15) ^ swz_wp(row)) * 8) * 2, ok);
+        const int tok = (toff + t) * kTT + row;
+        const bool ok = tok < L;
+        dma16(rk, sk + rb * 1024, (uint32_t)(tok * kD + ((ln & 15) ^ swz_w(row)) * 8) * 2, ok);
+        dma16(rvv, sk + kTailHalf + rb * 1024, (uint32_t)(tok * kD + ((ln & 15) ^ swz_wp(row)) * 8) * 2, ok);
       }
     };
     for (int t = 0; t < min(nt, kTailStages - 1); ++t) issue_tail(t);
@@ -616,7 +619,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
         for (int kk = 0; kk < kD / 32; ++kk) acc = mfma32(w_operand(sk, 16 * tt, kk, ln), qv[kk], acc);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int tok = t * kTT + 16 * tt + 4 * q4 + v;
+          const int tok = (toff + t) * kTT + 16 * tt + 4 * q4 + v;
           acc[v] = (tok < L && tok <= vis) ? acc[v] * p.scale_log2 - mref : kNegInf;
         }
         s[tt] = acc;
@@ -657,7 +660,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
 }  // namespace
 
 hipError_t launch_chunk(const ChunkParams& p, int group, hipStream_t s) {
-  const int64_t groups = (int64_t)p.batch * p.n_kv_heads * (p.n_ranges + 1);
+  const int64_t groups = (int64_t)p.batch * p.n_kv_heads * (p.n_ranges + p.tail_pieces);
   if (groups == 0) return hipSuccess;
   if (group < 1 || group > 16) return hipErrorInvalidValue;
   const int64_t wgs = (p.tail_units + 7) / 8 * 8 + (groups + 7) / 8 * 8 * p.n_qtiles;

@@ -62,6 +62,11 @@ struct ChunkParams {
   // batch * n_kv_heads of them, each the dense tail of that sequence's own
   // G query rows (q_len 1); 0 otherwise.
   int32_t tail_units;
+  // Slots n_ranges .. n_ranges + tail_pieces - 1 hold the dense tail: piece
+  // k covers its tiles [k * tpp, (k + 1) * tpp) of 64 tokens, tpp =
+  // ceil(ceil(tail_cap / 64) / tail_pieces).  1 unless a shared context
+  // spreads each tail over several trailing workgroups.
+  int32_t tail_pieces;
   float scale_log2;
 };
 
@@ -73,7 +78,7 @@ struct MergeParams {
   int32_t batch, q_len, n_q_heads, n_kv_heads, max_blocks;
   int32_t slots;            // work-unit slots per (sequence, KV head)
   int32_t rows_per_unit;    // query rows stored per unit slot (q_len * group)
-  int32_t tail_slot;        // slot of the dense-tail unit
+  int32_t tail_slot;        // first slot of the dense tail (every slot from it on is a tail piece)
   int32_t blocks_per_slot;  // slot s < tail_slot holds blocks [s*bps, (s+1)*bps)
   int32_t seq_stride;       // sequence i's block count is read at seq_blocks[i * seq_stride]
 };

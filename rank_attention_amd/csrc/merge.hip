@@ -50,7 +50,7 @@ __global__ __launch_bounds__(64 * W) void milo_merge_kernel(MergeParams p) {
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
       const int s = s0 + u * kMergeWaves;
-      const bool valid = s < p.slots && ((s == p.tail_slot) || (s < p.tail_slot && s * p.blocks_per_slot < nb));
+      const bool valid = s < p.slots && ((s >= p.tail_slot) || s * p.blocks_per_slot < nb);
       const size_t rec = rec0 + (size_t)(valid ? s : 0) * rstride;
       mu[u] = valid ? p.part.ml[rec * 2 + 0] : kNegInf;
       lu[u] = valid ? p.part.ml[rec * 2 + 1] : 0.f;

@@ -43,8 +43,8 @@ milo_status check_shape(const milo_attn_args* a, int32_t path) {
   // group sizes above 8 run on the MFMA kernel (bf16 storage, head_dim 128)
   if (group > 16) return MILO_ERR_UNSUPPORTED;
   if (group > 8 && (a->dtype != MILO_BF16 || a->head_dim != 128)) return MILO_ERR_UNSUPPORTED;
-  // partial records (query rows x unit slots) are indexed in 32 bits on the device
-  if ((int64_t)a->batch * a->q_len * a->n_q_heads * ((int64_t)a->max_blocks_per_seq + 1) > INT32_MAX)
+  // partial records (query rows x unit slots, up to 8 tail slots) are indexed in 32 bits on the device
+  if ((int64_t)a->batch * a->q_len * a->n_q_heads * ((int64_t)a->max_blocks_per_seq + 8) > INT32_MAX)
     return MILO_ERR_UNSUPPORTED;
   // the MFMA chunk kernel (chunk and shared paths) is built for bf16 storage and head_dim 128
   if (path != MILO_PATH_DECODE && (a->dtype != MILO_BF16 || a->head_dim != 128)) return MILO_ERR_UNSUPPORTED;
@@ -73,6 +73,14 @@ ChunkSplit chunk_split(const milo_attn_args* a, bool shared = false) {
   return c;
 }
 
+// A shared context spreads each sequence's dense tail over pieces of one
+// 64-token tile (at most 8), each its own trailing workgroup and unit slot:
+// the tails run after the block workgroups, and short pieces finish
+// together instead of one tail's whole length after the blocks.
+int32_t shared_tail_pieces(const milo_attn_args* a) {
+  return a->tail_cap > 0 ? std::min<int32_t>(8, (a->tail_cap + 63) / 64) : 1;
+}
+
 struct Layout {
   size_t o_bytes, ml_bytes, total;
   int64_t units;
@@ -90,7 +98,7 @@ Layout layout_of(const milo_attn_args* a, int32_t path) {
   const int group = a->n_q_heads / a->n_kv_heads;
   const bool ranges = path == MILO_PATH_CHUNK || (path == MILO_PATH_DECODE && decode_on_mfma(a));
   L.slots = ranges                     ? chunk_split(a).n_ranges + 1
-            : path == MILO_PATH_SHARED ? chunk_split(a, true).n_ranges + 1
+            : path == MILO_PATH_SHARED ? chunk_split(a, true).n_ranges + shared_tail_pieces(a)
                                        : a->max_blocks_per_seq + 1;
   L.rows_per_unit = a->q_len * group;
   L.units = (int64_t)a->batch * a->n_kv_heads * L.slots;
@@ -146,6 +154,7 @@ milo_status chunk_launch(const milo_attn_args* a, char* ws, hipStream_t stream) 
   p.blocks_per_range = cs.blocks_per_range;
   p.part_rows = a->q_len * group;
   p.no_tail = 0;
+  p.tail_pieces = 1;
   p.scale_log2 = a->scale * milo::kLog2eHost;
 
   milo::clear_stale_error();
@@ -315,7 +324,8 @@ milo_status milo_attn_decode_shared(const milo_attn_args* a, void* hip_stream) {
   p.blocks_per_range = cs.blocks_per_range;
   p.part_rows = group;
   p.no_tail = 1;
-  p.tail_units = a->batch * a->n_kv_heads;
+  p.tail_pieces = shared_tail_pieces(a);
+  p.tail_units = a->batch * a->n_kv_heads * p.tail_pieces;
   p.scale_log2 = a->scale * milo::kLog2eHost;
 
   milo::clear_stale_error();

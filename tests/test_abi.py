@@ -136,16 +136,19 @@ def test_shared_rejects_before_any_hip_call(over, code):
 
 def test_shared_workspace_query():
     """Shared path: the batch's B * G query rows form one tile set per KV head;
-    slots = block ranges + 1 tail slot per (sequence, KV head), G rows each."""
+    slots = block ranges + the tail's pieces (one per 64-token tile of the
+    tail capacity, at most 8; 1 without tails) per (sequence, KV head), G
+    rows each."""
     lib = _lib.load()
-    a = good_args(head_dim=128, batch=16, n_q_heads=28, n_kv_heads=4, max_blocks_per_seq=64)
-    need = lib.milo_attn_workspace_bytes(ctypes.byref(a), _lib.MILO_PATH_SHARED)
-    # 16 * 7 = 112 rows -> one 128-row tile; 4 KV heads -> base 4 workgroups;
-    # ranges = min(64, ceil(1024 / 4)) = 64 of one block each
-    units, rows = 16 * 4 * (64 + 1), 7
-    exp_o = -(-units * rows * 128 * 4 // 256) * 256
-    exp_ml = -(-units * rows * 2 * 4 // 256) * 256
-    assert need == exp_o + exp_ml
+    for cap, pieces in ((0, 1), (256, 4), (100, 2), (4096, 8)):
+        a = good_args(head_dim=128, batch=16, n_q_heads=28, n_kv_heads=4, max_blocks_per_seq=64, tail_cap=cap)
+        need = lib.milo_attn_workspace_bytes(ctypes.byref(a), _lib.MILO_PATH_SHARED)
+        # 16 * 7 = 112 rows -> one 128-row tile; 4 KV heads -> base 4 workgroups;
+        # ranges = min(64, ceil(1024 / 4)) = 64 of one block each
+        units, rows = 16 * 4 * (64 + pieces), 7
+        exp_o = -(-units * rows * 128 * 4 // 256) * 256
+        exp_ml = -(-units * rows * 2 * 4 // 256) * 256
+        assert need == exp_o + exp_ml, (cap, need, exp_o + exp_ml)
     assert lib.milo_attn_workspace_bytes(ctypes.byref(good_args(head_dim=64)), _lib.MILO_PATH_SHARED) == 0
 
 
