@@ -553,7 +553,8 @@ def main(argv=None):
     def pct(q):
         return kern_sorted[min(len(kern_sorted) - 1, int(q * (len(kern_sorted) - 1) + 0.5))] * 1e3
 
-    factor_bytes = wl.factor_bytes()
+    # the shared path reads sequence 0's factors once for the whole batch
+    factor_bytes = shared_factor_bytes if shared else wl.factor_bytes()
     if q8:
         # per KV head and row: n_tok codes, d bf16 of W or W', one fp32 (scale, bias) pair
         factor_bytes = sum(cfg.n_kv_heads * (b.rank_k + b.rank_v) * (b.n_tok + 2 * d + 8)

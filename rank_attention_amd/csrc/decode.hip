@@ -206,8 +206,9 @@ __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* U
 #pragma unroll
       for (int e = 1; e < NE; ++e) mx = fmaxf(mx, s[e][h]);
       mx = wave_max(mx);
-      const float mn = fmaxf(m_run[h], mx);
-      alpha[h] = fast_exp2(m_run[h] - mn);
+      // m, l and alpha are the same in every lane: kept in scalar registers
+      const float mn = uniform_f32(fmaxf(m_run[h], mx));
+      alpha[h] = uniform_f32(fast_exp2(m_run[h] - mn));
       float sum = 0.f;
 #pragma unroll
       for (int c = 0; c < CH; ++c)
@@ -218,7 +219,7 @@ __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* U
           sum += x0 + x1;
           e2[c][w][h] = pack_bf16(x0, x1);
         }
-      l_run[h] = l_run[h] * alpha[h] + wave_sum(sum);
+      l_run[h] = uniform_f32(l_run[h] * alpha[h] + wave_sum(sum));
       m_run[h] = mn;
     }
 #pragma unroll
@@ -1185,10 +1186,19 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, uint32_t* lds
     block_unit_f32<D, G>(p, i, g, unit, blk, lds);
 }
 
+// bf16 storage: the register budget is set to two waves per SIMD (the
+// allocator fits every group size without spills).
 template <int D, int G, int DT>
-__global__ __launch_bounds__(64) void milo_decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void milo_decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
   decode_wave<D, G, DT>(p, lds);
+}
+
+// fp32 storage
+template <int D, int G>
+__global__ __launch_bounds__(64) void milo_decode_f32_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
+  decode_wave<D, G, MILO_F32>(p, lds);
 }
 
 // The 8-bit kernel holds two chunks of code loads in flight; its register
@@ -1213,6 +1223,8 @@ void launch_decode_g(const DecodeParams& p, dim3 grid, hipStream_t s) {
     hipLaunchKernelGGL((milo_decode_q8_kernel<D, G>), grid, dim3(64), 0, s, p);
   else if constexpr (DT == MILO_BF16_KV4 || DT == MILO_BF16_KV2)
     hipLaunchKernelGGL((milo_decode_kv_kernel<D, G, DT>), grid, dim3(64), 0, s, p);
+  else if constexpr (DT == MILO_F32)
+    hipLaunchKernelGGL((milo_decode_f32_kernel<D, G>), grid, dim3(64), 0, s, p);
   else
     hipLaunchKernelGGL((milo_decode_kernel<D, G, DT>), grid, dim3(64), 0, s, p);
 }

@@ -103,6 +103,11 @@ __device__ __forceinline__ void swap32(float& x, float& y) {
   y = __uint_as_float(r[1]);
 }
 
+// Lane 0's value, as a wave-uniform (scalar register) value.
+__device__ __forceinline__ float uniform_f32(float v) {
+  return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v)));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp<kQuadXor1>(v));
   v = fmaxf(v, dpp<kQuadXor2>(v));
