@@ -51,6 +51,18 @@ def test_qwen7b_64k_sampled(variant):
             name=f"qwen7b_64k/{variant}")
 
 
+def test_qwen7b_64k_group8_sampled():
+    """The 64k workload with 32 query heads (group size 8, the largest group
+    the vector-ALU decode unit takes) on the sharp variant; oracle on two
+    whole sequences."""
+    cfg = synth.get_config("qwen7b_64k").with_(name="qwen7b_64k_g8", n_q_heads=32)
+    wl = synth.make_workload(cfg, variant="sharp")
+    out, lse = run_hip(wl)
+    seqs = [0, cfg.batch - 1]
+    ref_o, ref_l = oracle.attend(wl, seq_index=seqs)
+    compare(out[seqs], lse[seqs], ref_o, ref_l, sharp_gates=True, name="qwen7b_64k_g8/sharp")
+
+
 def test_qwen7b_128k_sampled():
     cfg = synth.get_config("qwen7b_128k")
     wl = synth.make_workload(cfg, variant="sharp")
