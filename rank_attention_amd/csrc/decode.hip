@@ -107,14 +107,26 @@ __device__ __forceinline__ void mfma_project_q(const uint16_t* W, const uint16_t
     }
 }
 
-constexpr int kRowsPerStep = 4;   // U^T rows per prefetch step of the score loop
-
-// Loads rows k0 .. k0+3 of U^T (clamped to r-1) at the lane's CH chunks.
+// U^T rows per prefetch step of the score loop (two steps in flight): 4
+// with two 8-token chunks per lane, 16 with one, whose scores take half
+// the registers.  Units of blocks of at most 512 tokens are latency-bound
+// (few units per wave slot), so fewer, larger round trips shorten them.
 template <int CH>
-__device__ __forceinline__ void load_rows4(const uint16_t* Ut, int ld, int k0, int r, const int (&tq)[CH],
-                                           u32x4_t (&A)[CH][kRowsPerStep]) {
+constexpr int rows_per_step() { return CH == 1 ? 16 : 4; }
+
+// U'^T rows of the next value group whose loads are issued during this
+// group's reduction: the whole group with one chunk per lane, else as many
+// as the two-waves-per-SIMD register budget leaves room for.
+template <int G, int CH, int R>
+constexpr int value_ring_rows() { return CH == 1 ? R : G >= 8 ? 0 : 4; }
+
+// Loads rows k0 .. k0 + rows_per_step - 1 of U^T (clamped to r-1) at the
+// lane's CH chunks.
+template <int CH>
+__device__ __forceinline__ void load_rows(const uint16_t* Ut, int ld, int k0, int r, const int (&tq)[CH],
+                                           u32x4_t (&A)[CH][rows_per_step<CH>()]) {
 #pragma unroll
-  for (int j = 0; j < kRowsPerStep; ++j) {
+  for (int j = 0; j < rows_per_step<CH>(); ++j) {
     const uint16_t* row = Ut + (size_t)min(k0 + j, r - 1) * ld;
 #pragma unroll
     for (int c = 0; c < CH; ++c) A[c][j] = ld16_stream(row + tq[c]);
@@ -122,10 +134,10 @@ __device__ __forceinline__ void load_rows4(const uint16_t* Ut, int ld, int k0, i
 }
 
 template <int G, int CH>
-__device__ __forceinline__ void score_rows4(const u32x4_t (&A)[CH][kRowsPerStep], int k0, int r,
+__device__ __forceinline__ void score_rows(const u32x4_t (&A)[CH][rows_per_step<CH>()], int k0, int r,
                                             const float* pf, float (&s)[8 * CH][G]) {
 #pragma unroll
-  for (int j = 0; j < kRowsPerStep; ++j) {
+  for (int j = 0; j < rows_per_step<CH>(); ++j) {
     if (k0 + j < r) {
       const f32x4_t pq0 = *reinterpret_cast<const f32x4_t*>(pf + (k0 + j) * 8);
       const f32x4_t pq1 = *reinterpret_cast<const f32x4_t*>(pf + (k0 + j) * 8 + 4);
@@ -158,7 +170,7 @@ __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* U
                                            const float* pf, float (&m_run)[G], float (&l_run)[G],
                                            float (&o)[G][D / 64], float* zs, int lane) {
   using S = Shape<D, G>;
-  constexpr int R = S::R, JPL = S::JPL, NE = 8 * CH;
+  constexpr int R = S::R, JPL = S::JPL, NE = 8 * CH, RING = value_ring_rows<G, CH, R>();
   for (int t0 = 0; t0 < T; t0 += 512 * CH) {
     int tc[CH], tq[CH];
     bool ok[CH];
@@ -179,13 +191,14 @@ __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* U
 #pragma unroll
       for (int h = 0; h < G; ++h) s[e][h] = 0.f;
     if (r > 0) {
+      constexpr int kRowsPerStep = rows_per_step<CH>();
       u32x4_t A0[CH][kRowsPerStep], A1[CH][kRowsPerStep];
-      load_rows4<CH>(Ut, ld, 0, r, tq, A0);
+      load_rows<CH>(Ut, ld, 0, r, tq, A0);
       for (int k0 = 0; k0 < r; k0 += 2 * kRowsPerStep) {
-        if (k0 + kRowsPerStep < r) load_rows4<CH>(Ut, ld, k0 + kRowsPerStep, r, tq, A1);
-        score_rows4<G, CH>(A0, k0, r, pf, s);
-        if (k0 + 2 * kRowsPerStep < r) load_rows4<CH>(Ut, ld, k0 + 2 * kRowsPerStep, r, tq, A0);
-        if (k0 + kRowsPerStep < r) score_rows4<G, CH>(A1, k0 + kRowsPerStep, r, pf, s);
+        if (k0 + kRowsPerStep < r) load_rows<CH>(Ut, ld, k0 + kRowsPerStep, r, tq, A1);
+        score_rows<G, CH>(A0, k0, r, pf, s);
+        if (k0 + 2 * kRowsPerStep < r) load_rows<CH>(Ut, ld, k0 + 2 * kRowsPerStep, r, tq, A0);
+        if (k0 + kRowsPerStep < r) score_rows<G, CH>(A1, k0 + kRowsPerStep, r, pf, s);
       }
     }
 #pragma unroll
@@ -243,14 +256,26 @@ __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* U
           mask[c][w] = (2 * w < n ? 0xffffu : 0u) | (2 * w + 1 < n ? 0xffff0000u : 0u);
       }
     }
-#pragma unroll 1
-    for (int gi = 0; gi * R < rv; ++gi) {
-      u32x4_t U[CH][R];
-      uint32_t wr[R];   // the lane's JPL columns of the group's W' rows
+    // The first RING rows of a group form a ring: once row rho's products
+    // are taken, its registers receive row rho of the next group, so those
+    // loads are in flight during this group's reduction and W' update; the
+    // group's other rows load at its start.
+    u32x4_t U[CH][R];
+    uint32_t wr[R];   // the lane's JPL columns of the group's W' rows
+    if (rv > 0) {
 #pragma unroll
-      for (int rho = 0; rho < R; ++rho) {
-        const int k = min(gi * R + rho, rv - 1);
-        const uint16_t* row = Upt + (size_t)k * ld;
+      for (int rho = 0; rho < RING; ++rho) {
+        const uint16_t* row = Upt + (size_t)min(rho, rv - 1) * ld;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) U[c][rho] = ld16_stream(row + tq[c]);
+      }
+    }
+    // group gi; when refill is true the ring takes the next group's rows
+    // (every group but the last, so no row is loaded twice)
+    auto group = [&](int gi, auto refill) {
+#pragma unroll
+      for (int rho = RING; rho < R; ++rho) {
+        const uint16_t* row = Upt + (size_t)min(gi * R + rho, rv - 1) * ld;
 #pragma unroll
         for (int c = 0; c < CH; ++c) U[c][rho] = ld16_stream(row + tq[c]);
       }
@@ -277,6 +302,11 @@ __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* U
           for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int c = 0; c < CH; ++c) acc[rho * G + h] = dot2bf(u[c][w], e2[c][w][h], acc[rho * G + h]);
+        if constexpr (decltype(refill)::value) if (rho < RING) {
+          const uint16_t* row = Upt + (size_t)min((gi + 1) * R + rho, rv - 1) * ld;
+#pragma unroll
+          for (int c = 0; c < CH; ++c) U[c][rho] = ld16_stream(row + tq[c]);
+        }
       }
       // lane l ends with z of slot l = (row rho, head h); staged in LDS as
       // zs[rho*8 + h] and read back as broadcasts
@@ -297,7 +327,11 @@ __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* U
         }
       }
       wave_lds_fence();
-    }
+    };
+    int gi = 0;
+#pragma unroll 1
+    for (; (gi + 1) * R < rv; ++gi) group(gi, std::true_type{});
+    if (gi * R < rv) group(gi, std::false_type{});
   }
 }
 
