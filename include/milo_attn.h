@@ -195,9 +195,10 @@ typedef struct milo_attn_args {
   float* lse;                  /* [batch][q_len][n_q_heads] fp32 natural-log; may be NULL   */
   void* workspace;             /* scratch of milo_attn_workspace_bytes(), 256-B aligned     */
   size_t workspace_bytes;
-  void* prof_events[2];        /* optional hipEvent_t pair: when both are set, the call
-                                  records [0] before and [1] after its main attention
-                                  kernel on the same stream (timing hook)                   */
+  void* prof_events[2];        /* optional hipEvent_t pair (created by the caller): when
+                                  both are set, [0] and [1] take the start and end time
+                                  of the call's main attention kernel, stamped by its
+                                  dispatch (timing hook)                                    */
   const int32_t* unit_order;   /* optional device array: the order in which the decode
                                   kernel takes its work units (see milo_attn_plan_decode);
                                   NULL = natural order.  Must be a permutation of

@@ -50,6 +50,8 @@
 // Precision: P and Z are split into bf16 hi + lo parts (two MFMAs each), so
 // scores and the value projection keep ~16 mantissa bits; e = exp2(s - m) is
 // rounded to bf16 once (relative 2^-9 per weight, averaging out over tokens).
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "mfma_common.h"
@@ -659,14 +661,17 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
 
 }  // namespace
 
-hipError_t launch_chunk(const ChunkParams& p, int group, hipStream_t s) {
+hipError_t launch_chunk(const ChunkParams& p, int group, hipStream_t s, LaunchEvents ev) {
   const int64_t groups = (int64_t)p.batch * p.n_kv_heads * (p.n_ranges + p.tail_pieces);
   if (groups == 0) return hipSuccess;
   if (group < 1 || group > 16) return hipErrorInvalidValue;
   const int64_t wgs = (p.tail_units + 7) / 8 * 8 + (groups + 7) / 8 * 8 * p.n_qtiles;
   ChunkParams q = p;
   q.group = group;
-  hipLaunchKernelGGL(milo_chunk_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, s, q);
+  if (ev.start && ev.stop)   // timing events stamped by the dispatch itself
+    hipExtLaunchKernelGGL(milo_chunk_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, s, ev.start, ev.stop, 0, q);
+  else
+    hipLaunchKernelGGL(milo_chunk_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, s, q);
   return hipGetLastError();
 }
 

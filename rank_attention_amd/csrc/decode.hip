@@ -34,6 +34,8 @@
 // the matrix cores instead (block_unit_q8 and milo_decode_q8_kernel below):
 // the codes are exact fp16 operands, so the vector ALUs are left with the
 // softmax and o~ += z W'.
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -1251,26 +1253,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void mi
   decode_wave<D, G, DT>(p, lds);
 }
 
-template <int D, int G, int DT>
-void launch_decode_g(const DecodeParams& p, dim3 grid, hipStream_t s) {
-  if constexpr (DT == MILO_BF16_Q8)
-    hipLaunchKernelGGL((milo_decode_q8_kernel<D, G>), grid, dim3(64), 0, s, p);
-  else if constexpr (DT == MILO_BF16_KV4 || DT == MILO_BF16_KV2)
-    hipLaunchKernelGGL((milo_decode_kv_kernel<D, G, DT>), grid, dim3(64), 0, s, p);
-  else if constexpr (DT == MILO_F32)
-    hipLaunchKernelGGL((milo_decode_f32_kernel<D, G>), grid, dim3(64), 0, s, p);
+// Plain launch, or with the caller's timing events attached to the dispatch.
+template <typename K>
+void launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t s, LaunchEvents ev, const DecodeParams& p) {
+  if (ev.start && ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, p);
   else
-    hipLaunchKernelGGL((milo_decode_kernel<D, G, DT>), grid, dim3(64), 0, s, p);
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, p);
+}
+
+template <int D, int G, int DT>
+void launch_decode_g(const DecodeParams& p, dim3 grid, hipStream_t s, LaunchEvents ev) {
+  if constexpr (DT == MILO_BF16_Q8)
+    launch_timed(milo_decode_q8_kernel<D, G>, grid, dim3(64), s, ev, p);
+  else if constexpr (DT == MILO_BF16_KV4 || DT == MILO_BF16_KV2)
+    launch_timed(milo_decode_kv_kernel<D, G, DT>, grid, dim3(64), s, ev, p);
+  else if constexpr (DT == MILO_F32)
+    launch_timed(milo_decode_f32_kernel<D, G>, grid, dim3(64), s, ev, p);
+  else
+    launch_timed(milo_decode_kernel<D, G, DT>, grid, dim3(64), s, ev, p);
 }
 
 template <int D, int DT>
-hipError_t launch_decode_dg(const DecodeParams& p, int group, hipStream_t s) {
+hipError_t launch_decode_dg(const DecodeParams& p, int group, hipStream_t s, LaunchEvents ev) {
   const int64_t units = decode_units(p.batch, p.n_kv_heads, p.max_blocks);
   if (units == 0) return hipSuccess;
   const dim3 grid((unsigned)units);
   switch (group) {
 #define MILO_G(GG) \
-  case GG: launch_decode_g<D, GG, DT>(p, grid, s); break;
+  case GG: launch_decode_g<D, GG, DT>(p, grid, s, ev); break;
     MILO_G(1) MILO_G(2) MILO_G(3) MILO_G(4) MILO_G(5) MILO_G(6) MILO_G(7) MILO_G(8)
 #undef MILO_G
     default: return hipErrorInvalidValue;
@@ -1284,8 +1295,8 @@ hipError_t launch_decode_dg(const DecodeParams& p, int group, hipStream_t s) {
 // -DMILO_INST_DT=<0|1|2> -DMILO_INST_D=<64|128>.
 #define MILO_CAT2(a, b, c) launch_decode_##a##_##b##_##c
 #define MILO_CAT(a, b, c) MILO_CAT2(a, b, c)
-hipError_t MILO_CAT(dt, MILO_INST_DT, MILO_INST_D)(const DecodeParams& p, int group, hipStream_t s) {
-  return launch_decode_dg<MILO_INST_D, MILO_INST_DT>(p, group, s);
+hipError_t MILO_CAT(dt, MILO_INST_DT, MILO_INST_D)(const DecodeParams& p, int group, hipStream_t s, LaunchEvents ev) {
+  return launch_decode_dg<MILO_INST_D, MILO_INST_DT>(p, group, s, ev);
 }
 
 }  // namespace milo

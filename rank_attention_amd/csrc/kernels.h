@@ -159,34 +159,40 @@ inline int64_t decode_units(int batch, int n_kv_heads, int max_blocks) {
   return (int64_t)batch * n_kv_heads * (max_blocks + 1);
 }
 
+// Optional timing events of a launch: when set, the runtime stamps them with
+// the kernel dispatch's own start and end (no separate stream commands).
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
 // One instantiation per (dtype, head_dim), each in its own translation unit.
-hipError_t launch_decode_dt_0_64(const DecodeParams& p, int group, hipStream_t s);
-hipError_t launch_decode_dt_0_128(const DecodeParams& p, int group, hipStream_t s);
-hipError_t launch_decode_dt_1_64(const DecodeParams& p, int group, hipStream_t s);
-hipError_t launch_decode_dt_1_128(const DecodeParams& p, int group, hipStream_t s);
-hipError_t launch_decode_dt_2_64(const DecodeParams& p, int group, hipStream_t s);
-hipError_t launch_decode_dt_2_128(const DecodeParams& p, int group, hipStream_t s);
-hipError_t launch_decode_dt_3_64(const DecodeParams& p, int group, hipStream_t s);
-hipError_t launch_decode_dt_3_128(const DecodeParams& p, int group, hipStream_t s);
-hipError_t launch_decode_dt_4_64(const DecodeParams& p, int group, hipStream_t s);
-hipError_t launch_decode_dt_4_128(const DecodeParams& p, int group, hipStream_t s);
+hipError_t launch_decode_dt_0_64(const DecodeParams& p, int group, hipStream_t s, LaunchEvents ev = {});
+hipError_t launch_decode_dt_0_128(const DecodeParams& p, int group, hipStream_t s, LaunchEvents ev = {});
+hipError_t launch_decode_dt_1_64(const DecodeParams& p, int group, hipStream_t s, LaunchEvents ev = {});
+hipError_t launch_decode_dt_1_128(const DecodeParams& p, int group, hipStream_t s, LaunchEvents ev = {});
+hipError_t launch_decode_dt_2_64(const DecodeParams& p, int group, hipStream_t s, LaunchEvents ev = {});
+hipError_t launch_decode_dt_2_128(const DecodeParams& p, int group, hipStream_t s, LaunchEvents ev = {});
+hipError_t launch_decode_dt_3_64(const DecodeParams& p, int group, hipStream_t s, LaunchEvents ev = {});
+hipError_t launch_decode_dt_3_128(const DecodeParams& p, int group, hipStream_t s, LaunchEvents ev = {});
+hipError_t launch_decode_dt_4_64(const DecodeParams& p, int group, hipStream_t s, LaunchEvents ev = {});
+hipError_t launch_decode_dt_4_128(const DecodeParams& p, int group, hipStream_t s, LaunchEvents ev = {});
 
 inline hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int group,
-                                hipStream_t s) {
-  if (dtype == MILO_F32 && head_dim == 64) return launch_decode_dt_0_64(p, group, s);
-  if (dtype == MILO_F32 && head_dim == 128) return launch_decode_dt_0_128(p, group, s);
-  if (dtype == MILO_BF16 && head_dim == 64) return launch_decode_dt_1_64(p, group, s);
-  if (dtype == MILO_BF16 && head_dim == 128) return launch_decode_dt_1_128(p, group, s);
-  if (dtype == MILO_BF16_Q8 && head_dim == 64) return launch_decode_dt_2_64(p, group, s);
-  if (dtype == MILO_BF16_Q8 && head_dim == 128) return launch_decode_dt_2_128(p, group, s);
-  if (dtype == MILO_BF16_KV4 && head_dim == 64) return launch_decode_dt_3_64(p, group, s);
-  if (dtype == MILO_BF16_KV4 && head_dim == 128) return launch_decode_dt_3_128(p, group, s);
-  if (dtype == MILO_BF16_KV2 && head_dim == 64) return launch_decode_dt_4_64(p, group, s);
-  if (dtype == MILO_BF16_KV2 && head_dim == 128) return launch_decode_dt_4_128(p, group, s);
+                                hipStream_t s, LaunchEvents ev = {}) {
+  if (dtype == MILO_F32 && head_dim == 64) return launch_decode_dt_0_64(p, group, s, ev);
+  if (dtype == MILO_F32 && head_dim == 128) return launch_decode_dt_0_128(p, group, s, ev);
+  if (dtype == MILO_BF16 && head_dim == 64) return launch_decode_dt_1_64(p, group, s, ev);
+  if (dtype == MILO_BF16 && head_dim == 128) return launch_decode_dt_1_128(p, group, s, ev);
+  if (dtype == MILO_BF16_Q8 && head_dim == 64) return launch_decode_dt_2_64(p, group, s, ev);
+  if (dtype == MILO_BF16_Q8 && head_dim == 128) return launch_decode_dt_2_128(p, group, s, ev);
+  if (dtype == MILO_BF16_KV4 && head_dim == 64) return launch_decode_dt_3_64(p, group, s, ev);
+  if (dtype == MILO_BF16_KV4 && head_dim == 128) return launch_decode_dt_3_128(p, group, s, ev);
+  if (dtype == MILO_BF16_KV2 && head_dim == 64) return launch_decode_dt_4_64(p, group, s, ev);
+  if (dtype == MILO_BF16_KV2 && head_dim == 128) return launch_decode_dt_4_128(p, group, s, ev);
   return hipErrorInvalidValue;
 }
 hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t s);
-hipError_t launch_chunk(const ChunkParams& p, int group, hipStream_t s);
+hipError_t launch_chunk(const ChunkParams& p, int group, hipStream_t s, LaunchEvents ev = {});
 
 // The decode entry point in two halves (milo_attn.cpp), shared by
 // milo_attn_decode and its variant with library-owned scratch: every

@@ -24,6 +24,17 @@ constexpr size_t kWsAlign = 256;
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// The caller's timing events (both or neither), stamped by the attention
+// kernel's dispatch.
+milo::LaunchEvents timing_events(const milo_attn_args* a) {
+  milo::LaunchEvents ev;
+  if (a->prof_events[0] && a->prof_events[1]) {
+    ev.start = reinterpret_cast<hipEvent_t>(a->prof_events[0]);
+    ev.stop = reinterpret_cast<hipEvent_t>(a->prof_events[1]);
+  }
+  return ev;
+}
+
 // Shape-only checks shared by the workspace query and the entry points.
 milo_status check_shape(const milo_attn_args* a, int32_t path) {
   if (!a) return MILO_ERR_INVALID;
@@ -158,12 +169,7 @@ milo_status chunk_launch(const milo_attn_args* a, char* ws, hipStream_t stream) 
   p.scale_log2 = a->scale * milo::kLog2eHost;
 
   milo::clear_stale_error();
-  const bool timing = a->prof_events[0] && a->prof_events[1];
-  if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[0]), stream) != hipSuccess)
-    return MILO_ERR_DEVICE;
-  if (milo::launch_chunk(p, group, stream) != hipSuccess) return MILO_ERR_DEVICE;
-  if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[1]), stream) != hipSuccess)
-    return MILO_ERR_DEVICE;
+  if (milo::launch_chunk(p, group, stream, timing_events(a)) != hipSuccess) return MILO_ERR_DEVICE;
 
   MergeParams m{};
   m.part = part;
@@ -228,12 +234,7 @@ milo_status decode_launch(const milo_attn_args* a, void* workspace, void* hip_st
   p.unit_order = a->unit_order;
 
   milo::clear_stale_error();
-  const bool timing = a->prof_events[0] && a->prof_events[1];
-  if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[0]), stream) != hipSuccess)
-    return MILO_ERR_DEVICE;
-  if (milo::launch_decode(p, a->dtype, a->head_dim, group, stream) != hipSuccess) return MILO_ERR_DEVICE;
-  if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[1]), stream) != hipSuccess)
-    return MILO_ERR_DEVICE;
+  if (milo::launch_decode(p, a->dtype, a->head_dim, group, stream, timing_events(a)) != hipSuccess) return MILO_ERR_DEVICE;
 
   MergeParams m{};
   m.part = part;
@@ -329,12 +330,7 @@ milo_status milo_attn_decode_shared(const milo_attn_args* a, void* hip_stream) {
   p.scale_log2 = a->scale * milo::kLog2eHost;
 
   milo::clear_stale_error();
-  const bool timing = a->prof_events[0] && a->prof_events[1];
-  if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[0]), stream) != hipSuccess)
-    return MILO_ERR_DEVICE;
-  if (milo::launch_chunk(p, group, stream) != hipSuccess) return MILO_ERR_DEVICE;
-  if (timing && hipEventRecord(reinterpret_cast<hipEvent_t>(a->prof_events[1]), stream) != hipSuccess)
-    return MILO_ERR_DEVICE;
+  if (milo::launch_chunk(p, group, stream, timing_events(a)) != hipSuccess) return MILO_ERR_DEVICE;
 
   MergeParams m{};
   m.part = part;
