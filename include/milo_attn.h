@@ -176,9 +176,9 @@ typedef struct milo_attn_args {
   int32_t q_len;               /* query tokens per sequence: 1 (decode) or Q >= 1 (chunk)   */
   int32_t n_q_heads;           /* >= 1, multiple of n_kv_heads                              */
   int32_t n_kv_heads;          /* >= 1; group size n_q_heads / n_kv_heads in [1, 16]; above
-                                  8 only with MILO_BF16 storage and head_dim 128 (decode
-                                  then runs on the matrix-core kernel of the chunked path,
-                                  and its workspace follows that path's layout)              */
+                                  8 only with MILO_BF16 storage (decode then runs on the
+                                  matrix-core kernel of the chunked path, and its
+                                  workspace follows that path's layout)                     */
   int32_t head_dim;            /* 64 or 128                                                 */
   float scale;                 /* softmax scale (e.g. 1/sqrt(head_dim)); finite             */
   const void* q;               /* [batch][q_len][n_q_heads][head_dim], 16-B aligned         */
@@ -216,7 +216,9 @@ milo_status milo_attn_decode(const milo_attn_args* args, void* hip_stream);
 
 /* Chunked query: q_len = Q >= 1 new tokens per sequence, whose own keys and
  * values are the last Q entries of the tail; query j sees every block token
- * and tail tokens l <= tail_len[i] - Q + j.  Writes out and lse. */
+ * and tail tokens l <= tail_len[i] - Q + j.  Writes out and lse.  Runs on
+ * the matrix cores: bf16 storage only (MILO_ERR_UNSUPPORTED otherwise),
+ * head_dim 64 or 128. */
 milo_status milo_attn_chunk(const milo_attn_args* args, void* hip_stream);
 
 /* Decode over one compressed context shared by the whole batch: the
@@ -227,7 +229,7 @@ milo_status milo_attn_chunk(const milo_attn_args* args, void* hip_stream);
  * sequences' lists are not read) plus its own tail.  The shared factors are
  * read once for all batch * group query rows of a KV head: the blocks are
  * evaluated as dense contractions on the MFMA path, so this entry point
- * needs bf16 storage and head_dim 128 (MILO_ERR_UNSUPPORTED otherwise).
+ * needs bf16 storage (MILO_ERR_UNSUPPORTED otherwise); head_dim 64 or 128.
  * The sequences' own tails are evaluated in the same kernel launch.
  * Workspace: milo_attn_workspace_bytes(args, MILO_PATH_SHARED). */
 milo_status milo_attn_decode_shared(const milo_attn_args* args, void* hip_stream);

@@ -155,7 +155,7 @@ __device__ __forceinline__ void wait_barrier() {
 struct BlockInfo {
   const uint16_t* head;   // this KV head's factors
   uint32_t bytes;         // their size
-  int T, ld, r, rv, nk, nv, ntiles;
+  int T, ld, r, rv, nk, nv, ntiles, hd;
   uint32_t w_off, v_off, wp_off;
 };
 
@@ -169,20 +169,22 @@ typedef __attribute__((address_space(4))) const milo_block const_milo_block;
 
 __device__ __forceinline__ void block_info(BlockInfo& io, const ChunkParams& p, int gblk, int g) {
   const_milo_block* blk = (const_milo_block*)p.blocks + gblk;
+  const int hd = p.head_dim;
   io.T = max(blk->n_tok, 0);
   io.ld = blk->ld_tok;
-  io.r = min(max(blk->rank_k, 0), kD);
-  io.rv = min(max(blk->rank_v, 0), kD);
+  io.r = min(max(blk->rank_k, 0), hd);
+  io.rv = min(max(blk->rank_v, 0), hd);
+  io.hd = hd;
   // 16-rank chunks: scores use at least one (a rank-0 block scores 0
   // against zero-padded factors); values use none for rank' 0
   io.nk = max(1, (io.r + 15) / 16);
   io.nv = (io.rv + 15) / 16;
   io.ntiles = max(1, (io.T + kTT - 1) / kTT);
   io.head = reinterpret_cast<const uint16_t*>(p.pool) + blk->off +
-            (int64_t)g * (io.r + io.rv) * (io.ld + kD);
-  io.bytes = (uint32_t)((io.r + io.rv) * (io.ld + kD)) * 2;
+            (int64_t)g * (io.r + io.rv) * (io.ld + hd);
+  io.bytes = (uint32_t)((io.r + io.rv) * (io.ld + hd)) * 2;
   io.w_off = (uint32_t)(io.r * io.ld) * 2;
-  io.v_off = io.w_off + (uint32_t)(io.r * kD) * 2;
+  io.v_off = io.w_off + (uint32_t)(io.r * hd) * 2;
   io.wp_off = io.v_off + (uint32_t)(io.rv * io.ld) * 2;
 }
 
@@ -216,8 +218,9 @@ __device__ __forceinline__ void issue_w(const BlockInfo& io, char* region, bool 
     const int rb = 8 * k + wave;
     const int row = rb * 4 + (lane >> 4);
     const int chunk = (lane & 15) ^ (wp ? swz_wp(row) : swz_w(row));
-    const uint32_t off = (wp ? io.wp_off : io.w_off) + (uint32_t)(row * kD + chunk * 8) * 2;
-    dma16(rs, region + rb * 1024, off, row < (wp ? io.rv : io.r));
+    // head_dim 64: the upper half of each 128-wide LDS row loads zeros
+    const uint32_t off = (wp ? io.wp_off : io.w_off) + (uint32_t)(row * io.hd + chunk * 8) * 2;
+    dma16(rs, region + rb * 1024, off, row < (wp ? io.rv : io.r) && chunk * 8 < io.hd);
   }
 }
 
@@ -295,9 +298,11 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
   auto load_q = [&]() {
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
                            (((int64_t)i * qlen + (row_ok ? j_l : 0)) * p.n_q_heads + g * G +
-                            (row_ok ? hl : 0)) * kD + 8 * q4;
+                            (row_ok ? hl : 0)) * p.head_dim + 8 * q4;
+    // dims past head_dim (64) are zero in every operand
 #pragma unroll
-    for (int kk = 0; kk < kD / 32; ++kk) qv[kk] = ld16(qrow + 32 * kk);
+    for (int kk = 0; kk < kD / 32; ++kk)
+      qv[kk] = 32 * kk + 8 * q4 < p.head_dim ? ld16(qrow + 32 * kk) : u32x4_t{0u, 0u, 0u, 0u};
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   };
 
@@ -574,10 +579,11 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
     // loads are pending, n = tiles issued after it.
     const int cap = p.tail_cap;
     const int L = cap > 0 ? min(max(p.tail_len[i], 0), cap) : 0;   // tail_len may be NULL if cap is 0
-    const uint16_t* kt = reinterpret_cast<const uint16_t*>(p.k_tail) + ((size_t)i * p.n_kv_heads + g) * cap * kD;
-    const uint16_t* vtp = reinterpret_cast<const uint16_t*>(p.v_tail) + ((size_t)i * p.n_kv_heads + g) * cap * kD;
-    const u32x4_t rk = rsrc_words(kt, (uint32_t)(cap * kD) * 2);
-    const u32x4_t rvv = rsrc_words(vtp, (uint32_t)(cap * kD) * 2);
+    const int hd = p.head_dim;
+    const uint16_t* kt = reinterpret_cast<const uint16_t*>(p.k_tail) + ((size_t)i * p.n_kv_heads + g) * cap * hd;
+    const uint16_t* vtp = reinterpret_cast<const uint16_t*>(p.v_tail) + ((size_t)i * p.n_kv_heads + g) * cap * hd;
+    const u32x4_t rk = rsrc_words(kt, (uint32_t)(cap * hd) * 2);
+    const u32x4_t rvv = rsrc_words(vtp, (uint32_t)(cap * hd) * 2);
     const int vis = L - qlen + j_l;   // last visible tail token of this row
     // this unit's piece of the tail: tiles toff .. toff + nt - 1
     const int tpp = ((cap + kTT - 1) / kTT + p.tail_pieces - 1) / p.tail_pieces;
@@ -592,9 +598,9 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
         const int rb = 8 * k + wave;
         const int row = rb * 4 + (ln >> 4);
         const int tok = (toff + t) * kTT + row;
-        const bool ok = tok < L;
-        dma16(rk, sk + rb * 1024, (uint32_t)(tok * kD + ((ln & 15) ^ swz_w(row)) * 8) * 2, ok);
-        dma16(rvv, sk + kTailHalf + rb * 1024, (uint32_t)(tok * kD + ((ln & 15) ^ swz_wp(row)) * 8) * 2, ok);
+        const int ck = (ln & 15) ^ swz_w(row), cv = (ln & 15) ^ swz_wp(row);
+        dma16(rk, sk + rb * 1024, (uint32_t)(tok * hd + ck * 8) * 2, tok < L && ck * 8 < hd);
+        dma16(rvv, sk + kTailHalf + rb * 1024, (uint32_t)(tok * hd + cv * 8) * 2, tok < L && cv * 8 < hd);
       }
     };
     for (int t = 0; t < min(nt, kTailStages - 1); ++t) issue_tail(t);
@@ -648,10 +654,10 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
   if (row_ok) {
     const int si = i + m_l / p.part_rows, ml = m_l % p.part_rows;
     const size_t rec = ((size_t)((si * p.n_kv_heads + g) * S + slot)) * p.part_rows + ml;
-    float* po = p.part.o + rec * kD;
+    float* po = p.part.o + rec * p.head_dim;
 #pragma unroll
     for (int dt = 0; dt < kD / 16; ++dt)
-      *reinterpret_cast<f32x4_t*>(po + 16 * dt + 4 * q4) = O[dt];
+      if (16 * dt < p.head_dim) *reinterpret_cast<f32x4_t*>(po + 16 * dt + 4 * q4) = O[dt];
     if (q4 == 0) {
       p.part.ml[rec * 2 + 0] = m_run;
       p.part.ml[rec * 2 + 1] = l_run;

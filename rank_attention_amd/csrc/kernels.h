@@ -67,6 +67,9 @@ struct ChunkParams {
   // ceil(ceil(tail_cap / 64) / tail_pieces).  1 unless a shared context
   // spreads each tail over several trailing workgroups.
   int32_t tail_pieces;
+  // 64 or 128.  The kernel's tiles are 128 wide; with 64, W, W', q and the
+  // tail rows are zero-padded to 128 in LDS and registers (exact).
+  int32_t head_dim;
   float scale_log2;
 };
 

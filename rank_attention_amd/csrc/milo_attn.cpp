@@ -51,14 +51,14 @@ milo_status check_shape(const milo_attn_args* a, int32_t path) {
   if (path == MILO_PATH_CHUNK && a->tail_cap < a->q_len) return MILO_ERR_INVALID;
   if (a->head_dim != 64 && a->head_dim != 128) return MILO_ERR_UNSUPPORTED;
   const int group = a->n_q_heads / a->n_kv_heads;
-  // group sizes above 8 run on the MFMA kernel (bf16 storage, head_dim 128)
+  // group sizes above 8 run on the MFMA kernel (bf16 storage)
   if (group > 16) return MILO_ERR_UNSUPPORTED;
-  if (group > 8 && (a->dtype != MILO_BF16 || a->head_dim != 128)) return MILO_ERR_UNSUPPORTED;
+  if (group > 8 && a->dtype != MILO_BF16) return MILO_ERR_UNSUPPORTED;
   // partial records (query rows x unit slots, up to 8 tail slots) are indexed in 32 bits on the device
   if ((int64_t)a->batch * a->q_len * a->n_q_heads * ((int64_t)a->max_blocks_per_seq + 8) > INT32_MAX)
     return MILO_ERR_UNSUPPORTED;
-  // the MFMA chunk kernel (chunk and shared paths) is built for bf16 storage and head_dim 128
-  if (path != MILO_PATH_DECODE && (a->dtype != MILO_BF16 || a->head_dim != 128)) return MILO_ERR_UNSUPPORTED;
+  // the MFMA chunk kernel (chunk and shared paths) reads bf16 storage
+  if (path != MILO_PATH_DECODE && a->dtype != MILO_BF16) return MILO_ERR_UNSUPPORTED;
   return MILO_OK;
 }
 
@@ -166,6 +166,7 @@ milo_status chunk_launch(const milo_attn_args* a, char* ws, hipStream_t stream) 
   p.part_rows = a->q_len * group;
   p.no_tail = 0;
   p.tail_pieces = 1;
+  p.head_dim = a->head_dim;
   p.scale_log2 = a->scale * milo::kLog2eHost;
 
   milo::clear_stale_error();
@@ -326,6 +327,7 @@ milo_status milo_attn_decode_shared(const milo_attn_args* a, void* hip_stream) {
   p.part_rows = group;
   p.no_tail = 1;
   p.tail_pieces = shared_tail_pieces(a);
+  p.head_dim = a->head_dim;
   p.tail_units = a->batch * a->n_kv_heads * p.tail_pieces;
   p.scale_log2 = a->scale * milo::kLog2eHost;
 

@@ -31,9 +31,10 @@ extern "C" hipError_t hipGetLastError(void) { return hipSuccess; }
 extern "C" hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return hipSuccess; }
 
 namespace milo {
-hipError_t launch_chunk(const ChunkParams& p, int group, hipStream_t) {
+hipError_t launch_chunk(const ChunkParams& p, int group, hipStream_t, LaunchEvents) {
   ++g_launches;
   EXPECT(group >= 1 && p.n_ranges >= 1 && p.blocks_per_range >= 1 && p.n_qtiles >= 1);
+  EXPECT(p.head_dim == 64 || p.head_dim == 128);
   EXPECT((int64_t)p.n_ranges * p.blocks_per_range >= p.max_blocks);
   return hipSuccess;
 }
@@ -53,7 +54,7 @@ hipError_t launch_read_probe(const void*, size_t, uint32_t*, int, hipStream_t) {
   return hipSuccess;
 }
 #define MILO_STUB_DECODE(name)                                        \
-  hipError_t name(const DecodeParams& p, int group, hipStream_t) {    \
+  hipError_t name(const DecodeParams& p, int group, hipStream_t, LaunchEvents) { \
     ++g_launches;                                                     \
     EXPECT(group >= 1 && group <= 8 && p.batch >= 1);                 \
     return hipSuccess;                                                \

@@ -91,7 +91,8 @@ def test_workspace_query():
     ({"dtype": 7}, _lib.MILO_ERR_UNSUPPORTED),
     ({"n_q_heads": 15}, _lib.MILO_ERR_INVALID),
     ({"head_dim": 96}, _lib.MILO_ERR_UNSUPPORTED),
-    ({"n_q_heads": 32, "n_kv_heads": 2}, _lib.MILO_ERR_UNSUPPORTED),
+    ({"n_q_heads": 34, "n_kv_heads": 2}, _lib.MILO_ERR_UNSUPPORTED),   # group size 17
+    ({"n_q_heads": 32, "n_kv_heads": 2, "dtype": _lib.MILO_F32}, _lib.MILO_ERR_UNSUPPORTED),  # G 16, fp32
     ({"scale": math.nan}, _lib.MILO_ERR_INVALID),
     ({"scale": math.inf}, _lib.MILO_ERR_INVALID),
     ({"q_len": 2}, _lib.MILO_ERR_INVALID),
@@ -121,7 +122,7 @@ def test_decode_rejects_before_any_hip_call(over, code):
 
 @pytest.mark.parametrize("over,code", [
     ({"dtype": _lib.MILO_F32}, _lib.MILO_ERR_UNSUPPORTED),   # the MFMA path is bf16 only
-    ({"head_dim": 64}, _lib.MILO_ERR_UNSUPPORTED),           # and head_dim 128 only
+    ({"head_dim": 96}, _lib.MILO_ERR_UNSUPPORTED),           # head_dim 64 or 128
     ({"q_len": 2}, _lib.MILO_ERR_INVALID),                  # one query token per sequence
     ({"n_q_heads": 34, "n_kv_heads": 2}, _lib.MILO_ERR_UNSUPPORTED),   # group size 17
     ({"workspace": None}, _lib.MILO_ERR_WORKSPACE),
@@ -149,20 +150,26 @@ def test_shared_workspace_query():
         exp_o = -(-units * rows * 128 * 4 // 256) * 256
         exp_ml = -(-units * rows * 2 * 4 // 256) * 256
         assert need == exp_o + exp_ml, (cap, need, exp_o + exp_ml)
-    assert lib.milo_attn_workspace_bytes(ctypes.byref(good_args(head_dim=64)), _lib.MILO_PATH_SHARED) == 0
+    # head_dim 64 (the kernel pads its tiles to 128): the same slots, 64 floats per row
+    a = good_args(head_dim=64, batch=16, n_q_heads=28, n_kv_heads=4, max_blocks_per_seq=64, tail_cap=256)
+    units, rows = 16 * 4 * (64 + 4), 7
+    exp = -(-units * rows * 64 * 4 // 256) * 256 + -(-units * rows * 2 * 4 // 256) * 256
+    assert lib.milo_attn_workspace_bytes(ctypes.byref(a), _lib.MILO_PATH_SHARED) == exp
+    assert lib.milo_attn_workspace_bytes(ctypes.byref(good_args(head_dim=96)), _lib.MILO_PATH_SHARED) == 0
 
 
 def test_group_sizes_above_eight():
     """Group sizes 9-16 are served by the MFMA kernel (bf16 storage, head_dim
-    128); decode then takes the chunked path's workspace layout (block ranges
-    + a tail slot per (sequence, KV head), G rows each).  Other storage,
-    head_dim 64 and groups above 16 are unsupported."""
+    64 or 128); decode then takes the chunked path's workspace layout (block
+    ranges + a tail slot per (sequence, KV head), G rows each).  Other
+    storage and groups above 16 are unsupported."""
     lib = _lib.load()
     for path in (_lib.MILO_PATH_DECODE, _lib.MILO_PATH_CHUNK, _lib.MILO_PATH_SHARED):
         q_len = 5 if path == _lib.MILO_PATH_CHUNK else 1
-        a = good_args(head_dim=128, n_q_heads=32, n_kv_heads=2, q_len=q_len)
-        assert lib.milo_attn_workspace_bytes(ctypes.byref(a), path) > 0
-        for over in ({"dtype": _lib.MILO_F32}, {"head_dim": 64}, {"n_q_heads": 34}):
+        for hd in (64, 128):
+            a = good_args(head_dim=hd, n_q_heads=32, n_kv_heads=2, q_len=q_len)
+            assert lib.milo_attn_workspace_bytes(ctypes.byref(a), path) > 0
+        for over in ({"dtype": _lib.MILO_F32}, {"n_q_heads": 34}):
             b = good_args(**{"head_dim": 128, "n_q_heads": 32, "n_kv_heads": 2, "q_len": q_len, **over})
             assert lib.milo_attn_workspace_bytes(ctypes.byref(b), path) == 0
             assert call(b, path) if path != _lib.MILO_PATH_SHARED else True
