@@ -155,7 +155,7 @@ __device__ __forceinline__ void wait_barrier() {
 struct BlockInfo {
   const uint16_t* head;   // this KV head's factors
   uint32_t bytes;         // their size
-  int T, ld, r, rv, nk, nv, ntiles, hd;
+  int T, ld, r, rv, nk, nv, ntiles;
   uint32_t w_off, v_off, wp_off;
 };
 
@@ -167,14 +167,14 @@ __device__ __forceinline__ u32x4_t rsrc_of(const BlockInfo& io) { return rsrc_wo
 // even though the DMA asm counts as a memory clobber.
 typedef __attribute__((address_space(4))) const milo_block const_milo_block;
 
+template <int HD>
 __device__ __forceinline__ void block_info(BlockInfo& io, const ChunkParams& p, int gblk, int g) {
   const_milo_block* blk = (const_milo_block*)p.blocks + gblk;
-  const int hd = p.head_dim;
+  constexpr int hd = HD;
   io.T = max(blk->n_tok, 0);
   io.ld = blk->ld_tok;
   io.r = min(max(blk->rank_k, 0), hd);
   io.rv = min(max(blk->rank_v, 0), hd);
-  io.hd = hd;
   // 16-rank chunks: scores use at least one (a rank-0 block scores 0
   // against zero-padded factors); values use none for rank' 0
   io.nk = max(1, (io.r + 15) / 16);
@@ -211,6 +211,7 @@ __device__ __forceinline__ void issue_tile(const BlockInfo& io, char* buf, int t
 }
 // W (wp = false) or W' rows of a block into their LDS region (4 loads per
 // wave: row block 8k + w of 32, 4 rows x 16 chunks each).
+template <int HD>
 __device__ __forceinline__ void issue_w(const BlockInfo& io, char* region, bool wp, int lane, int wave) {
   const u32x4_t rs = rsrc_of(io);
 #pragma unroll
@@ -219,8 +220,8 @@ __device__ __forceinline__ void issue_w(const BlockInfo& io, char* region, bool 
     const int row = rb * 4 + (lane >> 4);
     const int chunk = (lane & 15) ^ (wp ? swz_wp(row) : swz_w(row));
     // head_dim 64: the upper half of each 128-wide LDS row loads zeros
-    const uint32_t off = (wp ? io.wp_off : io.w_off) + (uint32_t)(row * io.hd + chunk * 8) * 2;
-    dma16(rs, region + rb * 1024, off, row < (wp ? io.rv : io.r) && chunk * 8 < io.hd);
+    const uint32_t off = (wp ? io.wp_off : io.w_off) + (uint32_t)(row * HD + chunk * 8) * 2;
+    dma16(rs, region + rb * 1024, off, row < (wp ? io.rv : io.r) && chunk * 8 < HD);
   }
 }
 
@@ -229,6 +230,7 @@ struct IntC {
   static constexpr int value = N;
 };
 
+template <int HD>
 __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const int tid = threadIdx.x, lane = tid & 63, q4 = lane >> 4;
@@ -298,11 +300,11 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
   auto load_q = [&]() {
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
                            (((int64_t)i * qlen + (row_ok ? j_l : 0)) * p.n_q_heads + g * G +
-                            (row_ok ? hl : 0)) * p.head_dim + 8 * q4;
+                            (row_ok ? hl : 0)) * HD + 8 * q4;
     // dims past head_dim (64) are zero in every operand
 #pragma unroll
     for (int kk = 0; kk < kD / 32; ++kk)
-      qv[kk] = 32 * kk + 8 * q4 < p.head_dim ? ld16(qrow + 32 * kk) : u32x4_t{0u, 0u, 0u, 0u};
+      qv[kk] = 32 * kk + 8 * q4 < HD ? ld16(qrow + 32 * kk) : u32x4_t{0u, 0u, 0u, 0u};
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   };
 
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
     // k - 1).  Every step waits with vmcnt(4): all loads but the newest tile
     // (issued at step k - 1, after any W / W' loads of that step) are done.
     BlockInfo cb, pb;                     // compute block, prefetch block
-    block_info(cb, p, b0 + blk_lo, g);
+    block_info<HD>(cb, p, b0 + blk_lo, g);
     pb = cb;
     int pblk = blk_lo, pt = 0;            // next tile to issue: block pblk, tile pt
     int kpre = 0;                         // global index of that tile
@@ -377,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
       if (++pt >= pb.ntiles) {
         pt = 0;
         if (++pblk < blk_hi) {
-          block_info(pb, p, b0 + pblk, g);
+          block_info<HD>(pb, p, b0 + pblk, g);
               }
       }
     };
@@ -393,11 +395,11 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
     int cur_b = blk_lo;
     auto issue_next_w = [&](int ln) {
       BlockInfo nb;
-      block_info(nb, p, b0 + cur_b + 1, g);
-      issue_w(nb, ldsW, false, ln, wave);
+      block_info<HD>(nb, p, b0 + cur_b + 1, g);
+      issue_w<HD>(nb, ldsW, false, ln, wave);
     };
-    issue_w(cb, ldsW, false, lane, wave);
-    issue_w(cb, ldsWp, true, lane, wave);
+    issue_w<HD>(cb, ldsW, false, lane, wave);
+    issue_w<HD>(cb, ldsWp, true, lane, wave);
     issue_next(lane);
     bool newest = issue_next(lane);           // was a tile issued at the previous step?
     load_q();
@@ -405,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
 
     for (int b = blk_lo; b < blk_hi; ++b) {
       cur_b = b;
-      if (b > blk_lo) block_info(cb, p, b0 + b, g);
+      if (b > blk_lo) block_info<HD>(cb, p, b0 + b, g);
       const int T = cb.T, r = cb.r, nv = cb.nv, ntiles = cb.ntiles;
       const bool has_next = b + 1 < blk_hi;
 #pragma unroll
@@ -426,7 +428,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
           const char* V = U + kHalfTile;
           const int t0 = t * kTT;
           if (t == 0) {
-            if (b > blk_lo) issue_w(cb, ldsWp, true, ln, wave);   // W' of this block
+            if (b > blk_lo) issue_w<HD>(cb, ldsWp, true, ln, wave);   // W' of this block
             // ---- P^T = W Q^T per 16-rank tile, scaled, split into hi/lo operands
             f32x4_t pt[NK];
             if (wave_live) {
@@ -579,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
     // loads are pending, n = tiles issued after it.
     const int cap = p.tail_cap;
     const int L = cap > 0 ? min(max(p.tail_len[i], 0), cap) : 0;   // tail_len may be NULL if cap is 0
-    const int hd = p.head_dim;
+    constexpr int hd = HD;
     const uint16_t* kt = reinterpret_cast<const uint16_t*>(p.k_tail) + ((size_t)i * p.n_kv_heads + g) * cap * hd;
     const uint16_t* vtp = reinterpret_cast<const uint16_t*>(p.v_tail) + ((size_t)i * p.n_kv_heads + g) * cap * hd;
     const u32x4_t rk = rsrc_words(kt, (uint32_t)(cap * hd) * 2);
@@ -654,10 +656,10 @@ __global__ __launch_bounds__(kThreads) void milo_chunk_kernel(ChunkParams p) {
   if (row_ok) {
     const int si = i + m_l / p.part_rows, ml = m_l % p.part_rows;
     const size_t rec = ((size_t)((si * p.n_kv_heads + g) * S + slot)) * p.part_rows + ml;
-    float* po = p.part.o + rec * p.head_dim;
+    float* po = p.part.o + rec * HD;
 #pragma unroll
     for (int dt = 0; dt < kD / 16; ++dt)
-      if (16 * dt < p.head_dim) *reinterpret_cast<f32x4_t*>(po + 16 * dt + 4 * q4) = O[dt];
+      if (16 * dt < HD) *reinterpret_cast<f32x4_t*>(po + 16 * dt + 4 * q4) = O[dt];
     if (q4 == 0) {
       p.part.ml[rec * 2 + 0] = m_run;
       p.part.ml[rec * 2 + 1] = l_run;
@@ -674,10 +676,11 @@ hipError_t launch_chunk(const ChunkParams& p, int group, hipStream_t s, LaunchEv
   const int64_t wgs = (p.tail_units + 7) / 8 * 8 + (groups + 7) / 8 * 8 * p.n_qtiles;
   ChunkParams q = p;
   q.group = group;
+  auto kernel = p.head_dim == 64 ? milo_chunk_kernel<64> : milo_chunk_kernel<128>;
   if (ev.start && ev.stop)   // timing events stamped by the dispatch itself
-    hipExtLaunchKernelGGL(milo_chunk_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, s, ev.start, ev.stop, 0, q);
+    hipExtLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(kThreads), 0, s, ev.start, ev.stop, 0, q);
   else
-    hipLaunchKernelGGL(milo_chunk_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, s, q);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(kThreads), 0, s, q);
   return hipGetLastError();
 }
 

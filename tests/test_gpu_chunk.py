@@ -176,12 +176,12 @@ def test_chunk_three_blocks_per_range_sharp():
     compare(out, lse, ref_o, ref_l, rows=sel, sharp_gates=True, name=cfg.name)
 
 
-def one_hot_ranges_workload():
+def one_hot_ranges_workload(d=128):
     """The workload of the one-hot probe below and its exact expected output
     [B][Q][Hq][d] (float32)."""
     from synth.gen import LogicalBlock, bf16_bits_to_f32
     from tests.gpu_util import bf16_bits, custom_workload
-    cfg = _range_cfg("chunk_onehot_ranges")
+    cfg = _range_cfg(f"chunk_onehot_ranges_d{d}").with_(head_dim=d)
     B, Q, Hq, Hkv, d = 2, cfg.q_len, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     G = Hq // Hkv
     n_dirs = 16
@@ -241,15 +241,17 @@ def one_hot_ranges_workload():
     return wl, bf16_bits_to_f32(bf16_bits(exp))
 
 
-def test_chunk_one_hot_ranges_of_three():
+@pytest.mark.parametrize("d", [128, 64])
+def test_chunk_one_hot_ranges_of_three(d):
     """Bit-exact indexing on the chunk path with three blocks per range.
     Query row (j, h) looks along one of 16 directions c; every block's W rows
     are distinct unit vectors (a per-block permutation), so a block scores
     through its own W only.  For each (sequence, KV head, c) one token of one
     block carries the key e_k with W_b[k] = e_c (score gap 200 nats) and the
     value one-hot on a rank row of W' whose integers encode (sequence, KV
-    head, block, rank); the row's output must equal that W' row exactly."""
-    wl, exp = one_hot_ranges_workload()
+    head, block, rank); the row's output must equal that W' row exactly.
+    At head_dim 64 the kernel's 128-wide tiles carry zero padding."""
+    wl, exp = one_hot_ranges_workload(d)
     import rank_attention_amd as ra
     dc = ra.DeviceCache(ra.pack(wl, ld_extra=8, shuffle_pool=9), scale=wl.scale)
     assert chunk_ranges(dc) == 8
