@@ -16,12 +16,17 @@
 //   - scores: lane owns 16 tokens of a 1024-token tile (two 1 KB wave-wide
 //     row segments); each row of U^T is unpacked to fp32 and met with fp32
 //     p held in LDS (broadcast reads), G FMAs per element;
+//     (a block of at most 512 tokens: 8 tokens per lane of a 512-token
+//     tile, and 16 rows per load stage instead of 4);
 //   - values: the same lane/token ownership; e is packed to bf16 token pairs
 //     against rows of U'^T; per-lane partial z of up to 64 (row, head) slots
-//     are summed across the wave by one transposing butterfly.
+//     are summed across the wave by one transposing butterfly; the next row
+//     group's first rows load during that reduction;
 //   - o~ += z W' is applied per row group as soon as the group's z is
 //     reduced; the group's W' rows load with its U'^T rows, so no memory
 //     round trip is left after the last group.
+// The softmax max, sum and rescale factor are wave-uniform and kept in
+// scalar registers.
 // The U^T and U'^T streams are read once and wave-coalesced, so they are
 // loaded non-temporally.  The projection p = W q (bf16 storage) runs on the
 // matrix cores with all of the unit's W loads in flight at once (one memory
