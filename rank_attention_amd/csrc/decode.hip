@@ -14,10 +14,12 @@
 // group share every factor load.  The block's token factors are streamed
 // once, rank-major, 16 bytes per lane:
 //   - scores: lane owns 16 tokens of a 1024-token tile (two 1 KB wave-wide
-//     row segments); each row of U^T is unpacked to fp32 and met with fp32
-//     p held in LDS (broadcast reads), G FMAs per element;
-//     (a block of at most 512 tokens: 8 tokens per lane of a 512-token
-//     tile, and 16 rows per load stage instead of 4);
+//     row segments; a block of at most 512 tokens: 8 tokens per lane of a
+//     512-token tile, and 16 rows per load stage instead of 4).  Every four
+//     rows of U^T are one K = 4 step of v_mfma_f32_4x4x4bf16_1k: the lane's
+//     token is a column of B (two byte permutes of its row loads), p of four
+//     heads the rows of A, split into bf16 hi + lo; the lane keeps the
+//     scores of its own tokens;
 //   - values: the same lane/token ownership; e is packed to bf16 token pairs
 //     against rows of U'^T; per-lane partial z of up to 64 (row, head) slots
 //     are summed across the wave by one transposing butterfly; the next row
@@ -53,7 +55,9 @@ constexpr float kNegInf = -__builtin_huge_valf();
 
 template <int D, int G>
 struct Shape {
-  static constexpr int R = (64 / G < 12) ? 64 / G : 12;  // value rows per butterfly group
+  // value rows per butterfly group (R * G <= 64 slots); G = 5 takes 11 so
+  // that the bf16 unit's value phase fits two waves per SIMD
+  static constexpr int R = G == 5 ? 11 : (64 / G < 12) ? 64 / G : 12;
   static constexpr int NG = (D + R - 1) / R;    // butterfly groups for rank <= D
   static constexpr int JPL = D / 64;            // output columns per lane
   static_assert(G >= 1 && G <= 8, "group size");
@@ -125,7 +129,7 @@ constexpr int rows_per_step() { return CH == 1 ? 16 : 4; }
 // group's reduction: the whole group with one chunk per lane, else as many
 // as the two-waves-per-SIMD register budget leaves room for.
 template <int G, int CH, int R>
-constexpr int value_ring_rows() { return CH == 1 ? R : G >= 8 ? 0 : 4; }
+constexpr int value_ring_rows() { return CH == 1 ? R : 0; }
 
 // Loads rows k0 .. k0 + rows_per_step - 1 of U^T (clamped to r-1) at the
 // lane's CH chunks.
@@ -140,30 +144,63 @@ __device__ __forceinline__ void load_rows(const uint16_t* Ut, int ld, int k0, in
   }
 }
 
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
+
+// v_mfma_f32_4x4x4bf16_1k: 16 independent 4x4x4 products, one per group of
+// four lanes 4b .. 4b+3.  Lane 4b + j supplies column j of B (K = 4 values)
+// and receives column j of D (rows 0..3); lane 4b + v supplies row v of A.
+__device__ __forceinline__ f32x4_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, const f32x4_t& c) {
+  const u32x2v_t a = {a0, a1}, b = {b0, b1};
+  return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b),
+                                                 c, 0, 0, 0);
+}
+
+// Scores of rows k0 .. k0 + rows_per_step - 1 of U^T on the matrix cores, in
+// groups of four rows (K = 4): the lane's token j is column j of B, built
+// from its four row loads by two byte permutes, and A holds p of heads
+// 4 hg .. 4 hg + 3 (lane 4b + v: head 4 hg + v) at those ranks, split into
+// bf16 hi + lo (two products; bf16 U times bf16 p is exact, sums in fp32).
+// acc[token][hg] row v = score of head 4 hg + v.  Ranks past r and heads
+// past G take p = 0, so the clamped row loads add nothing.
 template <int G, int CH>
-__device__ __forceinline__ void score_rows(const u32x4_t (&A)[CH][rows_per_step<CH>()], int k0, int r,
-                                            const float* pf, float (&s)[8 * CH][G]) {
+__device__ __forceinline__ void score_rows_mfma(const u32x4_t (&A)[CH][rows_per_step<CH>()], int k0, int r,
+                                                const float* pf, f32x4_t (&acc)[8 * CH][(G + 3) / 4], int lane) {
+  constexpr int RPS = rows_per_step<CH>(), HG = (G + 3) / 4;
+  const int hv = lane & 3;
 #pragma unroll
-  for (int j = 0; j < rows_per_step<CH>(); ++j) {
-    if (k0 + j < r) {
-      const f32x4_t pq0 = *reinterpret_cast<const f32x4_t*>(pf + (k0 + j) * 8);
-      const f32x4_t pq1 = *reinterpret_cast<const f32x4_t*>(pf + (k0 + j) * 8 + 4);
-      const float pp[8] = {pq0[0], pq0[1], pq0[2], pq0[3], pq1[0], pq1[1], pq1[2], pq1[3]};
+  for (int kq = 0; kq < RPS / 4; ++kq) {
+    const int kb = k0 + 4 * kq;
+    if (kb < r) {
+      uint32_t ahi[HG][2], alo[HG][2];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int hg = 0; hg < HG; ++hg) {
+        const int h = 4 * hg + hv;
+        float x[4];
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-          const float a0 = bf_lo(A[c][j][w]), a1 = bf_hi(A[c][j][w]);
+        for (int kk = 0; kk < 4; ++kk) x[kk] = (kb + kk < r && h < G) ? pf[(kb + kk) * 8 + h] : 0.f;
+        ahi[hg][0] = pack_bf16(x[0], x[1]);
+        ahi[hg][1] = pack_bf16(x[2], x[3]);
+        alo[hg][0] = pack_bf16(x[0] - bf_lo(ahi[hg][0]), x[1] - bf_hi(ahi[hg][0]));
+        alo[hg][1] = pack_bf16(x[2] - bf_lo(ahi[hg][1]), x[3] - bf_hi(ahi[hg][1]));
+      }
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            s[8 * c + 2 * w][h] = fmaf(a0, pp[h], s[8 * c + 2 * w][h]);
-            s[8 * c + 2 * w + 1][h] = fmaf(a1, pp[h], s[8 * c + 2 * w + 1][h]);
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+          const uint32_t b0 = __builtin_amdgcn_perm(A[c][4 * kq + 1][j >> 1], A[c][4 * kq][j >> 1], sel);
+          const uint32_t b1 = __builtin_amdgcn_perm(A[c][4 * kq + 3][j >> 1], A[c][4 * kq + 2][j >> 1], sel);
+#pragma unroll
+          for (int hg = 0; hg < HG; ++hg) {
+            acc[8 * c + j][hg] = mfma4(ahi[hg][0], ahi[hg][1], b0, b1, acc[8 * c + j][hg]);
+            acc[8 * c + j][hg] = mfma4(alo[hg][0], alo[hg][1], b0, b1, acc[8 * c + j][hg]);
           }
         }
-      }
     }
   }
 }
+
 
 // One tile of 512 CH tokens at a time (lane l holds tokens t0 + 512 c + 8 l
 // .. +7 of chunk c): scores, online softmax, then per group of R rows of
@@ -190,24 +227,31 @@ __device__ __forceinline__ void bf16_tiles(const uint16_t* Ut, const uint16_t* U
       tq[c] = ok[c] ? tc[c] : t0;
     }
 
-    // ---- scores s[c*8+e][h] for token tc_c + e: U rows unpacked to fp32
-    // and met with fp32 p (bf16 rounding of p would cost ~1% on sharp softmax)
-    float s[NE][G];
+    // ---- scores s[c*8+e][h] for token tc_c + e: bf16 U against p split
+    // into bf16 hi + lo on the matrix cores (bf16 rounding of p alone would
+    // cost ~1% on sharp softmax)
+    constexpr int HG = (G + 3) / 4;
+    f32x4_t acc[NE][HG];
 #pragma unroll
     for (int e = 0; e < NE; ++e)
 #pragma unroll
-      for (int h = 0; h < G; ++h) s[e][h] = 0.f;
+      for (int hg = 0; hg < HG; ++hg) acc[e][hg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (r > 0) {
       constexpr int kRowsPerStep = rows_per_step<CH>();
       u32x4_t A0[CH][kRowsPerStep], A1[CH][kRowsPerStep];
       load_rows<CH>(Ut, ld, 0, r, tq, A0);
       for (int k0 = 0; k0 < r; k0 += 2 * kRowsPerStep) {
         if (k0 + kRowsPerStep < r) load_rows<CH>(Ut, ld, k0 + kRowsPerStep, r, tq, A1);
-        score_rows<G, CH>(A0, k0, r, pf, s);
+        score_rows_mfma<G, CH>(A0, k0, r, pf, acc, lane);
         if (k0 + 2 * kRowsPerStep < r) load_rows<CH>(Ut, ld, k0 + 2 * kRowsPerStep, r, tq, A0);
-        if (k0 + kRowsPerStep < r) score_rows<G, CH>(A1, k0 + kRowsPerStep, r, pf, s);
+        if (k0 + kRowsPerStep < r) score_rows_mfma<G, CH>(A1, k0 + kRowsPerStep, r, pf, acc, lane);
       }
     }
+    float s[NE][G];
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[e][h] = acc[e][h >> 2][h & 3];
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
       const int tok = tc[e >> 3] + (e & 7);
