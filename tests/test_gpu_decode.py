@@ -80,6 +80,7 @@ RAGGED = [
     # (dtype, d, Hq, Hkv)
     ("bf16", 128, 7, 1), ("bf16", 128, 8, 1), ("bf16", 128, 10, 2), ("bf16", 64, 12, 4),
     ("bf16", 64, 3, 3), ("bf16", 128, 12, 2), ("bf16", 128, 6, 2), ("bf16", 64, 14, 2),
+    ("bf16", 128, 4, 2), ("bf16", 64, 8, 2), ("bf16", 128, 16, 4), ("bf16", 64, 4, 1),
     ("f32", 64, 4, 2), ("f32", 128, 7, 1), ("f32", 128, 5, 5),
 ]
 
