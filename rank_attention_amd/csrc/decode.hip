@@ -789,12 +789,18 @@ __device__ __forceinline__ void q8_body(const Q8Unit& u, const float* pf, const 
 template <int D, int G>
 __device__ __forceinline__ void store_zwp(const DecodeParams& p, int unit, const uint16_t* Wp, int rv,
                                           const float* zs, float m_run, float l_run, int lane) {
-  constexpr int JPL = D / 64;
-  float o[G][JPL];
+  // o~ = z W' on v_mfma_f32_4x4x4bf16_1k, four W' rows per K step: the
+  // lane's output column (dim lane * JPL + jj) is a column of B, packed from
+  // its row loads by two byte permutes; row v of A (lane 4b + v) holds z of
+  // head 4 hg + v at those rows, split into bf16 hi + lo.  Rows past rank'
+  // and heads past G take z = 0 (their W' loads are clamped copies).
+  constexpr int JPL = D / 64, HG = (G + 3) / 4;
+  const int hv = lane & 3;
+  f32x4_t oa[JPL][HG];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int jj = 0; jj < JPL; ++jj)
 #pragma unroll
-    for (int jj = 0; jj < JPL; ++jj) o[h][jj] = 0.f;
+    for (int hg = 0; hg < HG; ++hg) oa[jj][hg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   constexpr int kWRows = 32;
   auto load_w = [&](int k0, uint32_t (&wr)[kWRows]) {
 #pragma unroll
@@ -806,16 +812,33 @@ __device__ __forceinline__ void store_zwp(const DecodeParams& p, int unit, const
   uint32_t wa[kWRows], wb[kWRows];
   auto apply_w = [&](int k0, const uint32_t (&wr)[kWRows]) {
 #pragma unroll
-    for (int j = 0; j < kWRows; ++j) {
+    for (int j = 0; j < kWRows; j += 4) {
       if (k0 + j < rv) {
-        const f32x4_t z0 = *reinterpret_cast<const f32x4_t*>(zs + (k0 + j) * 8);
-        const f32x4_t z1 = *reinterpret_cast<const f32x4_t*>(zs + (k0 + j) * 8 + 4);
-        const float zz[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
-        const float wv[2] = {bf_lo(wr[j]), bf_hi(wr[j])};
+        uint32_t ahi[HG][2], alo[HG][2];
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+        for (int hg = 0; hg < HG; ++hg) {
+          const int h = 4 * hg + hv;
+          float x[4];
 #pragma unroll
-          for (int jj = 0; jj < JPL; ++jj) o[h][jj] = fmaf(zz[h], wv[JPL == 2 ? jj : 1], o[h][jj]);
+          for (int kk = 0; kk < 4; ++kk) x[kk] = (k0 + j + kk < rv && h < G) ? zs[(k0 + j + kk) * 8 + h] : 0.f;
+          ahi[hg][0] = pack_bf16(x[0], x[1]);
+          ahi[hg][1] = pack_bf16(x[2], x[3]);
+          alo[hg][0] = pack_bf16(x[0] - bf_lo(ahi[hg][0]), x[1] - bf_hi(ahi[hg][0]));
+          alo[hg][1] = pack_bf16(x[2] - bf_lo(ahi[hg][1]), x[3] - bf_hi(ahi[hg][1]));
+        }
+#pragma unroll
+        for (int jj = 0; jj < JPL; ++jj) {
+          // W'[row][dim] sits in the low half of wr for the first of two
+          // dims, in the high half for the second (and for JPL = 1)
+          const uint32_t sel = (JPL == 2 && jj == 0) ? 0x05040100u : 0x07060302u;
+          const uint32_t b0 = __builtin_amdgcn_perm(wr[j + 1], wr[j], sel);
+          const uint32_t b1 = __builtin_amdgcn_perm(wr[j + 3], wr[j + 2], sel);
+#pragma unroll
+          for (int hg = 0; hg < HG; ++hg) {
+            oa[jj][hg] = mfma4(ahi[hg][0], ahi[hg][1], b0, b1, oa[jj][hg]);
+            oa[jj][hg] = mfma4(alo[hg][0], alo[hg][1], b0, b1, oa[jj][hg]);
+          }
+        }
       }
     }
   };
@@ -831,7 +854,7 @@ __device__ __forceinline__ void store_zwp(const DecodeParams& p, int unit, const
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int jj = 0; jj < JPL; ++jj) po[h * D + lane * JPL + jj] = o[h][jj];
+    for (int jj = 0; jj < JPL; ++jj) po[h * D + lane * JPL + jj] = oa[jj][h >> 2][h & 3];
   if (lane < G) {
     p.part.ml[((size_t)unit * G + lane) * 2 + 0] = m_run;
     p.part.ml[((size_t)unit * G + lane) * 2 + 1] = l_run;
