@@ -131,6 +131,8 @@ typedef enum milo_path {
  * KV head g starts at byte off + g * H,
  *     H = 16 + nch * (32 ng8 + 64 BITS ng8 + 256 ngv + 128 BITS ntv)
  *         + 2 * head_dim * (rank_k + rank_v).
+ * H must stay below 2^32 bytes (the decode kernel addresses a head's tables
+ * with 32-bit offsets; at rank 128 that is about 28M tokens per block).
  * Per head, back to back:
  *     header  amax_k, amax_v (fp32: the largest key and value scale of the
  *             head), 8 zero bytes
@@ -297,8 +299,8 @@ milo_status milo_attn_plan_decode(const milo_block* blocks, int32_t n_descriptor
  * lists are not read by that path).  pool_elems is the pool size in
  * elements.  Host-checkable faults return a status as for the other entry
  * points (status must be 8-byte aligned).  With MILO_BF16_Q8, MILO_BF16_KV4
- * and MILO_BF16_KV2, pool_elems counts bytes, rule 4 asks for ld_tok a multiple of 64 and rule 5 for off a
- * multiple of 16.  When args->unit_order is set, rule 8 checks that it is a
+ * and MILO_BF16_KV2, pool_elems counts bytes, rule 4 asks for ld_tok a multiple of 64 (and, for the
+ * KIVI-style layouts, a KV head under 2^32 bytes) and rule 5 for off a multiple of 16.  When args->unit_order is set, rule 8 checks that it is a
  * permutation of the decode units; the check counts units in args->workspace
  * (256-B aligned, at least 4 bytes per unit, which a decode workspace always
  * has; its contents are overwritten) and returns MILO_ERR_WORKSPACE without it.
@@ -307,7 +309,7 @@ typedef enum milo_table_rule {
   MILO_TABLE_SEQ_RANGE = 1,        /* seq_blocks[i] < 0, decreasing, or past n_descriptors        */
   MILO_TABLE_TOO_MANY_BLOCKS = 2,  /* seq_blocks[i+1] - seq_blocks[i] > max_blocks_per_seq        */
   MILO_TABLE_RANK = 3,             /* rank_k or rank_v outside [0, head_dim]                      */
-  MILO_TABLE_TOKENS = 4,           /* n_tok < 0, ld_tok < n_tok, or ld_tok not a multiple of 8    */
+  MILO_TABLE_TOKENS = 4,           /* n_tok < 0, ld_tok < n_tok, ld_tok not a multiple of 8 (64), or a KIVI-style head of 2^32 bytes or more */
   MILO_TABLE_OFFSET = 5,           /* off < 0 or not a multiple of 8                              */
   MILO_TABLE_POOL_BOUNDS = 6,      /* the block's factors end past pool_elems                     */
   MILO_TABLE_TAIL_LEN = 7,         /* tail_len[i] outside [0, tail_cap] (decode, shared) or

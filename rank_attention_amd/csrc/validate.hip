@@ -39,8 +39,11 @@ __global__ __launch_bounds__(kValThreads) void milo_validate_kernel(ValidatePara
     int64_t size = (int64_t)p.n_kv_heads * (rk + rv) * (ld + d);
     if (p.dtype == MILO_BF16_Q8)
       size = (int64_t)p.n_kv_heads * (nt * rk16 + rv * ld + (rk + rv) * 2 * d + ((8 * (rk + rv) + 15) & ~15ll));
-    else if (p.dtype == MILO_BF16_KV4 || p.dtype == MILO_BF16_KV2)
-      size = (int64_t)p.n_kv_heads * kivi_head_bytes(ld / 64, rk, rv, d, p.dtype == MILO_BF16_KV4 ? 4 : 2);
+    else if (p.dtype == MILO_BF16_KV4 || p.dtype == MILO_BF16_KV2) {
+      const int64_t h = kivi_head_bytes(ld / 64, rk, rv, d, p.dtype == MILO_BF16_KV4 ? 4 : 2);
+      if (h > (int64_t)0xFFFFFFFFll) report(p.status, 4, idx);   // the kernel's 32-bit table offsets
+      size = (int64_t)p.n_kv_heads * h;
+    }
     if (blk.off >= 0 && blk.off + size > p.pool_elems) report(p.status, 6, idx);
   }
   if (idx < p.n_seqs_checked) {

@@ -303,3 +303,10 @@ def test_validate_kivi_tables(bits):
     bad["off"][2] = qc.pool.numel() - 16        # factors run past the end of the pool
     qc.blocks = torch.from_numpy(bad.view(np.uint8).copy()).to(qc.pool.device)
     assert qc.validate() == ("pool_bounds", 2)
+    # a KV head of 2^32 bytes or more (the decode kernel's table offsets
+    # are 32-bit): rule 4, ahead of the pool bound it also breaks
+    bad = qc.blocks_host.copy()
+    bad["n_tok"][0] = bad["ld_tok"][0] = 2**31 - 64
+    bad["rank_k"][0] = bad["rank_v"][0] = 64
+    qc.blocks = torch.from_numpy(bad.view(np.uint8).copy()).to(qc.pool.device)
+    assert qc.validate() == ("tokens", 0)
